@@ -1,0 +1,392 @@
+"""CPU oracle for the SERQ quantized linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module. The HIP library never calls it and shares no code with
+it: this is a plain, slow, step-by-step restatement of what the pages define,
+used to check the GPU path element by element.
+
+Sources (each cited below by its tag and a section of that page):
+  [N]   "SERQ: Saliency-Aware Low-Rank Error Reconstruction for LLM
+        Quantization", papernotes.org notes for ICLR 2026
+        (sections 核心 idea, 方法详解 / 整体框架, 关键设计 1-3, 消融实验)
+  [GDE] gist.science/de/paper/2603.08185, "Technische Zusammenfassung"
+        (sections 2.A-2.C, 3, 4)
+  [GJA] gist.science/ja/paper/2603.08185, "技術概要"
+        (section 2 and its "計算フローの革新" paragraph)
+  [RAD] AI Radio episode "SERQ: Saliency-Aware Low-Rank Error
+        Reconstruction for LLM Quantization" (the paper-summary dialogue)
+
+Notation (as on the pages): X is M x K (tokens x input channels), W is K x N
+with Y = X W; s is the per-channel smoothing factor, P the saliency
+permutation, X~ = X diag(s^-1), W~ = diag(s) W, W^ = P W~ = [W~_s; W~_r],
+X^ = X~ P^-1 = [X~_s X~_r], r the rank (number of salient rows), R the r x N
+compensator.
+
+Arithmetic rules of this oracle (the pages fix none of them; these are the
+readings the library must reproduce bit for bit):
+  * every fp32 step below is one IEEE binary32 operation, round to nearest
+    even, no fused multiply-add;
+  * ``rne`` is round-half-to-even;
+  * bf16 inputs widen exactly to fp32;
+  * the final output y is evaluated in fp64 from exact integer accumulators
+    and rounded once to fp32 or bf16.
+
+Pinning status: every function here is pinned by tests/test_oracle_pins.py
+(closed forms, identities the pages state, brute force on tiny inputs and
+hand-derived fixtures under tests/golden/). Three conventions are fixed by
+this contract rather than by the pages -- the smoothing-factor formula and its
+floor, the tie order of the saliency sort, and the quantizer's reciprocal
+rounding -- and are "parity unpinned" as far as the pages go: only their
+internal consequences (balance, sortedness, error bounds) are pinned.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F32 = np.float32
+I4_MIN, I4_MAX = -8, 7
+I8_MIN, I8_MAX = -128, 127
+S_FLOOR = 1e-5          # floor on both channel maxima before forming s
+ALPHA_DEFAULT = 0.5
+
+
+def qrange(bits: int) -> tuple[int, int]:
+    if bits == 4:
+        return I4_MIN, I4_MAX
+    if bits == 8:
+        return I8_MIN, I8_MAX
+    raise ValueError("bits must be 4 or 8")
+
+
+# ---------------------------------------------------------------------------
+# Step A -- static activation flattening.
+# [N] 关键设计 1: per-channel static scaling in the SmoothQuant style,
+# Y = XW = (X diag(s^-1))(diag(s) W), computed once at calibration and merged
+# offline. [GDE] 2.A: the factors come from calibration and are folded into
+# the weights. The pages do not print a formula for s; SmoothQuant's own
+# per-channel rule s_j = max|X_j|^a / max|W_j|^(1-a) is taken, with a = 0.5 and
+# a floor of 1e-5 on both maxima so that a dead channel gives a finite s.
+# ---------------------------------------------------------------------------
+
+def smoothing_factors(act_absmax: np.ndarray, w_rowmax: np.ndarray,
+                      alpha: float = ALPHA_DEFAULT) -> tuple[np.ndarray, np.ndarray]:
+    """Return (s, s_inv), both float32 vectors of length K.
+
+    s_j is formed in fp64 and rounded once to fp32; for alpha = 0.5 this is
+    fl32(sqrt(a_j) / sqrt(w_j)). s_inv_j = fl32(1 / s_j) (one fp32 divide).
+    """
+    a = np.maximum(np.asarray(act_absmax, dtype=np.float32).astype(np.float64), S_FLOOR)
+    w = np.maximum(np.asarray(w_rowmax, dtype=np.float32).astype(np.float64), S_FLOOR)
+    if alpha == 0.5:
+        s64 = np.sqrt(a) / np.sqrt(w)
+    else:
+        # libm pow element by element (no vectorised approximation)
+        s64 = np.array([math.pow(ai, alpha) / math.pow(wi, 1.0 - alpha) for ai, wi in zip(a, w)],
+                       dtype=np.float64)
+    s = s64.astype(np.float32)
+    s_inv = (np.float32(1.0) / s).astype(np.float32)
+    return s, s_inv
+
+
+# ---------------------------------------------------------------------------
+# Step B -- saliency ranking and the permutation P.
+# [N] 关键设计 2: after flattening, activation outliers sit in the matching
+# weight rows; assuming roughly normal original weights, salient rows of the
+# folded weight are identified directly by their scale, and rows are
+# permuted in descending saliency, W^ = P diag(s) W = [W~_s; W~_r].
+# [GDE] 2.B: identification is based on the activations' scaling factors.
+# Reading: saliency of row j is s_j; descending order; equal s keep the lower
+# original index first (the pages leave ties open; several orders are equally
+# valid, this one is fixed so that results are reproducible).
+# ---------------------------------------------------------------------------
+
+def saliency_order(s: np.ndarray) -> np.ndarray:
+    """perm[i] = original channel placed at position i (int32)."""
+    s = np.asarray(s, dtype=np.float32)
+    return np.argsort(-s.astype(np.float64), kind="stable").astype(np.int32)
+
+
+def fold_and_permute(W: np.ndarray, s: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    """W^[i, n] = fl32(s[perm[i]] * W[perm[i], n])  (K x N float32)."""
+    W = np.asarray(W, dtype=np.float32)
+    return (s[perm][:, None].astype(np.float32) * W[perm, :]).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# The symmetric round-to-nearest quantizer used for weights, the compensator
+# and activations. [GDE] 3: the method works with RTN (and GPTQ) and with the
+# INT4 format; the integer range is [-8, 7] for 4-bit and [-128, 127] for
+# 8-bit. Reading: scale = fl32(m / qmax) with m the group's absolute maximum,
+# codes = clamp(rne(fl32(v * fl32(qmax / m)))). A group whose reciprocal
+# fl32(qmax / m) overflows (an all-zero group in particular) gets scale 0
+# and all-zero codes.
+# ---------------------------------------------------------------------------
+
+def quantize_group(v: np.ndarray, m, bits: int) -> tuple[np.ndarray, np.float32]:
+    """Quantize one group ``v`` (any shape) with absolute maximum ``m``."""
+    lo, hi = qrange(bits)
+    v = np.asarray(v, dtype=np.float32)
+    m = np.float32(m)
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = np.float32(np.float32(hi) / m)
+    if not np.isfinite(inv):
+        return np.zeros(v.shape, np.int8), np.float32(0.0)
+    scale = np.float32(m / np.float32(hi))
+    t = (v * inv).astype(np.float32)
+    q = np.clip(np.rint(t), lo, hi).astype(np.int8)
+    return q, scale
+
+
+def quantize_columns(A: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-column quantization of a (rows x N) float32 matrix: one scale per
+    column over all of its rows. Returns (codes int8 rows x N, scales N)."""
+    A = np.asarray(A, dtype=np.float32)
+    codes = np.zeros(A.shape, np.int8)
+    scales = np.zeros(A.shape[1], np.float32)
+    if A.shape[0] == 0:
+        return codes, scales
+    for n in range(A.shape[1]):
+        col = A[:, n]
+        codes[:, n], scales[n] = quantize_group(col, np.abs(col).max(), bits)
+    return codes, scales
+
+
+def quantize_rows(A: np.ndarray, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row quantization (one scale per row, e.g. per token)."""
+    A = np.asarray(A, dtype=np.float32)
+    codes = np.zeros(A.shape, np.int8)
+    scales = np.zeros(A.shape[0], np.float32)
+    if A.shape[1] == 0:
+        return codes, scales
+    for i in range(A.shape[0]):
+        row = A[i]
+        codes[i], scales[i] = quantize_group(row, np.abs(row).max(), bits)
+    return codes, scales
+
+
+def dequantize_columns(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fl32(code * scale) per element, scale per column."""
+    return (codes.astype(np.float32) * scales[None, :].astype(np.float32)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Step C -- the single compensator R on the r salient rows.
+# [N] 核心 idea: R = W~_s - Q(W~_s), built only for the r chosen rows;
+# [RAD]: R is r by d and corrects the quantization error of the r salient
+# rows; [N] 关键设计 2: R itself is quantized, so the whole path stays in low
+# precision. Reading: Q(W~_s) is the main path's own dequantized weight for
+# those rows (per-column scales over all K rows), so that before R is
+# quantized X~_s (Q(W~_s) + R) = X~_s W~_s exactly in real arithmetic. R is
+# quantized to int4 with one scale per output column over its r rows.
+# ---------------------------------------------------------------------------
+
+def compensator(W_hat: np.ndarray, W_deq: np.ndarray, r: int) -> np.ndarray:
+    """R[i, n] = fl32(W^[i, n] - Q(W^)[i, n]) for i < r (r x N float32)."""
+    return (W_hat[:r].astype(np.float32) - W_deq[:r].astype(np.float32)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Canonical 4-bit packing: byte t of a row holds code 2t in bits 0-3 and code
+# 2t+1 in bits 4-7, each as 4-bit two's complement.
+# ---------------------------------------------------------------------------
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    if c.shape[-1] % 2:
+        raise ValueError("packing needs an even number of codes per row")
+    lo = c[..., 0::2] & 0xF
+    hi = c[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.int64)
+    lo = p & 0xF
+    hi = (p >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Offline calibration, end to end ([N] 整体框架: calibration fixes the scale
+# factors, the salient rows and the permutation order).
+# ---------------------------------------------------------------------------
+
+def calibrate(W: np.ndarray, act_absmax: np.ndarray, *, alpha: float = ALPHA_DEFAULT,
+              r: int, quantize_R: bool = True, s_override: np.ndarray | None = None) -> dict:
+    """Calibrate one layer. ``W`` is K x N float32 (bf16 values widen exactly).
+
+    Returns a dict with the library's outputs in their canonical layouts
+    (``perm``, ``s_hat_inv``, ``Wq`` N x K/2 bytes, ``sw``, ``Rq`` N x r/2
+    bytes, ``sr``) plus the intermediate values for tests (``s``, ``s_inv``,
+    ``W_hat``, ``Wq_codes`` K x N, ``W_deq``, ``R``, ``Rq_codes`` r x N).
+
+    Test hooks: ``s_override`` replaces s (e.g. all ones), ``quantize_R=False``
+    keeps R in float (the ``R_float`` entry) for the exact-reconstruction
+    special case.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    K, N = W.shape
+    if K % 2 or r % 2 or not (0 <= r <= K):
+        raise ValueError("need even K, even r with 0 <= r <= K")
+    if s_override is None:
+        s, s_inv = smoothing_factors(act_absmax, np.abs(W).max(axis=1), alpha)
+    else:
+        s = np.asarray(s_override, dtype=np.float32)
+        s_inv = (np.float32(1.0) / s).astype(np.float32)
+    perm = saliency_order(s)
+    s_hat_inv = s_inv[perm].astype(np.float32)
+    W_hat = fold_and_permute(W, s, perm)
+    Wq_codes, sw = quantize_columns(W_hat, 4)
+    W_deq = dequantize_columns(Wq_codes, sw)
+    R = compensator(W_hat, W_deq, r)
+    Rq_codes, sr = quantize_columns(R, 4)
+    out = dict(K=K, N=N, r=r, s=s, s_inv=s_inv, perm=perm, s_hat_inv=s_hat_inv,
+               W_hat=W_hat, Wq_codes=Wq_codes, sw=sw, W_deq=W_deq, R=R,
+               Rq_codes=Rq_codes, sr=sr,
+               Wq=pack_int4(Wq_codes.T), Rq=pack_int4(Rq_codes.T) if r else np.zeros((N, 0), np.uint8))
+    if not quantize_R:
+        out["R_float"] = R
+    return out
+
+
+def calibrate_columns(W: np.ndarray, act_absmax: np.ndarray, cols: np.ndarray, *,
+                      alpha: float = ALPHA_DEFAULT, r: int) -> dict:
+    """The same calibration, evaluated only for the output columns ``cols``.
+
+    Per-column quantization makes every output column independent once s and
+    P are known; s needs each input channel's maximum over all of W, which is
+    one pass. Used to check full-size layers on sampled columns.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    s, s_inv = smoothing_factors(act_absmax, np.abs(W).max(axis=1), alpha)
+    perm = saliency_order(s)
+    Wc = W[:, cols]
+    W_hat = fold_and_permute(Wc, s, perm)
+    Wq_codes, sw = quantize_columns(W_hat, 4)
+    W_deq = dequantize_columns(Wq_codes, sw)
+    R = compensator(W_hat, W_deq, r)
+    Rq_codes, sr = quantize_columns(R, 4)
+    return dict(s=s, s_inv=s_inv, perm=perm, s_hat_inv=s_inv[perm], cols=np.asarray(cols),
+                Wq_codes=Wq_codes, sw=sw, Rq_codes=Rq_codes, sr=sr,
+                Wq=pack_int4(Wq_codes.T), Rq=pack_int4(Rq_codes.T) if r else np.zeros((len(cols), 0), np.uint8))
+
+
+# ---------------------------------------------------------------------------
+# Offline propagation of a later layer's permutation into this layer's output
+# columns. [N] 关键设计 3: the activation order a layer needs is produced by
+# permuting the previous layer's weight columns offline (the down projection's
+# order P4 is pushed into the gate/up columns), so no layer reorders at run
+# time. [GDE] 2.C says the same.
+# ---------------------------------------------------------------------------
+
+def permute_outputs(layer: dict, perm_next: np.ndarray) -> dict:
+    """New output column i is old column perm_next[i] (applied to Wq rows of
+    the N-major layout, sw, Rq rows and sr)."""
+    p = np.asarray(perm_next)
+    out = dict(layer)
+    out["Wq"] = layer["Wq"][p]
+    out["sw"] = layer["sw"][p]
+    out["Rq"] = layer["Rq"][p]
+    out["sr"] = layer["sr"][p]
+    for key in ("Wq_codes", "Rq_codes", "W_hat", "W_deq", "R"):
+        if key in layer:
+            out[key] = layer[key][:, p]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Online step 1 -- activation quantization.
+# [N] 整体框架: at inference the main path is a pure 4-bit GEMM on Q(X^);
+# [N] 关键设计 3: activations arrive already in the saliency order (the
+# previous layer's columns were permuted offline), so nothing is gathered
+# here. Per-token symmetric quantization, int4 for W4A4 or int8 for W4A8
+# ([N] 整体框架 output node "W4A4/W4A8"). x^ = fl32(x * s_hat_inv[k]).
+# ---------------------------------------------------------------------------
+
+def quant_act(X_perm: np.ndarray, s_hat_inv: np.ndarray, a_bits: int) -> dict:
+    """Returns dict(codes M x K int8, sx M float32, packed bytes)."""
+    Xp = np.asarray(X_perm, dtype=np.float32)
+    x_hat = (Xp * np.asarray(s_hat_inv, dtype=np.float32)[None, :]).astype(np.float32)
+    codes, sx = quantize_rows(x_hat, a_bits)
+    packed = pack_int4(codes) if a_bits == 4 else codes.view(np.uint8).copy()
+    return dict(codes=codes, sx=sx, packed=packed, x_hat=x_hat)
+
+
+# ---------------------------------------------------------------------------
+# Online step 2 -- the SERQ linear.
+# [N] 关键设计 2: X^ W^ ~ X^_q W^_q + X~_{s,q} Q(R); the residual is a single
+# (tokens x r) x (r x d) product, R is itself quantized, and there is no
+# intermediate quantization. [GDE] 2.B writes the same operator with
+# Q(X~_s); [GJA] 2 ("計算フローの革新") contrasts X_q W_q + X_{s,q} R_q with
+# L2QER's serial two-factor form. Reading: X~_{s,q} is the first r columns of
+# the already quantized activations (same codes, same per-token scale), i.e.
+# no second quantization of the salient channels.
+# ---------------------------------------------------------------------------
+
+def linear_int(Xq_codes: np.ndarray, Wq_codes: np.ndarray, Rq_codes: np.ndarray,
+               r: int) -> tuple[np.ndarray, np.ndarray]:
+    """acc_main = Xq . Wq over all K, acc_res = Xq[:, :r] . Rq, exact int64.
+
+    ``Wq_codes`` is K x N and ``Rq_codes`` r x N (codes, not packed)."""
+    Xc = np.asarray(Xq_codes, dtype=np.int64)
+    acc_main = Xc @ np.asarray(Wq_codes, dtype=np.int64)
+    if r:
+        acc_res = Xc[:, :r] @ np.asarray(Rq_codes, dtype=np.int64)
+    else:
+        acc_res = np.zeros_like(acc_main)
+    if acc_main.size:
+        assert np.abs(acc_main).max() < 2**31 and np.abs(acc_res).max() < 2**31
+    return acc_main, acc_res
+
+
+def epilogue(acc_main: np.ndarray, acc_res: np.ndarray, sx: np.ndarray, sw: np.ndarray,
+             sr: np.ndarray) -> np.ndarray:
+    """y = sx_m * (sw_n * acc_main + sr_n * acc_res) evaluated in fp64."""
+    sx64 = np.asarray(sx, dtype=np.float64)[:, None]
+    sw64 = np.asarray(sw, dtype=np.float64)[None, :]
+    sr64 = np.asarray(sr, dtype=np.float64)[None, :]
+    return sx64 * (sw64 * acc_main.astype(np.float64) + sr64 * acc_res.astype(np.float64))
+
+
+def round_f64_to_bf16(y: np.ndarray) -> np.ndarray:
+    """Round fp64 values once to bf16 (nearest even); returns float32 arrays
+    holding the bf16 values. Values in the normal bf16 range only."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    u = y.view(np.uint64)
+    drop = np.uint64(52 - 7)
+    lsb = (u >> drop) & np.uint64(1)
+    bias = (np.uint64(1) << (drop - np.uint64(1))) - np.uint64(1) + lsb
+    u2 = ((u + bias) >> drop) << drop
+    return u2.view(np.float64).astype(np.float32)
+
+
+def linear(Xq: dict, layer: dict, *, out: str = "bf16") -> dict:
+    """The layer output for quantized activations ``Xq`` (from quant_act)."""
+    r = layer["r"]
+    acc_main, acc_res = linear_int(Xq["codes"], layer["Wq_codes"], layer["Rq_codes"], r)
+    y64 = epilogue(acc_main, acc_res, Xq["sx"], layer["sw"], layer["sr"])
+    if out == "f32":
+        y = y64.astype(np.float32)
+    elif out == "bf16":
+        y = round_f64_to_bf16(y64)
+    else:
+        raise ValueError("out must be 'f32' or 'bf16'")
+    return dict(acc_main=acc_main, acc_res=acc_res, y64=y64, y=y)
+
+
+def linear_float_residual(Xq: dict, layer: dict) -> np.ndarray:
+    """Test hook: the residual with an unquantized R (fp64), for the special
+    case r = K where the weight error is removed exactly."""
+    r = layer["r"]
+    xd = Xq["codes"].astype(np.float64) * Xq["sx"].astype(np.float64)[:, None]
+    main = xd @ (layer["Wq_codes"].astype(np.float64) * layer["sw"].astype(np.float64)[None, :])
+    res = xd[:, :r] @ layer["R"].astype(np.float64)
+    return main + res

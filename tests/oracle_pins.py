@@ -1,0 +1,388 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``check_*`` takes the oracle module and raises AssertionError when the
+oracle disagrees with a closed form, an identity the pages state, brute
+force on tiny inputs, or a hand-derived fixture under tests/golden/. They are
+run on the real oracle (must pass) and on deliberately broken copies of it
+(must fail) by test_oracle_pins.py, which shows that each plausible mistake
+is caught by at least one pin.
+
+Page tags: [N] papernotes.org ICLR 2026 notes on SERQ; [GDE]
+gist.science/de "Technische Zusammenfassung"; [GJA] gist.science/ja "技術概要";
+[RAD] AI Radio episode transcript.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f32_ulp(x: float) -> float:
+    x = abs(float(np.float32(x)))
+    return float(np.spacing(np.float32(x)))
+
+
+def _small_layer(seed=3, K=64, N=24, M=5, n_out=2, factor=30.0):
+    rng = np.random.default_rng(seed)
+    outl = rng.choice(K, n_out, replace=False)
+    W = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    Xc = rng.standard_normal((64, K)).astype(np.float32)
+    Xc[:, outl] *= factor
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[:, outl] *= factor
+    return W, np.abs(Xc).max(axis=0).astype(np.float32), X
+
+
+# ---------------------------------------------------------------- packing
+
+def check_pack(O):
+    g = golden("pack_int4.json")
+    for case in g["cases"]:
+        codes = np.array(case["codes"], np.int8)[None, :]
+        assert O.pack_int4(codes)[0].tolist() == case["bytes"], case
+        assert O.unpack_int4(np.array([case["bytes"]], np.uint8))[0].tolist() == case["codes"], case
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    assert np.array_equal(O.pack_int4(O.unpack_int4(allb)), allb)
+    # brute force: code 2t is byte t's low nibble as 4-bit two's complement
+    un = O.unpack_int4(allb)[0]
+    for b in range(256):
+        lo, hi = b & 15, b >> 4
+        assert un[2 * b] == (lo - 16 if lo >= 8 else lo)
+        assert un[2 * b + 1] == (hi - 16 if hi >= 8 else hi)
+
+
+# ---------------------------------------------------------------- quantizer
+
+def check_quantizer_golden(O):
+    g = golden("quantizer.json")
+    for case in g["cases"]:
+        q, sc = O.quantize_group(np.array(case["v"], np.float32), case["m"], case["bits"])
+        assert q.tolist() == case["codes"], case
+        assert float(sc) == case["scale"], case
+
+
+def _nearest_even_by_search(t: float, lo: int, hi: int) -> int:
+    """Pick the integer in [lo, hi] nearest to t, ties to the even one, by
+    exhaustive search (an independent statement of round-half-even + clamp)."""
+    best = None
+    for q in range(lo, hi + 1):
+        d = abs(Fraction(t) - q)
+        if best is None or d < best[0] or (d == best[0] and q % 2 == 0):
+            best = (d, q)
+    return best[1]
+
+
+def check_quantizer_bruteforce(O):
+    rng = np.random.default_rng(11)
+    for bits, (lo, hi) in ((4, (-8, 7)), (8, (-128, 127))):
+        for trial in range(40):
+            n = int(rng.integers(1, 9))
+            v = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+            if trial % 7 == 0:  # plant exact ties on the grid
+                v = (np.array(rng.integers(-2 * hi, 2 * hi + 1, n), np.float32) / 2).astype(np.float32)
+            m = np.float32(np.abs(v).max())
+            q, sc = O.quantize_group(v, m, bits)
+            if m == 0:
+                assert sc == 0 and not q.any()
+                continue
+            inv = np.float32(np.float32(hi) / m)
+            assert sc == np.float32(m / np.float32(hi))
+            for i in range(n):
+                t = float(np.float32(v[i] * inv))
+                assert q[i] == _nearest_even_by_search(t, lo, hi), (bits, v, i)
+                # absmax scaling never reaches the clamp's negative extreme
+                assert -hi <= q[i] <= hi
+                # reconstruction error at most half a step (plus reciprocal slack)
+                err = abs(Fraction(float(v[i])) - q[i] * Fraction(float(sc)))
+                assert err <= Fraction(float(sc)) * (Fraction(1, 2) + Fraction(1, 2 ** 19)), (v[i], q[i], sc)
+            # the absolute maximum maps to +-qmax
+            j = int(np.argmax(np.abs(v)))
+            assert abs(int(q[j])) == hi
+
+
+# ---------------------------------------------------------------- smoothing
+
+def _exact_s(a: float, w: float, alpha: float) -> Decimal:
+    getcontext().prec = 60
+    a = max(Decimal(float(np.float32(a))), Decimal(1e-5))
+    w = max(Decimal(float(np.float32(w))), Decimal(1e-5))
+    if alpha == 0.5:
+        return a.sqrt() / w.sqrt()
+    al = Decimal(alpha)
+    return (al * a.ln()).exp() / ((1 - al) * w.ln()).exp()
+
+
+def check_smoothing(O):
+    g = golden("smoothing.json")
+    for case in g["cases"]:
+        s, s_inv = O.smoothing_factors(np.array([case["a"]], np.float32), np.array([case["w"]], np.float32),
+                                       case["alpha"])
+        assert abs(float(s[0]) - case["s"]) <= f32_ulp(case["s"]), case
+    rng = np.random.default_rng(5)
+    a = (np.abs(rng.standard_normal(64)) * 10.0 ** rng.uniform(-4, 3, 64)).astype(np.float32)
+    w = (np.abs(rng.standard_normal(64)) * 10.0 ** rng.uniform(-4, 1, 64)).astype(np.float32)
+    for alpha in (0.5, 0.3, 0.8):
+        s, s_inv = O.smoothing_factors(a, w, alpha)
+        for j in range(64):
+            ex = float(_exact_s(a[j], w[j], alpha))
+            assert abs(float(s[j]) - ex) <= f32_ulp(ex), (alpha, a[j], w[j], s[j], ex)
+            # s_inv is the correctly rounded fp32 reciprocal
+            exr = Fraction(1) / Fraction(float(s[j]))
+            assert abs(Fraction(float(s_inv[j])) - exr) <= Fraction(f32_ulp(float(exr))) / 2
+    # SmoothQuant balance at alpha = 0.5: after flattening, channel j's
+    # activation maximum a/s equals its folded weight maximum s*w.
+    s, _ = O.smoothing_factors(a, w, 0.5)
+    af = np.maximum(a.astype(np.float64), 1e-5)
+    wf = np.maximum(w.astype(np.float64), 1e-5)
+    bal = (af / s) / (s * wf)
+    assert np.all(np.abs(bal - 1) < 3e-7), bal
+
+
+# ---------------------------------------------------------------- permutation
+
+def check_perm(O):
+    rng = np.random.default_rng(7)
+    s = rng.choice(np.array([0.5, 1.0, 2.0, 3.0, 7.0], np.float32), size=50)
+    perm = O.saliency_order(s)
+    assert sorted(perm.tolist()) == list(range(50))                  # bijection
+    sp = s[perm]
+    assert np.all(sp[:-1] >= sp[1:])                                    # descending saliency
+    for i in range(49):                                                 # ties: lower index first
+        if sp[i] == sp[i + 1]:
+            assert perm[i] < perm[i + 1]
+    # all equal -> identity
+    assert O.saliency_order(np.ones(9, np.float32)).tolist() == list(range(9))
+
+
+def check_fold_identity(O):
+    """[RAD] and [N] 关键设计 1: (X diag(s^-1) P^-1)(P diag(s) W) = XW."""
+    W, amax, X = _small_layer()
+    L = O.calibrate(W, amax, r=8)
+    perm, s = L["perm"], L["s"]
+    # exact in fp64 when both factors are formed in fp64 from s and perm
+    Xh = X.astype(np.float64)[:, perm] / s.astype(np.float64)[perm][None, :]
+    Wh = s.astype(np.float64)[perm][:, None] * W.astype(np.float64)[perm, :]
+    Y = X.astype(np.float64) @ W.astype(np.float64)
+    assert np.linalg.norm(Xh @ Wh - Y) <= 1e-12 * np.linalg.norm(Y)
+    # the oracle's own fp32 folded weight and flattened activations
+    q = O.quant_act(X[:, perm], L["s_hat_inv"], 4)
+    Yf = q["x_hat"].astype(np.float64) @ L["W_hat"].astype(np.float64)
+    assert np.linalg.norm(Yf - Y) <= 1e-5 * np.linalg.norm(Y)
+    # the folded rows are in descending-s order: row i is channel perm[i]
+    assert np.array_equal(L["W_hat"][0], (s[perm[0]] * W[perm[0]]).astype(np.float32))
+
+
+# ---------------------------------------------------------------- compensator
+
+def check_compensator(O):
+    """[N] 核心 idea: R = W~_s - Q(W~_s) on the r salient rows."""
+    W, amax, _ = _small_layer(seed=4, K=96, N=40)
+    r = 16
+    L = O.calibrate(W, amax, r=r)
+    Wh, Wd, R, sw = L["W_hat"][:r], L["W_deq"][:r], L["R"], L["sw"]
+    assert R.shape == (r, W.shape[1])                                   # r x d
+    recon = (Wd + R).astype(np.float32)
+    sterbenz = (L["Wq_codes"][:r] == 0) | ((np.abs(Wh) >= np.abs(Wd) / 2) & (np.abs(Wh) <= 2 * np.abs(Wd))
+                                           & (np.sign(Wh) == np.sign(Wd)))
+    assert np.array_equal(recon[sterbenz], Wh[sterbenz])
+    ulp = np.spacing(np.abs(Wh).astype(np.float32))
+    assert np.all(np.abs(recon - Wh)[~sterbenz] <= ulp[~sterbenz])
+    # R is a rounding error: at most half a quantization step per column
+    assert np.all(np.abs(R.astype(np.float64)) <= sw[None, :].astype(np.float64) * (0.5 + 2 ** -19))
+    # R covers exactly the r most salient rows
+    assert np.array_equal(L["W_hat"][:r], Wh)
+    assert L["Rq_codes"].shape == (r, W.shape[1])
+
+
+# ---------------------------------------------------------------- integer GEMM
+
+def check_int_gemm(O):
+    rng = np.random.default_rng(9)
+    for (M, K, N, r) in ((3, 8, 5, 2), (1, 16, 7, 0), (4, 12, 3, 12)):
+        Xc = rng.integers(-8, 8, (M, K))
+        Wc = rng.integers(-8, 8, (K, N))
+        Rc = rng.integers(-8, 8, (r, N))
+        am, ar = O.linear_int(Xc.astype(np.int8), Wc.astype(np.int8), Rc.astype(np.int8), r)
+        for m in range(M):
+            for n in range(N):
+                tot = 0
+                for k in range(K):
+                    tot += int(Xc[m, k]) * int(Wc[k, n])
+                assert am[m, n] == tot
+                tot = 0
+                for k in range(r):
+                    tot += int(Xc[m, k]) * int(Rc[k, n])
+                assert ar[m, n] == tot
+
+
+# ---------------------------------------------------------------- dequantized output
+
+def check_dequant_identity(O):
+    """[N] 关键设计 2: X^ W^ ~ X^_q W^_q + X~_{s,q} Q(R), with X~_{s,q} the
+    first r (salient) quantized activation columns. Summed term by term."""
+    W, amax, X = _small_layer(seed=6, K=32, N=6, M=3)
+    r = 8
+    L = O.calibrate(W, amax, r=r)
+    q = O.quant_act(X[:, L["perm"]], L["s_hat_inv"], 4)
+    out = O.linear(q, L, out="f32")
+    M, K = q["codes"].shape
+    N = W.shape[1]
+    for m in range(M):
+        xs = float(q["sx"][m])
+        for n in range(N):
+            tot = 0.0
+            for k in range(K):
+                tot += (q["codes"][m, k] * xs) * (int(L["Wq_codes"][k, n]) * float(L["sw"][n]))
+            for k in range(r):
+                tot += (q["codes"][m, k] * xs) * (int(L["Rq_codes"][k, n]) * float(L["sr"][n]))
+            assert abs(out["y64"][m, n] - tot) <= 1e-12 * max(1.0, abs(tot)), (m, n, out["y64"][m, n], tot)
+            assert out["y"][m, n] == np.float32(out["y64"][m, n])
+
+
+def check_special_cases(O):
+    W, amax, X = _small_layer(seed=8, K=48, N=10, M=4)
+    K, N = W.shape
+    # r = 0: SmoothQuant flattening + RTN W4A4, written as fake quantization
+    L = O.calibrate(W, amax, r=0)
+    q = O.quant_act(X[:, L["perm"]], L["s_hat_inv"], 4)
+    y0 = O.linear(q, L, out="f32")["y64"]
+    xf = q["codes"].astype(np.float64) * q["sx"].astype(np.float64)[:, None]
+    wf = L["Wq_codes"].astype(np.float64) * L["sw"].astype(np.float64)[None, :]
+    assert np.allclose(y0, xf @ wf, rtol=1e-12, atol=1e-12)
+    assert not L["Rq"].size
+    # s == 1 and r = 0: plain per-token x per-channel W4A4 on the original order
+    L1 = O.calibrate(W, amax, r=0, s_override=np.ones(K, np.float32))
+    assert L1["perm"].tolist() == list(range(K))
+    q1 = O.quant_act(X, L1["s_hat_inv"], 4)
+    y1 = O.linear(q1, L1, out="f32")["y64"]
+    for m in range(X.shape[0]):
+        am = float(np.abs(X[m]).max())
+        xc = [_nearest_even_by_search(float(np.float32(X[m, k] * np.float32(7 / np.float32(am)))), -8, 7)
+              for k in range(K)]
+        for n in range(N):
+            wm = float(np.abs(W[:, n]).max())
+            winv = np.float32(np.float32(7) / np.float32(wm))
+            wc = [_nearest_even_by_search(float(np.float32(W[k, n] * winv)), -8, 7) for k in range(K)]
+            ref = float(np.float32(am / np.float32(7))) * float(np.float32(np.float32(wm) / np.float32(7))) * \
+                sum(a * b for a, b in zip(xc, wc))
+            assert abs(y1[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    # r = K with an unquantized R removes the weight error exactly:
+    # y = deq(Xq) . W^ (fp64)
+    LK = O.calibrate(W, amax, r=K, quantize_R=False)
+    qK = O.quant_act(X[:, LK["perm"]], LK["s_hat_inv"], 4)
+    yK = O.linear_float_residual(qK, LK)
+    xd = qK["codes"].astype(np.float64) * qK["sx"].astype(np.float64)[:, None]
+    exact = xd @ LK["W_hat"].astype(np.float64)
+    assert np.allclose(yK, exact, rtol=1e-6, atol=1e-9)
+
+
+# ---------------------------------------------------------------- fixtures
+
+def check_worked_layer(O):
+    g = golden("worked_layer_4x2.json")
+    inp, ex = g["inputs"], g["expected"]
+    W = np.array(inp["W"], np.float32)
+    L = O.calibrate(W, np.array(inp["act_absmax"], np.float32), alpha=inp["alpha"], r=inp["r"])
+    assert L["s"].tolist() == ex["s"]
+    assert L["perm"].tolist() == ex["perm"]
+    assert L["s_hat_inv"].tolist() == ex["s_hat_inv"]
+    assert L["W_hat"].tolist() == ex["W_hat"]
+    assert L["Wq_codes"].tolist() == ex["Wq_codes"]
+    assert L["sw"].tolist() == ex["sw"]
+    assert L["W_deq"].tolist() == ex["W_deq"]
+    assert L["R"].tolist() == ex["R"]
+    assert L["Rq_codes"].tolist() == ex["Rq_codes"]
+    assert L["sr"].tolist() == ex["sr"]
+    assert L["Wq"].tolist() == ex["Wq_packed_N_major"]
+    assert L["Rq"].tolist() == ex["Rq_packed_N_major"]
+    X = np.array(inp["X"], np.float32)
+    q = O.quant_act(X[:, L["perm"]], L["s_hat_inv"], inp["a_bits"])
+    assert q["x_hat"].tolist() == ex["x_hat"]
+    assert q["codes"].tolist() == ex["Xq_codes"]
+    assert q["sx"].tolist() == ex["sx"]
+    o = O.linear(q, L, out="f32")
+    assert o["acc_main"].tolist() == ex["acc_main"]
+    assert o["acc_res"].tolist() == ex["acc_res"]
+    assert o["y"].tolist() == ex["y_f32"]
+    assert O.linear(q, L, out="bf16")["y"].tolist() == ex["y_bf16"]
+
+
+def check_bf16(O):
+    g = golden("bf16_round.json")
+    for case in g["cases"]:
+        assert float(O.round_f64_to_bf16(np.array([case["x"]]))[0]) == case["bf16"], case
+    # brute force: the result is the nearest bf16 value, ties to an even mantissa
+    rng = np.random.default_rng(2)
+    xs = rng.standard_normal(300) * 10.0 ** rng.uniform(-5, 5, 300)
+    got = O.round_f64_to_bf16(xs)
+    for x, g_ in zip(xs, got):
+        e = math.floor(math.log2(abs(x)))
+        step = 2.0 ** (e - 7)
+        lo = math.floor(x / step) * step
+        cands = [lo, lo + step]
+        d = [abs(Fraction(x) - Fraction(c)) for c in cands]
+        if d[0] != d[1]:
+            want = cands[0] if d[0] < d[1] else cands[1]
+        else:
+            want = cands[0] if int(round(cands[0] / step)) % 2 == 0 else cands[1]
+        assert float(g_) == want, (x, g_, want)
+
+
+def check_permute_outputs(O):
+    """[N] 关键设计 3: a later layer's order pushed into this layer's output
+    columns yields the permuted output with no run-time gather."""
+    W, amax, X = _small_layer(seed=12, K=32, N=20, M=3)
+    L = O.calibrate(W, amax, r=4)
+    q = O.quant_act(X[:, L["perm"]], L["s_hat_inv"], 4)
+    base = O.linear(q, L, out="f32")
+    p = np.random.default_rng(1).permutation(20).astype(np.int32)
+    Lp = O.permute_outputs(L, p)
+    got = O.linear(q, Lp, out="f32")
+    assert np.array_equal(got["acc_main"], base["acc_main"][:, p])
+    assert np.array_equal(got["acc_res"], base["acc_res"][:, p])
+    assert np.array_equal(got["y"], base["y"][:, p])
+    assert np.array_equal(O.unpack_int4(Lp["Wq"]).T, L["Wq_codes"][:, p])
+
+
+def check_rank_trend(O):
+    """[N] 消融实验 / 关键发现: error falls as the rank grows and saturates.
+    Statistical sanity on a synthetic outlier layer (not parity)."""
+    rng = np.random.default_rng(0)
+    K, N, M = 256, 128, 64
+    outl = rng.choice(K, 3, replace=False)
+    W = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    Xc = rng.standard_normal((128, K)).astype(np.float32)
+    Xc[:, outl] *= 40
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    X[:, outl] *= 40
+    amax = np.abs(Xc).max(axis=0)
+    Y = X.astype(np.float64) @ W.astype(np.float64)
+    errs = []
+    for r in (0, 16, 64, 128):
+        L = O.calibrate(W, amax, r=r)
+        q = O.quant_act(X[:, L["perm"]], L["s_hat_inv"], 4)
+        errs.append(np.linalg.norm(O.linear(q, L, out="f32")["y64"] - Y))
+    assert errs[0] > errs[1] > errs[2] > errs[3], errs
+    # flattening helps against channel outliers compared with plain W4A4
+    L1 = O.calibrate(W, amax, r=0, s_override=np.ones(K, np.float32))
+    q1 = O.quant_act(X, L1["s_hat_inv"], 4)
+    assert np.linalg.norm(O.linear(q1, L1, out="f32")["y64"] - Y) > errs[0]
+
+
+ALL_CHECKS = [check_pack, check_quantizer_golden, check_quantizer_bruteforce, check_smoothing,
+              check_perm, check_fold_identity, check_compensator, check_int_gemm,
+              check_dequant_identity, check_special_cases, check_worked_layer, check_bf16,
+              check_permute_outputs, check_rank_trend]

@@ -1,0 +1,149 @@
+"""The oracle against its pins, and planted mistakes against the pins.
+
+Every pin in oracle_pins.py must pass on the oracle. Each mutant below plants
+one plausible mistake in the oracle (on the CPU, through monkeypatch) and at
+least one pin must then fail: a dropped term, a wrong sign, a wrong index, a
+transposed or inverted permutation, a wrong rounding rule or a wrong scale.
+"""
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import serq_oracle as O
+
+
+@pytest.mark.parametrize("check", P.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_pin(check):
+    check(O)
+
+
+# ------------------------------------------------------------------ mutants
+
+def _mut_compensator_sign(orig):
+    return lambda Wh, Wd, r: (Wd[:r] - Wh[:r]).astype(np.float32)
+
+
+def _mut_saliency_ascending(orig):
+    return lambda s: np.argsort(np.asarray(s, np.float64), kind="stable").astype(np.int32)
+
+
+def _mut_round_half_up(orig):
+    def q(v, m, bits):
+        lo, hi = O.qrange(bits)
+        v = np.asarray(v, np.float32)
+        m = np.float32(m)
+        if m == 0:
+            return np.zeros(v.shape, np.int8), np.float32(0)
+        inv = np.float32(np.float32(hi) / m)
+        t = (v * inv).astype(np.float32)
+        return np.clip(np.floor(t + np.float32(0.5)), lo, hi).astype(np.int8), np.float32(m / np.float32(hi))
+    return q
+
+
+def _mut_scale_over_8(orig):
+    def q(v, m, bits):
+        lo, hi = O.qrange(bits)
+        v = np.asarray(v, np.float32)
+        m = np.float32(m)
+        if m == 0:
+            return np.zeros(v.shape, np.int8), np.float32(0)
+        inv = np.float32(np.float32(-lo) / m)
+        t = (v * inv).astype(np.float32)
+        return np.clip(np.rint(t), lo, hi).astype(np.int8), np.float32(m / np.float32(-lo))
+    return q
+
+
+def _mut_drop_residual(orig):
+    def f(Xc, Wc, Rc, r):
+        am, ar = orig(Xc, Wc, Rc, r)
+        return am, np.zeros_like(ar)
+    return f
+
+
+def _mut_residual_last_columns(orig):
+    def f(Xc, Wc, Rc, r):
+        am, _ = orig(Xc, Wc, Rc, 0)
+        Xc = np.asarray(Xc, np.int64)
+        ar = Xc[:, Xc.shape[1] - r:] @ np.asarray(Rc, np.int64) if r else np.zeros_like(am)
+        return am, ar
+    return f
+
+
+def _mut_inverse_perm_fold(orig):
+    def f(W, s, perm):
+        inv = np.argsort(perm)
+        return orig(W, s, inv)
+    return f
+
+
+def _mut_quant_act_ignores_sinv(orig):
+    return lambda X, s_hat_inv, a_bits: orig(X, np.ones_like(s_hat_inv), a_bits)
+
+
+def _mut_pack_swapped(orig):
+    def f(codes):
+        c = np.asarray(codes, np.int64)
+        return ((c[..., 1::2] & 0xF) | ((c[..., 0::2] & 0xF) << 4)).astype(np.uint8)
+    return f
+
+
+def _mut_epilogue_sw_for_both(orig):
+    return lambda am, ar, sx, sw, sr: orig(am, ar, sx, sw, sw)
+
+
+def _mut_per_tensor_weights(orig):
+    def f(A, bits):
+        A = np.asarray(A, np.float32)
+        codes = np.zeros(A.shape, np.int8)
+        scales = np.zeros(A.shape[1], np.float32)
+        if A.size:
+            codes, sc = O.quantize_group(A, np.abs(A).max(), bits)
+            scales[:] = sc
+        return codes, scales
+    return f
+
+
+def _mut_alpha_swapped(orig):
+    return lambda a, w, alpha=0.5: orig(w, a, alpha)
+
+
+def _mut_bf16_via_f32(orig):
+    def f(y):
+        y32 = np.asarray(y, np.float64).astype(np.float32)
+        u = y32.view(np.uint32).astype(np.uint64)
+        lsb = (u >> np.uint64(16)) & np.uint64(1)
+        u = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+        return u.astype(np.uint32).view(np.float32)
+    return f
+
+
+MUTANTS = {
+    "compensator_sign": ("compensator", _mut_compensator_sign),
+    "saliency_ascending": ("saliency_order", _mut_saliency_ascending),
+    "round_half_up": ("quantize_group", _mut_round_half_up),
+    "scale_over_8": ("quantize_group", _mut_scale_over_8),
+    "drop_residual": ("linear_int", _mut_drop_residual),
+    "residual_last_columns": ("linear_int", _mut_residual_last_columns),
+    "inverse_perm_fold": ("fold_and_permute", _mut_inverse_perm_fold),
+    "quant_act_ignores_sinv": ("quant_act", _mut_quant_act_ignores_sinv),
+    "pack_swapped": ("pack_int4", _mut_pack_swapped),
+    "epilogue_sw_for_both": ("epilogue", _mut_epilogue_sw_for_both),
+    "per_tensor_weights": ("quantize_columns", _mut_per_tensor_weights),
+    "alpha_swapped": ("smoothing_factors", _mut_alpha_swapped),
+    "bf16_double_rounding": ("round_f64_to_bf16", _mut_bf16_via_f32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, make = MUTANTS[name]
+    orig = getattr(O, attr)
+    monkeypatch.setattr(O, attr, make(orig))
+    caught = []
+    for check in P.ALL_CHECKS:
+        try:
+            check(O)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+    assert caught, f"no pin catches mutant {name}"
