@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the SERQ quantized linear layer on one MI355X.
+
+One step is one pass of the online hot path over one batch of synthetic
+input: per-token activation quantization (serq_quant_act) followed by the
+fused SERQ linear (serq_linear) -- the pure 4-bit GEMM, the salient-row
+residual and the dequantizing epilogue. Calibration is offline and not timed.
+
+Default workload: the LLaMA-2-7B-shaped q_proj layer (K = N = 4096, r = 64,
+W4A4, bf16 activations and output) at M = 2048 tokens; the other token counts
+of that layer (1, 16, 256) are reported in "sweep". Inputs are seeded
+synthetic data (Gaussian activations with 1 % outlier channels x50, Gaussian
+weights), resident in HBM before the timed region. The weights and
+activations are rotated through enough copies (>= 768 MiB) that every step
+reads them from HBM rather than from the 256 MB last-level cache.
+
+Prints one JSON line. `value` is whole-job throughput in TOP/s:
+2 * M * N * (K + r) integer operations per step / measured step time.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "serq_linear TOPS & HBM GB/s (% roofline) at M=1..4096, LLaMA-shaped K×N"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (no sparsity)
+ROTATE_BYTES = 768 << 20
+
+WORKLOADS = {
+    # name: (synth workload, layer, r, a_bits, default M, sweep Ms)
+    "q_proj": ("q_proj", "q_proj", 64, 4, 2048, (1, 16, 256, 2048)),
+    "gate_up": ("mlp8b", "gate_up", 128, 4, 4096, (1, 32, 4096)),
+    "down": ("mlp8b", "down", 128, 4, 4096, (1, 32, 4096)),
+    "gate_up_w4a8": ("mlp8b_w4a8", "gate_up", 128, 8, 2048, (2048,)),
+    "down_w4a8": ("mlp8b_w4a8", "down", 128, 8, 2048, (2048,)),
+    "up70": ("l70b", "up70", 256, 4, 8192, (1, 8192)),
+    "down70": ("l70b", "down70", 256, 4, 8192, (1, 8192)),
+}
+
+
+def linear_bytes(M, K, N, r, a_bits):
+    return M * K * a_bits // 8 + K * N // 2 + r * N // 2 + 4 * (M + 2 * N) + M * N * 2
+
+
+def quant_bytes(M, K, a_bits):
+    return M * K * 2 + 4 * K + M * K * a_bits // 8 + 4 * M
+
+
+def linear_ops(M, K, N, r):
+    return 2 * M * N * (K + r)
+
+
+def kernel_src_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a4_linear_layers_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Setup:
+    """Device buffers for one layer: C rotated copies of weights and inputs."""
+
+    def __init__(self, workload, M_max, seed=0):
+        import numpy as np
+        import torch
+
+        import w4a4_linear_layers_amd as S
+        from synth import workload_layer
+
+        wl, layer, r, a_bits, _, _ = WORKLOADS[workload]
+        li = workload_layer(wl, layer, M_max=M_max, seed=seed)
+        self.K, self.N, self.r, self.a_bits = li.K, li.N, r, a_bits
+        W = li.W_bits
+        if "W_up_bits" in li.meta:     # gate and up share the input: calibrate them as one
+            W = np.concatenate([W, li.meta["W_up_bits"]], axis=1)
+            self.N = W.shape[1]
+        t0 = time.time()
+        L = S.calibrate(W, li.act_absmax, r=r)
+        self.calib_s = time.time() - t0
+        self.li, self.L = li, L
+        dev = torch.device("cuda")
+        x = torch.from_numpy(np.ascontiguousarray(li.X_bits[:, L.perm]).view(np.int16)).to(dev)
+        x = x.view(torch.bfloat16)
+        per = x.numel() * 2 + L.Wq.nbytes + L.Rq.nbytes + 8 * self.N
+        self.copies = max(2, math.ceil(ROTATE_BYTES / per))
+        base = L.to(dev)
+        self.layers, self.xs = [], []
+        for _ in range(self.copies):
+            self.layers.append(S.DeviceLayer(K=L.K, N=self.N, r=r, perm=base.perm, s_hat_inv=base.s_hat_inv,
+                                             Wq=base.Wq.clone(), sw=base.sw.clone(), Rq=base.Rq.clone(),
+                                             sr=base.sr.clone()))
+            self.xs.append(x.clone())
+        self.xq = torch.empty((M_max, self.K // 2 if a_bits == 4 else self.K),
+                              dtype=torch.uint8 if a_bits == 4 else torch.int8, device=dev)
+        self.sx = torch.empty(M_max, dtype=torch.float32, device=dev)
+        self.y = torch.empty((M_max, self.N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, i, M):
+        import w4a4_linear_layers_amd as S
+        c = i % self.copies
+        L = self.layers[c]
+        xq, sx = S.quant_act(self.xs[c][:M], L, a_bits=self.a_bits, out=(self.xq[:M], self.sx[:M]))
+        S.linear(xq, sx, L, a_bits=self.a_bits, out=self.y[:M])
+
+    def time_kernels(self, M, n):
+        """Average duration of each kernel alone, n back-to-back launches
+        bracketed by events on the launch stream (the current stream)."""
+        import torch
+
+        import w4a4_linear_layers_amd as S
+        st = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for i in range(self.copies):       # make every copy's quantized input valid
+            S.quant_act(self.xs[i][:M], self.layers[i], a_bits=self.a_bits, out=(self.xq[:M], self.sx[:M]))
+        torch.cuda.synchronize()
+        ev[0].record(st)
+        for i in range(n):
+            c = i % self.copies
+            S.quant_act(self.xs[c][:M], self.layers[c], a_bits=self.a_bits, out=(self.xq[:M], self.sx[:M]))
+        ev[1].record(st)
+        xq, sx = self.xq[:M], self.sx[:M]
+        ev[2].record(st)
+        for i in range(n):
+            S.linear(xq, sx, self.layers[i % self.copies], a_bits=self.a_bits, out=self.y[:M])
+        ev[3].record(st)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / n, ev[2].elapsed_time(ev[3]) * 1e3 / n
+
+
+def cpu_baseline(setup, M, rows=None, budget_s=20.0):
+    """The CPU oracle as it stands, on a bounded row sample of the workload:
+    activation quantization + int64 matmuls + fp64 epilogue. Rows are
+    independent, so throughput scales exactly with the row count."""
+    import numpy as np
+
+    from oracle import serq_oracle as O
+    li, L = setup.li, setup.L
+    K, N, r = setup.K, setup.N, setup.r
+    Wc = O.unpack_int4(L.Wq).T.copy()
+    Rc = O.unpack_int4(L.Rq).T.copy() if r else np.zeros((0, N), np.int8)
+    layer = dict(r=r, Wq_codes=Wc, Rq_codes=Rc, sw=L.sw, sr=L.sr)
+    n = 8 if rows is None else rows
+    X = li.X[:, L.perm]
+    while True:
+        t0 = time.perf_counter()
+        q = O.quant_act(X[:n], L.s_hat_inv, setup.a_bits)
+        O.linear(q, layer, out="bf16")
+        dt = time.perf_counter() - t0
+        if rows is not None or dt > budget_s / 4 or n >= M:
+            break
+        n = min(M, max(n + 1, int(n * min(8.0, (budget_s / 2) / max(dt, 1e-3)))))
+    ops = linear_ops(n, K, N, r)
+    return dict(value=ops / dt / 1e12, unit="TOP/s", cores=1, kind="oracle",
+                sample=f"{n} of {M} rows of the same workload (quant_act + int64 matmuls + fp64 epilogue), "
+                       f"{dt:.1f} s; numpy integer matmul runs on one thread",
+                seconds=round(dt, 2), rows=n)
+
+
+def roofline_entry(M, K, N, r, a_bits, us, traffic):
+    ops = linear_ops(M, K, N, r)
+    byts = linear_bytes(M, K, N, r, a_bits)
+    if ops / byts > INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach = ops / (us * 1e-6) / 1e12
+        return dict(bound="mfma", achieved=round(ach, 1), peak=INT8_PEAK_TOPS, unit="TOP/s",
+                    frac=round(ach / INT8_PEAK_TOPS, 4), traffic=traffic, kernel="serq_linear",
+                    algorithmic_ops=ops, algorithmic_bytes=byts)
+    ach = byts / (us * 1e-6) / 1e9
+    return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic, kernel="serq_linear",
+                algorithmic_ops=ops, algorithmic_bytes=byts)
+
+
+def load_traffic(workload, M):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_M{M}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != kernel_src_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="q_proj", choices=sorted(WORKLOADS))
+    ap.add_argument("--M", type=int, default=None, help="tokens per step (default: the workload's)")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+    import w4a4_linear_layers_amd as S
+
+    torch.cuda.set_device(0)
+    wl, layer, r, a_bits, M_def, sweep_ms = WORKLOADS[args.workload]
+    M = args.M or M_def
+    M_max = max([M] + ([] if args.no_sweep else list(sweep_ms)))
+    setup = Setup(args.workload, M_max)
+    K, N = setup.K, setup.N
+    print(f"# setup: {args.workload} K={K} N={N} r={r} a_bits={a_bits} copies={setup.copies} "
+          f"calibrate {setup.calib_s:.1f}s", file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        setup.step(i, M)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        setup.step(i, M)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+    ops = linear_ops(M, K, N, r)
+    value = ops * args.steps / dt / 1e12
+
+    q_us, l_us = setup.time_kernels(M, max(args.steps, 50))
+    traffic = load_traffic(args.workload, M)
+    roof = roofline_entry(M, K, N, r, a_bits, l_us, traffic)
+    print(f"# step {ms_per_step * 1e3:.2f} us; quant_act {q_us:.2f} us, serq_linear {l_us:.2f} us "
+          f"({S.kernel_name(M, K, N, r, a_bits)})", file=sys.stderr, flush=True)
+
+    sweep = []
+    if not args.no_sweep:
+        for m in sweep_ms:
+            qu, lu = setup.time_kernels(m, 100)
+            e = roofline_entry(m, K, N, r, a_bits, lu, None)
+            hbm = linear_bytes(m, K, N, r, a_bits) / (lu * 1e-6) / 1e9
+            tops = linear_ops(m, K, N, r) / (lu * 1e-6) / 1e12
+            sweep.append(dict(M=m, kernel=S.kernel_name(m, K, N, r, a_bits), linear_us=round(lu, 2),
+                              quant_act_us=round(qu, 2), TOPS=round(tops, 2), HBM_GBs=round(hbm, 1),
+                              bound=e["bound"], frac=e["frac"],
+                              quant_act_GBs=round(quant_bytes(m, K, a_bits) / (qu * 1e-6) / 1e9, 1)))
+            print(f"# M={m}: linear {lu:.2f} us {tops:.1f} TOP/s {hbm:.0f} GB/s ({e['bound']} frac "
+                  f"{e['frac']:.3f}); quant_act {qu:.2f} us", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(setup, M)
+        print(f"# cpu oracle: {cpu['value']:.4f} TOP/s on {cpu['rows']} rows", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4" if a_bits == 4 else "int8xint4",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: SERQ linear K={K} N={N} r={r} "
+                               f"{'W4A4' if a_bits == 4 else 'W4A8'}, bf16 in/out, M={M} tokens per step",
+                   "M": M, "K": K, "N": N, "r": r, "a_bits": a_bits,
+                   "kernel": S.kernel_name(M, K, N, r, a_bits), "rotated_copies": setup.copies},
+        "kernels_us": {"serq_quant_act": round(q_us, 3), "serq_linear": round(l_us, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

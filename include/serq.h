@@ -1,0 +1,184 @@
+/*
+ * serq.h -- C ABI of libserq, the SERQ quantized linear layer for MI355X (gfx950).
+ *
+ * SERQ ("SERQ: Saliency-Aware Low-Rank Error Reconstruction for LLM
+ * Quantization") computes a linear layer Y = X W (X: M x K tokens by input
+ * channels, W: K x N) as a pure 4-bit GEMM plus one small residual product:
+ *
+ *     Y  ~  Q(X^) Q(W^)  +  X~_{s,q} Q(R)
+ *
+ * where, after calibration,
+ *   X~ = X diag(s^-1), W~ = diag(s) W          static per-channel flattening
+ *   W^ = P W~ = [W~_s; W~_r], X^ = X~ P^-1     rows in descending saliency
+ *   R  = W~_s - Q(W~_s)                        r x N compensator of the r
+ *                                              most salient rows
+ * and X~_{s,q} is the first r columns of the quantized activations.
+ * Sources: papernotes.org ICLR 2026 notes on SERQ, sections 核心 idea,
+ * 方法详解 / 整体框架 and 关键设计 1-3; gist.science/de/paper/2603.08185,
+ * "Technische Zusammenfassung" 2.A-2.C.
+ *
+ * Conventions for every call
+ *   - Sizes are element counts. Matrices are row-major and contiguous.
+ *   - 4-bit codes are packed two per byte: byte t of a row holds code 2t in
+ *     bits 0-3 and code 2t+1 in bits 4-7, each a 4-bit two's complement
+ *     value in [-8, 7]. int8 codes are plain signed bytes.
+ *   - Quantizer (weights, R, activations): symmetric, one scale per group,
+ *     scale = fl32(m / qmax), code = clamp(rne(fl32(v * fl32(qmax / m)))),
+ *     m the group's absolute maximum, qmax 7 (int4) or 127 (int8), rne round
+ *     half to even. A group whose fl32(qmax / m) overflows (an all-zero group
+ *     in particular) gets scale 0 and zero codes.
+ *   - The caller owns every buffer. The library keeps no global state,
+ *     allocates no memory and creates no streams.
+ *   - Argument errors are detected on the host and returned before anything
+ *     is launched; the output buffers are then untouched.
+ *   - Online calls only enqueue work on `stream` (a hipStream_t; NULL is the
+ *     null stream) and return without synchronizing. A launch failure
+ *     returns SERQ_EHIP.
+ */
+#ifndef SERQ_H_
+#define SERQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SERQ_OK = 0,
+  SERQ_EINVAL = -1,       /* bad size, NULL pointer, bad enum value           */
+  SERQ_EALIGN = -2,       /* a device pointer is not 16-byte aligned          */
+  SERQ_EUNSUPPORTED = -3, /* valid request this build does not implement      */
+  SERQ_EHIP = -4          /* the HIP runtime reported an error at launch      */
+} serq_status;
+
+typedef enum { SERQ_F32 = 0, SERQ_BF16 = 1 } serq_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* serq_strerror(int status);
+
+/* Version of the ABI described by this header (major * 100 + minor). */
+int serq_abi_version(void);
+
+/*
+ * serq_calibrate -- offline, host memory, synchronous, deterministic.
+ *
+ * Follows the calibration phase of the pages (papernotes.org SERQ notes,
+ * 方法详解 / 整体框架: calibration fixes the scale factors, the salient rows
+ * and the permutation; 关键设计 1: SmoothQuant-style static per-channel s;
+ * 关键设计 2: salient rows identified by their scale, rows permuted in
+ * descending saliency, compensator R on the first r rows, R itself
+ * quantized; 核心 idea: R = W~_s - Q(W~_s)).
+ *
+ *   W          K x N, dtype w_dtype (SERQ_F32 or SERQ_BF16), Y = X W.
+ *   act_absmax K floats: max over the calibration tokens of |X[t, j]|.
+ *   alpha      smoothing exponent in [0, 1]:
+ *              s_j = fl32( max(a_j,1e-5)^alpha / max(w_j,1e-5)^(1-alpha) ),
+ *              a_j = act_absmax[j], w_j = max_n |W[j, n]|, evaluated in
+ *              double (for alpha = 0.5 exactly sqrt(a)/sqrt(w)).
+ *   r          number of salient rows, 0 <= r <= K, r even.
+ * Outputs (caller-allocated host buffers):
+ *   perm       K int32: perm[i] = original channel placed at position i,
+ *              descending s, equal s keep ascending channel order.
+ *   s_hat_inv  K floats: fl32(1 / s[perm[i]]), the activation multiplier
+ *              in saliency order.
+ *   Wq         N x K/2 bytes: column n of Q(W^) as packed int4 along K
+ *              (N-major), W^[i, n] = fl32(s[perm[i]] * W[perm[i], n]).
+ *   sw         N floats: per-output-channel weight scale.
+ *   Rq         N x r/2 bytes: column n of Q(R) packed along r, where
+ *              R[i, n] = fl32(W^[i, n] - fl32(Wq[n, i] * sw[n])), i < r.
+ *              May be NULL when r == 0.
+ *   sr         N floats: per-output-channel scale of R (all 0 when r == 0).
+ *              May be NULL when r == 0.
+ * Errors: SERQ_EINVAL for NULL inputs/outputs, K or N <= 0, odd K, odd r,
+ * r outside [0, K], alpha outside [0, 1], unknown w_dtype.
+ */
+int serq_calibrate(const void* W, serq_dtype w_dtype, int K, int N,
+                   const float* act_absmax, float alpha, int r,
+                   int32_t* perm, float* s_hat_inv,
+                   uint8_t* Wq, float* sw, uint8_t* Rq, float* sr);
+
+/*
+ * serq_permute_outputs -- offline, host memory, in place.
+ *
+ * Pushes the next layer's input order into this layer's output channels so
+ * that its output already arrives in that order and no layer reorders at run
+ * time (papernotes.org SERQ notes, 关键设计 3: the down projection's order P4
+ * is propagated into the gate/up weight columns; gist.science/de
+ * "Technische Zusammenfassung" 2.C).
+ *
+ *   perm_next  N int32, a permutation of 0..N-1: new output channel i is old
+ *              channel perm_next[i].
+ *   Wq (N x K/2 bytes), sw (N), Rq (N x r/2 bytes), sr (N) are reordered in
+ *   place. Rq and sr may be NULL when r == 0.
+ * Errors: SERQ_EINVAL for NULL pointers, bad sizes, or perm_next not a
+ * permutation (detected before anything is modified).
+ */
+int serq_permute_outputs(const int32_t* perm_next, int N, int K, int r,
+                         uint8_t* Wq, float* sw, uint8_t* Rq, float* sr);
+
+/*
+ * serq_quant_act -- online, device memory, asynchronous on `stream`.
+ *
+ * Per-token symmetric quantization of the flattened activations
+ * (papernotes.org SERQ notes, 方法详解 / 整体框架: the main path runs on
+ * Q(X^); output node "W4A4/W4A8"). X arrives already in saliency order
+ * (关键设计 3), so no gather is done: x^[m, k] = fl32(X[m, k] * s_hat_inv[k]),
+ * then one scale per row over all K columns.
+ *
+ *   X          M x K, dtype x_dtype (SERQ_F32 or SERQ_BF16), device.
+ *   s_hat_inv  K floats, device (from serq_calibrate).
+ *   a_bits     4 (W4A4) or 8 (W4A8).
+ *   Xq         device, M x K/2 bytes (a_bits 4, packed) or M x K int8.
+ *   sx         device, M floats: per-token scale.
+ * M == 0 is a no-op. Errors: SERQ_EINVAL (NULL pointer, M < 0, K <= 0, odd K,
+ * bad a_bits or dtype), SERQ_EALIGN (pointer not 16-byte aligned), SERQ_EHIP.
+ */
+int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
+                   const float* s_hat_inv, int a_bits,
+                   void* Xq, float* sx, void* stream);
+
+/*
+ * serq_linear -- online, device memory, asynchronous on `stream`.
+ *
+ * The SERQ linear: acc_main = Xq . Q(W^) over all K, acc_res = Xq[:, :r] . Q(R)
+ * over the r salient channels, reusing the same activation codes (no second
+ * quantization; papernotes.org SERQ notes, 关键设计 2: the residual is one
+ * (tokens x r)(r x d) product on the salient activation channels, R is
+ * quantized, no intermediate quantization), and
+ *     Y[m, n] = sx[m] * (sw[n] * acc_main[m, n] + sr[n] * acc_res[m, n])
+ * evaluated in fp32 and stored as y_dtype (bf16 with round to nearest even).
+ * Integer accumulation is exact (int32).
+ *
+ *   Xq, sx     from serq_quant_act with the same a_bits (device).
+ *   Wq, sw     N x K/2 bytes and N floats (device).
+ *   Rq, sr     N x r/2 bytes and N floats (device); may be NULL when r == 0.
+ *   M, K, N, r sizes; 0 <= r <= K, r even, K even. M == 0 is a no-op.
+ *   Y          device, M x N of y_dtype.
+ *   acc_main_dbg, acc_res_dbg
+ *              NULL on the hot path; when non-NULL, device M x N int32
+ *              buffers that receive the exact integer accumulators (both
+ *              must then be given).
+ * Errors: SERQ_EINVAL (NULL pointer, bad sizes, bad a_bits or dtype, only one
+ * debug buffer), SERQ_EALIGN (pointer not 16-byte aligned), SERQ_EHIP.
+ */
+int serq_linear(const void* Xq, const float* sx, int a_bits,
+                const uint8_t* Wq, const float* sw,
+                const uint8_t* Rq, const float* sr,
+                int M, int K, int N, int r,
+                void* Y, serq_dtype y_dtype,
+                int32_t* acc_main_dbg, int32_t* acc_res_dbg,
+                void* stream);
+
+/*
+ * serq_linear_kernel_name -- which kernel serq_linear would launch for these
+ * sizes (static string: "decode", "tile256x256", ..., "generic"), or NULL
+ * for invalid sizes. Host only; launches nothing. For profiling and tests.
+ */
+const char* serq_linear_kernel_name(int M, int K, int N, int r, int a_bits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SERQ_H_ */

@@ -78,6 +78,8 @@ def smoothing_factors(act_absmax: np.ndarray, w_rowmax: np.ndarray,
     s_j is formed in fp64 and rounded once to fp32; for alpha = 0.5 this is
     fl32(sqrt(a_j) / sqrt(w_j)). s_inv_j = fl32(1 / s_j) (one fp32 divide).
     """
+    # alpha is a binary32 parameter of the calibration call; use that value
+    alpha = float(np.float32(alpha))
     a = np.maximum(np.asarray(act_absmax, dtype=np.float32).astype(np.float64), S_FLOOR)
     w = np.maximum(np.asarray(w_rowmax, dtype=np.float32).astype(np.float64), S_FLOOR)
     if alpha == 0.5:

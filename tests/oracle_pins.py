@@ -121,7 +121,7 @@ def _exact_s(a: float, w: float, alpha: float) -> Decimal:
     w = max(Decimal(float(np.float32(w))), Decimal(1e-5))
     if alpha == 0.5:
         return a.sqrt() / w.sqrt()
-    al = Decimal(alpha)
+    al = Decimal(float(np.float32(alpha)))  # the calibration takes alpha as binary32
     return (al * a.ln()).exp() / ((1 - al) * w.ln()).exp()
 
 

@@ -1,0 +1,216 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/serq.h declares;
+* argument errors are reported before anything is launched;
+* the offline calls (serq_calibrate, serq_permute_outputs) match the oracle
+  bit for bit on packed tensors, scales and the permutation.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import w4a4_linear_layers_amd as S
+from w4a4_linear_layers_amd import _lib
+from oracle import serq_oracle as O
+from synth import make_layer, workload_layer
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "serq.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(serq_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(_lib.lib, n), n
+        assert ctypes.cast(getattr(_lib.lib, n), ctypes.c_void_p).value
+
+
+def test_strerror_and_version():
+    assert _lib.lib.serq_abi_version() == 100
+    for code in (0, -1, -2, -3, -4, 7):
+        assert _lib.lib.serq_strerror(code)
+
+
+# ---------------------------------------------------------------- argument errors
+# Only rejected calls (and M == 0 no-ops) are made here: the fake addresses
+# below are never dereferenced because validation happens first.
+
+A16 = 0x10000          # an aligned fake device address
+A_BAD = 0x10004        # a misaligned one
+
+
+def quant(X=A16, dt=_lib.SERQ_BF16, M=4, K=64, sinv=A16, bits=4, xq=A16, sx=A16):
+    return _lib.lib.serq_quant_act(X, dt, M, K, sinv, bits, xq, sx, None)
+
+
+def lin(xq=A16, sx=A16, bits=4, wq=A16, sw=A16, rq=A16, sr=A16, M=4, K=64, N=32, r=8, y=A16,
+        dt=_lib.SERQ_BF16, dm=None, dr=None):
+    return _lib.lib.serq_linear(xq, sx, bits, wq, sw, rq, sr, M, K, N, r, y, dt, dm, dr, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), _lib.SERQ_EINVAL), (dict(bits=2), _lib.SERQ_EINVAL), (dict(M=-1), _lib.SERQ_EINVAL),
+    (dict(K=0), _lib.SERQ_EINVAL), (dict(K=63), _lib.SERQ_EINVAL), (dict(X=None), _lib.SERQ_EINVAL),
+    (dict(sinv=None), _lib.SERQ_EINVAL), (dict(xq=None), _lib.SERQ_EINVAL), (dict(sx=None), _lib.SERQ_EINVAL),
+    (dict(X=A_BAD), _lib.SERQ_EALIGN), (dict(xq=A_BAD), _lib.SERQ_EALIGN), (dict(sx=A_BAD), _lib.SERQ_EALIGN),
+    (dict(M=0), _lib.SERQ_OK),
+])
+def test_quant_act_argument_errors(kw, code):
+    assert quant(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=3), _lib.SERQ_EINVAL), (dict(dt=9), _lib.SERQ_EINVAL), (dict(M=-2), _lib.SERQ_EINVAL),
+    (dict(K=0), _lib.SERQ_EINVAL), (dict(K=33), _lib.SERQ_EINVAL), (dict(N=0), _lib.SERQ_EINVAL),
+    (dict(r=-2), _lib.SERQ_EINVAL), (dict(r=7), _lib.SERQ_EINVAL), (dict(r=66), _lib.SERQ_EINVAL),
+    (dict(xq=None), _lib.SERQ_EINVAL), (dict(wq=None), _lib.SERQ_EINVAL), (dict(y=None), _lib.SERQ_EINVAL),
+    (dict(rq=None), _lib.SERQ_EINVAL), (dict(sr=None), _lib.SERQ_EINVAL),
+    (dict(dm=A16), _lib.SERQ_EINVAL), (dict(dr=A16), _lib.SERQ_EINVAL),
+    (dict(wq=A_BAD), _lib.SERQ_EALIGN), (dict(y=A_BAD), _lib.SERQ_EALIGN), (dict(sw=A_BAD), _lib.SERQ_EALIGN),
+    (dict(rq=A_BAD), _lib.SERQ_EALIGN), (dict(dm=A16, dr=A_BAD), _lib.SERQ_EALIGN),
+    (dict(M=0), _lib.SERQ_OK), (dict(M=0, r=0, rq=None, sr=None), _lib.SERQ_OK),
+])
+def test_linear_argument_errors(kw, code):
+    assert lin(**kw) == code
+
+
+def test_python_wrapper_raises():
+    with pytest.raises(S.SerqError):
+        S.calibrate(np.zeros((5, 4), np.float32), np.ones(5, np.float32), r=2)   # odd K
+    with pytest.raises(S.SerqError):
+        S.calibrate(np.zeros((4, 4), np.float32), np.ones(4, np.float32), r=6)   # r > K
+
+
+def test_calibrate_argument_errors():
+    W = np.zeros((8, 4), np.float32)
+    a = np.ones(8, np.float32)
+    out = [np.zeros(8, np.int32), np.zeros(8, np.float32), np.zeros((4, 4), np.uint8), np.zeros(4, np.float32),
+           np.zeros((4, 1), np.uint8), np.zeros(4, np.float32)]
+    p = [o.ctypes.data for o in out]
+    c = _lib.lib.serq_calibrate
+    assert c(W.ctypes.data, 0, 8, 4, a.ctypes.data, 0.5, 2, *p) == _lib.SERQ_OK
+    assert c(W.ctypes.data, 0, 8, 4, a.ctypes.data, 1.5, 2, *p) == _lib.SERQ_EINVAL
+    assert c(W.ctypes.data, 3, 8, 4, a.ctypes.data, 0.5, 2, *p) == _lib.SERQ_EINVAL
+    assert c(W.ctypes.data, 0, 8, 4, a.ctypes.data, 0.5, 3, *p) == _lib.SERQ_EINVAL
+    assert c(None, 0, 8, 4, a.ctypes.data, 0.5, 2, *p) == _lib.SERQ_EINVAL
+    assert c(W.ctypes.data, 0, 8, 4, a.ctypes.data, 0.5, 2, *p[:4], None, None) == _lib.SERQ_EINVAL
+    # an all-zero weight: every column quantizes to zero codes with scale 0
+    assert np.all(out[3] == 0) and np.all(out[2] == 0)
+
+
+# ---------------------------------------------------------------- calibration parity
+
+def assert_layer_equal(L, R, cols=None):
+    sel = slice(None) if cols is None else np.asarray(cols)
+    assert np.array_equal(L.perm, R["perm"])
+    assert np.array_equal(L.s_hat_inv.view(np.uint32), np.asarray(R["s_hat_inv"], np.float32).view(np.uint32))
+    assert np.array_equal(L.Wq[sel], R["Wq"])
+    assert np.array_equal(L.sw[sel].view(np.uint32), R["sw"].view(np.uint32))
+    assert np.array_equal(L.Rq[sel], R["Rq"])
+    assert np.array_equal(L.sr[sel].view(np.uint32), R["sr"].view(np.uint32))
+
+
+@pytest.mark.parametrize("K,N,r,dtype,alpha,seed", [
+    (256, 256, 8, "f32", 0.5, 0), (64, 40, 0, "f32", 0.5, 1), (96, 33, 96, "bf16", 0.5, 2),
+    (130, 17, 6, "bf16", 0.5, 3), (512, 64, 64, "f32", 0.3, 4), (512, 64, 128, "bf16", 0.8, 5),
+    (2, 1, 2, "f32", 0.5, 6),
+])
+def test_calibrate_matches_oracle(K, N, r, dtype, alpha, seed):
+    li = make_layer(K, N, 1, n_out=max(1, K // 100), factor=50.0, seed=seed, tag=7, dtype=dtype)
+    W = li.W_bits if dtype == "bf16" else li.W
+    L = S.calibrate(W, li.act_absmax, r=r, alpha=alpha)
+    R = O.calibrate(li.W, li.act_absmax, r=r, alpha=alpha)
+    assert_layer_equal(L, R)
+
+
+def test_calibrate_ties_and_dead_channels():
+    # equal smoothing factors (ties), dead activation channels, zero weight rows/columns
+    K, N = 64, 24
+    rng = np.random.default_rng(3)
+    W = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    W[5] = 0.0
+    W[:, 7] = 0.0
+    amax = np.ones(K, np.float32)
+    amax[[1, 9, 33]] = 0.0
+    W[[2, 3, 4]] = W[2]     # identical rows -> identical s
+    L = S.calibrate(W, amax, r=16)
+    R = O.calibrate(W, amax, r=16)
+    assert_layer_equal(L, R)
+    assert L.sw[7] == 0 and not L.Wq[7].any()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("workload,layer", [
+    ("q_proj", "q_proj"), ("mlp8b", "down"), ("l70b", "up70"), ("l70b", "down70"),
+])
+def test_calibrate_full_size_sampled_columns(workload, layer):
+    li = workload_layer(workload, layer, M_max=1, draw_x=False)
+    r = li.meta["r"]
+    L = S.calibrate(li.W_bits, li.act_absmax, r=r)
+    cols = np.random.default_rng(0).choice(li.N, 48, replace=False)
+    R = O.calibrate_columns(li.W, li.act_absmax, cols, r=r)
+    assert_layer_equal(L, R, cols)
+
+
+@pytest.mark.slow
+def test_calibrate_gate_up_shared_input():
+    """gate and up share their input, hence s and P: calibrated on [W_g | W_u]."""
+    li = workload_layer("mlp8b", "gate_up", M_max=1, draw_x=False)
+    Wcat = np.concatenate([li.W_bits, li.meta["W_up_bits"]], axis=1)
+    L = S.calibrate(Wcat, li.act_absmax, r=128)
+    Wf = np.concatenate([li.W, li.meta["W_up"]], axis=1)
+    cols = np.random.default_rng(1).choice(Wf.shape[1], 48, replace=False)
+    R = O.calibrate_columns(Wf, li.act_absmax, cols, r=128)
+    assert_layer_equal(L, R, cols)
+
+
+def test_permute_outputs_matches_oracle():
+    li = make_layer(64, 40, 1, n_out=2, factor=30.0, seed=9, tag=1, dtype="f32")
+    L = S.calibrate(li.W, li.act_absmax, r=16)
+    R = O.calibrate(li.W, li.act_absmax, r=16)
+    p = np.random.default_rng(4).permutation(40).astype(np.int32)
+    S.permute_outputs(L, p)
+    assert_layer_equal(L, O.permute_outputs(R, p))
+
+
+def test_permute_outputs_rejects_non_permutation():
+    li = make_layer(16, 8, 1, n_out=1, factor=30.0, seed=9, tag=1, dtype="f32")
+    L = S.calibrate(li.W, li.act_absmax, r=4)
+    before = L.Wq.copy()
+    with pytest.raises(S.SerqError):
+        S.permute_outputs(L, np.array([0, 1, 2, 3, 4, 5, 6, 6], np.int32))
+    with pytest.raises(S.SerqError):
+        S.permute_outputs(L, np.array([0, 1, 2, 3, 4, 5, 6, 8], np.int32))
+    assert np.array_equal(before, L.Wq)
+
+
+def test_layer_save_load_roundtrip(tmp_path):
+    li = make_layer(64, 24, 1, n_out=2, factor=30.0, seed=2, tag=1, dtype="bf16")
+    L = S.calibrate(li.W_bits, li.act_absmax, r=8)
+    L.save(str(tmp_path / "layer.npz"))
+    L2 = S.SerqLayer.load(str(tmp_path / "layer.npz"))
+    for k in ("perm", "s_hat_inv", "Wq", "sw", "Rq", "sr"):
+        assert np.array_equal(getattr(L, k), getattr(L2, k))
+
+
+def test_kernel_dispatch_rules():
+    assert S.kernel_name(1, 4096, 4096, 64) == "decode16"
+    assert S.kernel_name(16, 4096, 4096, 64) == "decode16"
+    assert S.kernel_name(32, 4096, 14336, 128) == "decode32"
+    assert S.kernel_name(4096, 4096, 14336, 128) == "tile256x256"
+    assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x256"
+    assert S.kernel_name(16, 4100, 64, 8) == "generic"      # K % 32 != 0
+    assert S.kernel_name(16, 4096, 64, 6) == "generic"      # r % 8 != 0
+    assert S.kernel_name(16, 4096, 64, 512) == "generic"    # r > 256
+    assert S.kernel_name(16, 63, 64, 8) is None

@@ -1,0 +1,289 @@
+"""GPU parity: the HIP kernels against the CPU oracle, element by element.
+
+Bit-exact: activation codes and per-token scales (serq_quant_act), the int32
+accumulators acc_main and acc_res (serq_linear's debug outputs). Within the
+tolerance derived in gpu_helpers.py: the dequantized output Y.
+
+Shapes cover every kernel the library dispatches to (decode16, decode32, the
+four macro tiles, the generic kernel), W4A4 and W4A8, fp32 and bf16, ragged M,
+N and K tails, r = 0, r not a multiple of the MFMA depth, zero rows, and the
+five layer workloads at their full sizes (checked on sampled rows/columns).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import w4a4_linear_layers_amd as S
+from gpu_helpers import bf16_tensor, check_y, dev, host, sample
+from oracle import serq_oracle as O
+from synth import random_codes, round_to_bf16_bits, workload_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------- quant_act
+
+def _act_input(M, K, dtype, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    outl = rng.choice(K, max(1, K // 100), replace=False)
+    X[:, outl] *= 50
+    if M > 2:
+        X[1] = 0.0                      # all-zero row -> scale 0, zero codes
+        X[2, :] = 0.0
+        X[2, K // 3] = -3.5             # single non-zero element
+    if M > 3:
+        X[3] = np.round(X[3] * 2) / 2   # half-integer values: rounding ties
+    sinv = (np.exp(rng.uniform(-2, 1, K))).astype(np.float32)
+    if M > 3:
+        sinv[:] = np.where(np.arange(K) % 2 == 0, sinv, np.float32(1.0))
+    if dtype == "bf16":
+        bits = round_to_bf16_bits(X).reshape(M, K)
+        Xf = (bits.astype(np.uint32) << 16).view(np.float32)
+        return Xf, bf16_tensor(bits), sinv
+    return X, dev(X), sinv
+
+
+@pytest.mark.parametrize("M,K", [(16, 256), (7, 4096), (33, 14336), (5, 28672), (9, 1000), (4, 1002),
+                                 (3, 40000), (1, 2), (64, 8)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quant_act_bit_exact(M, K, dtype, bits):
+    X, Xt, sinv = _act_input(M, K, dtype, seed=M * 7 + K)
+    xq, sx = S.quant_act(Xt, dev(sinv), a_bits=bits)
+    _sync()
+    ref = O.quant_act(X, sinv, bits)
+    assert np.array_equal(host(sx).view(np.uint32), ref["sx"].view(np.uint32))
+    got = host(xq).view(np.uint8)
+    assert np.array_equal(got, ref["packed"].view(np.uint8)), np.argwhere(got != ref["packed"].view(np.uint8))[:5]
+
+
+def test_quant_act_empty_is_noop():
+    xq = torch.full((0, 32), 7, dtype=torch.uint8, device="cuda")
+    sx = torch.empty(0, device="cuda")
+    S.quant_act(torch.empty((0, 64), device="cuda"), torch.ones(64, device="cuda"), a_bits=4, out=(xq, sx))
+    _sync()
+
+
+# ------------------------------------------------------- linear on raw codes
+
+def _codes_case(M, K, N, r, bits, seed, zero_scales=True):
+    rng = np.random.default_rng(seed)
+    Xc = random_codes(rng, (M, K), bits)
+    Wc = random_codes(rng, (K, N), 4)
+    Rc = random_codes(rng, (r, N), 4)
+    sx = rng.uniform(0.01, 2.0, M).astype(np.float32)
+    sw = rng.uniform(0.001, 0.1, N).astype(np.float32)
+    sr = rng.uniform(0.0001, 0.01, N).astype(np.float32) if r else np.zeros(N, np.float32)
+    if zero_scales and M > 1:
+        sx[M // 2] = 0.0
+    if zero_scales and N > 1:
+        sw[N // 3] = 0.0
+    Xq = O.pack_int4(Xc) if bits == 4 else Xc.view(np.uint8)
+    layer = S.DeviceLayer(K=K, N=N, r=r, perm=None, s_hat_inv=None, Wq=dev(O.pack_int4(Wc.T)), sw=dev(sw),
+                          Rq=dev(O.pack_int4(Rc.T) if r else np.zeros((N, 0), np.uint8)), sr=dev(sr))
+    return Xc, Wc, Rc, sx, sw, sr, Xq, layer
+
+
+def _run_codes(M, K, N, r, bits, out, seed, col_sample=None):
+    Xc, Wc, Rc, sx, sw, sr, Xq, layer = _codes_case(M, K, N, r, bits, seed)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    y, am, ar = S.linear(dev(Xq), dev(sx), layer, a_bits=bits, out_dtype=odt, debug=True)
+    _sync()
+    cols = np.arange(N) if col_sample is None else sample(N, col_sample, seed)
+    am_ref, ar_ref = O.linear_int(Xc, Wc[:, cols], Rc[:, cols], r)
+    am_g, ar_g = host(am)[:, cols], host(ar)[:, cols]
+    assert np.array_equal(am_g, am_ref), np.argwhere(am_g != am_ref)[:5]
+    assert np.array_equal(ar_g, ar_ref), np.argwhere(ar_g != ar_ref)[:5]
+    check_y(host(y)[:, cols], am_ref, ar_ref, sx, sw[cols], sr[cols], out)
+
+
+LINEAR_CASES = [
+    # M, K, N, r, expected kernel
+    (1, 4096, 256, 64, "decode16"),
+    (5, 1024, 100, 40, "decode16"),       # N % 16 and N % 4 ragged, r % 64 != 0
+    (16, 2080, 64, 0, "decode16"),        # K % 128 != 0, r = 0
+    (16, 512, 48, 256, "decode16"),
+    (17, 1024, 50, 24, "decode32"),
+    (32, 512, 64, 256, "decode32"),
+    (40, 1056, 130, 72, "tile64x128"),
+    (64, 96, 256, 96, "tile64x128"),      # K shorter than one k-tile, r = K
+    (100, 512, 300, 64, "tile128x128"),
+    (129, 800, 258, 8, "tile128x128"),
+    (200, 256, 32768, 64, "tile128x256"),
+    (300, 256, 32768, 128, "tile256x256"),
+    (7, 100, 30, 6, "generic"),           # K % 32 != 0, r % 8 != 0
+    (3, 384, 10, 320, "generic"),         # r > 256
+]
+
+
+@pytest.mark.parametrize("M,K,N,r,kern", LINEAR_CASES, ids=[c[4] + f"-{c[0]}x{c[1]}x{c[2]}r{c[3]}" for c in LINEAR_CASES])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_linear_codes_bit_exact(M, K, N, r, kern, bits, out):
+    assert S.kernel_name(M, K, N, r, bits) == kern
+    _run_codes(M, K, N, r, bits, out, seed=M + K + N + r + bits, col_sample=512 if N > 2048 else None)
+
+
+def test_linear_extreme_codes():
+    """All codes at the int4/int8 extremes: the largest accumulators."""
+    for bits in (4, 8):
+        M, K, N, r = 48, 4096, 64, 256
+        lo = -8 if bits == 4 else -128
+        Xc = np.full((M, K), lo, np.int8)
+        Wc = np.full((K, N), -8, np.int8)
+        Rc = np.full((r, N), -8, np.int8)
+        Xq = O.pack_int4(Xc) if bits == 4 else Xc.view(np.uint8)
+        sx = np.ones(M, np.float32)
+        sw = np.full(N, 2.0 ** -10, np.float32)
+        sr = np.full(N, 2.0 ** -12, np.float32)
+        layer = S.DeviceLayer(K=K, N=N, r=r, perm=None, s_hat_inv=None, Wq=dev(O.pack_int4(Wc.T)), sw=dev(sw),
+                              Rq=dev(O.pack_int4(Rc.T)), sr=dev(sr))
+        y, am, ar = S.linear(dev(Xq), dev(sx), layer, a_bits=bits, out_dtype=torch.float32, debug=True)
+        _sync()
+        am_ref, ar_ref = O.linear_int(Xc, Wc, Rc, r)
+        assert np.array_equal(host(am), am_ref) and np.array_equal(host(ar), ar_ref)
+        check_y(host(y), am_ref, ar_ref, sx, sw, sr, "f32")
+
+
+def test_linear_on_side_stream_and_empty():
+    Xc, Wc, Rc, sx, sw, sr, Xq, layer = _codes_case(64, 512, 96, 64, 4, seed=5)
+    s = torch.cuda.Stream()
+    xq_d, sx_d = dev(Xq), dev(sx)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y, am, ar = S.linear(xq_d, sx_d, layer, a_bits=4, out_dtype=torch.float32, debug=True)
+    s.synchronize()
+    am_ref, ar_ref = O.linear_int(Xc, Wc, Rc, 64)
+    assert np.array_equal(host(am), am_ref)
+    y0 = S.linear(xq_d[:0], sx_d[:0], layer, a_bits=4)
+    _sync()
+    assert y0.shape == (0, 96)
+
+
+# ------------------------------------------------ the layer workloads, end to end
+
+def _end_to_end(li, r, bits, out, Ms, *, row_sample=48, col_sample=192, seed=0, layer=None):
+    """Library calibration + GPU quant_act + GPU linear vs the oracle's
+    calibration, activation quantization and linear on sampled rows/columns."""
+    W_in = li.W_bits if li.dtype == "bf16" else li.W
+    L = S.calibrate(W_in, li.act_absmax, r=r) if layer is None else layer
+    D = L.to("cuda")
+    cols = sample(li.N, col_sample, seed + 1)
+    R = O.calibrate_columns(li.W, li.act_absmax, cols, r=r)
+    assert np.array_equal(L.perm, R["perm"])
+    assert np.array_equal(L.Wq[cols], R["Wq"]) and np.array_equal(L.Rq[cols], R["Rq"])
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    for M in Ms:
+        if li.dtype == "bf16":
+            xt = bf16_tensor(li.X_bits[:M][:, L.perm])
+        else:
+            xt = dev(li.X[:M][:, L.perm])
+        xq, sx = S.quant_act(xt, D, a_bits=bits)
+        y, am, ar = S.linear(xq, sx, D, a_bits=bits, out_dtype=odt, debug=True)
+        _sync()
+        rows = sample(M, row_sample, seed + M)
+        q = O.quant_act(li.X[rows][:, R["perm"]], R["s_hat_inv"], bits)
+        assert np.array_equal(host(xq)[rows].view(np.uint8), q["packed"].view(np.uint8))
+        assert np.array_equal(host(sx)[rows].view(np.uint32), q["sx"].view(np.uint32))
+        am_ref, ar_ref = O.linear_int(q["codes"], R["Wq_codes"], R["Rq_codes"], r)
+        assert np.array_equal(host(am)[np.ix_(rows, cols)], am_ref)
+        assert np.array_equal(host(ar)[np.ix_(rows, cols)], ar_ref)
+        check_y(host(y)[np.ix_(rows, cols)], am_ref, ar_ref, q["sx"], R["sw"], R["sr"], out)
+    return L
+
+
+def test_workload_tiny_full():
+    """256 -> 256, r = 8, M = 16, fp32 in and out: every output checked."""
+    li = workload_layer("tiny", "tiny")
+    _end_to_end(li, 8, 4, "f32", [16], row_sample=16, col_sample=256)
+
+
+@pytest.mark.slow
+def test_workload_q_proj():
+    li = workload_layer("q_proj", "q_proj")
+    _end_to_end(li, 64, 4, "bf16", [1, 16, 256, 2048])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", ["gate_up", "down"])
+def test_workload_mlp8b(layer):
+    li = workload_layer("mlp8b", layer)
+    _end_to_end(li, 128, 4, "bf16", [1, 32, 4096])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", ["gate_up", "down"])
+def test_workload_mlp8b_w4a8(layer):
+    li = workload_layer("mlp8b_w4a8", layer)
+    _end_to_end(li, 128, 8, "bf16", [2048])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", ["up70", "down70"])
+def test_workload_l70b(layer):
+    li = workload_layer("l70b", layer)
+    _end_to_end(li, 256, 4, "bf16", [1, 8192], row_sample=32, col_sample=128)
+
+
+@pytest.mark.slow
+def test_mlp8b_p4_propagation():
+    """The down projection's order P4 pushed into the gate/up output channels
+    (serq_permute_outputs): gate/up then produce their outputs already in P4
+    order, bit for bit the permuted outputs, and down consumes
+    h = silu(g) * u with no gather."""
+    M = 32
+    gu = workload_layer("mlp8b", "gate_up", M_max=M)
+    dn = workload_layer("mlp8b", "down", M_max=1, draw_x=False)
+    N = gu.N
+    Wcat = np.concatenate([gu.W_bits, gu.meta["W_up_bits"]], axis=1)
+    Lgu = S.calibrate(Wcat, gu.act_absmax, r=128)
+    Ld = S.calibrate(dn.W_bits, dn.act_absmax, r=128)
+    p4 = Ld.perm
+
+    def part(lo, hi):
+        return S.SerqLayer(K=Lgu.K, N=N, r=128, perm=Lgu.perm, s_hat_inv=Lgu.s_hat_inv,
+                           Wq=Lgu.Wq[lo:hi].copy(), sw=Lgu.sw[lo:hi].copy(), Rq=Lgu.Rq[lo:hi].copy(),
+                           sr=Lgu.sr[lo:hi].copy())
+
+    gate, up = part(0, N), part(N, 2 * N)
+    gate_p = S.permute_outputs(part(0, N), p4)
+    up_p = S.permute_outputs(part(N, 2 * N), p4)
+    xq, sx = S.quant_act(bf16_tensor(gu.X_bits[:, Lgu.perm]), dev(Lgu.s_hat_inv), a_bits=4)
+    outs = {}
+    for name, L in (("g", gate), ("u", up), ("gp", gate_p), ("up", up_p)):
+        outs[name] = S.linear(xq, sx, L.to("cuda"), a_bits=4, out_dtype=torch.bfloat16, debug=True)
+    _sync()
+    for a, b in (("g", "gp"), ("u", "up")):
+        y0, am0, ar0 = (host(t) for t in outs[a])
+        y1, am1, ar1 = (host(t) for t in outs[b])
+        assert np.array_equal(am1, am0[:, p4]) and np.array_equal(ar1, ar0[:, p4])
+        assert np.array_equal(y1, y0[:, p4])
+
+    def silu_mul(g_bits, u_bits):      # glue between the layers (host, not timed)
+        g = (g_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        u = (u_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return round_to_bf16_bits((g / (1.0 + np.exp(-g)) * u).astype(np.float32)).reshape(g_bits.shape)
+
+    h = silu_mul(host(outs["g"][0]), host(outs["u"][0]))
+    h_p4 = silu_mul(host(outs["gp"][0]), host(outs["up"][0]))
+    assert np.array_equal(h_p4, h[:, p4])          # arrives in P4 order, no gather needed
+    D = Ld.to("cuda")
+    xq_d, sx_d = S.quant_act(bf16_tensor(h_p4), D, a_bits=4)
+    y, am, ar = S.linear(xq_d, sx_d, D, a_bits=4, out_dtype=torch.bfloat16, debug=True)
+    _sync()
+    cols = sample(dn.N, 192, 3)
+    R = O.calibrate_columns(dn.W, dn.act_absmax, cols, r=128)
+    hf = (h.astype(np.uint32) << 16).view(np.float32)
+    q = O.quant_act(hf[:, R["perm"]], R["s_hat_inv"], 4)
+    assert np.array_equal(host(xq_d).view(np.uint8), q["packed"])
+    am_ref, ar_ref = O.linear_int(q["codes"], R["Wq_codes"], R["Rq_codes"], 128)
+    assert np.array_equal(host(am)[:, cols], am_ref) and np.array_equal(host(ar)[:, cols], ar_ref)
+    check_y(host(y)[:, cols], am_ref, ar_ref, q["sx"], R["sw"], R["sr"], "bf16")

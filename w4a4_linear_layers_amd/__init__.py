@@ -1,0 +1,194 @@
+"""SERQ quantized linear layer for AMD MI355X (gfx950).
+
+Thin Python front end of libserq (include/serq.h): argument marshalling
+only. Calibration runs in the library's host code; ``quant_act`` and
+``linear`` enqueue the library's HIP kernels on the current torch stream.
+PyTorch provides device memory and streams, nothing else.
+
+    layer = calibrate(W, act_absmax, r=64)          # offline, host
+    dev = layer.to("cuda")
+    xq, sx = quant_act(x_perm, dev)                  # x already in saliency order
+    y = linear(xq, sx, dev, out_dtype=torch.bfloat16)
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _lib
+from ._lib import SERQ_BF16, SERQ_F32, SerqError, check
+
+lib = _lib.lib
+
+__all__ = ["SerqLayer", "DeviceLayer", "calibrate", "permute_outputs", "quant_act", "linear",
+           "kernel_name", "SerqError"]
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(__import__("ctypes").c_void_p) if a is not None and a.size else None
+
+
+@dataclass
+class SerqLayer:
+    """Calibrated layer in host memory (canonical layouts of include/serq.h)."""
+
+    K: int
+    N: int
+    r: int
+    perm: np.ndarray        # K int32
+    s_hat_inv: np.ndarray   # K float32
+    Wq: np.ndarray          # N x K/2 uint8
+    sw: np.ndarray          # N float32
+    Rq: np.ndarray          # N x r/2 uint8
+    sr: np.ndarray          # N float32
+
+    def to(self, device="cuda") -> "DeviceLayer":
+        import torch
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+        return DeviceLayer(K=self.K, N=self.N, r=self.r, perm=t(self.perm), s_hat_inv=t(self.s_hat_inv),
+                           Wq=t(self.Wq), sw=t(self.sw), Rq=t(self.Rq), sr=t(self.sr))
+
+    def save(self, path: str) -> None:
+        np.savez(path, K=self.K, N=self.N, r=self.r, perm=self.perm, s_hat_inv=self.s_hat_inv,
+                 Wq=self.Wq, sw=self.sw, Rq=self.Rq, sr=self.sr)
+
+    @staticmethod
+    def load(path: str) -> "SerqLayer":
+        z = np.load(path, allow_pickle=False)
+        return SerqLayer(K=int(z["K"]), N=int(z["N"]), r=int(z["r"]), perm=z["perm"], s_hat_inv=z["s_hat_inv"],
+                         Wq=z["Wq"], sw=z["sw"], Rq=z["Rq"], sr=z["sr"])
+
+
+@dataclass
+class DeviceLayer:
+    """Calibrated layer in device memory (torch tensors)."""
+
+    K: int
+    N: int
+    r: int
+    perm: "object"
+    s_hat_inv: "object"
+    Wq: "object"
+    sw: "object"
+    Rq: "object"
+    sr: "object"
+
+
+def calibrate(W, act_absmax, *, r: int, alpha: float = 0.5, w_dtype: str | None = None) -> SerqLayer:
+    """Offline calibration (serq_calibrate). ``W`` is K x N: a float32 array,
+    a uint16 array of bf16 bit patterns (``w_dtype="bf16"``), or a CPU torch
+    tensor of dtype float32 / bfloat16."""
+    try:
+        import torch
+        if isinstance(W, torch.Tensor):
+            if W.dtype == torch.bfloat16:
+                W = W.contiguous().view(torch.int16).numpy().view(np.uint16)
+                w_dtype = "bf16"
+            else:
+                W = W.contiguous().float().numpy()
+        if isinstance(act_absmax, torch.Tensor):
+            act_absmax = act_absmax.float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    W = np.ascontiguousarray(W)
+    if w_dtype is None:
+        w_dtype = "bf16" if W.dtype == np.uint16 else "f32"
+    if w_dtype == "bf16":
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        dt = SERQ_BF16
+    else:
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        dt = SERQ_F32
+    K, N = W.shape
+    amax = np.ascontiguousarray(act_absmax, dtype=np.float32)
+    if amax.shape != (K,):
+        raise ValueError("act_absmax must have K entries")
+    perm = np.empty(K, np.int32)
+    shi = np.empty(K, np.float32)
+    Wq = np.empty((N, K // 2), np.uint8)
+    sw = np.empty(N, np.float32)
+    Rq = np.empty((N, r // 2), np.uint8)
+    sr = np.zeros(N, np.float32)
+    check("serq_calibrate", lib.serq_calibrate(_ptr(W), dt, K, N, _ptr(amax), float(alpha), r, _ptr(perm),
+                                               _ptr(shi), _ptr(Wq), _ptr(sw), _ptr(Rq) if r else None,
+                                               _ptr(sr) if r else None))
+    return SerqLayer(K=K, N=N, r=r, perm=perm, s_hat_inv=shi, Wq=Wq, sw=sw, Rq=Rq, sr=sr)
+
+
+def permute_outputs(layer: SerqLayer, perm_next) -> SerqLayer:
+    """Push the next layer's input order into this layer's output channels
+    (serq_permute_outputs), in place on the host arrays; returns ``layer``."""
+    p = np.ascontiguousarray(perm_next, dtype=np.int32)
+    check("serq_permute_outputs",
+          lib.serq_permute_outputs(_ptr(p), layer.N, layer.K, layer.r, _ptr(layer.Wq), _ptr(layer.sw),
+                                   _ptr(layer.Rq) if layer.r else None, _ptr(layer.sr) if layer.r else None))
+    return layer
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("device tensors must be contiguous CUDA tensors")
+
+
+def quant_act(x, layer_or_sinv, *, a_bits: int = 4, out=None):
+    """Per-token activation quantization (serq_quant_act) on the current
+    stream. ``x`` is M x K float32 or bfloat16, already in saliency order.
+    Returns (xq, sx): uint8 M x K/2 (a_bits 4) or int8 M x K, float32 M."""
+    import torch
+    sinv = layer_or_sinv.s_hat_inv if isinstance(layer_or_sinv, DeviceLayer) else layer_or_sinv
+    _need_cuda(x, sinv)
+    M, K = x.shape
+    if x.dtype == torch.bfloat16:
+        dt = SERQ_BF16
+    elif x.dtype == torch.float32:
+        dt = SERQ_F32
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    if out is None:
+        xq = torch.empty((M, K // 2 if a_bits == 4 else K), dtype=torch.uint8 if a_bits == 4 else torch.int8,
+                         device=x.device)
+        sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    else:
+        xq, sx = out
+    check("serq_quant_act", lib.serq_quant_act(x.data_ptr(), dt, M, K, sinv.data_ptr(), a_bits,
+                                               xq.data_ptr(), sx.data_ptr(), _stream()))
+    return xq, sx
+
+
+def linear(xq, sx, layer: DeviceLayer, *, a_bits: int = 4, out_dtype=None, out=None, debug: bool = False):
+    """The SERQ linear (serq_linear) on the current stream. Returns Y (M x N)
+    or, with ``debug=True``, (Y, acc_main, acc_res)."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    _need_cuda(xq, sx, layer.Wq, layer.sw, layer.Rq if layer.r else None, layer.sr if layer.r else None)
+    M = xq.shape[0]
+    K, N, r = layer.K, layer.N, layer.r
+    if out_dtype == torch.bfloat16:
+        dt = SERQ_BF16
+    elif out_dtype == torch.float32:
+        dt = SERQ_F32
+    else:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    am = ar = None
+    if debug:
+        am = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+        ar = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    check("serq_linear", lib.serq_linear(
+        xq.data_ptr(), sx.data_ptr(), a_bits, layer.Wq.data_ptr(), layer.sw.data_ptr(),
+        layer.Rq.data_ptr() if r else None, layer.sr.data_ptr() if r else None, M, K, N, r,
+        y.data_ptr(), dt, am.data_ptr() if debug else None, ar.data_ptr() if debug else None, _stream()))
+    return (y, am, ar) if debug else y
+
+
+def kernel_name(M: int, K: int, N: int, r: int, a_bits: int = 4) -> str | None:
+    s = lib.serq_linear_kernel_name(M, K, N, r, a_bits)
+    return s.decode() if s else None

@@ -1,0 +1,59 @@
+"""ctypes binding to libserq.so (include/serq.h).
+
+Loads the in-tree library and declares the C signatures. There is no
+fallback: if the library is missing or cannot be loaded, importing the
+package raises, so nothing can silently run on the CPU instead of the HIP
+kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SERQ_LIB", os.path.join(PKG, "libserq.so"))
+
+SERQ_OK, SERQ_EINVAL, SERQ_EALIGN, SERQ_EUNSUPPORTED, SERQ_EHIP = 0, -1, -2, -3, -4
+SERQ_F32, SERQ_BF16 = 0, 1
+
+# every symbol include/serq.h declares
+EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_permute_outputs",
+           "serq_quant_act", "serq_linear", "serq_linear_kernel_name")
+
+
+class SerqError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libserq.so not found at {LIB_PATH}; build it with "
+                          f"`python -m w4a4_linear_layers_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ip, fp, i32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int
+    lib.serq_strerror.argtypes = [ip]
+    lib.serq_strerror.restype = ctypes.c_char_p
+    lib.serq_abi_version.argtypes = []
+    lib.serq_abi_version.restype = ip
+    lib.serq_calibrate.argtypes = [vp, i32, ip, ip, vp, fp, ip, vp, vp, vp, vp, vp, vp]
+    lib.serq_calibrate.restype = ip
+    lib.serq_permute_outputs.argtypes = [vp, ip, ip, ip, vp, vp, vp, vp]
+    lib.serq_permute_outputs.restype = ip
+    lib.serq_quant_act.argtypes = [vp, i32, ip, ip, vp, ip, vp, vp, vp]
+    lib.serq_quant_act.restype = ip
+    lib.serq_linear.argtypes = [vp, vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, vp, i32, vp, vp, vp]
+    lib.serq_linear.restype = ip
+    lib.serq_linear_kernel_name.argtypes = [ip, ip, ip, ip, ip]
+    lib.serq_linear_kernel_name.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def check(fn: str, status: int) -> None:
+    if status != SERQ_OK:
+        raise SerqError(fn, status, lib.serq_strerror(status).decode())

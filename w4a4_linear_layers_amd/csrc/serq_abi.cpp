@@ -1,0 +1,86 @@
+// C ABI entry points of libserq: host-side argument validation and dispatch
+// of the online calls onto the caller's HIP stream. The offline calls
+// (serq_calibrate, serq_permute_outputs) live in calibrate.cpp.
+
+#include <hip/hip_runtime.h>
+
+#include "serq.h"
+#include "serq_internal.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool valid_sizes(int M, int K, int N, int r) {
+  return M >= 0 && K > 0 && N > 0 && (K % 2) == 0 && r >= 0 && r <= K && (r % 2) == 0;
+}
+
+}  // namespace
+
+extern "C" const char* serq_strerror(int status) {
+  switch (status) {
+    case SERQ_OK: return "SERQ_OK";
+    case SERQ_EINVAL: return "SERQ_EINVAL: invalid argument";
+    case SERQ_EALIGN: return "SERQ_EALIGN: device pointer not 16-byte aligned";
+    case SERQ_EUNSUPPORTED: return "SERQ_EUNSUPPORTED: unsupported request";
+    case SERQ_EHIP: return "SERQ_EHIP: HIP runtime error";
+    default: return "SERQ: unknown status";
+  }
+}
+
+extern "C" int serq_abi_version(void) { return 100; }
+
+extern "C" int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
+                              const float* s_hat_inv, int a_bits, void* Xq, float* sx,
+                              void* stream) {
+  if (x_dtype != SERQ_F32 && x_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (a_bits != 4 && a_bits != 8) return SERQ_EINVAL;
+  if (M < 0 || K <= 0 || (K % 2) != 0) return SERQ_EINVAL;
+  if (!X || !s_hat_inv || !Xq || !sx) return SERQ_EINVAL;
+  if (!aligned16(X) || !aligned16(s_hat_inv) || !aligned16(Xq) || !aligned16(sx)) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;
+  hipError_t e = serq::launch_quant_act(X, x_dtype == SERQ_BF16, M, K, s_hat_inv, a_bits, Xq, sx,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
+}
+
+extern "C" int serq_linear(const void* Xq, const float* sx, int a_bits, const uint8_t* Wq,
+                           const float* sw, const uint8_t* Rq, const float* sr, int M, int K, int N,
+                           int r, void* Y, serq_dtype y_dtype, int32_t* acc_main_dbg,
+                           int32_t* acc_res_dbg, void* stream) {
+  if (a_bits != 4 && a_bits != 8) return SERQ_EINVAL;
+  if (y_dtype != SERQ_F32 && y_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (!valid_sizes(M, K, N, r)) return SERQ_EINVAL;
+  if (!Xq || !sx || !Wq || !sw || !Y) return SERQ_EINVAL;
+  if (r > 0 && (!Rq || !sr)) return SERQ_EINVAL;
+  if ((acc_main_dbg == nullptr) != (acc_res_dbg == nullptr)) return SERQ_EINVAL;
+  if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y))
+    return SERQ_EALIGN;
+  if (r > 0 && (!aligned16(Rq) || !aligned16(sr))) return SERQ_EALIGN;
+  if (acc_main_dbg && (!aligned16(acc_main_dbg) || !aligned16(acc_res_dbg))) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;
+  serq::LinearArgs a{};
+  a.Xq = static_cast<const uint8_t*>(Xq);
+  a.sx = sx;
+  a.Wq = Wq;
+  a.sw = sw;
+  a.Rq = r > 0 ? Rq : nullptr;
+  a.sr = r > 0 ? sr : nullptr;
+  a.Y = Y;
+  a.dbg_main = acc_main_dbg;
+  a.dbg_res = acc_res_dbg;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.r = r;
+  a.a_bits = a_bits;
+  a.y_bf16 = y_dtype == SERQ_BF16;
+  const serq::LinearPlan plan = serq::plan_linear(M, K, N, r, a_bits);
+  hipError_t e = serq::launch_linear(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
+}
+
+extern "C" const char* serq_linear_kernel_name(int M, int K, int N, int r, int a_bits) {
+  if ((a_bits != 4 && a_bits != 8) || !valid_sizes(M, K, N, r)) return nullptr;
+  return serq::plan_linear(M, K, N, r, a_bits).name;
+}

@@ -1,0 +1,41 @@
+// Internal declarations of libserq: kernel launchers called by the C ABI
+// layer (serq_abi.cpp) and device helpers shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace serq {
+
+// Arguments of one serq_linear call (device pointers, validated sizes).
+struct LinearArgs {
+  const uint8_t* Xq;   // M x K/2 bytes (a_bits 4) or M x K int8 (a_bits 8)
+  const float* sx;     // M
+  const uint8_t* Wq;   // N x K/2 bytes
+  const float* sw;     // N
+  const uint8_t* Rq;   // N x r/2 bytes (may be null when r == 0)
+  const float* sr;     // N (may be null when r == 0)
+  void* Y;             // M x N, fp32 or bf16
+  int32_t* dbg_main;   // optional M x N int32
+  int32_t* dbg_res;    // optional M x N int32
+  int M, K, N, r;
+  int a_bits;
+  int y_bf16;
+};
+
+// Kernel families serq_linear chooses between.
+enum class LinearKernel { kDecode16, kDecode32, kTile, kGeneric };
+
+struct LinearPlan {
+  LinearKernel kind;
+  int tn, tm;          // per-wave 16x16 block counts (kTile only)
+  const char* name;
+};
+
+LinearPlan plan_linear(int M, int K, int N, int r, int a_bits);
+
+hipError_t launch_quant_act(const void* X, int x_bf16, int M, int K, const float* s_hat_inv,
+                            int a_bits, void* Xq, float* sx, hipStream_t stream);
+hipError_t launch_linear(const LinearArgs& a, const LinearPlan& plan, hipStream_t stream);
+
+}  // namespace serq
