@@ -214,3 +214,16 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(16, 4096, 64, 6) == "generic"      # r % 8 != 0
     assert S.kernel_name(16, 4096, 64, 512) == "generic"    # r > 256
     assert S.kernel_name(16, 63, 64, 8) is None
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the package before torch must not load a second HIP runtime
+    next to the one PyTorch ships (they would not share streams or memory)."""
+    import subprocess
+    import sys
+    code = ("import re, w4a4_linear_layers_amd, torch\n"
+            "m = open('/proc/self/maps').read()\n"
+            "print(len(set(re.findall(r'/\\S*libamdhip64\\S*', m))))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1", out.stdout

@@ -29,6 +29,14 @@ class SerqError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # libserq.so needs libamdhip64.so.7. PyTorch ships its own HIP runtime
+    # under that soname; if torch is imported first the library binds to that
+    # same runtime, otherwise a second runtime would be loaded next to torch's
+    # and the two would not share devices, streams or allocations.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - library use without PyTorch
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libserq.so not found at {LIB_PATH}; build it with "
                           f"`python -m w4a4_linear_layers_amd.build` (or __graft_entry__.build())")

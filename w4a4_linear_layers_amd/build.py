@@ -36,7 +36,8 @@ def hipcc() -> str:
 
 
 def common_flags() -> list[str]:
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
+            "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-command-line-argument", "-Wno-unknown-warning-option",
             "-I", INCLUDE, "-I", CSRC]
@@ -62,7 +63,7 @@ def build(verbose: bool = False, asm_dir: str | None = None) -> str:
             subprocess.run([cc] + common_flags() + lang + ["--cuda-device-only", "-S", path, "-o", out],
                            check=True)
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lpthread"]
+    cmd = [cc, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp] + objs + ["-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
