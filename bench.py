@@ -14,6 +14,10 @@ weights), resident in HBM before the timed region. The weights and
 activations are rotated through enough copies (>= 768 MiB) that every step
 reads them from HBM rather than from the 256 MB last-level cache.
 
+The K timed steps are captured once into a HIP graph (the library's kernels
+are enqueued on torch's capture stream) and replayed once between two device
+synchronizations, so the measurement is not bound by Python launch overhead.
+
 Prints one JSON line. `value` is whole-job throughput in TOP/s:
 2 * M * N * (K + r) integer operations per step / measured step time.
 """
@@ -115,29 +119,45 @@ class Setup:
         xq, sx = S.quant_act(self.xs[c][:M], L, a_bits=self.a_bits, out=(self.xq[:M], self.sx[:M]))
         S.linear(xq, sx, L, a_bits=self.a_bits, out=self.y[:M])
 
+    def graph(self, fn, n):
+        """Capture n calls fn(i) into one HIP graph (the kernels are enqueued on
+        torch's capture stream), so that replays are not bound by Python
+        launch overhead."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()            # upload + one untimed pass
+        torch.cuda.synchronize()
+        return g
+
     def time_kernels(self, M, n):
-        """Average duration of each kernel alone, n back-to-back launches
-        bracketed by events on the launch stream (the current stream)."""
+        """Average duration of each kernel alone: n back-to-back launches in
+        one graph, bracketed by events on the replay stream."""
         import torch
 
         import w4a4_linear_layers_amd as S
-        st = torch.cuda.current_stream()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for i in range(self.copies):       # make every copy's quantized input valid
-            S.quant_act(self.xs[i][:M], self.layers[i], a_bits=self.a_bits, out=(self.xq[:M], self.sx[:M]))
-        torch.cuda.synchronize()
-        ev[0].record(st)
-        for i in range(n):
-            c = i % self.copies
-            S.quant_act(self.xs[c][:M], self.layers[c], a_bits=self.a_bits, out=(self.xq[:M], self.sx[:M]))
-        ev[1].record(st)
         xq, sx = self.xq[:M], self.sx[:M]
-        ev[2].record(st)
-        for i in range(n):
+
+        def q(i):
+            c = i % self.copies
+            S.quant_act(self.xs[c][:M], self.layers[c], a_bits=self.a_bits, out=(xq, sx))
+
+        def lin(i):
             S.linear(xq, sx, self.layers[i % self.copies], a_bits=self.a_bits, out=self.y[:M])
-        ev[3].record(st)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) * 1e3 / n, ev[2].elapsed_time(ev[3]) * 1e3 / n
+
+        out = []
+        for fn in (q, lin):
+            g = self.graph(fn, n)
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            g.replay()
+            e1.record(st)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / n)
+        return tuple(out)
 
 
 def cpu_baseline(setup, M, rows=None, budget_s=20.0):
@@ -224,9 +244,11 @@ def main(argv=None):
     for i in range(args.warmup):
         setup.step(i, M)
     torch.cuda.synchronize()
+    # the K timed steps are captured once as a HIP graph and replayed once
+    g = setup.graph(lambda i: setup.step(i, M), args.steps)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        setup.step(i, M)
+    g.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps

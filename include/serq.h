@@ -131,8 +131,9 @@ int serq_permute_outputs(const int32_t* perm_next, int N, int K, int r,
  *   a_bits     4 (W4A4) or 8 (W4A8).
  *   Xq         device, M x K/2 bytes (a_bits 4, packed) or M x K int8.
  *   sx         device, M floats: per-token scale.
- * M == 0 is a no-op. Errors: SERQ_EINVAL (NULL pointer, M < 0, K <= 0, odd K,
- * bad a_bits or dtype), SERQ_EALIGN (pointer not 16-byte aligned), SERQ_EHIP.
+ * M == 0 is a no-op; X, Xq and sx may then be NULL. Errors: SERQ_EINVAL
+ * (NULL pointer, M < 0, K <= 0, odd K, bad a_bits or dtype), SERQ_EALIGN
+ * (pointer not 16-byte aligned), SERQ_EHIP.
  */
 int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
                    const float* s_hat_inv, int a_bits,
@@ -153,7 +154,9 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
  *   Xq, sx     from serq_quant_act with the same a_bits (device).
  *   Wq, sw     N x K/2 bytes and N floats (device).
  *   Rq, sr     N x r/2 bytes and N floats (device); may be NULL when r == 0.
- *   M, K, N, r sizes; 0 <= r <= K, r even, K even. M == 0 is a no-op.
+ *   M, K, N, r sizes; 0 <= r <= K, r even, K even. M == 0 is a no-op (the
+ *              M-sized buffers Xq, sx, Y and the debug buffers may then be
+ *              NULL; the weights are still validated).
  *   Y          device, M x N of y_dtype.
  *   acc_main_dbg, acc_res_dbg
  *              NULL on the hot path; when non-NULL, device M x N int32

@@ -64,7 +64,8 @@ def lin(xq=A16, sx=A16, bits=4, wq=A16, sw=A16, rq=A16, sr=A16, M=4, K=64, N=32,
     (dict(K=0), _lib.SERQ_EINVAL), (dict(K=63), _lib.SERQ_EINVAL), (dict(X=None), _lib.SERQ_EINVAL),
     (dict(sinv=None), _lib.SERQ_EINVAL), (dict(xq=None), _lib.SERQ_EINVAL), (dict(sx=None), _lib.SERQ_EINVAL),
     (dict(X=A_BAD), _lib.SERQ_EALIGN), (dict(xq=A_BAD), _lib.SERQ_EALIGN), (dict(sx=A_BAD), _lib.SERQ_EALIGN),
-    (dict(M=0), _lib.SERQ_OK),
+    (dict(M=0), _lib.SERQ_OK), (dict(M=0, X=None, xq=None, sx=None), _lib.SERQ_OK),
+    (dict(M=0, sinv=None), _lib.SERQ_EINVAL),
 ])
 def test_quant_act_argument_errors(kw, code):
     assert quant(**kw) == code
@@ -80,6 +81,7 @@ def test_quant_act_argument_errors(kw, code):
     (dict(wq=A_BAD), _lib.SERQ_EALIGN), (dict(y=A_BAD), _lib.SERQ_EALIGN), (dict(sw=A_BAD), _lib.SERQ_EALIGN),
     (dict(rq=A_BAD), _lib.SERQ_EALIGN), (dict(dm=A16, dr=A_BAD), _lib.SERQ_EALIGN),
     (dict(M=0), _lib.SERQ_OK), (dict(M=0, r=0, rq=None, sr=None), _lib.SERQ_OK),
+    (dict(M=0, xq=None, sx=None, y=None), _lib.SERQ_OK), (dict(M=0, wq=None), _lib.SERQ_EINVAL),
 ])
 def test_linear_argument_errors(kw, code):
     assert lin(**kw) == code

@@ -36,9 +36,11 @@ extern "C" int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
   if (x_dtype != SERQ_F32 && x_dtype != SERQ_BF16) return SERQ_EINVAL;
   if (a_bits != 4 && a_bits != 8) return SERQ_EINVAL;
   if (M < 0 || K <= 0 || (K % 2) != 0) return SERQ_EINVAL;
-  if (!X || !s_hat_inv || !Xq || !sx) return SERQ_EINVAL;
-  if (!aligned16(X) || !aligned16(s_hat_inv) || !aligned16(Xq) || !aligned16(sx)) return SERQ_EALIGN;
-  if (M == 0) return SERQ_OK;
+  if (!s_hat_inv) return SERQ_EINVAL;
+  if (!aligned16(s_hat_inv)) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;  // the M-sized buffers may then be empty (NULL)
+  if (!X || !Xq || !sx) return SERQ_EINVAL;
+  if (!aligned16(X) || !aligned16(Xq) || !aligned16(sx)) return SERQ_EALIGN;
   hipError_t e = serq::launch_quant_act(X, x_dtype == SERQ_BF16, M, K, s_hat_inv, a_bits, Xq, sx,
                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
@@ -51,14 +53,15 @@ extern "C" int serq_linear(const void* Xq, const float* sx, int a_bits, const ui
   if (a_bits != 4 && a_bits != 8) return SERQ_EINVAL;
   if (y_dtype != SERQ_F32 && y_dtype != SERQ_BF16) return SERQ_EINVAL;
   if (!valid_sizes(M, K, N, r)) return SERQ_EINVAL;
-  if (!Xq || !sx || !Wq || !sw || !Y) return SERQ_EINVAL;
+  if (!Wq || !sw) return SERQ_EINVAL;
   if (r > 0 && (!Rq || !sr)) return SERQ_EINVAL;
   if ((acc_main_dbg == nullptr) != (acc_res_dbg == nullptr)) return SERQ_EINVAL;
-  if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Wq) || !aligned16(sw) || !aligned16(Y))
-    return SERQ_EALIGN;
+  if (!aligned16(Wq) || !aligned16(sw)) return SERQ_EALIGN;
   if (r > 0 && (!aligned16(Rq) || !aligned16(sr))) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;  // the M-sized buffers may then be empty (NULL)
+  if (!Xq || !sx || !Y) return SERQ_EINVAL;
+  if (!aligned16(Xq) || !aligned16(sx) || !aligned16(Y)) return SERQ_EALIGN;
   if (acc_main_dbg && (!aligned16(acc_main_dbg) || !aligned16(acc_res_dbg))) return SERQ_EALIGN;
-  if (M == 0) return SERQ_OK;
   serq::LinearArgs a{};
   a.Xq = static_cast<const uint8_t*>(Xq);
   a.sx = sx;
