@@ -210,8 +210,8 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(1, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(16, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(32, 4096, 14336, 128) == "decode32"
-    assert S.kernel_name(4096, 4096, 14336, 128) == "tile256x256"
-    assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x256"
+    assert S.kernel_name(4096, 4096, 14336, 128) == "tile128x128"
+    assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x128"
     assert S.kernel_name(16, 4100, 64, 8) == "generic"      # K % 32 != 0
     assert S.kernel_name(16, 4096, 64, 6) == "generic"      # r % 8 != 0
     assert S.kernel_name(16, 4096, 64, 512) == "generic"    # r > 256

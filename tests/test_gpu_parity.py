@@ -117,8 +117,8 @@ LINEAR_CASES = [
     (64, 96, 256, 96, "tile64x128"),      # K shorter than one k-tile, r = K
     (100, 512, 300, 64, "tile128x128"),
     (129, 800, 258, 8, "tile128x128"),
-    (200, 256, 32768, 64, "tile128x256"),
-    (300, 256, 32768, 128, "tile256x256"),
+    (200, 256, 32768, 64, "tile128x128"),     # many workgroups
+    (300, 288, 32768, 128, "tile128x128"),    # K not a multiple of the k-tile
     (7, 100, 30, 6, "generic"),           # K % 32 != 0, r % 8 != 0
     (3, 384, 10, 320, "generic"),         # r > 256
 ]

@@ -28,7 +28,7 @@ enum class LinearKernel { kDecode16, kDecode32, kTile, kGeneric };
 
 struct LinearPlan {
   LinearKernel kind;
-  int tn, tm;          // per-wave 16x16 block counts (kTile only)
+  int tn, tm;          // per-wave 32x32 block counts (kTile only)
   const char* name;
 };
 
