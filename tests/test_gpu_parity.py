@@ -51,7 +51,7 @@ def _act_input(M, K, dtype, seed):
     return X, dev(X), sinv
 
 
-@pytest.mark.parametrize("M,K", [(16, 256), (7, 4096), (33, 14336), (5, 28672), (9, 1000), (4, 1002),
+@pytest.mark.parametrize("M,K", [(16, 256), (7, 4096), (33, 14336), (5, 28672), (9, 1000), (4, 1002), (11, 8192), (6, 2048),
                                  (3, 40000), (1, 2), (64, 8)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bits", [4, 8])

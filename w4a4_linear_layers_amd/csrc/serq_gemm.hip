@@ -540,61 +540,129 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 32): the packed weights are streamed from HBM exactly
 // once. A workgroup owns 16 output channels; its four waves take interleaved
-// 128-code chunks of K, so together they read 256 contiguous bytes of each
-// weight row per step. Activations (a few KB) come through L2. The residual
-// chunks are spread over the waves the same way, then the partial int32
-// accumulators are summed through LDS and wave 0 runs the epilogue.
+// 256-code chunks of K (128 bytes of each of the 16 weight rows), with two
+// register groups of chunks in flight per wave. Activations (a few KB) come
+// through L2. One wave also takes the residual (r <= 256 codes: one chunk),
+// then the partial int32 accumulators are summed through LDS and wave 0 runs
+// the epilogue.
 // ---------------------------------------------------------------------------
 
 template <int MG, int A_BITS>
 __global__ __launch_bounds__(kThreads) void serq_decode_kernel(LinearArgs a) {
   constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
-  constexpr int XCB = kKTileCodes * A_BITS / 8;       // activation bytes per chunk
-  constexpr int UNROLL = 4;
+  constexpr int CC = 256;                             // codes per chunk
+  constexpr int CWB = CC / 2;                         // weight bytes per row and chunk
+  constexpr int CXB = CC * A_BITS / 8;                // activation bytes per row and chunk
+  constexpr int LW = CWB / 4 / 16;                    // 16-byte weight loads per lane and chunk (2)
+  constexpr int LX = CXB / 4 / 16;                    // 16-byte activation loads per lane and chunk
+  constexpr int U = MG * LX <= 2 ? 2 : 1;             // chunks per register group
+  static_assert(kMaxResidual <= CC, "the residual fits in one chunk");
   __shared__ v4i red[2][kThreads / 64 - 1][MG][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int Kb = a.K / 2, Xrow = a.K * A_BITS / 8;
-  const uint8_t* wp = a.Wq + static_cast<size_t>(min(n0 + l16, a.N - 1)) * Kb + g * 16;
+  const int nrow = min(n0 + l16, a.N - 1);
+  // Lane (row l16, group g) holds codes [CC c + 64 g, CC c + 64 g + 64) of
+  // chunk c for both operands: 32 contiguous weight bytes, so the four lanes
+  // of a row cover its whole 128-byte chunk.
+  const uint8_t* wp = a.Wq + static_cast<size_t>(nrow) * Kb + g * (CWB / 4);
   const uint8_t* xp[MG];
   bool xv[MG];
 #pragma unroll
   for (int j = 0; j < MG; ++j) {
     const int m = j * 16 + l16;
     xv[j] = m < a.M;
-    xp[j] = a.Xq + static_cast<size_t>(min(m, a.M - 1)) * Xrow + g * (XCB / 4);
+    xp[j] = a.Xq + static_cast<size_t>(min(m, a.M - 1)) * Xrow + g * (CXB / 4);
   }
-  const int nchunks = (Kb + kKTileW - 1) / kKTileW;
-  // epilogue scales, loaded before the K loop so their latency is hidden
+  const int nchunks = (a.K + CC - 1) / CC;
+
+  // Everything but the streamed weights is loaded up front so that its
+  // latency overlaps the K loop: the epilogue scales and, in wave 1, the
+  // (at most one chunk of) Q(R) and salient activation codes.
   float sxv[MG];
 #pragma unroll
   for (int j = 0; j < MG; ++j) sxv[j] = a.sx[min(j * 16 + l16, a.M - 1)];
   const float4 sw4 = load_scales4(a.sw, n0 + 4 * g, a.N);
   const float4 sr4 = a.r > 0 ? load_scales4(a.sr, n0 + 4 * g, a.N) : make_float4(0.f, 0.f, 0.f, 0.f);
-
-  auto chunk = [&](int c, v4i (&acc)[MG], const uint8_t* wbase, int wlimit, int xlimit) {
-    const int wo = c * kKTileW + g * 16;
-    const uint4 w = wo < wlimit ? *reinterpret_cast<const uint4*>(wbase + c * kKTileW)
-                                : make_uint4(0, 0, 0, 0);
-    const v4i w0 = widen16(w.x, w.y), w1 = widen16(w.z, w.w);
+  const int r = a.r;
+  const int rb = r / 2;                                 // packed residual bytes per row
+  constexpr int kResWave = 1;
+  uint4 rw[LW];
+  uint4 rx[MG][LX];
+#pragma unroll
+  for (int l = 0; l < LW; ++l) rw[l] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < MG; ++j)
+#pragma unroll
+    for (int l = 0; l < LX; ++l) rx[j][l] = make_uint4(0, 0, 0, 0);
+  if (r > 0 && wave == kResWave) {
+    const uint8_t* rrow = a.Rq + static_cast<size_t>(nrow) * rb;
+#pragma unroll
+    for (int l = 0; l < LW; ++l) {
+      const int wo = g * (CWB / 4) + 16 * l;
+      rw[l] = make_uint4(load_dword_masked(rrow, wo, rb), load_dword_masked(rrow, wo + 4, rb),
+                         load_dword_masked(rrow, wo + 8, rb), load_dword_masked(rrow, wo + 12, rb));
+    }
+    const int xlim = r * A_BITS / 8;
 #pragma unroll
     for (int j = 0; j < MG; ++j) {
-      const int xo = c * XCB + g * (XCB / 4);
-      if constexpr (A_BITS == 4) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (xv[j] && xo < xlimit) x = *reinterpret_cast<const uint4*>(xp[j] + c * XCB);
-        acc[j] = mfma(w0, widen16(x.x, x.y), acc[j]);
-        acc[j] = mfma(w1, widen16(x.z, x.w), acc[j]);
-      } else {
-        uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-        if (xv[j] && xo < xlimit) {
-          x0 = *reinterpret_cast<const uint4*>(xp[j] + c * XCB);
-          x1 = *reinterpret_cast<const uint4*>(xp[j] + c * XCB + 16);
+      if (!xv[j]) continue;
+      const uint8_t* xrow = xp[j] - g * (CXB / 4);
+#pragma unroll
+      for (int l = 0; l < LX; ++l) {
+        const int xo = g * (CXB / 4) + 16 * l;
+        rx[j][l] = make_uint4(load_dword_masked(xrow, xo, xlim), load_dword_masked(xrow, xo + 4, xlim),
+                              load_dword_masked(xrow, xo + 8, xlim), load_dword_masked(xrow, xo + 12, xlim));
+      }
+    }
+  }
+
+  // The K loop streams groups of U chunks per wave (chunk c = wave + 4 u);
+  // the loads of the next group are issued into a second register buffer
+  // before the current group is consumed.
+  struct Group {
+    uint4 w[U][LW];
+    uint4 x[U][MG][LX];
+  };
+  auto load_group = [&](int c0, Group& gr) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+#pragma unroll
+      for (int l = 0; l < LW; ++l) {
+        const int o = c * CWB + g * (CWB / 4) + 16 * l;
+        gr.w[u][l] = (c < nchunks && o < Kb) ? *reinterpret_cast<const uint4*>(wp + c * CWB + 16 * l)
+                                             : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < MG; ++j)
+#pragma unroll
+        for (int l = 0; l < LX; ++l) {
+          const int o = c * CXB + g * (CXB / 4) + 16 * l;
+          gr.x[u][j][l] = (c < nchunks && xv[j] && o < Xrow)
+                              ? *reinterpret_cast<const uint4*>(xp[j] + c * CXB + 16 * l)
+                              : make_uint4(0, 0, 0, 0);
         }
-        acc[j] = mfma(w0, split16(x0), acc[j]);
-        acc[j] = mfma(w1, split16(x1), acc[j]);
+    }
+  };
+  // One chunk: four MFMA steps of 16 codes per lane.
+  auto dot_chunk = [&](const uint4 (&w)[LW], const uint4 (&x)[MG][LX], v4i (&acc)[MG]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 ww = w[s >> 1];
+      const v4i wa = (s & 1) ? widen16(ww.z, ww.w) : widen16(ww.x, ww.y);
+#pragma unroll
+      for (int j = 0; j < MG; ++j) {
+        v4i xb;
+        if constexpr (A_BITS == 4) {
+          const uint4 xx = x[j][s >> 1];
+          xb = (s & 1) ? widen16(xx.z, xx.w) : widen16(xx.x, xx.y);
+        } else {
+          xb = split16(x[j][s]);
+        }
+        acc[j] = mfma(wa, xb, acc[j]);
       }
     }
   };
@@ -602,63 +670,24 @@ __global__ __launch_bounds__(kThreads) void serq_decode_kernel(LinearArgs a) {
   v4i acc[MG];
 #pragma unroll
   for (int j = 0; j < MG; ++j) acc[j] = v4i{0, 0, 0, 0};
-  int c = wave;
-  for (; c + 4 * (UNROLL - 1) < nchunks; c += 4 * UNROLL) {
+  {
+    Group g0, g1;
+    int c0 = wave;
+    load_group(c0, g0);
+    for (; c0 < nchunks; c0 += 8 * U) {
+      if (c0 + 4 * U < nchunks) load_group(c0 + 4 * U, g1);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) chunk(c + 4 * u, acc, wp, Kb, Xrow);
+      for (int u = 0; u < U; ++u) dot_chunk(g0.w[u], g0.x[u], acc);
+      if (c0 + 4 * U >= nchunks) break;
+      if (c0 + 8 * U < nchunks) load_group(c0 + 8 * U, g0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) dot_chunk(g1.w[u], g1.x[u], acc);
+    }
   }
-  for (; c < nchunks; c += 4) chunk(c, acc, wp, Kb, Xrow);
-
-  // residual: r codes against Q(R), chunks of 128 codes spread over the waves
   v4i accr[MG];
 #pragma unroll
   for (int j = 0; j < MG; ++j) accr[j] = v4i{0, 0, 0, 0};
-  const int r = a.r;
-  if (r > 0) {
-    const int rb = r / 2;
-    const uint8_t* rrow = a.Rq + static_cast<size_t>(min(n0 + l16, a.N - 1)) * rb;
-    const int rchunks = (rb + kKTileW - 1) / kKTileW;
-    const int xlim = r * A_BITS / 8;
-    for (int cr = wave; cr < rchunks; cr += 4) {
-      const int wo = cr * kKTileW + g * 16;
-      uint4 w;
-      w.x = load_dword_masked(rrow, wo, rb);
-      w.y = load_dword_masked(rrow, wo + 4, rb);
-      w.z = load_dword_masked(rrow, wo + 8, rb);
-      w.w = load_dword_masked(rrow, wo + 12, rb);
-      const v4i w0 = widen16(w.x, w.y), w1 = widen16(w.z, w.w);
-#pragma unroll
-      for (int j = 0; j < MG; ++j) {
-        const uint8_t* xrow = xp[j] - g * (XCB / 4);
-        const int xo = cr * XCB + g * (XCB / 4);
-        if constexpr (A_BITS == 4) {
-          uint4 x = make_uint4(0, 0, 0, 0);
-          if (xv[j]) {
-            x.x = load_dword_masked(xrow, xo, xlim);
-            x.y = load_dword_masked(xrow, xo + 4, xlim);
-            x.z = load_dword_masked(xrow, xo + 8, xlim);
-            x.w = load_dword_masked(xrow, xo + 12, xlim);
-          }
-          accr[j] = mfma(w0, widen16(x.x, x.y), accr[j]);
-          accr[j] = mfma(w1, widen16(x.z, x.w), accr[j]);
-        } else {
-          uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-          if (xv[j]) {
-            x0.x = load_dword_masked(xrow, xo, xlim);
-            x0.y = load_dword_masked(xrow, xo + 4, xlim);
-            x0.z = load_dword_masked(xrow, xo + 8, xlim);
-            x0.w = load_dword_masked(xrow, xo + 12, xlim);
-            x1.x = load_dword_masked(xrow, xo + 16, xlim);
-            x1.y = load_dword_masked(xrow, xo + 20, xlim);
-            x1.z = load_dword_masked(xrow, xo + 24, xlim);
-            x1.w = load_dword_masked(xrow, xo + 28, xlim);
-          }
-          accr[j] = mfma(w0, split16(x0), accr[j]);
-          accr[j] = mfma(w1, split16(x1), accr[j]);
-        }
-      }
-    }
-  }
+  if (r > 0 && wave == kResWave) dot_chunk(rw, rx, accr);
 
   // cross-wave reduction through LDS
   if (wave > 0) {
