@@ -214,6 +214,20 @@ def load_traffic(workload, M):
     return t.get("bytes_per_launch")
 
 
+def copy_probe(mib, reps=10):
+    """Device-to-device copies of a known size: a reference for the HBM
+    byte counters (each copy reads and writes mib MiB)."""
+    import torch
+    torch.cuda.set_device(0)
+    a = torch.ones(mib << 19, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": mib << 20, "copies": reps}))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,7 +237,12 @@ def main(argv=None):
     ap.add_argument("--M", type=int, default=None, help="tokens per step (default: the workload's)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (a reference kernel of known "
+                         "traffic for scaling HBM byte counters), then exit")
     args = ap.parse_args(argv)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path)", file=sys.stderr)
