@@ -170,7 +170,7 @@ def cpu_baseline(setup, M, rows=None, budget_s=20.0):
     li, L = setup.li, setup.L
     K, N, r = setup.K, setup.N, setup.r
     Wc = O.unpack_int4(L.Wq).T.copy()
-    Rc = O.unpack_int4(L.Rq).T.copy() if r else np.zeros((0, N), np.int8)
+    Rc = O.unpack_int4(np.ascontiguousarray(L.Rq[:, : r // 2])).T.copy() if r else np.zeros((0, N), np.int8)
     layer = dict(r=r, Wq_codes=Wc, Rq_codes=Rc, sw=L.sw, sr=L.sr)
     n = 8 if rows is None else rows
     X = li.X[:, L.perm]

@@ -60,6 +60,14 @@ const char* serq_strerror(int status);
 /* Version of the ABI described by this header (major * 100 + minor). */
 int serq_abi_version(void);
 
+/* Bytes per row of the packed Q(R) buffer for r salient rows: r codes
+ * padded with zero codes to a multiple of 32 (16 bytes). */
+#define SERQ_RQ_ROW_BYTES(r) ((((r) + 31) / 32) * 16)
+
+/* SERQ_RQ_ROW_BYTES as a function (for bindings that cannot use macros);
+ * returns -1 for r < 0. */
+int serq_rq_row_bytes(int r);
+
 /*
  * serq_calibrate -- offline, host memory, synchronous, deterministic.
  *
@@ -85,8 +93,10 @@ int serq_abi_version(void);
  *   Wq         N x K/2 bytes: column n of Q(W^) as packed int4 along K
  *              (N-major), W^[i, n] = fl32(s[perm[i]] * W[perm[i], n]).
  *   sw         N floats: per-output-channel weight scale.
- *   Rq         N x r/2 bytes: column n of Q(R) packed along r, where
- *              R[i, n] = fl32(W^[i, n] - fl32(Wq[n, i] * sw[n])), i < r.
+ *   Rq         N x SERQ_RQ_ROW_BYTES(r) bytes: column n of Q(R) packed
+ *              along r, where R[i, n] = fl32(W^[i, n] - fl32(Wq[n, i] * sw[n])),
+ *              i < r; each row is padded with zero codes to a multiple of 32
+ *              codes (16 bytes), so rows stay 16-byte aligned.
  *              May be NULL when r == 0.
  *   sr         N floats: per-output-channel scale of R (all 0 when r == 0).
  *              May be NULL when r == 0.
@@ -109,7 +119,7 @@ int serq_calibrate(const void* W, serq_dtype w_dtype, int K, int N,
  *
  *   perm_next  N int32, a permutation of 0..N-1: new output channel i is old
  *              channel perm_next[i].
- *   Wq (N x K/2 bytes), sw (N), Rq (N x r/2 bytes), sr (N) are reordered in
+ *   Wq (N x K/2 bytes), sw (N), Rq (N x SERQ_RQ_ROW_BYTES(r)), sr (N) are reordered in
  *   place. Rq and sr may be NULL when r == 0.
  * Errors: SERQ_EINVAL for NULL pointers, bad sizes, or perm_next not a
  * permutation (detected before anything is modified).
@@ -153,7 +163,9 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
  *
  *   Xq, sx     from serq_quant_act with the same a_bits (device).
  *   Wq, sw     N x K/2 bytes and N floats (device).
- *   Rq, sr     N x r/2 bytes and N floats (device); may be NULL when r == 0.
+ *   Rq, sr     N x SERQ_RQ_ROW_BYTES(r) bytes (the layout serq_calibrate
+ *              writes, zero codes in the padding) and N floats (device);
+ *              may be NULL when r == 0.
  *   M, K, N, r sizes; 0 <= r <= K, r even, K even. M == 0 is a no-op (the
  *              M-sized buffers Xq, sx, Y and the debug buffers may then be
  *              NULL; the weights are still validated).

@@ -15,6 +15,7 @@ import pytest
 
 import w4a4_linear_layers_amd as S
 from w4a4_linear_layers_amd import _lib
+from layouts import pad_rq, rq_row_bytes
 from oracle import serq_oracle as O
 from synth import make_layer, workload_layer
 
@@ -37,9 +38,20 @@ def test_header_declarations_are_exported():
 
 
 def test_strerror_and_version():
-    assert _lib.lib.serq_abi_version() == 100
+    assert _lib.lib.serq_abi_version() == 200
     for code in (0, -1, -2, -3, -4, 7):
         assert _lib.lib.serq_strerror(code)
+
+
+def test_rq_row_bytes():
+    """Q(R) rows are padded to 32 codes (16 bytes); calibration writes zero
+    codes into the padding."""
+    assert _lib.lib.serq_rq_row_bytes(-2) == -1
+    for r in range(0, 300, 2):
+        assert _lib.lib.serq_rq_row_bytes(r) == rq_row_bytes(r) == S.rq_row_bytes(r)
+    li = make_layer(96, 40, 1, n_out=2, factor=20.0, seed=3, tag=7)
+    L = S.calibrate(li.W, li.act_absmax, r=10)
+    assert L.Rq.shape == (40, 16) and not L.Rq[:, 5:].any() and L.Rq[:, :5].any()
 
 
 # ---------------------------------------------------------------- argument errors
@@ -98,7 +110,7 @@ def test_calibrate_argument_errors():
     W = np.zeros((8, 4), np.float32)
     a = np.ones(8, np.float32)
     out = [np.zeros(8, np.int32), np.zeros(8, np.float32), np.zeros((4, 4), np.uint8), np.zeros(4, np.float32),
-           np.zeros((4, 1), np.uint8), np.zeros(4, np.float32)]
+           np.zeros((4, rq_row_bytes(2)), np.uint8), np.zeros(4, np.float32)]
     p = [o.ctypes.data for o in out]
     c = _lib.lib.serq_calibrate
     assert c(W.ctypes.data, 0, 8, 4, a.ctypes.data, 0.5, 2, *p) == _lib.SERQ_OK
@@ -119,7 +131,7 @@ def assert_layer_equal(L, R, cols=None):
     assert np.array_equal(L.s_hat_inv.view(np.uint32), np.asarray(R["s_hat_inv"], np.float32).view(np.uint32))
     assert np.array_equal(L.Wq[sel], R["Wq"])
     assert np.array_equal(L.sw[sel].view(np.uint32), R["sw"].view(np.uint32))
-    assert np.array_equal(L.Rq[sel], R["Rq"])
+    assert np.array_equal(L.Rq[sel], pad_rq(R["Rq"], L.r))
     assert np.array_equal(L.sr[sel].view(np.uint32), R["sr"].view(np.uint32))
 
 

@@ -18,6 +18,7 @@ import torch
 
 import w4a4_linear_layers_amd as S
 from gpu_helpers import bf16_tensor, check_y, dev, host, sample
+from layouts import pack_rq, pad_rq
 from oracle import serq_oracle as O
 from synth import random_codes, round_to_bf16_bits, workload_layer
 
@@ -88,7 +89,7 @@ def _codes_case(M, K, N, r, bits, seed, zero_scales=True):
         sw[N // 3] = 0.0
     Xq = O.pack_int4(Xc) if bits == 4 else Xc.view(np.uint8)
     layer = S.DeviceLayer(K=K, N=N, r=r, perm=None, s_hat_inv=None, Wq=dev(O.pack_int4(Wc.T)), sw=dev(sw),
-                          Rq=dev(O.pack_int4(Rc.T) if r else np.zeros((N, 0), np.uint8)), sr=dev(sr))
+                          Rq=dev(pack_rq(Rc)), sr=dev(sr))
     return Xc, Wc, Rc, sx, sw, sr, Xq, layer
 
 
@@ -145,7 +146,7 @@ def test_linear_extreme_codes():
         sw = np.full(N, 2.0 ** -10, np.float32)
         sr = np.full(N, 2.0 ** -12, np.float32)
         layer = S.DeviceLayer(K=K, N=N, r=r, perm=None, s_hat_inv=None, Wq=dev(O.pack_int4(Wc.T)), sw=dev(sw),
-                              Rq=dev(O.pack_int4(Rc.T)), sr=dev(sr))
+                              Rq=dev(pack_rq(Rc)), sr=dev(sr))
         y, am, ar = S.linear(dev(Xq), dev(sx), layer, a_bits=bits, out_dtype=torch.float32, debug=True)
         _sync()
         am_ref, ar_ref = O.linear_int(Xc, Wc, Rc, r)
@@ -179,7 +180,7 @@ def _end_to_end(li, r, bits, out, Ms, *, row_sample=48, col_sample=192, seed=0, 
     cols = sample(li.N, col_sample, seed + 1)
     R = O.calibrate_columns(li.W, li.act_absmax, cols, r=r)
     assert np.array_equal(L.perm, R["perm"])
-    assert np.array_equal(L.Wq[cols], R["Wq"]) and np.array_equal(L.Rq[cols], R["Rq"])
+    assert np.array_equal(L.Wq[cols], R["Wq"]) and np.array_equal(L.Rq[cols], pad_rq(R["Rq"], r))
     odt = torch.float32 if out == "f32" else torch.bfloat16
     for M in Ms:
         if li.dtype == "bf16":

@@ -23,7 +23,7 @@ from ._lib import SERQ_BF16, SERQ_F32, SerqError, check
 lib = _lib.lib
 
 __all__ = ["SerqLayer", "DeviceLayer", "calibrate", "permute_outputs", "quant_act", "linear",
-           "kernel_name", "SerqError"]
+           "kernel_name", "rq_row_bytes", "SerqError"]
 
 
 def _ptr(a: np.ndarray):
@@ -41,7 +41,7 @@ class SerqLayer:
     s_hat_inv: np.ndarray   # K float32
     Wq: np.ndarray          # N x K/2 uint8
     sw: np.ndarray          # N float32
-    Rq: np.ndarray          # N x r/2 uint8
+    Rq: np.ndarray          # N x rq_row_bytes(r) uint8 (zero codes past r)
     sr: np.ndarray          # N float32
 
     def to(self, device="cuda") -> "DeviceLayer":
@@ -74,6 +74,15 @@ class DeviceLayer:
     sw: "object"
     Rq: "object"
     sr: "object"
+
+
+def rq_row_bytes(r: int) -> int:
+    """Bytes per row of the packed Q(R) buffer (serq_rq_row_bytes): r codes
+    padded with zero codes to a multiple of 32."""
+    b = lib.serq_rq_row_bytes(int(r))
+    if b < 0:
+        raise ValueError("r must be >= 0")
+    return b
 
 
 def calibrate(W, act_absmax, *, r: int, alpha: float = 0.5, w_dtype: str | None = None) -> SerqLayer:
@@ -109,7 +118,7 @@ def calibrate(W, act_absmax, *, r: int, alpha: float = 0.5, w_dtype: str | None 
     shi = np.empty(K, np.float32)
     Wq = np.empty((N, K // 2), np.uint8)
     sw = np.empty(N, np.float32)
-    Rq = np.empty((N, r // 2), np.uint8)
+    Rq = np.zeros((N, rq_row_bytes(r)), np.uint8)
     sr = np.zeros(N, np.float32)
     check("serq_calibrate", lib.serq_calibrate(_ptr(W), dt, K, N, _ptr(amax), float(alpha), r, _ptr(perm),
                                                _ptr(shi), _ptr(Wq), _ptr(sw), _ptr(Rq) if r else None,

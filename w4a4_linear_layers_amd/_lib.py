@@ -19,7 +19,7 @@ SERQ_F32, SERQ_BF16 = 0, 1
 
 # every symbol include/serq.h declares
 EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_permute_outputs",
-           "serq_quant_act", "serq_linear", "serq_linear_kernel_name")
+           "serq_quant_act", "serq_linear", "serq_linear_kernel_name", "serq_rq_row_bytes")
 
 
 class SerqError(RuntimeError):
@@ -39,7 +39,7 @@ def _load() -> ctypes.CDLL:
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libserq.so not found at {LIB_PATH}; build it with "
-                          f"`python -m w4a4_linear_layers_amd.build` (or __graft_entry__.build())")
+                          f"`python w4a4_linear_layers_amd/build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     vp, ip, fp, i32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int
     lib.serq_strerror.argtypes = [ip]
@@ -56,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.serq_linear.restype = ip
     lib.serq_linear_kernel_name.argtypes = [ip, ip, ip, ip, ip]
     lib.serq_linear_kernel_name.restype = ctypes.c_char_p
+    lib.serq_rq_row_bytes.argtypes = [ip]
+    lib.serq_rq_row_bytes.restype = ip
     return lib
 
 

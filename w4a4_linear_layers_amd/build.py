@@ -1,7 +1,10 @@
 """Build libserq.so in-tree with hipcc for gfx950.
 
-    python -m w4a4_linear_layers_amd.build            # build (always recompiles)
-    python -m w4a4_linear_layers_amd.build --asm DIR  # also dump device assembly
+    python w4a4_linear_layers_amd/build.py            # build (always recompiles)
+    python w4a4_linear_layers_amd/build.py --asm DIR  # also dump device assembly
+
+(Run as a script: importing the package would first load the library being
+rebuilt.)
 
 The library is one shared object: host C++ (calibration, C ABI) and the HIP
 kernels, linked against the HIP runtime. Every floating-point step of the

@@ -125,13 +125,14 @@ void calibrate_columns(const WeightView& W, int K, int r, const float* s, const 
       for (int c = 0; c < nb; ++c) sr[n0 + c] = 0.0f;
     return;
   }
-  const size_t rb = static_cast<size_t>(r) / 2;
+  const size_t rb = static_cast<size_t>(SERQ_RQ_ROW_BYTES(r));
   for (int c = 0; c < nb; ++c) {
     float m = 0.0f;
     for (int i = 0; i < r; ++i) m = std::max(m, std::fabs(R[static_cast<size_t>(i) * nb + c]));
     Quantizer qr(m, 7.0f);
     sr[n0 + c] = qr.scale;
     uint8_t* row = Rq + static_cast<size_t>(n0 + c) * rb;
+    std::memset(row, 0, rb);                    // zero codes in the padding
     for (int i = 0; i < r; i += 2) {
       int c0 = qr.code(R[static_cast<size_t>(i) * nb + c], -8, 7);
       int c1 = qr.code(R[static_cast<size_t>(i + 1) * nb + c], -8, 7);
@@ -206,7 +207,7 @@ extern "C" int serq_permute_outputs(const int32_t* perm_next, int N, int K, int 
     if (p < 0 || p >= N || seen[p]) return SERQ_EINVAL;
     seen[p] = 1;
   }
-  const size_t Kb = static_cast<size_t>(K) / 2, rb = static_cast<size_t>(r) / 2;
+  const size_t Kb = static_cast<size_t>(K) / 2, rb = static_cast<size_t>(SERQ_RQ_ROW_BYTES(r));
   std::vector<uint8_t> wtmp(static_cast<size_t>(N) * Kb);
   std::vector<float> ftmp(N);
   for (int i = 0; i < N; ++i)

@@ -28,7 +28,9 @@ extern "C" const char* serq_strerror(int status) {
   }
 }
 
-extern "C" int serq_abi_version(void) { return 100; }
+extern "C" int serq_abi_version(void) { return 200; }
+
+extern "C" int serq_rq_row_bytes(int r) { return r < 0 ? -1 : SERQ_RQ_ROW_BYTES(r); }
 
 extern "C" int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
                               const float* s_hat_inv, int a_bits, void* Xq, float* sx,

@@ -68,11 +68,6 @@ __device__ __forceinline__ v4i widen16(uint32_t p0, uint32_t p1) {
   return r;
 }
 
-// Two packed int4 dwords -> split-order int8 (x16) as a uint2 (for LDS).
-__device__ __forceinline__ uint2 widen8(uint32_t p) {
-  return make_uint2((p << 4) & 0xF0F0F0F0u, p & 0xF0F0F0F0u);
-}
-
 // 8 int8 codes in natural order (two dwords) -> even codes, odd codes.
 __device__ __forceinline__ uint2 split8(uint32_t d0, uint32_t d1) {
   return make_uint2(__builtin_amdgcn_perm(d1, d0, 0x06040200u),
@@ -90,10 +85,16 @@ __device__ __forceinline__ v4i split16(uint4 d) {
   return r;
 }
 
+// Two fp32 values -> two bf16 (round to nearest even) packed in a dword,
+// `lo` in the low half: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f));
 }
 
 // Bytes [off, off + 4) of a row with `valid` bytes; zero beyond. Dword load
@@ -133,9 +134,7 @@ __device__ __forceinline__ void store4(const LinearArgs& a, v4i am, v4i ar, int 
   }
   if (n + 3 < a.N && (a.N & 3) == 0) {
     if (a.y_bf16) {
-      uint2 o;
-      o.x = f32_to_bf16_rne(y[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(y[1])) << 16);
-      o.y = f32_to_bf16_rne(y[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(y[3])) << 16);
+      const uint2 o = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.Y) + base) = o;
     } else {
       *reinterpret_cast<float4*>(static_cast<float*>(a.Y) + base) = make_float4(y[0], y[1], y[2], y[3]);
@@ -177,20 +176,28 @@ __device__ __forceinline__ float4 load_scales4(const float* p, int n, int N) {
 // the next load is issued into. (Left to itself the compiler would drain every
 // outstanding load before each LDS read, serializing the pipeline.)
 //
-// LDS rows are 64 bytes (packed int4, 128 codes) or 128 bytes (int8). A
-// 16-byte slot is placed at position part ^ f(row) -- (row >> 1) & 3 for 64-byte
-// rows, row & 7 for 128-byte rows -- so the lanes that read the same part of
-// consecutive rows hit distinct bank groups.
+// The residual rides in the same pipeline: after the K/128 main k-tiles come
+// ceil(r / 128) residual k-tiles (rows of Q(R) for the weights, the first
+// codes of the same activation rows), loaded by the same instructions, so
+// they are already in LDS when the K loop ends. The epilogue scales are
+// loaded into LDS at kernel start, before the first k-tile. Every wave issues
+// the same number of load instructions per k-tile, which is what the vmcnt
+// thresholds count.
+//
+// LDS rows are 64 bytes (packed int4, 128 codes) or 128 bytes (int8); each
+// 16-byte part is stored at a row-dependent XOR-swizzled slot (swz64,
+// swz128) so that the lanes that read the same part of consecutive rows hit
+// distinct bank groups.
 //
 // Fragment k layout inside a k-tile: lane half h = lane / 32 of both operands
 // holds codes [64 h, 64 h + 64); MFMA step s (0..3) takes its codes
 // [64 h + 16 s, 64 h + 16 s + 16). The two halves together cover 32 codes per
 // step and the four steps cover the 128 codes of the k-tile.
 //
-// After the K loop the LDS is reused for the residual: the r salient
-// activation columns and Q(R) are widened once into LDS, and each block's
-// residual MFMAs run right before its epilogue, so the residual needs only
-// one 16-register accumulator at a time.
+// Epilogue: each block's residual MFMAs run from the residual k-tiles, the
+// scales turn the two accumulators into fp32 outputs in place, the output
+// tile is written to LDS (swizzled, conflict-free) and then copied to Y with
+// 16-byte stores along its rows.
 // ---------------------------------------------------------------------------
 
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -220,6 +227,49 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// LDS slot swizzles. A 16-byte part of a 64-byte row goes to slot
+// part ^ swz64(row); of a 128-byte row to part ^ swz128(row). Chosen so that
+// the 16-byte reads of 16 consecutive rows at one part hit distinct bank
+// groups whether the LDS serves 8 or 16 lanes of a ds_read_b128 per cycle.
+__device__ __forceinline__ int swz64(int row) {
+  return (((row >> 1) ^ (row >> 2)) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1);
+}
+__device__ __forceinline__ int swz128(int row) {
+  return ((row >> 1) & 3) | ((((row >> 3) ^ row) & 1) << 2);
+}
+
+// Workgroup -> tile order. Workgroups are dispatched round-robin over the
+// eight XCDs (each with its own L2), so workgroup b runs on XCD b % 8. The
+// grid is first regrouped so that each XCD gets a contiguous range of the
+// tile order, and the tile order walks groups of kGroupM tile rows with the
+// tile column fastest inside a group: the tiles resident on one XCD then
+// share a few weight column blocks and activation row blocks.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void tile_coords(int b, int nb, int n_tiles, int& tn, int& tm) {
+  int l = b;
+  if (nb % kXcds == 0) l = (b % kXcds) * (nb / kXcds) + b / kXcds;
+  const int m_tiles = nb / n_tiles;
+  const int per_group = kGroupM * n_tiles;
+  const int grp = l / per_group;
+  const int first_m = grp * kGroupM;
+  const int gm = min(kGroupM, m_tiles - first_m);      // rows in this (possibly last) group
+  const int in = l - grp * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+
+// One 4-byte direct global->LDS load per lane: lane i moves the dword at
+// sbase + voff into lds_dst + 4 i (same conventions as dma16).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_dst) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int TN, int TM, int A_BITS>
 struct TileCfg {
   static constexpr int WN = 32 * TN, WM = 32 * TM;       // wave tile
@@ -232,15 +282,27 @@ struct TileCfg {
   static constexpr int CW = W_CHUNKS / 4;                // weight chunks per wave and stage
   static constexpr int CX = X_CHUNKS / 4;                // activation chunks per wave and stage
   static constexpr int CHUNKS_PER_WAVE = CW + CX;
-  // Two workgroups share a CU: keep each under 80 KB of LDS.
-  static constexpr int STAGES = (4 * STAGE <= 73728) ? 4 : (3 * STAGE <= 73728 ? 3 : 2);
+  static constexpr int SCALE_BYTES = 4 * (2 * BN + BM);  // sw, sr, sx of the tile
+  // Two workgroups share a CU: keep each within 80 KB of LDS.
+  static constexpr int kLdsCap = 80 * 1024;
+  static constexpr int STAGES = (4 * STAGE + SCALE_BYTES <= kLdsCap) ? 4 : (3 * STAGE + SCALE_BYTES <= kLdsCap ? 3 : 2);
+  static constexpr int SCALE_OFF = STAGES * STAGE;
+  static constexpr int OUT_BYTES = BM * BN * 4;          // fp32 output tile (bf16 takes half)
+  static constexpr int LDS_BYTES = SCALE_OFF + SCALE_BYTES > OUT_BYTES ? SCALE_OFF + SCALE_BYTES : OUT_BYTES;
   static constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
-  static constexpr int pipeline_bytes() { return STAGES * STAGE; }
-  static constexpr int residual_bytes(int rp) { return (BN + BM) * (rp + 16) + 4 * (2 * BN + BM); }
   static_assert(W_CHUNKS % 4 == 0 && X_CHUNKS % 4 == 0, "stage must split over four waves");
-  static_assert(STAGES * STAGE <= 80 * 1024, "LDS");
-  static_assert(BN * 0 + (BN + BM) * (kMaxResidual + 16) + 4 * (2 * BN + BM) <= 80 * 1024, "LDS");
+  static_assert(BN % 64 == 0 && BM % 64 == 0, "scale rows are loaded 64 at a time");
+  // The residual k-tiles (at most two) stay in their buffers while the last
+  // main k-tile is computed from another one.
+  static_assert(STAGES >= (kMaxResidual / 2 + kKTileW - 1) / kKTileW + 1, "residual k-tiles need free stages");
+  static_assert(LDS_BYTES <= kLdsCap, "LDS");
 };
+
+// Output-tile swizzle for bf16 rows (16 chunks of 16 bytes): the 8-byte half
+// a lane writes moves to the other half of its chunk when half_swap(row).
+// With chunk ^ (row & 15) this keeps the eight-byte writes of 16 (and of 32)
+// consecutive rows at one column on distinct banks.
+__device__ __forceinline__ int half_swap(int row) { return ((row >> 3) ^ (row >> 4)) & 1; }
 
 template <int TN, int TM, int A_BITS>
 __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, int n_tiles) {
@@ -252,59 +314,95 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave >> 1, wm = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
-  const int tile_n = blockIdx.x % n_tiles, tile_m = blockIdx.x / n_tiles;
-  const int n0 = tile_n * C::BN, m0 = tile_m * C::BM;
+  int tile_n, tile_m;
+  tile_coords(blockIdx.x, gridDim.x, n_tiles, tile_n, tile_m);
+  const int n0 = __builtin_amdgcn_readfirstlane(tile_n * C::BN);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile_m * C::BM);
   const int Kb = a.K / 2;                      // packed weight bytes per row
   const int Xrow = a.K * A_BITS / 8;           // activation bytes per row
-  const int nkt = (Kb + kKTileW - 1) / kKTileW;
+  const int Rb = rq_row_bytes(a.r);            // Q(R) bytes per row (zero-padded)
+  const int nkt = (Kb + kKTileW - 1) / kKTileW;  // main k-tiles
+  const int ntot = nkt + (Rb + kKTileW - 1) / kKTileW;   // plus residual k-tiles
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+  // Epilogue scales into LDS first, so that every wave's k-tile waits below
+  // also cover them: wave 0 loads sw, wave 1 sr, wave 2 sx of the tile.
+  {
+    const uint32_t sbase = lds_base + C::SCALE_OFF;
+    if (wv == 0) {
+#pragma unroll
+      for (int c = 0; c < C::BN / 64; ++c)
+        if (n0 + 64 * c + lane < a.N) dma4(a.sw + n0 + 64 * c, 4 * lane, sbase + 256 * c);
+    } else if (wv == 1) {
+      if (a.r > 0) {
+#pragma unroll
+        for (int c = 0; c < C::BN / 64; ++c)
+          if (n0 + 64 * c + lane < a.N) dma4(a.sr + n0 + 64 * c, 4 * lane, sbase + 4 * C::BN + 256 * c);
+      } else {                                  // no residual: sr = 0
+#pragma unroll
+        for (int c = 0; c < C::BN / 64; ++c)
+          reinterpret_cast<float*>(lds + C::SCALE_OFF + 4 * C::BN)[64 * c + lane] = 0.0f;
+      }
+    } else if (wv == 2) {
+#pragma unroll
+      for (int c = 0; c < C::BM / 64; ++c)
+        if (m0 + 64 * c + lane < a.M) dma4(a.sx + m0 + 64 * c, 4 * lane, sbase + 8 * C::BN + 256 * c);
+    }
+  }
 
   // Wave w loads weight chunks [w CW, (w + 1) CW) and activation chunks
   // [w CX, (w + 1) CX) of every stage: 16 rows x 64 bytes per chunk (8 rows x
   // 128 bytes for int8 activations). Per lane: the byte offset of its row and
   // swizzled part at k-tile 0; the k-tile advances the (scalar) base pointer.
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int part64 = (lane & 3) ^ ((lane >> 3) & 3);   // row (lane >> 2): (row >> 1) & 3
-  const int part128 = (lane & 7) ^ ((lane >> 3) & 7);  // row (lane >> 3): row & 7
-  uint32_t woff[C::CW], xoff[C::CX];
+  const int part64 = (lane & 3) ^ swz64(lane >> 2);    // 16-row chunks: row & 15 = lane >> 2
+  uint32_t woff[C::CW], roff[C::CW], xoff[C::CX];
+  int xpart[C::CX];                                     // this lane's 16-byte part of each activation chunk
 #pragma unroll
   for (int i = 0; i < C::CW; ++i) {
-    const int row = (wv * C::CW + i) * 16 + (lane >> 2);
-    woff[i] = static_cast<uint32_t>(min(n0 + row, a.N - 1)) * Kb + part64 * 16;
+    const int row = min(n0 + (wv * C::CW + i) * 16 + (lane >> 2), a.N - 1);
+    woff[i] = static_cast<uint32_t>(row) * Kb + part64 * 16;
+    roff[i] = static_cast<uint32_t>(row) * Rb + part64 * 16;
   }
 #pragma unroll
   for (int i = 0; i < C::CX; ++i) {
     if constexpr (A_BITS == 4) {
       const int row = (wv * C::CX + i) * 16 + (lane >> 2);
+      xpart[i] = part64;
       xoff[i] = static_cast<uint32_t>(min(m0 + row, a.M - 1)) * Xrow + part64 * 16;
     } else {
       const int row = (wv * C::CX + i) * 8 + (lane >> 3);
-      xoff[i] = static_cast<uint32_t>(min(m0 + row, a.M - 1)) * Xrow + part128 * 16;
+      xpart[i] = (lane & 7) ^ swz128(row);
+      xoff[i] = static_cast<uint32_t>(min(m0 + row, a.M - 1)) * Xrow + xpart[i] * 16;
     }
   }
-  // Issue the loads of k-tile kt into LDS stage `stage`. Only the last
-  // k-tile can run past the end of K; its missing slots are zero-filled with
-  // an ordinary LDS store instead.
-  const bool k_exact = (Kb % kKTileW) == 0;
+  // Issue the loads of k-tile kt (main k-tiles, then residual ones) into LDS
+  // stage `stage`. A k-tile that runs past the end of its rows (the last
+  // main one when K % 128 != 0, the last residual one) zero-fills its missing
+  // 16-byte slots with an ordinary LDS store instead; every instruction still
+  // has at least one loading lane, so the per-wave load count is the same
+  // for every k-tile.
   auto issue = [&](int kt, int stage) {
     const uint32_t sbase = lds_base + stage * C::STAGE;
-    const uint8_t* wsrc = a.Wq + static_cast<size_t>(kt) * kKTileW;
-    const uint8_t* xsrc = a.Xq + static_cast<size_t>(kt) * C::XB;
-    const bool full = k_exact || kt + 1 < nkt;
-    const int wpos = kt * kKTileW + part64 * 16;                       // this lane's k byte
-    const int xpos = kt * C::XB + (A_BITS == 4 ? part64 : part128) * 16;
+    const bool res = kt >= nkt;
+    const int kx = res ? kt - nkt : kt;        // k-tile index within its source rows
+    const uint8_t* wsrc = (res ? a.Rq : a.Wq) + kx * kKTileW;
+    const uint8_t* xsrc = a.Xq + kx * C::XB;
+    const int wleft = (res ? Rb : Kb) - kx * kKTileW;     // row bytes left from the k-tile start
+    const int xleft = Xrow - kx * C::XB;
 #pragma unroll
     for (int i = 0; i < C::CW; ++i) {
       const uint32_t chunk = sbase + (wv * C::CW + i) * 1024;
-      if (full || wpos < Kb)
-        dma16(wsrc, woff[i], chunk);
+      const uint32_t off = res ? roff[i] : woff[i];
+      if (wleft >= kKTileW || part64 * 16 < wleft)
+        dma16(wsrc, off, chunk);
       else
         *reinterpret_cast<uint4*>(lds + (chunk - lds_base) + lane * 16) = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::CX; ++i) {
       const uint32_t chunk = sbase + C::W_BYTES + (wv * C::CX + i) * 1024;
-      if (full || xpos < Xrow)
+      if (xleft >= C::XB || xpart[i] * 16 < xleft)
         dma16(xsrc, xoff[i], chunk);
       else
         *reinterpret_cast<uint4*>(lds + (chunk - lds_base) + lane * 16) = make_uint4(0, 0, 0, 0);
@@ -322,13 +420,13 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
   int wrd[2], xrd[XP];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
-    wrd[p] = (wn * C::WN + l32) * kKTileW + (((2 * h + p) ^ ((l32 >> 1) & 3)) * 16);
+    wrd[p] = (wn * C::WN + l32) * kKTileW + (((2 * h + p) ^ swz64(l32)) * 16);
 #pragma unroll
   for (int p = 0; p < XP; ++p) {
     if constexpr (A_BITS == 4)
-      xrd[p] = C::W_BYTES + (wm * C::WM + l32) * C::XB + (((2 * h + p) ^ ((l32 >> 1) & 3)) * 16);
+      xrd[p] = C::W_BYTES + (wm * C::WM + l32) * C::XB + (((2 * h + p) ^ swz64(l32)) * 16);
     else
-      xrd[p] = C::W_BYTES + (wm * C::WM + l32) * C::XB + (((4 * h + p) ^ (l32 & 7)) * 16);
+      xrd[p] = C::W_BYTES + (wm * C::WM + l32) * C::XB + (((4 * h + p) ^ swz128(l32)) * 16);
   }
 
   // This lane's packed fragments of one k-tile: two 16-byte parts per weight
@@ -348,27 +446,35 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
 #pragma unroll
       for (int j = 0; j < TM; ++j) f.x[p][j] = *reinterpret_cast<const uint4*>(sb + xrd[p] + j * 32 * C::XB);
   };
+  // Widened MFMA operands of step s from a weight / activation fragment.
+  auto wop = [&](const uint4& w0, const uint4& w1, int s) {
+    const uint4 w = (s >> 1) ? w1 : w0;
+    return (s & 1) ? widen16(w.z, w.w) : widen16(w.x, w.y);
+  };
+  auto xop = [&](const uint4 (&x)[XP], int s) {
+    if constexpr (A_BITS == 4) {
+      const uint4 v = x[s >> 1];
+      return (s & 1) ? widen16(v.z, v.w) : widen16(v.x, v.y);
+    } else {
+      return split16(x[s]);
+    }
+  };
   // MFMA step s takes dwords (2 (s & 1), 2 (s & 1) + 1) of weight part s >> 1.
   auto unpack = [&](const Frags& f, int s, v4i (&wa)[TN], v4i (&xb)[TM]) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const uint4 w = f.w[s >> 1][i];
-      wa[i] = (s & 1) ? widen16(w.z, w.w) : widen16(w.x, w.y);
-    }
+    for (int i = 0; i < TN; ++i) wa[i] = wop(f.w[0][i], f.w[1][i], s);
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      if constexpr (A_BITS == 4) {
-        const uint4 x = f.x[s >> 1][j];
-        xb[j] = (s & 1) ? widen16(x.z, x.w) : widen16(x.x, x.y);
-      } else {
-        xb[j] = split16(f.x[s][j]);
-      }
+      uint4 xj[XP];
+#pragma unroll
+      for (int p = 0; p < XP; ++p) xj[p] = f.x[p][j];
+      xb[j] = xop(xj, s);
     }
   };
   // The four MFMA steps of one k-tile, software-pipelined: the widening for
   // step s + 1 is issued between the MFMAs of step s, so the VALU work runs
   // while the matrix core is busy.
-  auto compute = [&](const Frags& f) {
+  auto compute = [&](const Frags& f, v16i (&acc)[TN][TM]) {
     v4i wa[TN], xb[TM];
     unpack(f, 0, wa, xb);
 #pragma unroll
@@ -399,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
   // `next`, then run k-tile kt's MFMAs from `cur` while those reads land.
   auto step = [&](int kt, const Frags& cur, Frags& next) {
     if (kt + 1 < nkt) {
-      const int ahead = min(STAGES - 2, nkt - 2 - kt);   // later k-tiles still in flight
+      const int ahead = min(STAGES - 2, ntot - 2 - kt);   // later k-tiles still in flight
       if (ahead >= 2) {
         wait_vmcnt<CPW * 2>();
       } else if (ahead == 1) {
@@ -409,17 +515,17 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): earlier fragment reads and zero-fills done
       __builtin_amdgcn_s_barrier();
-      if (kt + STAGES < nkt) issue(kt + STAGES, kt % STAGES);
+      if (kt + STAGES < ntot) issue(kt + STAGES, kt % STAGES);
       read_frags((kt + 1) % STAGES, next);
     }
-    compute(cur);
+    compute(cur, acc);
   };
 
 #pragma unroll
   for (int st = 0; st < STAGES; ++st)
-    if (st < nkt) issue(st, st);
+    if (st < ntot) issue(st, st);
   {
-    const int inflight = min(STAGES, nkt);     // wait for k-tile 0 only
+    const int inflight = min(STAGES, ntot);    // wait for k-tile 0 (and the scales) only
     if (inflight >= 4) {
       wait_vmcnt<CPW * 3>();
     } else if (inflight == 3) {
@@ -438,103 +544,157 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
     step(kt, f0, f1);
     if (kt + 1 < nkt) step(kt + 1, f1, f0);
   }
-  __syncthreads();                              // every wave is done with the pipeline buffers
 
-  // ---- Epilogue operands, staged once into LDS (reusing the pipeline space)
-  // with back-to-back wide loads: the widened residual operands -- Q(R) rows
-  // and the r salient activation codes of the tile's tokens -- and the
-  // token and channel scales. The per-block epilogue then reads only LDS.
-  const int r = a.r;
-  const bool has_res = r > 0;
-  const int rp = (r + 31) & ~31;             // padded with zero codes to the MFMA depth
-  const int RS = rp + 16;                    // LDS row stride of the widened operands
-  uint8_t* Rw = lds;
-  uint8_t* Rx = lds + C::BN * RS;
-  float* s_sw = reinterpret_cast<float*>(lds + (C::BN + C::BM) * RS);
-  float* s_sr = s_sw + C::BN;
-  float* s_sx = s_sr + C::BN;
-  if (tid < C::BN) {
-    const int n = min(n0 + tid, a.N - 1);
-    s_sw[tid] = a.sw[n];
-    s_sr[tid] = has_res ? a.sr[n] : 0.0f;
-  }
-  if (tid < C::BM) s_sx[tid] = a.sx[min(m0 + tid, a.M - 1)];
-  if (has_res) {
-    const int rbytes = r / 2;
-    const bool wide = (r % 32) == 0;         // packed rows 16-byte aligned
-    for (int row = tid; row < C::BN + C::BM; row += kThreads) {
-      const bool is_w = row < C::BN;
-      const uint8_t* src = is_w ? a.Rq + static_cast<size_t>(min(n0 + row, a.N - 1)) * rbytes
-                                : a.Xq + static_cast<size_t>(min(m0 + row - C::BN, a.M - 1)) * Xrow;
-      uint8_t* dst = is_w ? Rw + row * RS : Rx + (row - C::BN) * RS;
+  // ---- Epilogue. The residual k-tiles were issued during the last main
+  // iterations; wait for them, then publish them (and the zero-fills).
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  const float* s_sw = reinterpret_cast<const float*>(lds + C::SCALE_OFF);
+  const float* s_sr = s_sw + C::BN;
+  const float* s_sx = s_sr + C::BN;
+  const int nres = ntot - nkt;
+  // Residual MFMAs for all blocks, from the residual k-tiles.
+  v16i ar[TN][TM];
 #pragma unroll
-      for (int q = 0; q < kMaxResidual / 32; ++q) {   // 32 codes per piece
-        if (32 * q >= rp) break;
-        uint4 lo, hi;                        // widened codes 32q .. 32q + 31
-        if (A_BITS == 8 && !is_w) {
-          uint4 d0, d1;
-          if (wide && 32 * q + 32 <= r) {
-            d0 = *reinterpret_cast<const uint4*>(src + 32 * q);
-            d1 = *reinterpret_cast<const uint4*>(src + 32 * q + 16);
-          } else {
-            d0 = make_uint4(load_dword_masked(src, 32 * q, r), load_dword_masked(src, 32 * q + 4, r),
-                            load_dword_masked(src, 32 * q + 8, r), load_dword_masked(src, 32 * q + 12, r));
-            d1 = make_uint4(load_dword_masked(src, 32 * q + 16, r), load_dword_masked(src, 32 * q + 20, r),
-                            load_dword_masked(src, 32 * q + 24, r), load_dword_masked(src, 32 * q + 28, r));
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) ar[i][j] = v16i{};
+  for (int t = 0; t < nres; ++t) {
+    Frags fr;
+    read_frags((nkt + t) % STAGES, fr);
+    compute(fr, ar);
+  }
+  if (a.dbg_main) {                            // exact accumulators, for tests
+    static_for<TM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int m = m0 + wm * C::WM + j * 32 + l32;
+      static_for<TN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int nb = n0 + wn * C::WN + i * 32 + 4 * h;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int n = nb + 8 * (e >> 2) + (e & 3);
+          if (m < a.M && n < a.N) {
+            a.dbg_main[static_cast<size_t>(m) * a.N + n] = acc[i][j][e] >> C::SHIFT;
+            a.dbg_res[static_cast<size_t>(m) * a.N + n] = ar[i][j][e] >> C::SHIFT;
           }
-          const uint2 e0 = split8(d0.x, d0.y), e1 = split8(d0.z, d0.w);
-          const uint2 e2 = split8(d1.x, d1.y), e3 = split8(d1.z, d1.w);
-          lo = make_uint4(e0.x, e0.y, e1.x, e1.y);
-          hi = make_uint4(e2.x, e2.y, e3.x, e3.y);
-        } else {
-          uint4 p;
-          if (wide && 16 * q + 16 <= rbytes) {
-            p = *reinterpret_cast<const uint4*>(src + 16 * q);
-          } else {
-            p = make_uint4(load_dword_masked(src, 16 * q, rbytes), load_dword_masked(src, 16 * q + 4, rbytes),
-                           load_dword_masked(src, 16 * q + 8, rbytes), load_dword_masked(src, 16 * q + 12, rbytes));
-          }
-          const uint2 e0 = widen8(p.x), e1 = widen8(p.y), e2 = widen8(p.z), e3 = widen8(p.w);
-          lo = make_uint4(e0.x, e0.y, e1.x, e1.y);
-          hi = make_uint4(e2.x, e2.y, e3.x, e3.y);
         }
-        *reinterpret_cast<uint4*>(dst + 32 * q) = lo;
-        *reinterpret_cast<uint4*>(dst + 32 * q + 16) = hi;
-      }
-    }
+      });
+    });
   }
-  __syncthreads();
-  const int nks = rp / 32;                   // 32-code MFMA steps; lane half h takes 16 of each
-
-  // ---- per block: residual MFMAs, then the epilogue
-  static_for<TM>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    v4i xr[kMaxResidual / 32];
+  // y = sx (sw acc_main + sr acc_res) in fp32, kept in place of the main
+  // accumulator. The scales of a channel block are read once for its TM
+  // token blocks.
+  float sxm[TM];
 #pragma unroll
-    for (int s = 0; s < kMaxResidual / 32; ++s)
-      xr[s] = s < nks ? *reinterpret_cast<const v4i*>(Rx + (wm * C::WM + j * 32 + l32) * RS + s * 32 + h * 16)
-                      : v4i{0, 0, 0, 0};
-    const int mt = wm * C::WM + j * 32 + l32;   // token within the tile
-    const float sxm = s_sx[mt];
-    static_for<TN>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      v16i ar = v16i{};
+  for (int j = 0; j < TM; ++j) sxm[j] = s_sx[wm * C::WM + j * 32 + l32];
+  static_for<TN>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int nt = wn * C::WN + i * 32 + 4 * h;   // first channel (within the tile) of group q = 0
+    float4 w4[4], r4[4];
 #pragma unroll
-      for (int s = 0; s < kMaxResidual / 32; ++s)
-        if (s < nks)
-          ar = mfma32(*reinterpret_cast<const v4i*>(Rw + (wn * C::WN + i * 32 + l32) * RS + s * 32 + h * 16),
-                      xr[s], ar);
-      const int nt = wn * C::WN + i * 32 + 4 * h;   // channel within the tile
+    for (int q = 0; q < 4; ++q) {
+      w4[q] = *reinterpret_cast<const float4*>(s_sw + nt + 8 * q);
+      r4[q] = *reinterpret_cast<const float4*>(s_sr + nt + 8 * q);
+    }
+    static_for<TM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 w4 = *reinterpret_cast<const float4*>(s_sw + nt + 8 * q);
-        const float4 r4 = *reinterpret_cast<const float4*>(s_sr + nt + 8 * q);
-        const v4i am4 = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        const v4i ar4 = v4i{ar[4 * q], ar[4 * q + 1], ar[4 * q + 2], ar[4 * q + 3]};
-        store4<C::SHIFT>(a, am4, ar4, m0 + mt, n0 + nt + 8 * q, sxm, w4, r4);
+        const float wv4[4] = {w4[q].x, w4[q].y, w4[q].z, w4[q].w};
+        const float rv4[4] = {r4[q].x, r4[q].y, r4[q].z, r4[q].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float fm = static_cast<float>(acc[i][j][4 * q + c] >> C::SHIFT);
+          const float fr = static_cast<float>(ar[i][j][4 * q + c] >> C::SHIFT);
+          acc[i][j][4 * q + c] = __float_as_int(sxm[j] * __builtin_fmaf(rv4[c], fr, wv4[c] * fm));
+        }
       }
     });
   });
+  __syncthreads();                              // residual buffers and scales no longer read
+
+  // Output tile into LDS, row = token, swizzled 16-byte chunks.
+  if (a.y_bf16) {
+    constexpr int RB = C::BN * 2;
+    static_for<TM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int row = wm * C::WM + j * 32 + l32;
+      uint8_t* rp = lds + row * RB;
+      const int hs = (h ^ half_swap(row)) * 8;
+      static_for<TN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (wn * C::WN + i * 32) / 8 + q;
+          const uint2 o = make_uint2(
+              pack_bf16x2(__int_as_float(acc[i][j][4 * q]), __int_as_float(acc[i][j][4 * q + 1])),
+              pack_bf16x2(__int_as_float(acc[i][j][4 * q + 2]), __int_as_float(acc[i][j][4 * q + 3])));
+          *reinterpret_cast<uint2*>(rp + 16 * (c ^ (row & 15)) + hs) = o;
+        }
+      });
+    });
+  } else {
+    constexpr int RB = C::BN * 4;
+    static_for<TM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int row = wm * C::WM + j * 32 + l32;
+      uint8_t* rp = lds + row * RB;
+      static_for<TN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (wn * C::WN + i * 32 + 8 * q + 4 * h) / 4;
+          *reinterpret_cast<v4i*>(rp + 16 * (c ^ (row & 15))) =
+              v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+      });
+    });
+  }
+  __syncthreads();
+
+  // Copy-out: 16-byte chunks along the rows of Y (every LDS read first, then
+  // the stores); ragged tails element by element.
+  auto copy_out = [&](auto ebc) {
+    constexpr int EB = decltype(ebc)::value;  // bytes per element
+    constexpr int CPR = C::BN * EB / 16;      // chunks per tile row
+    constexpr int EPC = 16 / EB;              // elements per chunk
+    constexpr int RPP = kThreads / CPR;       // rows per pass
+    constexpr int PASSES = C::BM / RPP;
+    const int c = tid % CPR;
+    const int n = n0 + c * EPC;
+    const bool vec = (a.N % EPC) == 0 && n + EPC <= a.N;
+    uint4 v[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = p * RPP + tid / CPR;
+      v[p] = *reinterpret_cast<const uint4*>(lds + row * C::BN * EB + 16 * (c ^ (row & 15)));
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = p * RPP + tid / CPR;
+      if (m0 + row >= a.M) break;
+      uint4 w = v[p];
+      if (EB == 2 && half_swap(row)) w = make_uint4(w.z, w.w, w.x, w.y);
+      uint8_t* dst = static_cast<uint8_t*>(a.Y) + (static_cast<size_t>(m0 + row) * a.N + n) * EB;
+      if (vec) {
+        *reinterpret_cast<uint4*>(dst) = w;
+      } else {
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+        for (int e = 0; e < EPC && n + e < a.N; ++e) {
+          if (EB == 2)
+            reinterpret_cast<uint16_t*>(dst)[e] = static_cast<uint16_t>(d[e >> 1] >> (16 * (e & 1)));
+          else
+            reinterpret_cast<uint32_t*>(dst)[e] = d[e];
+        }
+      }
+    }
+  };
+  if (a.y_bf16)
+    copy_out(std::integral_constant<int, 2>{});
+  else
+    copy_out(std::integral_constant<int, 4>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -587,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void serq_decode_kernel(LinearArgs a) {
   const float4 sw4 = load_scales4(a.sw, n0 + 4 * g, a.N);
   const float4 sr4 = a.r > 0 ? load_scales4(a.sr, n0 + 4 * g, a.N) : make_float4(0.f, 0.f, 0.f, 0.f);
   const int r = a.r;
-  const int rb = r / 2;                                 // packed residual bytes per row
+  const int rb = rq_row_bytes(r);                       // Q(R) row stride (zero-padded)
   constexpr int kResWave = 1;
   uint4 rw[LW];
   uint4 rx[MG][LX];
@@ -734,7 +894,7 @@ __global__ __launch_bounds__(kThreads) void serq_generic_kernel(LinearArgs a) {
   int ar = 0;
   float srn = 0.0f;
   if (a.r > 0) {
-    const uint8_t* rr = a.Rq + static_cast<size_t>(n) * (a.r / 2);
+    const uint8_t* rr = a.Rq + static_cast<size_t>(n) * rq_row_bytes(a.r);
     for (int k = 0; k < a.r; ++k) ar += code_at(xr, k, a.a_bits) * code_at(rr, k, 4);
     srn = a.sr[n];
   }
@@ -752,21 +912,16 @@ __global__ __launch_bounds__(kThreads) void serq_generic_kernel(LinearArgs a) {
 template <int TN, int TM, int A_BITS>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
   using C = TileCfg<TN, TM, A_BITS>;
-  const int rp = (a.r + 31) & ~31;
-  const int lds = max(C::pipeline_bytes(), C::residual_bytes(rp));
   static bool attr_set = false;  // idempotent; the attribute is per function
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_tile_kernel<TN, TM, A_BITS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::residual_bytes(kMaxResidual) > C::pipeline_bytes()
-                                           ? C::residual_bytes(kMaxResidual)
-                                           : C::pipeline_bytes());
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int n_tiles = (a.N + C::BN - 1) / C::BN;
   const int m_tiles = (a.M + C::BM - 1) / C::BM;
-  serq_tile_kernel<TN, TM, A_BITS><<<dim3(n_tiles * m_tiles), dim3(kThreads), lds, st>>>(a, n_tiles);
+  serq_tile_kernel<TN, TM, A_BITS><<<dim3(n_tiles * m_tiles), dim3(kThreads), C::LDS_BYTES, st>>>(a, n_tiles);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ struct LinearArgs {
   const float* sx;     // M
   const uint8_t* Wq;   // N x K/2 bytes
   const float* sw;     // N
-  const uint8_t* Rq;   // N x r/2 bytes (may be null when r == 0)
+  const uint8_t* Rq;   // N x rq_row_bytes(r) bytes (may be null when r == 0)
   const float* sr;     // N (may be null when r == 0)
   void* Y;             // M x N, fp32 or bf16
   int32_t* dbg_main;   // optional M x N int32
@@ -22,6 +22,10 @@ struct LinearArgs {
   int a_bits;
   int y_bf16;
 };
+
+// Row bytes of the packed Q(R): r codes padded with zero codes to a
+// multiple of 32 codes (16 bytes).
+__host__ __device__ constexpr int rq_row_bytes(int r) { return (r + 31) / 32 * 16; }
 
 // Kernel families serq_linear chooses between.
 enum class LinearKernel { kDecode16, kDecode32, kTile, kGeneric };
