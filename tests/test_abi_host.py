@@ -219,11 +219,21 @@ def test_layer_save_load_roundtrip(tmp_path):
 
 
 def test_kernel_dispatch_rules():
-    assert S.kernel_name(1, 4096, 4096, 64) == "decode16"
+    assert S.kernel_name(1, 4096, 4096, 64) == "gemv"
+    assert S.kernel_name(4, 4096, 4096, 64) == "gemv"
+    assert S.kernel_name(4, 4096, 4096, 64, 8) == "decode16"     # W4A8: no int4 dot products
+    assert S.kernel_name(4, 65536, 4096, 64) == "decode16"       # activation rows beyond the LDS budget
+    assert S.kernel_name(5, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(16, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(32, 4096, 14336, 128) == "decode32"
     assert S.kernel_name(4096, 4096, 14336, 128) == "tile128x128"
     assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x128"
+    assert S.kernel_name(65, 4096, 4096, 64) == "tile64x64"
+    assert S.kernel_name(256, 4096, 4096, 64) == "tile64x64"         # 256 tiles of 64 x 64
+    assert S.kernel_name(64, 4096, 32768, 64) == "tile64x128"        # 256 tiles of 64 x 128
+    assert S.kernel_name(768, 4096, 4096, 64) == "tile64x128"        # 192 tiles of 128 x 128 would be too few
+    assert S.kernel_name(1024, 4096, 4096, 64) == "tile128x128"
+    assert S.kernel_name(64, 4096, 4096, 64) == "tile64x64"
     assert S.kernel_name(16, 4100, 64, 8) == "generic"      # K % 32 != 0
     assert S.kernel_name(16, 4096, 64, 6) == "generic"      # r % 8 != 0
     assert S.kernel_name(16, 4096, 64, 512) == "generic"    # r > 256

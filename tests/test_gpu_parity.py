@@ -108,18 +108,26 @@ def _run_codes(M, K, N, r, bits, out, seed, col_sample=None):
 
 LINEAR_CASES = [
     # M, K, N, r, expected kernel
-    (1, 4096, 256, 64, "decode16"),
+    (1, 4096, 256, 64, "gemv"),
+    (2, 1056, 100, 40, "gemv"),           # K % 2048 != 0: partial 1 KB slice; N % 16 != 0
+    (3, 96, 40, 96, "gemv"),              # K < one slice, r = K
+    (4, 14336, 4096, 128, "gemv"),
+    (1, 2080, 1000, 0, "gemv"),           # r = 0
     (5, 1024, 100, 40, "decode16"),       # N % 16 and N % 4 ragged, r % 64 != 0
     (16, 2080, 64, 0, "decode16"),        # K % 128 != 0, r = 0
     (16, 512, 48, 256, "decode16"),
     (17, 1024, 50, 24, "decode32"),
     (32, 512, 64, 256, "decode32"),
-    (40, 1056, 130, 72, "tile64x128"),
-    (64, 96, 256, 96, "tile64x128"),      # K shorter than one k-tile, r = K
-    (100, 512, 300, 64, "tile128x128"),
-    (129, 800, 258, 8, "tile128x128"),
+    (40, 1056, 130, 72, "tile64x64"),
+    (64, 96, 256, 96, "tile64x64"),       # K shorter than one k-tile, r = K
+    (100, 512, 300, 64, "tile64x64"),
+    (129, 800, 258, 8, "tile64x64"),
+    (256, 4096, 4096, 64, "tile64x64"),       # deep pipeline, one workgroup per CU
+    (60, 1056, 32800, 72, "tile64x128"),      # ragged M and N
+    (100, 288, 16400, 128, "tile64x128"),
     (200, 256, 32768, 64, "tile128x128"),     # many workgroups
-    (300, 288, 32768, 128, "tile128x128"),    # K not a multiple of the k-tile
+    (300, 288, 32768, 128, "tile128x128"),    # K not a multiple of the k-tile, ragged M
+    (520, 1056, 16400, 72, "tile128x128"),    # ragged M and N, r % 32 != 0
     (7, 100, 30, 6, "generic"),           # K % 32 != 0, r % 8 != 0
     (3, 384, 10, 320, "generic"),         # r > 256
 ]
@@ -129,6 +137,8 @@ LINEAR_CASES = [
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_linear_codes_bit_exact(M, K, N, r, kern, bits, out):
+    if kern == "gemv" and bits == 8:
+        kern = "decode16"                 # the int4 dot-product kernel is W4A4 only
     assert S.kernel_name(M, K, N, r, bits) == kern
     _run_codes(M, K, N, r, bits, out, seed=M + K + N + r + bits, col_sample=512 if N > 2048 else None)
 

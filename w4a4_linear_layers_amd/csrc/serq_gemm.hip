@@ -39,6 +39,7 @@ namespace serq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kCUs = 256;                   // compute units of an MI355X
 constexpr int kKTileCodes = 128;            // codes per k-tile
 constexpr int kKTileW = kKTileCodes / 2;    // packed weight bytes per row per k-tile
 constexpr int kMaxResidual = 256;           // largest r handled by the tile kernels
@@ -97,16 +98,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(pack_bf16x2(f, 0.0f));
 }
 
-// Bytes [off, off + 4) of a row with `valid` bytes; zero beyond. Dword load
-// when the row length keeps dwords aligned.
-__device__ __forceinline__ uint32_t load_dword_masked(const uint8_t* row, int off, int valid) {
-  if (off >= valid) return 0u;
-  if ((valid & 3) == 0) return *reinterpret_cast<const uint32_t*>(row + off);
-  uint32_t w = 0;
-  for (int b = 0; b < 4 && off + b < valid; ++b) w |= static_cast<uint32_t>(row[off + b]) << (8 * b);
-  return w;
-}
-
 // Epilogue for four consecutive output channels n..n+3 of token m, given
 // the token scale and the four channel scales (no memory reads here).
 template <int SHIFT>
@@ -149,15 +140,6 @@ __device__ __forceinline__ void store4(const LinearArgs& a, v4i am, v4i ar, int 
     else
       static_cast<float*>(a.Y)[base + i] = y[i];
   }
-}
-
-// The scales of channels n..n+3 (zero past N), from global memory.
-__device__ __forceinline__ float4 load_scales4(const float* p, int n, int N) {
-  if (n + 3 < N && (N & 3) == 0) return *reinterpret_cast<const float4*>(p + n);
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = n + i < N ? p[n + i] : 0.0f;
-  return make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -220,6 +202,14 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+// Workgroup barrier for LDS data only: this wave's LDS accesses complete,
+// then s_barrier. Unlike __syncthreads it does not wait for outstanding
+// global loads, so prefetches stay in flight; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt with vmcnt <= n (n < 64) and no wait on lgkm/exp counters.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -270,28 +260,42 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
 }
 #pragma clang diagnostic pop
 
-template <int TN, int TM, int A_BITS>
+// Tile shape: each wave owns TN x TM blocks of 32 x 32; the workgroup is a
+// 2 (channels) x WGM (tokens) grid of waves; OCC workgroups share a CU.
+template <int TN, int TM, int A_BITS, int WGM>
 struct TileCfg {
+  static constexpr int NW = 2 * WGM;                     // waves per workgroup
+  static constexpr int NT = 64 * NW;                     // lanes per workgroup
+  static constexpr int OCC = WGM == 2 ? 2 : 1;           // workgroups per CU
   static constexpr int WN = 32 * TN, WM = 32 * TM;       // wave tile
-  static constexpr int BN = 2 * WN, BM = 2 * WM;         // workgroup tile
+  static constexpr int BN = 2 * WN, BM = WGM * WM;       // workgroup tile
   static constexpr int XB = kKTileCodes * A_BITS / 8;    // activation bytes / row / k-tile
   static constexpr int W_BYTES = BN * kKTileW;
   static constexpr int STAGE = W_BYTES + BM * XB;        // bytes per LDS stage
   static constexpr int W_CHUNKS = W_BYTES / 1024;        // 1 KB wave chunks per stage
   static constexpr int X_CHUNKS = BM * XB / 1024;
-  static constexpr int CW = W_CHUNKS / 4;                // weight chunks per wave and stage
-  static constexpr int CX = X_CHUNKS / 4;                // activation chunks per wave and stage
+  static constexpr int CW = W_CHUNKS / NW;               // weight chunks per wave and stage
+  static constexpr int CX = X_CHUNKS / NW;               // activation chunks per wave and stage
   static constexpr int CHUNKS_PER_WAVE = CW + CX;
   static constexpr int SCALE_BYTES = 4 * (2 * BN + BM);  // sw, sr, sx of the tile
-  // Two workgroups share a CU: keep each within 80 KB of LDS.
-  static constexpr int kLdsCap = 80 * 1024;
-  static constexpr int STAGES = (4 * STAGE + SCALE_BYTES <= kLdsCap) ? 4 : (3 * STAGE + SCALE_BYTES <= kLdsCap ? 3 : 2);
+  static constexpr int kLdsCap = 160 * 1024 / OCC;       // the CU's LDS split between its workgroups
+  static constexpr int kMaxStages = 12;
+  static constexpr int stages() {
+    int st = kMaxStages;
+    while (st > 2 && st * STAGE + SCALE_BYTES > kLdsCap) --st;
+    return st;
+  }
+  static constexpr int STAGES = stages();
   static constexpr int SCALE_OFF = STAGES * STAGE;
   static constexpr int OUT_BYTES = BM * BN * 4;          // fp32 output tile (bf16 takes half)
   static constexpr int LDS_BYTES = SCALE_OFF + SCALE_BYTES > OUT_BYTES ? SCALE_OFF + SCALE_BYTES : OUT_BYTES;
   static constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
-  static_assert(W_CHUNKS % 4 == 0 && X_CHUNKS % 4 == 0, "stage must split over four waves");
+  // Output-tile chunk swizzle mask for rows of `eb`-byte elements: XOR with
+  // the row's low bits, within the row's 16-byte chunks.
+  static constexpr int out_swz(int eb) { return BN * eb / 16 >= 16 ? 15 : BN * eb / 16 - 1; }
+  static_assert(W_CHUNKS % NW == 0 && X_CHUNKS % NW == 0, "stage must split over the waves");
   static_assert(BN % 64 == 0 && BM % 64 == 0, "scale rows are loaded 64 at a time");
+  static_assert(CHUNKS_PER_WAVE * (STAGES - 1) < 64, "vmcnt range");
   // The residual k-tiles (at most two) stay in their buffers while the last
   // main k-tile is computed from another one.
   static_assert(STAGES >= (kMaxResidual / 2 + kKTileW - 1) / kKTileW + 1, "residual k-tiles need free stages");
@@ -304,15 +308,17 @@ struct TileCfg {
 // consecutive rows at one column on distinct banks.
 __device__ __forceinline__ int half_swap(int row) { return ((row >> 3) ^ (row >> 4)) & 1; }
 
-template <int TN, int TM, int A_BITS>
-__global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, int n_tiles) {
-  using C = TileCfg<TN, TM, A_BITS>;
+template <int TN, int TM, int A_BITS, int WGM>
+__global__ __launch_bounds__(128 * WGM, WGM == 2 ? 2 : 1)   // NT lanes, OCC workgroups per CU
+void serq_tile_kernel(LinearArgs a, int n_tiles) {
+  using C = TileCfg<TN, TM, A_BITS, WGM>;
+  static_assert(C::NT == 128 * WGM && C::OCC == (WGM == 2 ? 2 : 1), "launch bounds");
   constexpr int STAGES = C::STAGES;
   constexpr int CPW = C::CHUNKS_PER_WAVE;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = wave / WGM, wm = wave % WGM;
   const int l32 = lane & 31, h = lane >> 5;
   int tile_n, tile_m;
   tile_coords(blockIdx.x, gridDim.x, n_tiles, tile_n, tile_m);
@@ -503,18 +509,18 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
   // the buffer of k-tile kt -- its fragments are already in registers -- for
   // the loads of k-tile kt + STAGES, read k-tile kt + 1's fragments into
   // `next`, then run k-tile kt's MFMAs from `cur` while those reads land.
+  // Wait until at most `n` k-tiles of this wave's loads are outstanding
+  // (n < STAGES, wave-uniform): vmcnt counts instructions, CPW per k-tile.
+  auto wait_tiles = [&](int n) {
+    static_for<STAGES>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if (n == k) wait_vmcnt<CPW * k>();
+    });
+  };
   auto step = [&](int kt, const Frags& cur, Frags& next) {
     if (kt + 1 < nkt) {
-      const int ahead = min(STAGES - 2, ntot - 2 - kt);   // later k-tiles still in flight
-      if (ahead >= 2) {
-        wait_vmcnt<CPW * 2>();
-      } else if (ahead == 1) {
-        wait_vmcnt<CPW>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): earlier fragment reads and zero-fills done
-      __builtin_amdgcn_s_barrier();
+      wait_tiles(min(STAGES - 2, ntot - 2 - kt));   // later k-tiles may stay in flight
+      lds_barrier();                           // earlier fragment reads and zero-fills done
       if (kt + STAGES < ntot) issue(kt + STAGES, kt % STAGES);
       read_frags((kt + 1) % STAGES, next);
     }
@@ -524,20 +530,8 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
 #pragma unroll
   for (int st = 0; st < STAGES; ++st)
     if (st < ntot) issue(st, st);
-  {
-    const int inflight = min(STAGES, ntot);    // wait for k-tile 0 (and the scales) only
-    if (inflight >= 4) {
-      wait_vmcnt<CPW * 3>();
-    } else if (inflight == 3) {
-      wait_vmcnt<CPW * 2>();
-    } else if (inflight == 2) {
-      wait_vmcnt<CPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-  }
+  wait_tiles(min(STAGES, ntot) - 1);           // k-tile 0 (and the scales) landed
+  lds_barrier();
   Frags f0, f1;
   read_frags(0, f0);
   for (int kt = 0; kt < nkt; kt += 2) {
@@ -548,8 +542,7 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
   // ---- Epilogue. The residual k-tiles were issued during the last main
   // iterations; wait for them, then publish them (and the zero-fills).
   wait_vmcnt<0>();
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   const float* s_sw = reinterpret_cast<const float*>(lds + C::SCALE_OFF);
   const float* s_sr = s_sw + C::BN;
   const float* s_sx = s_sr + C::BN;
@@ -617,7 +610,7 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
 
   // Output tile into LDS, row = token, swizzled 16-byte chunks.
   if (a.y_bf16) {
-    constexpr int RB = C::BN * 2;
+    constexpr int RB = C::BN * 2, SWZ = C::out_swz(2);
     static_for<TM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int row = wm * C::WM + j * 32 + l32;
@@ -631,12 +624,12 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
           const uint2 o = make_uint2(
               pack_bf16x2(__int_as_float(acc[i][j][4 * q]), __int_as_float(acc[i][j][4 * q + 1])),
               pack_bf16x2(__int_as_float(acc[i][j][4 * q + 2]), __int_as_float(acc[i][j][4 * q + 3])));
-          *reinterpret_cast<uint2*>(rp + 16 * (c ^ (row & 15)) + hs) = o;
+          *reinterpret_cast<uint2*>(rp + 16 * (c ^ (row & SWZ)) + hs) = o;
         }
       });
     });
   } else {
-    constexpr int RB = C::BN * 4;
+    constexpr int RB = C::BN * 4, SWZ = C::out_swz(4);
     static_for<TM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int row = wm * C::WM + j * 32 + l32;
@@ -646,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = (wn * C::WN + i * 32 + 8 * q + 4 * h) / 4;
-          *reinterpret_cast<v4i*>(rp + 16 * (c ^ (row & 15))) =
+          *reinterpret_cast<v4i*>(rp + 16 * (c ^ (row & SWZ))) =
               v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
       });
@@ -660,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
     constexpr int EB = decltype(ebc)::value;  // bytes per element
     constexpr int CPR = C::BN * EB / 16;      // chunks per tile row
     constexpr int EPC = 16 / EB;              // elements per chunk
-    constexpr int RPP = kThreads / CPR;       // rows per pass
+    constexpr int RPP = C::NT / CPR;          // rows per pass
     constexpr int PASSES = C::BM / RPP;
     const int c = tid % CPR;
     const int n = n0 + c * EPC;
@@ -669,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = p * RPP + tid / CPR;
-      v[p] = *reinterpret_cast<const uint4*>(lds + row * C::BN * EB + 16 * (c ^ (row & 15)));
+      v[p] = *reinterpret_cast<const uint4*>(lds + row * C::BN * EB + 16 * (c ^ (row & C::out_swz(EB))));
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -699,175 +692,353 @@ __global__ __launch_bounds__(kThreads, 2) void serq_tile_kernel(LinearArgs a, in
 
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 32): the packed weights are streamed from HBM exactly
-// once. A workgroup owns 16 output channels; its four waves take interleaved
-// 256-code chunks of K (128 bytes of each of the 16 weight rows), with two
-// register groups of chunks in flight per wave. Activations (a few KB) come
-// through L2. One wave also takes the residual (r <= 256 codes: one chunk),
-// then the partial int32 accumulators are summed through LDS and wave 0 runs
-// the epilogue.
+// once and the kernel is bound by how many bytes of them are in flight.
+//
+// One persistent eight-wave workgroup per CU (fewer when N is small) walks a
+// strided list of 16-channel groups. K is cut into 256-code chunks (128
+// bytes of each of the 16 weight rows); wave w takes chunks w, w + 8, ... of
+// every group, and the last group of the salient-row residual (r <= 256
+// codes: one chunk of Q(R)) goes to the wave that has one main chunk fewer.
+// Each wave streams its chunks, group after group, through a ring of D
+// register buffers, so D chunks are always in flight and the stream does not
+// drain between groups. Lane (row l16, quarter g) of a chunk holds codes
+// [64 g, 64 g + 64): 32 contiguous weight bytes (16-byte loads), the
+// activations of the same codes for its token, and v_mfma_i32_16x16x64_i8
+// takes them in four steps.
+//
+// At the end of a group every wave leaves its int32 partial sums in LDS
+// (double-buffered by group parity); after one barrier, wave g % 8 adds them
+// up and writes the 16 channels x M tokens, while the others go on with the
+// next group. The scales of all the workgroup's channels are loaded into LDS
+// at kernel start (direct LDS loads, oldest in every wave's load queue).
 // ---------------------------------------------------------------------------
 
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecMaxGroups = 64;          // 16-channel groups per workgroup
+
 template <int MG, int A_BITS>
-__global__ __launch_bounds__(kThreads) void serq_decode_kernel(LinearArgs a) {
-  constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
-  constexpr int CC = 256;                             // codes per chunk
-  constexpr int CWB = CC / 2;                         // weight bytes per row and chunk
-  constexpr int CXB = CC * A_BITS / 8;                // activation bytes per row and chunk
-  constexpr int LW = CWB / 4 / 16;                    // 16-byte weight loads per lane and chunk (2)
-  constexpr int LX = CXB / 4 / 16;                    // 16-byte activation loads per lane and chunk
-  constexpr int U = MG * LX <= 2 ? 2 : 1;             // chunks per register group
-  static_assert(kMaxResidual <= CC, "the residual fits in one chunk");
-  __shared__ v4i red[2][kThreads / 64 - 1][MG][64];
+struct DecCfg {
+  static constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
+  static constexpr int CC = 256;                      // codes per chunk
+  static constexpr int CWB = CC / 2;                  // weight bytes per row and chunk
+  static constexpr int CXB = CC * A_BITS / 8;         // activation bytes per row and chunk
+  static constexpr int LW = CWB / 4 / 16;             // 16-byte weight loads per lane and chunk (2)
+  static constexpr int LX = CXB / 4 / 16;             // 16-byte activation loads per lane and chunk
+  static constexpr int REGS = 4 * (LW + MG * LX);     // VGPRs per buffered chunk
+  static constexpr int D = REGS <= 24 ? 4 : 2;        // ring depth: chunks in flight per wave
+};
+
+template <int MG, int A_BITS>
+__global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs a, int ngroups) {
+  using C = DecCfg<MG, A_BITS>;
+  constexpr int D = C::D, LW = C::LW, LX = C::LX;
+  __shared__ v4i red[2][kDecWaves][2][MG][64];         // [group parity][wave][main, residual][token block][lane]
+  __shared__ float s_sw[kDecMaxGroups * 16], s_sr[kDecMaxGroups * 16], s_sx[64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int l16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
   const int Kb = a.K / 2, Xrow = a.K * A_BITS / 8;
-  const int nrow = min(n0 + l16, a.N - 1);
-  // Lane (row l16, group g) holds codes [CC c + 64 g, CC c + 64 g + 64) of
-  // chunk c for both operands: 32 contiguous weight bytes, so the four lanes
-  // of a row cover its whole 128-byte chunk.
-  const uint8_t* wp = a.Wq + static_cast<size_t>(nrow) * Kb + g * (CWB / 4);
-  const uint8_t* xp[MG];
-  bool xv[MG];
-#pragma unroll
-  for (int j = 0; j < MG; ++j) {
-    const int m = j * 16 + l16;
-    xv[j] = m < a.M;
-    xp[j] = a.Xq + static_cast<size_t>(min(m, a.M - 1)) * Xrow + g * (CXB / 4);
-  }
-  const int nchunks = (a.K + CC - 1) / CC;
+  const int Rb = rq_row_bytes(a.r);
+  const int nchunks = (a.K + C::CC - 1) / C::CC;
+  const int my_groups = (ngroups - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
+  const bool has_res = a.r > 0;
+  const int cpw = (nchunks - wv + kDecWaves - 1) / kDecWaves;      // main chunks of this wave per group
+  const int res_wave = nchunks % kDecWaves;                         // first wave with the smaller count
+  const int items = cpw + (has_res && wv == res_wave ? 1 : 0);     // chunks of this wave per group
+  const int total = my_groups * items;
 
-  // Everything but the streamed weights is loaded up front so that its
-  // latency overlaps the K loop: the epilogue scales and, in wave 1, the
-  // (at most one chunk of) Q(R) and salient activation codes.
-  float sxv[MG];
-#pragma unroll
-  for (int j = 0; j < MG; ++j) sxv[j] = a.sx[min(j * 16 + l16, a.M - 1)];
-  const float4 sw4 = load_scales4(a.sw, n0 + 4 * g, a.N);
-  const float4 sr4 = a.r > 0 ? load_scales4(a.sr, n0 + 4 * g, a.N) : make_float4(0.f, 0.f, 0.f, 0.f);
-  const int r = a.r;
-  const int rb = rq_row_bytes(r);                       // Q(R) row stride (zero-padded)
-  constexpr int kResWave = 1;
-  uint4 rw[LW];
-  uint4 rx[MG][LX];
-#pragma unroll
-  for (int l = 0; l < LW; ++l) rw[l] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int j = 0; j < MG; ++j)
-#pragma unroll
-    for (int l = 0; l < LX; ++l) rx[j][l] = make_uint4(0, 0, 0, 0);
-  if (r > 0 && wave == kResWave) {
-    const uint8_t* rrow = a.Rq + static_cast<size_t>(nrow) * rb;
+  // Scales of every channel this workgroup writes, and the token scales, into
+  // LDS: lane i of a load covers channel 16 (group slot) + (i % 16).
+  {
+    const uint32_t lsw = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_sw));
+    const uint32_t lsr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_sr));
+    const uint32_t lsx = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_sx));
+    for (int q = wv; q < (my_groups + 3) / 4 * 2 + 1; q += kDecWaves) {
+      if (q == 0) {                                     // token scales
+        if (lane < a.M) dma4(a.sx, 4 * lane, lsx);
+        continue;
+      }
+      const int qq = q - 1, arr = qq & 1, blk = qq >> 1;   // 4 groups (64 channels) per load
+      const int slot = 4 * blk + (lane >> 4);
+      const int n = (static_cast<int>(blockIdx.x) + slot * static_cast<int>(gridDim.x)) * 16 + l16;
+      if (arr == 1 && !has_res) continue;
+      if (slot < my_groups && n < a.N)
+        dma4(arr ? a.sr : a.sw, 4 * n, (arr ? lsr : lsw) + 256 * blk);
+    }
+  }
+
+  // Item i of this wave's stream: group slot i / items, main chunk
+  // wv + 8 (i % items) or, as the last item of the residual wave, Q(R).
+  struct Buf {
+    uint4 w[LW];
+    uint4 x[MG][LX];
+  };
+  auto load = [&](int i, Buf& b) {
+    const int gs = i / items, j = i - gs * items;
+    const int n = (static_cast<int>(blockIdx.x) + gs * static_cast<int>(gridDim.x)) * 16 + l16;
+    const int nrow = min(n, a.N - 1);
+    const bool res = j >= cpw;
+    const int c = res ? 0 : wv + kDecWaves * j;
+    const uint8_t* wp = res ? a.Rq + static_cast<size_t>(nrow) * Rb : a.Wq + static_cast<size_t>(nrow) * Kb;
+    const int wlim = res ? Rb : Kb;
 #pragma unroll
     for (int l = 0; l < LW; ++l) {
-      const int wo = g * (CWB / 4) + 16 * l;
-      rw[l] = make_uint4(load_dword_masked(rrow, wo, rb), load_dword_masked(rrow, wo + 4, rb),
-                         load_dword_masked(rrow, wo + 8, rb), load_dword_masked(rrow, wo + 12, rb));
+      const int o = c * C::CWB + g * (C::CWB / 4) + 16 * l;
+      b.w[l] = o < wlim ? *reinterpret_cast<const uint4*>(wp + o) : make_uint4(0, 0, 0, 0);
     }
-    const int xlim = r * A_BITS / 8;
 #pragma unroll
-    for (int j = 0; j < MG; ++j) {
-      if (!xv[j]) continue;
-      const uint8_t* xrow = xp[j] - g * (CXB / 4);
+    for (int t = 0; t < MG; ++t) {
+      const int m = t * 16 + l16;
+      const uint8_t* xp = a.Xq + static_cast<size_t>(min(m, a.M - 1)) * Xrow;
 #pragma unroll
       for (int l = 0; l < LX; ++l) {
-        const int xo = g * (CXB / 4) + 16 * l;
-        rx[j][l] = make_uint4(load_dword_masked(xrow, xo, xlim), load_dword_masked(xrow, xo + 4, xlim),
-                              load_dword_masked(xrow, xo + 8, xlim), load_dword_masked(xrow, xo + 12, xlim));
+        const int o = c * C::CXB + g * (C::CXB / 4) + 16 * l;
+        b.x[t][l] = (m < a.M && o < Xrow) ? *reinterpret_cast<const uint4*>(xp + o) : make_uint4(0, 0, 0, 0);
       }
-    }
-  }
-
-  // The K loop streams groups of U chunks per wave (chunk c = wave + 4 u);
-  // the loads of the next group are issued into a second register buffer
-  // before the current group is consumed.
-  struct Group {
-    uint4 w[U][LW];
-    uint4 x[U][MG][LX];
-  };
-  auto load_group = [&](int c0, Group& gr) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 4 * u;
-#pragma unroll
-      for (int l = 0; l < LW; ++l) {
-        const int o = c * CWB + g * (CWB / 4) + 16 * l;
-        gr.w[u][l] = (c < nchunks && o < Kb) ? *reinterpret_cast<const uint4*>(wp + c * CWB + 16 * l)
-                                             : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < MG; ++j)
-#pragma unroll
-        for (int l = 0; l < LX; ++l) {
-          const int o = c * CXB + g * (CXB / 4) + 16 * l;
-          gr.x[u][j][l] = (c < nchunks && xv[j] && o < Xrow)
-                              ? *reinterpret_cast<const uint4*>(xp[j] + c * CXB + 16 * l)
-                              : make_uint4(0, 0, 0, 0);
-        }
     }
   };
   // One chunk: four MFMA steps of 16 codes per lane.
-  auto dot_chunk = [&](const uint4 (&w)[LW], const uint4 (&x)[MG][LX], v4i (&acc)[MG]) {
+  auto dot = [&](const Buf& b, v4i (&acc)[MG]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint4 ww = w[s >> 1];
+      const uint4 ww = b.w[s >> 1];
       const v4i wa = (s & 1) ? widen16(ww.z, ww.w) : widen16(ww.x, ww.y);
 #pragma unroll
-      for (int j = 0; j < MG; ++j) {
+      for (int t = 0; t < MG; ++t) {
         v4i xb;
         if constexpr (A_BITS == 4) {
-          const uint4 xx = x[j][s >> 1];
+          const uint4 xx = b.x[t][s >> 1];
           xb = (s & 1) ? widen16(xx.z, xx.w) : widen16(xx.x, xx.y);
         } else {
-          xb = split16(x[j][s]);
+          xb = split16(b.x[t][s]);
         }
-        acc[j] = mfma(wa, xb, acc[j]);
+        acc[t] = mfma(wa, xb, acc[t]);
       }
     }
   };
 
-  v4i acc[MG];
+  v4i acc[MG], accr[MG];
 #pragma unroll
-  for (int j = 0; j < MG; ++j) acc[j] = v4i{0, 0, 0, 0};
-  {
-    Group g0, g1;
-    int c0 = wave;
-    load_group(c0, g0);
-    for (; c0 < nchunks; c0 += 8 * U) {
-      if (c0 + 4 * U < nchunks) load_group(c0 + 4 * U, g1);
-#pragma unroll
-      for (int u = 0; u < U; ++u) dot_chunk(g0.w[u], g0.x[u], acc);
-      if (c0 + 4 * U >= nchunks) break;
-      if (c0 + 8 * U < nchunks) load_group(c0 + 8 * U, g0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) dot_chunk(g1.w[u], g1.x[u], acc);
-    }
-  }
-  v4i accr[MG];
-#pragma unroll
-  for (int j = 0; j < MG; ++j) accr[j] = v4i{0, 0, 0, 0};
-  if (r > 0 && wave == kResWave) dot_chunk(rw, rx, accr);
+  for (int t = 0; t < MG; ++t) acc[t] = accr[t] = v4i{0, 0, 0, 0};
 
-  // cross-wave reduction through LDS
-  if (wave > 0) {
+  // End of group slot gs: partial sums to LDS, one barrier, then wave gs % 8
+  // reduces and writes the outputs.
+  auto group_end = [&](int gs) {
+    const int par = gs & 1;
 #pragma unroll
-    for (int j = 0; j < MG; ++j) {
-      red[0][wave - 1][j][lane] = acc[j];
-      red[1][wave - 1][j][lane] = accr[j];
+    for (int t = 0; t < MG; ++t) {
+      red[par][wv][0][t][lane] = acc[t];
+      red[par][wv][1][t][lane] = accr[t];
+      acc[t] = accr[t] = v4i{0, 0, 0, 0};
+    }
+    lds_barrier();                              // the chunk loads in flight stay in flight
+    if (wv != gs % kDecWaves) return;
+    v4i sm[MG], sr[MG];
+#pragma unroll
+    for (int t = 0; t < MG; ++t) {
+      sm[t] = red[par][0][0][t][lane];
+      sr[t] = red[par][0][1][t][lane];
+#pragma unroll
+      for (int w = 1; w < kDecWaves; ++w) {
+        sm[t] += red[par][w][0][t][lane];
+        sr[t] += red[par][w][1][t][lane];
+      }
+    }
+    const int n0 = (static_cast<int>(blockIdx.x) + gs * static_cast<int>(gridDim.x)) * 16;
+    const float4 w4 = *reinterpret_cast<const float4*>(s_sw + 16 * gs + 4 * g);
+    const float4 r4 = has_res ? *reinterpret_cast<const float4*>(s_sr + 16 * gs + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < MG; ++t) {
+      const int m = t * 16 + l16;
+      store4<C::SHIFT>(a, sm[t], sr[t], m, n0 + 4 * g, m < a.M ? s_sx[m] : 0.0f, w4, r4);
+    }
+  };
+
+  // The scale loads must have landed before the first group_end barrier: a
+  // wave with chunks waits for its first chunk (issued after them) before
+  // that barrier; a wave without chunks waits here.
+  Buf buf[D];
+  if (items == 0) {
+    wait_vmcnt<0>();
+    for (int gs = 0; gs < my_groups; ++gs) group_end(gs);
+    return;
+  }
+  static_for<D>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if (k < total) load(k, buf[k]);
+  });
+  for (int base = 0; base < total; base += D) {
+    static_for<D>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const int i = base + k;
+      if (i < total) {
+        const int j = i % items;
+        if (j < cpw)
+          dot(buf[k], acc);
+        else
+          dot(buf[k], accr);
+        if (i + D < total) load(i + D, buf[k]);
+        if (j == items - 1) group_end(i / items);
+      }
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMV kernel (W4A4, M <= 4 tokens): v_dot8c_i32_i4 multiplies eight packed
+// int4 codes of each operand and adds to an int32, in the canonical nibble
+// order of both Q(W^) and the activation codes, so the packed bytes are used
+// as loaded -- no widening, and no matrix-core work thrown away on missing
+// tokens.
+//
+// A wave streams 8 weight rows over a K range: each load instruction takes
+// 128 contiguous bytes (one cache line) of each of the 8 rows, lane (row
+// l / 8, part l % 8) 16 of them, with kGemvRing instructions in flight. A
+// four-wave workgroup covers 4 / KP row octets, each split into KP K ranges
+// (KP from N, so that small layers still spread over every CU). The
+// activation rows (M x K/2 bytes) are loaded into LDS once per workgroup and
+// read back in broadcast. At the end each row's partial sums are added over
+// its 8 lanes, then over the KP waves through LDS, and the K range 0 wave
+// writes the outputs. The salient-row residual is one more instruction of the
+// last K range: the zero-padded Q(R) rows (at most 128 bytes) against the
+// first activation codes.
+// ---------------------------------------------------------------------------
+
+constexpr int kGemvRing = 8;                // load instructions in flight per wave
+constexpr int kGemvMaxX = 64 * 1024;        // LDS bytes for the activation rows
+constexpr int kGemvMaxTokens = 4;
+
+template <int MT, int KP>
+__global__ __launch_bounds__(kThreads) void serq_gemv_kernel(LinearArgs a) {
+  constexpr int OCT = 4 / KP;                         // row octets per workgroup
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];   // [MT][Kb] activation codes
+  __shared__ int red[4][2][MT][64];                   // [wave][main, residual][token][lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int oct = wv / KP, kp = wv % KP;
+  const int r8 = lane >> 3, part = lane & 7;
+  const int Kb = a.K / 2;
+  const int Rb = rq_row_bytes(a.r);
+  const int n = (static_cast<int>(blockIdx.x) * OCT + oct) * 8 + r8;   // this lane's channel
+  const int nrow = min(n, a.N - 1);
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+
+  // Scales of this lane's channel and the token scales, oldest loads first.
+  const float swn = a.sw[nrow];
+  const float srn = a.r > 0 ? a.sr[nrow] : 0.0f;
+  float sxv[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) sxv[t] = a.sx[t];
+  // Activation rows into LDS, 1 KB per load instruction over the four waves.
+  const int nx = (MT * Kb + 1023) / 1024;
+  for (int q = wv; q < nx; q += 4) {
+    const int off = 1024 * q + 16 * lane;
+    if (off < MT * Kb) dma16(a.Xq, static_cast<uint32_t>(off), lds_base + 1024 * q);
+  }
+
+  // This wave's K range: 128-byte lines [l0, l1) of its 8 rows, plus the
+  // residual line for the last range.
+  const int lines = (Kb + 127) / 128;
+  const int per = (lines + KP - 1) / KP;
+  const int l0 = min(kp * per, lines), l1 = min(l0 + per, lines);
+  const bool res_here = a.r > 0 && kp == KP - 1;
+  const int total = (l1 - l0) + (res_here ? 1 : 0);
+  const uint8_t* wrow = a.Wq + static_cast<size_t>(nrow) * Kb + 16 * part;
+  const uint8_t* rrow = a.r > 0 ? a.Rq + static_cast<size_t>(nrow) * Rb + 16 * part : nullptr;
+  auto load = [&](int i, uint4& w) {
+    if (l0 + i < l1) {
+      const int off = 128 * (l0 + i) + 16 * part;
+      w = off < Kb ? *reinterpret_cast<const uint4*>(wrow + 128 * (l0 + i)) : make_uint4(0, 0, 0, 0);
+    } else {
+      w = 16 * part < Rb ? *reinterpret_cast<const uint4*>(rrow) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 buf[kGemvRing];
+  static_for<kGemvRing>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if (k < total) load(k, buf[k]);
+  });
+  // This wave's activation loads are older than its weight loads: once at
+  // most the weight loads are outstanding, its part of LDS is written.
+  const int issued = min(total, kGemvRing);
+  static_for<kGemvRing + 1>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if (issued == k) wait_vmcnt<k>();
+  });
+  lds_barrier();
+
+  int acc[MT], accr[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = accr[t] = 0;
+  auto consume = [&](int i, const uint4& w) {
+    const bool res = l0 + i >= l1;
+    const int off = (res ? 0 : 128 * (l0 + i)) + 16 * part;
+    const bool inx = off < Kb;                        // (Q(R)'s padding is zero)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint4 x = inx ? *reinterpret_cast<const uint4*>(lds + t * Kb + off) : make_uint4(0, 0, 0, 0);
+      int d = res ? accr[t] : acc[t];
+      d = __builtin_amdgcn_sdot8(static_cast<int>(w.x), static_cast<int>(x.x), d, false);
+      d = __builtin_amdgcn_sdot8(static_cast<int>(w.y), static_cast<int>(x.y), d, false);
+      d = __builtin_amdgcn_sdot8(static_cast<int>(w.z), static_cast<int>(x.z), d, false);
+      d = __builtin_amdgcn_sdot8(static_cast<int>(w.w), static_cast<int>(x.w), d, false);
+      if (res) accr[t] = d; else acc[t] = d;
+    }
+  };
+  for (int base = 0; base < total; base += kGemvRing) {
+    static_for<kGemvRing>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const int i = base + k;
+      if (i < total) {
+        const uint4 w = buf[k];
+        if (i + kGemvRing < total) load(i + kGemvRing, buf[k]);
+        consume(i, w);
+      }
+    });
+  }
+
+  // Sum over the row's 8 lanes, then over the KP waves of the row octet.
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      acc[t] += __shfl_xor(acc[t], off, 64);
+      accr[t] += __shfl_xor(accr[t], off, 64);
     }
   }
-  __syncthreads();
-  if (wave != 0) return;
+  if (KP > 1) {
 #pragma unroll
-  for (int w = 0; w < kThreads / 64 - 1; ++w)
-#pragma unroll
-    for (int j = 0; j < MG; ++j) {
-      acc[j] += red[0][w][j][lane];
-      accr[j] += red[1][w][j][lane];
+    for (int t = 0; t < MT; ++t) {
+      red[wv][0][t][lane] = acc[t];
+      red[wv][1][t][lane] = accr[t];
     }
+    lds_barrier();
+    if (kp != 0) return;
 #pragma unroll
-  for (int j = 0; j < MG; ++j) store4<SHIFT>(a, acc[j], accr[j], j * 16 + l16, n0 + 4 * g, sxv[j], sw4, sr4);
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int k = 1; k < KP; ++k) {
+        acc[t] += red[wv + k][0][t][lane];
+        accr[t] += red[wv + k][1][t][lane];
+      }
+  }
+  if (part != 0 || n >= a.N) return;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    if (t >= a.M) break;
+    const size_t idx = static_cast<size_t>(t) * a.N + n;
+    if (a.dbg_main) {
+      a.dbg_main[idx] = acc[t];
+      a.dbg_res[idx] = accr[t];
+    }
+    const float y = sxv[t] * __builtin_fmaf(srn, static_cast<float>(accr[t]), swn * static_cast<float>(acc[t]));
+    if (a.y_bf16)
+      static_cast<uint16_t*>(a.Y)[idx] = f32_to_bf16_rne(y);
+    else
+      static_cast<float*>(a.Y)[idx] = y;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -909,26 +1080,62 @@ __global__ __launch_bounds__(kThreads) void serq_generic_kernel(LinearArgs a) {
     static_cast<float*>(a.Y)[idx] = y;
 }
 
-template <int TN, int TM, int A_BITS>
+template <int TN, int TM, int A_BITS, int WGM>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
-  using C = TileCfg<TN, TM, A_BITS>;
+  using C = TileCfg<TN, TM, A_BITS, WGM>;
   static bool attr_set = false;  // idempotent; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_tile_kernel<TN, TM, A_BITS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_tile_kernel<TN, TM, A_BITS, WGM>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int n_tiles = (a.N + C::BN - 1) / C::BN;
   const int m_tiles = (a.M + C::BM - 1) / C::BM;
-  serq_tile_kernel<TN, TM, A_BITS><<<dim3(n_tiles * m_tiles), dim3(kThreads), C::LDS_BYTES, st>>>(a, n_tiles);
+  serq_tile_kernel<TN, TM, A_BITS, WGM><<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS_BYTES, st>>>(a, n_tiles);
   return hipGetLastError();
+}
+
+// One persistent workgroup per CU (one per 16-channel group when there are
+// fewer groups), more only if a workgroup would own over kDecMaxGroups groups.
+template <int MG, int A_BITS>
+hipError_t launch_decode(const LinearArgs& a, hipStream_t st) {
+  const int ngroups = (a.N + 15) / 16;
+  int grid = min(ngroups, kCUs);
+  grid = max(grid, (ngroups + kDecMaxGroups - 1) / kDecMaxGroups);
+  serq_decode_kernel<MG, A_BITS><<<dim3(grid), dim3(kDecThreads), 0, st>>>(a, ngroups);
+  return hipGetLastError();
+}
+
+template <int MT, int KP>
+hipError_t launch_gemv_kp(const LinearArgs& a, hipStream_t st) {
+  const int octets = (a.N + 7) / 8;
+  const int grid = (octets + (4 / KP) - 1) / (4 / KP);
+  const int lds = (MT * (a.K / 2) + 15) / 16 * 16;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_gemv_kernel<MT, KP>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxX);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  serq_gemv_kernel<MT, KP><<<dim3(grid), dim3(kThreads), lds, st>>>(a);
+  return hipGetLastError();
+}
+
+// Four K ranges per row octet: short-lived waves with a shallow ring
+// measured faster than longer ones on every LLaMA shape (more resident
+// workgroups per CU, more lines in flight).
+template <int MT>
+hipError_t launch_gemv(const LinearArgs& a, hipStream_t st) {
+  return launch_gemv_kp<MT, 4>(a, st);
 }
 
 template <int A_BITS>
 hipError_t launch_tile_bits(const LinearArgs& a, const LinearPlan& p, hipStream_t st) {
-  if (p.tn == 2 && p.tm == 2) return launch_tile<2, 2, A_BITS>(a, st);
-  if (p.tn == 2 && p.tm == 1) return launch_tile<2, 1, A_BITS>(a, st);
+  if (p.tn == 2 && p.tm == 2 && p.wgm == 2) return launch_tile<2, 2, A_BITS, 2>(a, st);
+  if (p.tn == 2 && p.tm == 1 && p.wgm == 2) return launch_tile<2, 1, A_BITS, 2>(a, st);
+  if (p.tn == 1 && p.tm == 1 && p.wgm == 2) return launch_tile<1, 1, A_BITS, 2>(a, st);
   return hipErrorInvalidValue;
 }
 
@@ -939,33 +1146,36 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   const bool small = static_cast<uint64_t>(N) * (K / 2) < (1ull << 32) &&
                      static_cast<uint64_t>(M) * K * a_bits / 8 < (1ull << 32);
   const bool fast = (K % 32 == 0) && (r % 8 == 0) && r <= kMaxResidual && small;
-  if (!fast) return {LinearKernel::kGeneric, 0, 0, "generic"};
-  if (M <= 16) return {LinearKernel::kDecode16, 0, 0, "decode16"};
-  if (M <= 32) return {LinearKernel::kDecode32, 0, 0, "decode32"};
-  // Macro tiles of 128 x 128 (64 x 128 for up to 64 tokens), two
-  // workgroups per CU.
-  if (M > 64) return {LinearKernel::kTile, 2, 2, "tile128x128"};
-  return {LinearKernel::kTile, 2, 1, "tile64x128"};
+  if (!fast) return {LinearKernel::kGeneric, 0, 0, 0, "generic"};
+  // A few tokens of W4A4 whose activation rows fit in LDS: int4 dot products.
+  if (a_bits == 4 && M <= kGemvMaxTokens && static_cast<long>(M) * (K / 2) <= kGemvMaxX)
+    return {LinearKernel::kGemv, 0, 0, 0, "gemv"};
+  if (M <= 16) return {LinearKernel::kDecode16, 0, 0, 0, "decode16"};
+  if (M <= 32) return {LinearKernel::kDecode32, 0, 0, 0, "decode32"};
+  // Macro tiles, two four-wave workgroups per CU: the two run independently,
+  // so one's barrier and load waits are covered by the other's MFMAs. (One
+  // eight-wave 256 x 128 workgroup per CU, lockstep at every k-tile barrier,
+  // measured 12-20 % slower on the LLaMA shapes.) The largest tile that still
+  // gives every CU a workgroup; smaller tiles keep more k-tiles in flight.
+  auto tiles = [&](int bm, int bn) { return static_cast<long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (M > 64 && tiles(128, 128) >= kCUs) return {LinearKernel::kTile, 2, 2, 2, "tile128x128"};
+  if (tiles(64, 128) >= kCUs) return {LinearKernel::kTile, 2, 1, 2, "tile64x128"};
+  return {LinearKernel::kTile, 1, 1, 2, "tile64x64"};
 }
 
 hipError_t launch_linear(const LinearArgs& a, const LinearPlan& p, hipStream_t st) {
   switch (p.kind) {
-    case LinearKernel::kDecode16: {
-      const dim3 grid((a.N + 15) / 16);
-      if (a.a_bits == 4)
-        serq_decode_kernel<1, 4><<<grid, dim3(kThreads), 0, st>>>(a);
-      else
-        serq_decode_kernel<1, 8><<<grid, dim3(kThreads), 0, st>>>(a);
-      return hipGetLastError();
-    }
-    case LinearKernel::kDecode32: {
-      const dim3 grid((a.N + 15) / 16);
-      if (a.a_bits == 4)
-        serq_decode_kernel<2, 4><<<grid, dim3(kThreads), 0, st>>>(a);
-      else
-        serq_decode_kernel<2, 8><<<grid, dim3(kThreads), 0, st>>>(a);
-      return hipGetLastError();
-    }
+    case LinearKernel::kGemv:
+      switch (a.M) {
+        case 1: return launch_gemv<1>(a, st);
+        case 2: return launch_gemv<2>(a, st);
+        case 3: return launch_gemv<3>(a, st);
+        default: return launch_gemv<4>(a, st);
+      }
+    case LinearKernel::kDecode16:
+      return a.a_bits == 4 ? launch_decode<1, 4>(a, st) : launch_decode<1, 8>(a, st);
+    case LinearKernel::kDecode32:
+      return a.a_bits == 4 ? launch_decode<2, 4>(a, st) : launch_decode<2, 8>(a, st);
     case LinearKernel::kTile:
       return a.a_bits == 4 ? launch_tile_bits<4>(a, p, st) : launch_tile_bits<8>(a, p, st);
     case LinearKernel::kGeneric: {

@@ -28,11 +28,12 @@ struct LinearArgs {
 __host__ __device__ constexpr int rq_row_bytes(int r) { return (r + 31) / 32 * 16; }
 
 // Kernel families serq_linear chooses between.
-enum class LinearKernel { kDecode16, kDecode32, kTile, kGeneric };
+enum class LinearKernel { kGemv, kDecode16, kDecode32, kTile, kGeneric };
 
 struct LinearPlan {
   LinearKernel kind;
   int tn, tm;          // per-wave 32x32 block counts (kTile only)
+  int wgm;             // wave rows (token direction) per workgroup (kTile only)
   const char* name;
 };
 
