@@ -118,6 +118,8 @@ LINEAR_CASES = [
     (16, 512, 48, 256, "decode16"),
     (17, 1024, 50, 24, "decode32"),
     (32, 512, 64, 256, "decode32"),
+    (16, 1056, 4112, 72, "decode16"),     # activations resident in LDS; some workgroups take two groups
+    (24, 2080, 8200, 0, "decode32"),      # resident activations, r = 0
     (40, 1056, 130, 72, "tile64x64"),
     (64, 96, 256, 96, "tile64x64"),       # K shorter than one k-tile, r = K
     (100, 512, 300, 64, "tile64x64"),

@@ -697,27 +697,33 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
 // One persistent eight-wave workgroup per CU (fewer when N is small) walks a
 // strided list of 16-channel groups. K is cut into 256-code chunks (128
 // bytes of each of the 16 weight rows); wave w takes chunks w, w + 8, ... of
-// every group, and the last group of the salient-row residual (r <= 256
-// codes: one chunk of Q(R)) goes to the wave that has one main chunk fewer.
-// Each wave streams its chunks, group after group, through a ring of D
-// register buffers, so D chunks are always in flight and the stream does not
-// drain between groups. Lane (row l16, quarter g) of a chunk holds codes
-// [64 g, 64 g + 64): 32 contiguous weight bytes (16-byte loads), the
-// activations of the same codes for its token, and v_mfma_i32_16x16x64_i8
-// takes them in four steps.
+// every group, and the salient-row residual (r <= 256 codes: one chunk of
+// Q(R)) goes to the wave that has one main chunk fewer. Each wave streams its
+// chunks, group after group, through a ring of D register buffers, so D
+// chunks are always in flight and the stream does not drain between groups.
+// Lane (row l16, quarter g) of a chunk holds codes [64 g, 64 g + 64): 32
+// contiguous weight bytes (16-byte loads), the activations of the same codes
+// for its token, and v_mfma_i32_16x16x64_i8 takes them in four steps.
 //
-// At the end of a group every wave leaves its int32 partial sums in LDS
-// (double-buffered by group parity); after one barrier, wave g % 8 adds them
-// up and writes the 16 channels x M tokens, while the others go on with the
-// next group. The scales of all the workgroup's channels are loaded into LDS
-// at kernel start (direct LDS loads, oldest in every wave's load queue).
+// When all M activation rows fit in LDS (XL) they are loaded there once, at
+// kernel start, with rows padded by 16 bytes so that the 16 tokens of a read
+// fall on distinct banks; the ring then carries only weights. Otherwise the
+// activation codes ride in the ring beside them, read through L2.
+//
+// At the end of a group every wave adds its int32 partial sums into an LDS
+// accumulator (double-buffered by group parity); after one barrier, wave
+// g % 8 reads it back, clears it and writes the 16 channels x M tokens, while
+// the others go on with the next group. The scales of all the workgroup's
+// channels are loaded into LDS at kernel start (direct LDS loads, oldest in
+// every wave's load queue).
 // ---------------------------------------------------------------------------
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecMaxGroups = 64;          // 16-channel groups per workgroup
+constexpr int kDecMaxX = 136 * 1024;       // LDS bytes for resident activation rows
 
-template <int MG, int A_BITS>
+template <int MG, int A_BITS, bool XL>
 struct DecCfg {
   static constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
   static constexpr int CC = 256;                      // codes per chunk
@@ -725,21 +731,31 @@ struct DecCfg {
   static constexpr int CXB = CC * A_BITS / 8;         // activation bytes per row and chunk
   static constexpr int LW = CWB / 4 / 16;             // 16-byte weight loads per lane and chunk (2)
   static constexpr int LX = CXB / 4 / 16;             // 16-byte activation loads per lane and chunk
-  static constexpr int REGS = 4 * (LW + MG * LX);     // VGPRs per buffered chunk
-  static constexpr int D = REGS <= 24 ? 4 : 2;        // ring depth: chunks in flight per wave
+  static constexpr int REGS = 4 * (LW + (XL ? 0 : MG * LX));   // VGPRs per buffered chunk
+  static constexpr int D = REGS <= 8 ? 8 : (REGS <= 24 ? 4 : 2);   // ring depth: chunks in flight per wave
+  static constexpr int SCALE_BYTES = 4 * (32 * kDecMaxGroups + 64);
+  static constexpr int RED_BYTES = 2 * 2 * MG * 64 * 16;           // [parity][main, residual][token block][lane] v4i
 };
 
-template <int MG, int A_BITS>
-__global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs a, int ngroups) {
-  using C = DecCfg<MG, A_BITS>;
-  constexpr int D = C::D, LW = C::LW, LX = C::LX;
-  __shared__ v4i red[2][kDecWaves][2][MG][64];         // [group parity][wave][main, residual][token block][lane]
-  __shared__ float s_sw[kDecMaxGroups * 16], s_sr[kDecMaxGroups * 16], s_sx[64];
+// LDS bytes of the decode kernel: resident activations (XL), scales, sums.
+template <int MG, int A_BITS, bool XL>
+constexpr int dec_x_stride(int K) { return K * A_BITS / 8 + 16; }
 
+template <int MG, int A_BITS, bool XL>
+__global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs a, int ngroups) {
+  using C = DecCfg<MG, A_BITS, XL>;
+  constexpr int D = C::D, LW = C::LW, LX = C::LX;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int l16 = lane & 15, g = lane >> 4;
   const int Kb = a.K / 2, Xrow = a.K * A_BITS / 8;
+  const int XS = dec_x_stride<MG, A_BITS, XL>(a.K);   // LDS row stride of resident activations
+  const int xbytes = XL ? a.M * XS : 0;
+  float* s_sw = reinterpret_cast<float*>(lds + xbytes);
+  float* s_sr = s_sw + 16 * kDecMaxGroups;
+  float* s_sx = s_sr + 16 * kDecMaxGroups;
+  int* red = reinterpret_cast<int*>(lds + xbytes + C::SCALE_BYTES);
   const int Rb = rq_row_bytes(a.r);
   const int nchunks = (a.K + C::CC - 1) / C::CC;
   const int my_groups = (ngroups - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
@@ -748,13 +764,22 @@ __global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs 
   const int res_wave = nchunks % kDecWaves;                         // first wave with the smaller count
   const int items = cpw + (has_res && wv == res_wave ? 1 : 0);     // chunks of this wave per group
   const int total = my_groups * items;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
 
-  // Scales of every channel this workgroup writes, and the token scales, into
-  // LDS: lane i of a load covers channel 16 (group slot) + (i % 16).
+  // Direct LDS loads first (the oldest in every wave's queue): the
+  // activation rows (XL), the scales of every channel this workgroup writes
+  // (lane i of a load covers channel 16 (group slot) + (i % 16)) and the
+  // token scales. The partial-sum buffers start at zero.
+  if constexpr (XL) {
+    const int per_row = (Xrow + 1023) / 1024;
+    for (int q = wv; q < a.M * per_row; q += kDecWaves) {
+      const int t = q / per_row, c = q - t * per_row;
+      if (1024 * c + 16 * lane < Xrow)
+        dma16(a.Xq + static_cast<size_t>(t) * Xrow, 1024 * c + 16 * lane, lds_base + t * XS + 1024 * c);
+    }
+  }
   {
-    const uint32_t lsw = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_sw));
-    const uint32_t lsr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_sr));
-    const uint32_t lsx = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_sx));
+    const uint32_t lsw = lds_base + xbytes, lsr = lsw + 64 * kDecMaxGroups, lsx = lsr + 64 * kDecMaxGroups;
     for (int q = wv; q < (my_groups + 3) / 4 * 2 + 1; q += kDecWaves) {
       if (q == 0) {                                     // token scales
         if (lane < a.M) dma4(a.sx, 4 * lane, lsx);
@@ -764,16 +789,20 @@ __global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs 
       const int slot = 4 * blk + (lane >> 4);
       const int n = (static_cast<int>(blockIdx.x) + slot * static_cast<int>(gridDim.x)) * 16 + l16;
       if (arr == 1 && !has_res) continue;
-      if (slot < my_groups && n < a.N)
-        dma4(arr ? a.sr : a.sw, 4 * n, (arr ? lsr : lsw) + 256 * blk);
+      if (slot < my_groups && n < a.N) dma4(arr ? a.sr : a.sw, 4 * n, (arr ? lsr : lsw) + 256 * blk);
     }
   }
+  for (int i = threadIdx.x; i < C::RED_BYTES / 4; i += kDecThreads) red[i] = 0;
 
   // Item i of this wave's stream: group slot i / items, main chunk
   // wv + 8 (i % items) or, as the last item of the residual wave, Q(R).
+  // Every load is issued (past the end of a row it reads the row's last 16
+  // bytes and the value is dropped), so a chunk is always LPC load
+  // instructions -- the count the start-up wait below relies on.
+  constexpr int LPC = LW + (XL ? 0 : MG * LX);
   struct Buf {
     uint4 w[LW];
-    uint4 x[MG][LX];
+    uint4 x[XL ? 1 : MG][XL ? 1 : LX];
   };
   auto load = [&](int i, Buf& b) {
     const int gs = i / items, j = i - gs * items;
@@ -786,21 +815,39 @@ __global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs 
 #pragma unroll
     for (int l = 0; l < LW; ++l) {
       const int o = c * C::CWB + g * (C::CWB / 4) + 16 * l;
-      b.w[l] = o < wlim ? *reinterpret_cast<const uint4*>(wp + o) : make_uint4(0, 0, 0, 0);
+      const uint4 v = *reinterpret_cast<const uint4*>(wp + min(o, wlim - 16));
+      b.w[l] = o < wlim ? v : make_uint4(0, 0, 0, 0);
     }
+    if constexpr (!XL) {
 #pragma unroll
-    for (int t = 0; t < MG; ++t) {
-      const int m = t * 16 + l16;
-      const uint8_t* xp = a.Xq + static_cast<size_t>(min(m, a.M - 1)) * Xrow;
+      for (int t = 0; t < MG; ++t) {
+        const int m = t * 16 + l16;
+        const uint8_t* xp = a.Xq + static_cast<size_t>(min(m, a.M - 1)) * Xrow;
 #pragma unroll
-      for (int l = 0; l < LX; ++l) {
-        const int o = c * C::CXB + g * (C::CXB / 4) + 16 * l;
-        b.x[t][l] = (m < a.M && o < Xrow) ? *reinterpret_cast<const uint4*>(xp + o) : make_uint4(0, 0, 0, 0);
+        for (int l = 0; l < LX; ++l) {
+          const int o = c * C::CXB + g * (C::CXB / 4) + 16 * l;
+          const uint4 v = *reinterpret_cast<const uint4*>(xp + min(o, Xrow - 16));
+          b.x[t][l] = (m < a.M && o < Xrow) ? v : make_uint4(0, 0, 0, 0);
+        }
       }
     }
   };
-  // One chunk: four MFMA steps of 16 codes per lane.
-  auto dot = [&](const Buf& b, v4i (&acc)[MG]) {
+  // One chunk (main chunk c, or the residual chunk at c = 0): four MFMA
+  // steps of 16 codes per lane.
+  auto dot = [&](const Buf& b, int c, v4i (&acc)[MG]) {
+    uint4 xs[MG][LX];
+#pragma unroll
+    for (int t = 0; t < MG; ++t)
+#pragma unroll
+      for (int l = 0; l < LX; ++l) {
+        if constexpr (XL) {
+          const int o = c * C::CXB + g * (C::CXB / 4) + 16 * l;
+          const int m = t * 16 + l16;
+          xs[t][l] = (m < a.M && o < Xrow) ? *reinterpret_cast<const uint4*>(lds + m * XS + o) : make_uint4(0, 0, 0, 0);
+        } else {
+          xs[t][l] = b.x[t][l];
+        }
+      }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint4 ww = b.w[s >> 1];
@@ -809,10 +856,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs 
       for (int t = 0; t < MG; ++t) {
         v4i xb;
         if constexpr (A_BITS == 4) {
-          const uint4 xx = b.x[t][s >> 1];
+          const uint4 xx = xs[t][s >> 1];
           xb = (s & 1) ? widen16(xx.z, xx.w) : widen16(xx.x, xx.y);
         } else {
-          xb = split16(b.x[t][s]);
+          xb = split16(xs[t][s]);
         }
         acc[t] = mfma(wa, xb, acc[t]);
       }
@@ -823,28 +870,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs 
 #pragma unroll
   for (int t = 0; t < MG; ++t) acc[t] = accr[t] = v4i{0, 0, 0, 0};
 
-  // End of group slot gs: partial sums to LDS, one barrier, then wave gs % 8
-  // reduces and writes the outputs.
+  // End of group slot gs: partial sums added into LDS, one barrier, then
+  // wave gs % 8 reads them back, clears them and writes the outputs.
   auto group_end = [&](int gs) {
-    const int par = gs & 1;
+    int* rp = red + (gs & 1) * (2 * MG * 64 * 4);
 #pragma unroll
-    for (int t = 0; t < MG; ++t) {
-      red[par][wv][0][t][lane] = acc[t];
-      red[par][wv][1][t][lane] = accr[t];
-      acc[t] = accr[t] = v4i{0, 0, 0, 0};
-    }
+    for (int t = 0; t < MG; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        atomicAdd(rp + ((0 * MG + t) * 64 + lane) * 4 + e, acc[t][e]);
+        atomicAdd(rp + ((1 * MG + t) * 64 + lane) * 4 + e, accr[t][e]);
+      }
+#pragma unroll
+    for (int t = 0; t < MG; ++t) acc[t] = accr[t] = v4i{0, 0, 0, 0};
     lds_barrier();                              // the chunk loads in flight stay in flight
     if (wv != gs % kDecWaves) return;
     v4i sm[MG], sr[MG];
 #pragma unroll
     for (int t = 0; t < MG; ++t) {
-      sm[t] = red[par][0][0][t][lane];
-      sr[t] = red[par][0][1][t][lane];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) {
-        sm[t] += red[par][w][0][t][lane];
-        sr[t] += red[par][w][1][t][lane];
-      }
+      v4i* pm = reinterpret_cast<v4i*>(rp) + (0 * MG + t) * 64 + lane;
+      v4i* pr = reinterpret_cast<v4i*>(rp) + (1 * MG + t) * 64 + lane;
+      sm[t] = *pm;
+      sr[t] = *pr;
+      *pm = v4i{0, 0, 0, 0};
+      *pr = v4i{0, 0, 0, 0};
     }
     const int n0 = (static_cast<int>(blockIdx.x) + gs * static_cast<int>(gridDim.x)) * 16;
     const float4 w4 = *reinterpret_cast<const float4*>(s_sw + 16 * gs + 4 * g);
@@ -856,30 +905,38 @@ __global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs 
     }
   };
 
-  // The scale loads must have landed before the first group_end barrier: a
-  // wave with chunks waits for its first chunk (issued after them) before
-  // that barrier; a wave without chunks waits here.
+  // The first D chunks are requested right away; then each wave waits for
+  // its own direct LDS loads (older than every chunk load: at most the chunk
+  // loads may still be outstanding) and one barrier publishes them, and the
+  // cleared sums, to every wave.
   Buf buf[D];
-  if (items == 0) {
-    wait_vmcnt<0>();
-    for (int gs = 0; gs < my_groups; ++gs) group_end(gs);
-    return;
-  }
   static_for<D>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     if (k < total) load(k, buf[k]);
   });
+  const int issued = min(total, D);
+  static_for<D + 1>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if (issued == k) wait_vmcnt<k * LPC>();
+  });
+  lds_barrier();
+  if (items == 0) {
+    for (int gs = 0; gs < my_groups; ++gs) group_end(gs);
+    return;
+  }
   for (int base = 0; base < total; base += D) {
     static_for<D>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       const int i = base + k;
       if (i < total) {
         const int j = i % items;
-        if (j < cpw)
-          dot(buf[k], acc);
-        else
-          dot(buf[k], accr);
+        const bool res = j >= cpw;
+        const Buf b = buf[k];
         if (i + D < total) load(i + D, buf[k]);
+        if (res)
+          dot(b, 0, accr);
+        else
+          dot(b, wv + kDecWaves * j, acc);
         if (j == items - 1) group_end(i / items);
       }
     });
@@ -1098,13 +1155,34 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
 
 // One persistent workgroup per CU (one per 16-channel group when there are
 // fewer groups), more only if a workgroup would own over kDecMaxGroups groups.
-template <int MG, int A_BITS>
-hipError_t launch_decode(const LinearArgs& a, hipStream_t st) {
+template <int MG, int A_BITS, bool XL>
+hipError_t launch_decode_x(const LinearArgs& a, hipStream_t st) {
+  using C = DecCfg<MG, A_BITS, XL>;
   const int ngroups = (a.N + 15) / 16;
   int grid = min(ngroups, kCUs);
   grid = max(grid, (ngroups + kDecMaxGroups - 1) / kDecMaxGroups);
-  serq_decode_kernel<MG, A_BITS><<<dim3(grid), dim3(kDecThreads), 0, st>>>(a, ngroups);
+  const int lds = (XL ? a.M * dec_x_stride<MG, A_BITS, XL>(a.K) : 0) + C::SCALE_BYTES + C::RED_BYTES;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_decode_kernel<MG, A_BITS, XL>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (XL ? kDecMaxX : 0) + C::SCALE_BYTES + C::RED_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  serq_decode_kernel<MG, A_BITS, XL><<<dim3(grid), dim3(kDecThreads), lds, st>>>(a, ngroups);
   return hipGetLastError();
+}
+
+// Resident activations pay off once a workgroup serves several groups (one
+// activation load per workgroup, reused); with one group per workgroup the
+// L2 path measured faster.
+template <int MG, int A_BITS>
+hipError_t launch_decode(const LinearArgs& a, hipStream_t st) {
+  const int ngroups = (a.N + 15) / 16;
+  if (ngroups > kCUs && static_cast<long>(a.M) * dec_x_stride<MG, A_BITS, true>(a.K) <= kDecMaxX)
+    return launch_decode_x<MG, A_BITS, true>(a, st);
+  return launch_decode_x<MG, A_BITS, false>(a, st);
 }
 
 template <int MT, int KP>
