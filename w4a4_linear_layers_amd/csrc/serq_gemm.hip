@@ -204,10 +204,12 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 
 // Workgroup barrier for LDS data only: this wave's LDS accesses complete,
 // then s_barrier. Unlike __syncthreads it does not wait for outstanding
-// global loads, so prefetches stay in flight; the memory clobber keeps the
-// compiler from moving LDS accesses across it.
+// global loads, so prefetches stay in flight. The wait is the builtin, so the
+// compiler knows every earlier LDS read has landed; the memory clobber on the
+// barrier keeps it from moving LDS accesses across.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0), no vmcnt / expcnt wait
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // s_waitcnt with vmcnt <= n (n < 64) and no wait on lgkm/exp counters.
@@ -279,7 +281,7 @@ struct TileCfg {
   static constexpr int CHUNKS_PER_WAVE = CW + CX;
   static constexpr int SCALE_BYTES = 4 * (2 * BN + BM);  // sw, sr, sx of the tile
   static constexpr int kLdsCap = 160 * 1024 / OCC;       // the CU's LDS split between its workgroups
-  static constexpr int kMaxStages = 12;
+  static constexpr int kMaxStages = 8;
   static constexpr int stages() {
     int st = kMaxStages;
     while (st > 2 && st * STAGE + SCALE_BYTES > kLdsCap) --st;
@@ -331,6 +333,13 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   const int ntot = nkt + (Rb + kKTileW - 1) / kKTileW;   // plus residual k-tiles
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // The operand bases, held in registers: selecting between fields of the
+  // argument block inside the loop would reload them from memory (a scalar
+  // load, whose out-of-order return forces lgkmcnt(0) waits that also drain
+  // the fragment reads in flight).
+  const uint8_t* const Wq = a.Wq;
+  const uint8_t* const Rq = a.Rq;
+  const uint8_t* const Xq = a.Xq;
 
   // Epilogue scales into LDS first, so that every wave's k-tile waits below
   // also cover them: wave 0 loads sw, wave 1 sr, wave 2 sx of the tile.
@@ -392,10 +401,18 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
     const uint32_t sbase = lds_base + stage * C::STAGE;
     const bool res = kt >= nkt;
     const int kx = res ? kt - nkt : kt;        // k-tile index within its source rows
-    const uint8_t* wsrc = (res ? a.Rq : a.Wq) + kx * kKTileW;
-    const uint8_t* xsrc = a.Xq + kx * C::XB;
+    const uint8_t* wsrc = (res ? Rq : Wq) + kx * kKTileW;
+    const uint8_t* xsrc = Xq + kx * C::XB;
     const int wleft = (res ? Rb : Kb) - kx * kKTileW;     // row bytes left from the k-tile start
     const int xleft = Xrow - kx * C::XB;
+    // Full main k-tiles take a path with no per-lane masks.
+    if (!res && wleft >= kKTileW && xleft >= C::XB) {
+#pragma unroll
+      for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + (wv * C::CW + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + C::W_BYTES + (wv * C::CX + i) * 1024);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < C::CW; ++i) {
       const uint32_t chunk = sbase + (wv * C::CW + i) * 1024;
@@ -415,11 +432,17 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
     }
   };
 
-  v16i acc[TN][TM];
+  // With fewer than four blocks per wave, consecutive MFMA steps go to AS
+  // separate accumulator sets (added up after the loop), so that no MFMA
+  // waits for the previous one's result.
+  constexpr int AS = TN * TM >= 4 ? 1 : 4 / (TN * TM);
+  v16i accs[AS][TN][TM];
 #pragma unroll
-  for (int i = 0; i < TN; ++i)
+  for (int k = 0; k < AS; ++k)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = v16i{};
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) accs[k][i][j] = v16i{};
 
   // fragment read offsets within a stage (the swizzle depends on l32 only)
   constexpr int XP = A_BITS == 4 ? 2 : 4;    // 16-byte parts per activation row and lane
@@ -480,7 +503,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   // The four MFMA steps of one k-tile, software-pipelined: the widening for
   // step s + 1 is issued between the MFMAs of step s, so the VALU work runs
   // while the matrix core is busy.
-  auto compute = [&](const Frags& f, v16i (&acc)[TN][TM]) {
+  auto compute = [&](const Frags& f, v16i (&acc)[AS][TN][TM]) {
     v4i wa[TN], xb[TM];
     unpack(f, 0, wa, xb);
 #pragma unroll
@@ -490,7 +513,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32(wa[i], xb[j], acc[i][j]);
+        for (int j = 0; j < TM; ++j) acc[s % AS][i][j] = mfma32(wa[i], xb[j], acc[s % AS][i][j]);
       if (s < 3) {
         constexpr int kValuPerMfma = (6 * (TN + TM) + TN * TM - 1) / (TN * TM);
 #pragma unroll
@@ -512,19 +535,27 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   // Wait until at most `n` k-tiles of this wave's loads are outstanding
   // (n < STAGES, wave-uniform): vmcnt counts instructions, CPW per k-tile.
   auto wait_tiles = [&](int n) {
+    if (n >= STAGES - 2) {                       // the steady state, tested first
+      wait_vmcnt<CPW * (STAGES - 2)>();
+      return;
+    }
     static_for<STAGES>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       if (n == k) wait_vmcnt<CPW * k>();
     });
   };
-  auto step = [&](int kt, const Frags& cur, Frags& next) {
+  // k-tile kt lives in stage st = kt % STAGES (a constant at every call).
+  auto step = [&](int kt, int st, const Frags& cur, Frags& next) {
+    // cur's fragment reads and the last zero-fills have landed (on every
+    // path, so the compiler does not wait again after the next reads).
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     if (kt + 1 < nkt) {
       wait_tiles(min(STAGES - 2, ntot - 2 - kt));   // later k-tiles may stay in flight
-      lds_barrier();                           // earlier fragment reads and zero-fills done
-      if (kt + STAGES < ntot) issue(kt + STAGES, kt % STAGES);
-      read_frags((kt + 1) % STAGES, next);
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + STAGES < ntot) issue(kt + STAGES, st);
+      read_frags((st + 1) % STAGES, next);
     }
-    compute(cur, acc);
+    compute(cur, accs);
   };
 
 #pragma unroll
@@ -532,11 +563,50 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
     if (st < ntot) issue(st, st);
   wait_tiles(min(STAGES, ntot) - 1);           // k-tile 0 (and the scales) landed
   lds_barrier();
+  // Steady state: k-tile kt + 1 is the oldest load still awaited, STAGES - 2
+  // more are in flight, and k-tile kt + STAGES is a full main k-tile -- no
+  // test at all.
+  auto fast_step = [&](int kt, int st, const Frags& cur, Frags& next) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wait_vmcnt<CPW * (STAGES - 2)>();
+    asm volatile("s_barrier" ::: "memory");
+    const uint32_t sbase = lds_base + st * C::STAGE;
+    const uint8_t* wsrc = Wq + (kt + STAGES) * kKTileW;
+    const uint8_t* xsrc = Xq + (kt + STAGES) * C::XB;
+#pragma unroll
+    for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + (wv * C::CW + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + C::W_BYTES + (wv * C::CX + i) * 1024);
+    read_frags((st + 1) % STAGES, next);
+    compute(cur, accs);
+  };
+
+  // The loop is unrolled over a whole period of (stage, fragment buffer)
+  // pairs so that every LDS offset is a constant.
   Frags f0, f1;
   read_frags(0, f0);
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(kt, f0, f1);
-    if (kt + 1 < nkt) step(kt + 1, f1, f0);
+  constexpr int UNR = STAGES % 2 ? 2 * STAGES : STAGES;
+  const int nfull = min(Kb / kKTileW, Xrow / C::XB);   // main k-tiles with no ragged end
+  int kt0 = 0;
+  for (; kt0 + UNR <= nfull - STAGES; kt0 += UNR) {
+    static_for<UNR>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i % 2 == 0)
+        fast_step(kt0 + i, i % STAGES, f0, f1);
+      else
+        fast_step(kt0 + i, i % STAGES, f1, f0);
+    });
+  }
+  for (; kt0 < nkt; kt0 += UNR) {
+    static_for<UNR>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (kt0 + i < nkt) {
+        if constexpr (i % 2 == 0)
+          step(kt0 + i, i % STAGES, f0, f1);
+        else
+          step(kt0 + i, i % STAGES, f1, f0);
+      }
+    });
   }
 
   // ---- Epilogue. The residual k-tiles were issued during the last main
@@ -548,16 +618,29 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   const float* s_sx = s_sr + C::BN;
   const int nres = ntot - nkt;
   // Residual MFMAs for all blocks, from the residual k-tiles.
-  v16i ar[TN][TM];
+  v16i ars[AS][TN][TM];
 #pragma unroll
-  for (int i = 0; i < TN; ++i)
+  for (int k = 0; k < AS; ++k)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) ar[i][j] = v16i{};
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) ars[k][i][j] = v16i{};
   for (int t = 0; t < nres; ++t) {
     Frags fr;
     read_frags((nkt + t) % STAGES, fr);
-    compute(fr, ar);
+    compute(fr, ars);
   }
+  v16i (&acc)[TN][TM] = accs[0];
+  v16i (&ar)[TN][TM] = ars[0];
+#pragma unroll
+  for (int k = 1; k < AS; ++k)
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        acc[i][j] += accs[k][i][j];
+        ar[i][j] += ars[k][i][j];
+      }
   if (a.dbg_main) {                            // exact accumulators, for tests
     static_for<TM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
