@@ -53,7 +53,8 @@ def _act_input(M, K, dtype, seed):
 
 
 @pytest.mark.parametrize("M,K", [(16, 256), (7, 4096), (33, 14336), (5, 28672), (9, 1000), (4, 1002), (11, 8192), (6, 2048),
-                                 (3, 40000), (1, 2), (64, 8)])
+                                 (3, 40000), (1, 2), (64, 8),
+                                 (600, 1000), (1030, 4096), (520, 8192)])    # several rows per workgroup
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_quant_act_bit_exact(M, K, dtype, bits):
