@@ -119,8 +119,12 @@ LINEAR_CASES = [
     (16, 512, 48, 256, "decode16"),
     (17, 1024, 50, 24, "decode32"),
     (32, 512, 64, 256, "decode32"),
-    (16, 1056, 4112, 72, "decode16"),     # activations resident in LDS; some workgroups take two groups
-    (24, 2080, 8200, 0, "decode32"),      # resident activations, r = 0
+    (16, 1056, 4112, 72, "decode16"),     # K % 256 == 32: the last chunk holds one 16-byte piece per row
+    (24, 2080, 8200, 0, "decode32"),      # four waves per group, r = 0
+    (8, 32, 64, 8, "decode16"),           # one chunk and the residual: most waves have no item
+    (12, 28672, 48, 256, "decode16"),     # long rows: several rounds of loads per wave
+    (32, 28672, 40, 32, "decode32"),      # long rows, two token blocks, r <= 32 (16-byte Q(R) rows)
+    (20, 4128, 80, 16, "decode32"),
     (40, 1056, 130, 72, "tile64x64"),
     (64, 96, 256, 96, "tile64x64"),       # K shorter than one k-tile, r = K
     (100, 512, 300, 64, "tile64x64"),

@@ -662,9 +662,13 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   // y = sx (sw acc_main + sr acc_res) in fp32, kept in place of the main
   // accumulator. The scales of a channel block are read once for its TM
   // token blocks.
+  // The accumulators hold 2^SHIFT times the code dot products; the factor is
+  // taken out of the token scale instead of shifting every accumulator. A
+  // power-of-two factor commutes with fp32 rounding, so the result is the
+  // same as converting the shifted integers.
   float sxm[TM];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) sxm[j] = s_sx[wm * C::WM + j * 32 + l32];
+  for (int j = 0; j < TM; ++j) sxm[j] = s_sx[wm * C::WM + j * 32 + l32] * (1.0f / (1 << C::SHIFT));
   static_for<TN>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int nt = wn * C::WN + i * 32 + 4 * h;   // first channel (within the tile) of group q = 0
@@ -682,8 +686,8 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
         const float rv4[4] = {r4[q].x, r4[q].y, r4[q].z, r4[q].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float fm = static_cast<float>(acc[i][j][4 * q + c] >> C::SHIFT);
-          const float fr = static_cast<float>(ar[i][j][4 * q + c] >> C::SHIFT);
+          const float fm = static_cast<float>(acc[i][j][4 * q + c]);
+          const float fr = static_cast<float>(ar[i][j][4 * q + c]);
           acc[i][j][4 * q + c] = __float_as_int(sxm[j] * __builtin_fmaf(rv4[c], fr, wv4[c] * fm));
         }
       }
@@ -774,255 +778,259 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel (M <= 32): the packed weights are streamed from HBM exactly
-// once and the kernel is bound by how many bytes of them are in flight.
+// Skinny kernel (5..32 tokens, and W4A8 up to 4): one eight-wave workgroup
+// per CU (more when there are over 8 groups per CU) walks G <= 8 16-channel
+// groups, with the activation rows resident in LDS -- all of K at once when
+// they fit, else in K segments of `seg` 256-code chunks, reloaded between
+// segments (the workgroup's groups are walked once per segment; their sums
+// accumulate in LDS across segments).
 //
-// One persistent eight-wave workgroup per CU (fewer when N is small) walks a
-// strided list of 16-channel groups. K is cut into 256-code chunks (128
-// bytes of each of the 16 weight rows); wave w takes chunks w, w + 8, ... of
-// every group, and the salient-row residual (r <= 256 codes: one chunk of
-// Q(R)) goes to the wave that has one main chunk fewer. Each wave streams its
-// chunks, group after group, through a ring of D register buffers, so D
-// chunks are always in flight and the stream does not drain between groups.
-// Lane (row l16, quarter g) of a chunk holds codes [64 g, 64 g + 64): 32
-// contiguous weight bytes (16-byte loads), the activations of the same codes
-// for its token, and v_mfma_i32_16x16x64_i8 takes them in four steps.
-//
-// When all M activation rows fit in LDS (XL) they are loaded there once, at
-// kernel start, with rows padded by 16 bytes so that the 16 tokens of a read
-// fall on distinct banks; the ring then carries only weights. Otherwise the
-// activation codes ride in the ring beside them, read through L2.
-//
-// At the end of a group every wave adds its int32 partial sums into an LDS
-// accumulator (double-buffered by group parity); after one barrier, wave
-// g % 8 reads it back, clears it and writes the 16 channels x M tokens, while
-// the others go on with the next group. The scales of all the workgroup's
-// channels are loaded into LDS at kernel start (direct LDS loads, oldest in
-// every wave's load queue).
+// An item is 256 codes of the 16 weight rows of a group (128 bytes of each
+// row) or, last in segment 0, the zero-padded Q(R) rows against the first
+// activation codes. Wave w takes items w, w + 8, ... of a (segment, group),
+// at most IPW of them per unit, issues all of their loads, then computes
+// them and adds its sums into the group's LDS slot; the next unit's loads
+// are issued before the current unit is computed. So at any moment a CU's
+// loads fall in one or two groups' rows (a few tens of KB of contiguous
+// weights): measured faster than deeper per-wave rings spread over several
+// groups, whose many scattered requests streamed at about two thirds of the
+// rate. Every load is unconditional (clamped addresses, zeroed activation
+// side) and every slot is computed, so the compiler's load counters stay
+// exact. Lane (row l16, quarter g) of an item holds weight bytes
+// [32 g, 32 g + 32) of its row's 128 (codes [64 g, 64 g + 64)) and reads
+// the activation codes at the same positions for tokens l16 and 16 + l16
+// from LDS (rows padded by 16 bytes: the 16 tokens of a read hit distinct
+// banks); v_mfma_i32_16x16x64_i8 takes them in four steps. One barrier at
+// the end, then wave j writes group j with the scales it loaded at kernel
+// start.
 // ---------------------------------------------------------------------------
 
-constexpr int kDecWaves = 8;
-constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecMaxGroups = 64;          // 16-channel groups per workgroup
-constexpr int kDecMaxX = 136 * 1024;       // LDS bytes for resident activation rows
+constexpr int kSkxWaves = 8;
+constexpr int kSkxMaxGroups = 8;            // groups per workgroup
+constexpr int kSkxLds = 160 * 1024;         // LDS bytes: activation segment + group slots
 
-template <int MG, int A_BITS, bool XL>
-struct DecCfg {
-  static constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
-  static constexpr int CC = 256;                      // codes per chunk
-  static constexpr int CWB = CC / 2;                  // weight bytes per row and chunk
-  static constexpr int CXB = CC * A_BITS / 8;         // activation bytes per row and chunk
-  static constexpr int LW = CWB / 4 / 16;             // 16-byte weight loads per lane and chunk (2)
-  static constexpr int LX = CXB / 4 / 16;             // 16-byte activation loads per lane and chunk
-  static constexpr int REGS = 4 * (LW + (XL ? 0 : MG * LX));   // VGPRs per buffered chunk
-  static constexpr int D = REGS <= 8 ? 8 : (REGS <= 24 ? 4 : 2);   // ring depth: chunks in flight per wave
-  static constexpr int SCALE_BYTES = 4 * (32 * kDecMaxGroups + 64);
-  static constexpr int RED_BYTES = 2 * 2 * MG * 64 * 16;           // [parity][main, residual][token block][lane] v4i
-};
+template <int MG>
+constexpr int skx_slot_bytes() { return 2 * MG * 64 * 16; }
 
-// LDS bytes of the decode kernel: resident activations (XL), scales, sums.
-template <int MG, int A_BITS, bool XL>
-constexpr int dec_x_stride(int K) { return K * A_BITS / 8 + 16; }
-
-template <int MG, int A_BITS, bool XL>
-__global__ __launch_bounds__(kDecThreads, 1) void serq_decode_kernel(LinearArgs a, int ngroups) {
-  using C = DecCfg<MG, A_BITS, XL>;
-  constexpr int D = C::D, LW = C::LW, LX = C::LX;
+// SEG: several segments or rounds; without it all of K is one segment and a
+// wave's items of a group fit one unit (the common case, with less
+// bookkeeping per unit).
+template <int MG, int A_BITS, int IPW, bool SEG>
+__global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearArgs a, int ngroups, int seg) {
+  constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
+  constexpr int CWB = 128;                  // weight bytes per row and item
+  constexpr int CXB = 2 * A_BITS * 16;      // activation bytes per row and item
+  constexpr int LW = 2;                     // 16-byte weight loads per lane and item
+  constexpr int LX = CXB / 64;              // 16-byte activation reads per lane and item
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int Kb = a.K / 2, Xrow = a.K * A_BITS / 8;
-  const int XS = dec_x_stride<MG, A_BITS, XL>(a.K);   // LDS row stride of resident activations
-  const int xbytes = XL ? a.M * XS : 0;
-  float* s_sw = reinterpret_cast<float*>(lds + xbytes);
-  float* s_sr = s_sw + 16 * kDecMaxGroups;
-  float* s_sx = s_sr + 16 * kDecMaxGroups;
-  int* red = reinterpret_cast<int*>(lds + xbytes + C::SCALE_BYTES);
+  const int XS = seg * CXB + 16;            // LDS row stride of the activation segment
   const int Rb = rq_row_bytes(a.r);
-  const int nchunks = (a.K + C::CC - 1) / C::CC;
-  const int my_groups = (ngroups - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
+  const int C = (a.K + 255) / 256;          // main items (chunks) per group
+  const int S = SEG ? (C + seg - 1) / seg : 1;   // activation segments
   const bool has_res = a.r > 0;
-  const int cpw = (nchunks - wv + kDecWaves - 1) / kDecWaves;      // main chunks of this wave per group
-  const int res_wave = nchunks % kDecWaves;                         // first wave with the smaller count
-  const int items = cpw + (has_res && wv == res_wave ? 1 : 0);     // chunks of this wave per group
-  const int total = my_groups * items;
+  const int G = (ngroups - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+  int* slots = reinterpret_cast<int*>(lds + a.M * XS);   // [G][main, residual][token block][lane] v4i
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  auto group_n0 = [&](int j) { return (static_cast<int>(blockIdx.x) + j * static_cast<int>(gridDim.x)) * 16; };
+  // Segment s: main chunks [s seg, s seg + mains(s)), plus the residual item
+  // in segment 0. Only the first and the last segment differ from the rest.
+  auto rounds_of = [&](int n) { return SEG ? ((n + kSkxWaves - 1) / kSkxWaves + IPW - 1) / IPW : 1; };
+  const int m_last = C - (S - 1) * seg;
+  const int i_first = (S == 1 ? m_last : seg) + (has_res ? 1 : 0);
+  const int i_last = S == 1 ? i_first : m_last;
+  const int r_first = rounds_of(i_first), r_mid = rounds_of(seg), r_last = rounds_of(i_last);
+  auto mains = [&](int s) { return s == S - 1 ? m_last : seg; };
+  auto items = [&](int s) { return s == 0 ? i_first : (s == S - 1 ? i_last : seg); };
+  auto rounds = [&](int s) { return s == 0 ? r_first : (s == S - 1 ? r_last : r_mid); };
 
-  // Direct LDS loads first (the oldest in every wave's queue): the
-  // activation rows (XL), the scales of every channel this workgroup writes
-  // (lane i of a load covers channel 16 (group slot) + (i % 16)) and the
-  // token scales. The partial-sum buffers start at zero.
-  if constexpr (XL) {
-    const int per_row = (Xrow + 1023) / 1024;
-    for (int q = wv; q < a.M * per_row; q += kDecWaves) {
+  // Activation segment s into LDS (direct loads; this wave's share).
+  auto load_x = [&](int s) {
+    const int off = s * seg * CXB;
+    const int len = min(seg * CXB, Xrow - off);
+    const int per_row = (len + 1023) / 1024;
+    for (int q = wv; q < a.M * per_row; q += kSkxWaves) {
       const int t = q / per_row, c = q - t * per_row;
-      if (1024 * c + 16 * lane < Xrow)
-        dma16(a.Xq + static_cast<size_t>(t) * Xrow, 1024 * c + 16 * lane, lds_base + t * XS + 1024 * c);
+      if (1024 * c + 16 * lane < len)
+        dma16(a.Xq + static_cast<size_t>(t) * Xrow + off, 1024 * c + 16 * lane, lds_base + t * XS + 1024 * c);
     }
-  }
+  };
+
+  // Scales of the group this wave writes at the end (group wv), then
+  // segment 0 of the activations; both are older than every weight load.
+  float wsc[4], rsc[4], sxv[MG];
   {
-    const uint32_t lsw = lds_base + xbytes, lsr = lsw + 64 * kDecMaxGroups, lsx = lsr + 64 * kDecMaxGroups;
-    for (int q = wv; q < (my_groups + 3) / 4 * 2 + 1; q += kDecWaves) {
-      if (q == 0) {                                     // token scales
-        if (lane < a.M) dma4(a.sx, 4 * lane, lsx);
-        continue;
-      }
-      const int qq = q - 1, arr = qq & 1, blk = qq >> 1;   // 4 groups (64 channels) per load
-      const int slot = 4 * blk + (lane >> 4);
-      const int n = (static_cast<int>(blockIdx.x) + slot * static_cast<int>(gridDim.x)) * 16 + l16;
-      if (arr == 1 && !has_res) continue;
-      if (slot < my_groups && n < a.N) dma4(arr ? a.sr : a.sw, 4 * n, (arr ? lsr : lsw) + 256 * blk);
+    const int nb = group_n0(min(wv, G - 1));
+    const float* srp = has_res ? a.sr : a.sw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = min(nb + 4 * g + e, a.N - 1);
+      wsc[e] = a.sw[n];
+      rsc[e] = srp[n];                      // replaced by zeros at the end when r == 0
     }
+#pragma unroll
+    for (int t = 0; t < MG; ++t) sxv[t] = a.sx[min(t * 16 + l16, a.M - 1)];
   }
-  for (int i = threadIdx.x; i < C::RED_BYTES / 4; i += kDecThreads) red[i] = 0;
+  load_x(0);
+  for (int i = threadIdx.x; i < G * skx_slot_bytes<MG>() / 4; i += 64 * kSkxWaves) slots[i] = 0;
 
-  // Item i of this wave's stream: group slot i / items, main chunk
-  // wv + 8 (i % items) or, as the last item of the residual wave, Q(R).
-  // Every load is issued (past the end of a row it reads the row's last 16
-  // bytes and the value is dropped), so a chunk is always LPC load
-  // instructions -- the count the start-up wait below relies on.
-  constexpr int LPC = LW + (XL ? 0 : MG * LX);
+  // A unit is (segment s, group j, round q): items t = wv + 8 (q IPW + k),
+  // k < IPW, of that segment and group. Past the end of the list the cursor
+  // stays on valid bytes; slots past a segment's items are computed against
+  // zero activations.
+  struct Unit {
+    int s, j, q;
+  };
+  auto advance = [&](Unit& u) {
+    if constexpr (!SEG) {
+      ++u.j;
+      return;
+    }
+    if (++u.q == rounds(u.s)) {
+      u.q = 0;
+      if (++u.j == G) {
+        u.j = 0;
+        ++u.s;
+      }
+    }
+  };
   struct Buf {
-    uint4 w[LW];
-    uint4 x[XL ? 1 : MG][XL ? 1 : LX];
+    uint4 w[IPW][LW];
   };
-  auto load = [&](int i, Buf& b) {
-    const int gs = i / items, j = i - gs * items;
-    const int n = (static_cast<int>(blockIdx.x) + gs * static_cast<int>(gridDim.x)) * 16 + l16;
-    const int nrow = min(n, a.N - 1);
-    const bool res = j >= cpw;
-    const int c = res ? 0 : wv + kDecWaves * j;
-    const uint8_t* wp = res ? a.Rq + static_cast<size_t>(nrow) * Rb : a.Wq + static_cast<size_t>(nrow) * Kb;
-    const int wlim = res ? Rb : Kb;
-#pragma unroll
-    for (int l = 0; l < LW; ++l) {
-      const int o = c * C::CWB + g * (C::CWB / 4) + 16 * l;
-      const uint4 v = *reinterpret_cast<const uint4*>(wp + min(o, wlim - 16));
-      b.w[l] = o < wlim ? v : make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (!XL) {
-#pragma unroll
-      for (int t = 0; t < MG; ++t) {
-        const int m = t * 16 + l16;
-        const uint8_t* xp = a.Xq + static_cast<size_t>(min(m, a.M - 1)) * Xrow;
-#pragma unroll
-        for (int l = 0; l < LX; ++l) {
-          const int o = c * C::CXB + g * (C::CXB / 4) + 16 * l;
-          const uint4 v = *reinterpret_cast<const uint4*>(xp + min(o, Xrow - 16));
-          b.x[t][l] = (m < a.M && o < Xrow) ? v : make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  };
-  // One chunk (main chunk c, or the residual chunk at c = 0): four MFMA
-  // steps of 16 codes per lane.
-  auto dot = [&](const Buf& b, int c, v4i (&acc)[MG]) {
-    uint4 xs[MG][LX];
-#pragma unroll
-    for (int t = 0; t < MG; ++t)
-#pragma unroll
-      for (int l = 0; l < LX; ++l) {
-        if constexpr (XL) {
-          const int o = c * C::CXB + g * (C::CXB / 4) + 16 * l;
-          const int m = t * 16 + l16;
-          xs[t][l] = (m < a.M && o < Xrow) ? *reinterpret_cast<const uint4*>(lds + m * XS + o) : make_uint4(0, 0, 0, 0);
-        } else {
-          xs[t][l] = b.x[t][l];
-        }
-      }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 ww = b.w[s >> 1];
-      const v4i wa = (s & 1) ? widen16(ww.z, ww.w) : widen16(ww.x, ww.y);
-#pragma unroll
-      for (int t = 0; t < MG; ++t) {
-        v4i xb;
-        if constexpr (A_BITS == 4) {
-          const uint4 xx = xs[t][s >> 1];
-          xb = (s & 1) ? widen16(xx.z, xx.w) : widen16(xx.x, xx.y);
-        } else {
-          xb = split16(xs[t][s]);
-        }
-        acc[t] = mfma(wa, xb, acc[t]);
-      }
-    }
-  };
-
-  v4i acc[MG], accr[MG];
-#pragma unroll
-  for (int t = 0; t < MG; ++t) acc[t] = accr[t] = v4i{0, 0, 0, 0};
-
-  // End of group slot gs: partial sums added into LDS, one barrier, then
-  // wave gs % 8 reads them back, clears them and writes the outputs.
-  auto group_end = [&](int gs) {
-    int* rp = red + (gs & 1) * (2 * MG * 64 * 4);
-#pragma unroll
-    for (int t = 0; t < MG; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        atomicAdd(rp + ((0 * MG + t) * 64 + lane) * 4 + e, acc[t][e]);
-        atomicAdd(rp + ((1 * MG + t) * 64 + lane) * 4 + e, accr[t][e]);
-      }
-#pragma unroll
-    for (int t = 0; t < MG; ++t) acc[t] = accr[t] = v4i{0, 0, 0, 0};
-    lds_barrier();                              // the chunk loads in flight stay in flight
-    if (wv != gs % kDecWaves) return;
-    v4i sm[MG], sr[MG];
-#pragma unroll
-    for (int t = 0; t < MG; ++t) {
-      v4i* pm = reinterpret_cast<v4i*>(rp) + (0 * MG + t) * 64 + lane;
-      v4i* pr = reinterpret_cast<v4i*>(rp) + (1 * MG + t) * 64 + lane;
-      sm[t] = *pm;
-      sr[t] = *pr;
-      *pm = v4i{0, 0, 0, 0};
-      *pr = v4i{0, 0, 0, 0};
-    }
-    const int n0 = (static_cast<int>(blockIdx.x) + gs * static_cast<int>(gridDim.x)) * 16;
-    const float4 w4 = *reinterpret_cast<const float4*>(s_sw + 16 * gs + 4 * g);
-    const float4 r4 = has_res ? *reinterpret_cast<const float4*>(s_sr + 16 * gs + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int t = 0; t < MG; ++t) {
-      const int m = t * 16 + l16;
-      store4<C::SHIFT>(a, sm[t], sr[t], m, n0 + 4 * g, m < a.M ? s_sx[m] : 0.0f, w4, r4);
-    }
-  };
-
-  // The first D chunks are requested right away; then each wave waits for
-  // its own direct LDS loads (older than every chunk load: at most the chunk
-  // loads may still be outstanding) and one barrier publishes them, and the
-  // cleared sums, to every wave.
-  Buf buf[D];
-  static_for<D>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    if (k < total) load(k, buf[k]);
-  });
-  const int issued = min(total, D);
-  static_for<D + 1>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    if (issued == k) wait_vmcnt<k * LPC>();
-  });
-  lds_barrier();
-  if (items == 0) {
-    for (int gs = 0; gs < my_groups; ++gs) group_end(gs);
-    return;
-  }
-  for (int base = 0; base < total; base += D) {
-    static_for<D>([&](auto kc) {
+  auto issue = [&](const Unit& u, Buf& b) {
+    const int s = SEG ? min(u.s, S - 1) : 0, j = min(u.j, G - 1);
+    const int nrow = min(group_n0(j) + l16, a.N - 1);
+    const int ms = mains(s), ts = items(s);
+    static_for<IPW>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      const int i = base + k;
-      if (i < total) {
-        const int j = i % items;
-        const bool res = j >= cpw;
-        const Buf b = buf[k];
-        if (i + D < total) load(i + D, buf[k]);
-        if (res)
-          dot(b, 0, accr);
-        else
-          dot(b, wv + kDecWaves * j, acc);
-        if (j == items - 1) group_end(i / items);
+      const int t = min(wv + kSkxWaves * (u.q * IPW + k), ts - 1);
+      const bool res = t >= ms;
+      const uint8_t* wp = res ? a.Rq + static_cast<size_t>(nrow) * Rb : a.Wq + static_cast<size_t>(nrow) * Kb;
+      const int wlim = res ? Rb : Kb;
+      const int c = res ? 0 : s * seg + t;
+#pragma unroll
+      for (int l = 0; l < LW; ++l) {
+        const int o = c * CWB + g * (CWB / 4) + 16 * l;
+        b.w[k][l] = *reinterpret_cast<const uint4*>(wp + min(o, wlim - 16));
       }
     });
+  };
+  auto consume = [&](const Unit& u, const Buf& b) {
+    const bool live = SEG ? u.s < S : u.j < G;
+    const int s = min(u.s, S - 1);
+    const int ms = mains(s), ts = items(s);
+    v4i acc[MG], accr[MG];
+#pragma unroll
+    for (int t = 0; t < MG; ++t) acc[t] = accr[t] = v4i{0, 0, 0, 0};
+    static_for<IPW>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const int ti = wv + kSkxWaves * (u.q * IPW + k);
+      const bool used = live && ti < ts;
+      const int t = min(ti, ts - 1);
+      const bool res = t >= ms;
+      // Activation bytes of this item: offset within the segment row, and
+      // the bytes that take part (the row's end, or the residual's codes).
+      const int xo = res ? 0 : t * CXB;
+      const int xlim = !used ? 0 : (res ? Rb * A_BITS / 4 : Xrow - s * seg * CXB);
+      uint4 xs[MG][LX];
+#pragma unroll
+      for (int tb = 0; tb < MG; ++tb)
+#pragma unroll
+        for (int l = 0; l < LX; ++l) {
+          const int o = xo + g * (CXB / 4) + 16 * l;
+          const int m = tb * 16 + l16;
+          xs[tb][l] = (m < a.M && o < xlim) ? *reinterpret_cast<const uint4*>(lds + m * XS + o)
+                                            : make_uint4(0, 0, 0, 0);
+        }
+      v4i p[MG];
+#pragma unroll
+      for (int tb = 0; tb < MG; ++tb) p[tb] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint4 ww = b.w[k][st >> 1];
+        const v4i wa = (st & 1) ? widen16(ww.z, ww.w) : widen16(ww.x, ww.y);
+#pragma unroll
+        for (int tb = 0; tb < MG; ++tb) {
+          v4i xv;
+          if constexpr (A_BITS == 4) {
+            const uint4 xx = xs[tb][st >> 1];
+            xv = (st & 1) ? widen16(xx.z, xx.w) : widen16(xx.x, xx.y);
+          } else {
+            xv = split16(xs[tb][st]);
+          }
+          p[tb] = mfma(wa, xv, p[tb]);
+        }
+      }
+      if (res) {
+#pragma unroll
+        for (int tb = 0; tb < MG; ++tb) accr[tb] += p[tb];
+      } else {
+#pragma unroll
+        for (int tb = 0; tb < MG; ++tb) acc[tb] += p[tb];
+      }
+    });
+    if (live && wv < ts) {
+      int* sp = slots + u.j * (skx_slot_bytes<MG>() / 4);
+#pragma unroll
+      for (int tb = 0; tb < MG; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(sp + (tb * 64 + lane) * 4 + e, acc[tb][e]);
+      if (has_res && s == 0) {
+#pragma unroll
+        for (int tb = 0; tb < MG; ++tb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) atomicAdd(sp + ((MG + tb) * 64 + lane) * 4 + e, accr[tb][e]);
+      }
+    }
+    // After the last unit of a segment: every wave is done with it, then the
+    // next segment replaces it (this wave's loads all land, including the
+    // unit already issued) and a barrier publishes it.
+    if (SEG && live && u.s + 1 < S && u.j == G - 1 && u.q == rounds(u.s) - 1) {
+      lds_barrier();
+      load_x(u.s + 1);
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+  };
+
+  // The first unit's loads go out first; then this wave's scale and direct
+  // loads (older) are waited for and one barrier publishes the activation
+  // rows and the cleared slots. Unit n + 1 is issued before unit n is
+  // computed, the loop unrolled by two so each buffer keeps its registers.
+  const int total = G * (S == 1 ? r_first : r_first + r_last + (S - 2) * r_mid);
+  Unit uc{0, 0, 0}, ui{0, 0, 0};
+  Buf A, B;
+  issue(ui, A);
+  advance(ui);
+  wait_vmcnt<IPW * LW>();
+  lds_barrier();
+  int n = 0;
+  for (; n + 2 <= total; n += 2) {
+    issue(ui, B);
+    advance(ui);
+    consume(uc, A);
+    advance(uc);
+    issue(ui, A);
+    advance(ui);
+    consume(uc, B);
+    advance(uc);
+  }
+  if (n < total) consume(uc, A);
+  wait_vmcnt<0>();                           // the last issue, past the end, unused
+  lds_barrier();
+  if (wv >= G) return;
+  const int* sp = slots + wv * (skx_slot_bytes<MG>() / 4);
+  const float4 w4 = make_float4(wsc[0], wsc[1], wsc[2], wsc[3]);
+  const float4 r4 = has_res ? make_float4(rsc[0], rsc[1], rsc[2], rsc[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const int nb = group_n0(wv);
+#pragma unroll
+  for (int t = 0; t < MG; ++t) {
+    const v4i sm = *reinterpret_cast<const v4i*>(sp + (t * 64 + lane) * 4);
+    const v4i sr = *reinterpret_cast<const v4i*>(sp + ((MG + t) * 64 + lane) * 4);
+    store4<SHIFT>(a, sm, sr, t * 16 + l16, nb + 4 * g, sxv[t], w4, r4);
   }
 }
 
@@ -1236,36 +1244,43 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// One persistent workgroup per CU (one per 16-channel group when there are
-// fewer groups), more only if a workgroup would own over kDecMaxGroups groups.
-template <int MG, int A_BITS, bool XL>
-hipError_t launch_decode_x(const LinearArgs& a, hipStream_t st) {
-  using C = DecCfg<MG, A_BITS, XL>;
-  const int ngroups = (a.N + 15) / 16;
-  int grid = min(ngroups, kCUs);
-  grid = max(grid, (ngroups + kDecMaxGroups - 1) / kDecMaxGroups);
-  const int lds = (XL ? a.M * dec_x_stride<MG, A_BITS, XL>(a.K) : 0) + C::SCALE_BYTES + C::RED_BYTES;
+// Groups per workgroup G <= 8; the activation segment takes what LDS has
+// left after the group slots; IPW items per wave and unit (up to 8).
+template <int MG, int A_BITS, int IPW, bool SEG>
+hipError_t launch_skinny_ipw(const LinearArgs& a, int grid, int ngroups, int seg, hipStream_t st) {
+  constexpr int CXB = 2 * A_BITS * 16;
+  const int G = (ngroups + grid - 1) / grid;
+  const int lds = a.M * (seg * CXB + 16) + G * skx_slot_bytes<MG>();
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_decode_kernel<MG, A_BITS, XL>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (XL ? kDecMaxX : 0) + C::SCALE_BYTES + C::RED_BYTES);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_skinny_kernel<MG, A_BITS, IPW, SEG>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSkxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  serq_decode_kernel<MG, A_BITS, XL><<<dim3(grid), dim3(kDecThreads), lds, st>>>(a, ngroups);
+  serq_skinny_kernel<MG, A_BITS, IPW, SEG><<<dim3(grid), dim3(64 * kSkxWaves), lds, st>>>(a, ngroups, seg);
   return hipGetLastError();
 }
 
-// Resident activations pay off once a workgroup serves several groups (one
-// activation load per workgroup, reused); with one group per workgroup the
-// L2 path measured faster.
 template <int MG, int A_BITS>
-hipError_t launch_decode(const LinearArgs& a, hipStream_t st) {
+hipError_t launch_skinny(const LinearArgs& a, hipStream_t st) {
+  constexpr int CXB = 2 * A_BITS * 16;
   const int ngroups = (a.N + 15) / 16;
-  if (ngroups > kCUs && static_cast<long>(a.M) * dec_x_stride<MG, A_BITS, true>(a.K) <= kDecMaxX)
-    return launch_decode_x<MG, A_BITS, true>(a, st);
-  return launch_decode_x<MG, A_BITS, false>(a, st);
+  const int grid = max(min(ngroups, kCUs), (ngroups + kSkxMaxGroups - 1) / kSkxMaxGroups);
+  const int G = (ngroups + grid - 1) / grid;
+  const int C = (a.K + 255) / 256;
+  const int row_budget = (kSkxLds - G * skx_slot_bytes<MG>()) / a.M - 16;
+  int seg = min(C, row_budget / CXB);
+  if (seg < 1) return hipErrorInvalidValue;
+  const int S = (C + seg - 1) / seg;
+  seg = (C + S - 1) / S;                      // equal segments
+  const int per = (seg + (a.r > 0 ? 1 : 0) + kSkxWaves - 1) / kSkxWaves;   // items of the busiest wave
+  if (S > 1 || per > 8) return launch_skinny_ipw<MG, A_BITS, 8, true>(a, grid, ngroups, seg, st);
+  if (per <= 2) return launch_skinny_ipw<MG, A_BITS, 2, false>(a, grid, ngroups, seg, st);
+  if (per <= 3) return launch_skinny_ipw<MG, A_BITS, 3, false>(a, grid, ngroups, seg, st);
+  if (per <= 4) return launch_skinny_ipw<MG, A_BITS, 4, false>(a, grid, ngroups, seg, st);
+  if (per <= 5) return launch_skinny_ipw<MG, A_BITS, 5, false>(a, grid, ngroups, seg, st);
+  return launch_skinny_ipw<MG, A_BITS, 8, false>(a, grid, ngroups, seg, st);
 }
 
 template <int MT, int KP>
@@ -1334,9 +1349,9 @@ hipError_t launch_linear(const LinearArgs& a, const LinearPlan& p, hipStream_t s
         default: return launch_gemv<4>(a, st);
       }
     case LinearKernel::kDecode16:
-      return a.a_bits == 4 ? launch_decode<1, 4>(a, st) : launch_decode<1, 8>(a, st);
+      return a.a_bits == 4 ? launch_skinny<1, 4>(a, st) : launch_skinny<1, 8>(a, st);
     case LinearKernel::kDecode32:
-      return a.a_bits == 4 ? launch_decode<2, 4>(a, st) : launch_decode<2, 8>(a, st);
+      return a.a_bits == 4 ? launch_skinny<2, 4>(a, st) : launch_skinny<2, 8>(a, st);
     case LinearKernel::kTile:
       return a.a_bits == 4 ? launch_tile_bits<4>(a, p, st) : launch_tile_bits<8>(a, p, st);
     case LinearKernel::kGeneric: {
