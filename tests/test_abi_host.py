@@ -220,7 +220,8 @@ def test_layer_save_load_roundtrip(tmp_path):
 
 def test_kernel_dispatch_rules():
     assert S.kernel_name(1, 4096, 4096, 64) == "gemv"
-    assert S.kernel_name(4, 4096, 4096, 64) == "gemv"
+    assert S.kernel_name(3, 4096, 4096, 64) == "gemv"
+    assert S.kernel_name(4, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(4, 4096, 4096, 64, 8) == "decode16"     # W4A8: no int4 dot products
     assert S.kernel_name(4, 65536, 4096, 64) == "decode16"       # activation rows beyond the LDS budget
     assert S.kernel_name(5, 4096, 4096, 64) == "decode16"

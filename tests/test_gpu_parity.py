@@ -112,7 +112,8 @@ LINEAR_CASES = [
     (1, 4096, 256, 64, "gemv"),
     (2, 1056, 100, 40, "gemv"),           # K % 2048 != 0: partial 1 KB slice; N % 16 != 0
     (3, 96, 40, 96, "gemv"),              # K < one slice, r = K
-    (4, 14336, 4096, 128, "gemv"),
+    (3, 14336, 4096, 128, "gemv"),
+    (4, 14336, 4096, 128, "decode16"),
     (1, 2080, 1000, 0, "gemv"),           # r = 0
     (5, 1024, 100, 40, "decode16"),       # N % 16 and N % 4 ragged, r % 64 != 0
     (16, 2080, 64, 0, "decode16"),        # K % 128 != 0, r = 0

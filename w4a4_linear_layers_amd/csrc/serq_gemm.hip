@@ -29,6 +29,7 @@
 // operands holds codes [32 g, 32 g + 32) (16 packed bytes); MFMA step 0 uses
 // its first 16 codes and step 1 the next 16.
 
+#include <mutex>
 #include <utility>
 
 #include "serq_internal.h"
@@ -778,92 +779,92 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel (5..32 tokens, and W4A8 up to 4): one eight-wave workgroup
-// per CU (more when there are over 8 groups per CU) walks G <= 8 16-channel
-// groups, with the activation rows resident in LDS -- all of K at once when
-// they fit, else in K segments of `seg` 256-code chunks, reloaded between
-// segments (the workgroup's groups are walked once per segment; their sums
-// accumulate in LDS across segments).
+// Skinny kernel (4..32 tokens, and W4A8 from one token): eight-wave
+// workgroups, each owning G <= 8 consecutive 16-channel groups and one K
+// slice of `seg` 256-code chunks (KS slices in all). The workgroup's slice of
+// the activation rows is loaded into LDS once and shared by its G groups.
+// Few groups per workgroup with the whole of K would reload the activations
+// for every group (for 16 tokens as many bytes as the weights themselves);
+// the host picks G and KS to keep that traffic, plus the partial sums below,
+// small while still launching about one workgroup per CU.
 //
-// An item is 256 codes of the 16 weight rows of a group (128 bytes of each
-// row) or, last in segment 0, the zero-padded Q(R) rows against the first
-// activation codes. Wave w takes items w, w + 8, ... of a (segment, group),
-// at most IPW of them per unit, issues all of their loads, then computes
-// them and adds its sums into the group's LDS slot; the next unit's loads
-// are issued before the current unit is computed. So at any moment a CU's
-// loads fall in one or two groups' rows (a few tens of KB of contiguous
-// weights): measured faster than deeper per-wave rings spread over several
-// groups, whose many scattered requests streamed at about two thirds of the
-// rate. Every load is unconditional (clamped addresses, zeroed activation
-// side) and every slot is computed, so the compiler's load counters stay
-// exact. Lane (row l16, quarter g) of an item holds weight bytes
-// [32 g, 32 g + 32) of its row's 128 (codes [64 g, 64 g + 64)) and reads
-// the activation codes at the same positions for tokens l16 and 16 + l16
-// from LDS (rows padded by 16 bytes: the 16 tokens of a read hit distinct
-// banks); v_mfma_i32_16x16x64_i8 takes them in four steps. One barrier at
-// the end, then wave j writes group j with the scales it loaded at kernel
-// start.
+// The workgroup's work is the flat list of G x Ts items, group-major: an
+// item is 256 codes of a group's 16 weight rows (128 bytes of each row) or,
+// last in slice 0, the zero-padded Q(R) rows against the first activation
+// codes. Wave w takes items w, w + 8, ... in units of IPW, issues a unit's
+// loads, then computes it while the next unit's loads are in flight (a unit
+// is about one group's items per wave). So at
+// any moment a CU's loads fall in a few tens of KB of contiguous weight rows
+// (measured faster than deeper per-wave rings spread over several groups,
+// whose scattered requests streamed at about two thirds of the rate). Every
+// load is unconditional (clamped addresses, zeroed activation side) and
+// every slot is computed, so the compiler's load counters stay exact. Lane
+// (row l16, quarter g) of an item holds weight bytes [32 g, 32 g + 32) of its
+// row's 128 (codes [64 g, 64 g + 64)) and reads the activation codes at the
+// same positions for tokens l16 and 16 + l16 from LDS (rows padded by 16
+// bytes: the 16 tokens of a read hit distinct banks); v_mfma_i32_16x16x64_i8
+// takes them in four steps, and the item's sums are added into its group's
+// LDS slot.
+//
+// With one slice, wave j then writes group j. With several, every
+// workgroup stores its int32 slot sums in a workspace, and the last of a
+// group set's KS workgroups to finish (an agent-scope counter) adds the KS
+// partial sums, writes the outputs and resets the counter for the next call.
 // ---------------------------------------------------------------------------
 
 constexpr int kSkxWaves = 8;
 constexpr int kSkxMaxGroups = 8;            // groups per workgroup
-constexpr int kSkxLds = 160 * 1024;         // LDS bytes: activation segment + group slots
+constexpr int kSkxLds = 159 * 1024;         // dynamic LDS bytes: activation slice + group slots
+                                            // (the rest of the 160 KB holds the static flag)
+constexpr int kSkxCounters = 16384;         // group-set counters at the start of the workspace
 
 template <int MG>
 constexpr int skx_slot_bytes() { return 2 * MG * 64 * 16; }
 
-// SEG: several segments or rounds; without it all of K is one segment and a
-// wave's items of a group fit one unit (the common case, with less
-// bookkeeping per unit).
-template <int MG, int A_BITS, int IPW, bool SEG>
-__global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearArgs a, int ngroups, int seg) {
+struct SkinnySplit {
+  int G, nb, KS, seg;       // groups per workgroup, group sets, K slices, chunks per slice
+  int* cnt;                 // kSkxCounters zeroed counters (KS > 1)
+  v4i* part;                // KS x ngroups x [main, residual][token block][lane] partial sums (KS > 1)
+};
+
+template <int MG, int A_BITS, int IPW>
+__global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearArgs a, SkinnySplit sp) {
   constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
   constexpr int CWB = 128;                  // weight bytes per row and item
   constexpr int CXB = 2 * A_BITS * 16;      // activation bytes per row and item
   constexpr int LW = 2;                     // 16-byte weight loads per lane and item
   constexpr int LX = CXB / 64;              // 16-byte activation reads per lane and item
+  constexpr int SLOT = skx_slot_bytes<MG>() / 16;   // v4i per group slot
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int Kb = a.K / 2, Xrow = a.K * A_BITS / 8;
-  const int XS = seg * CXB + 16;            // LDS row stride of the activation segment
   const int Rb = rq_row_bytes(a.r);
-  const int C = (a.K + 255) / 256;          // main items (chunks) per group
-  const int S = SEG ? (C + seg - 1) / seg : 1;   // activation segments
   const bool has_res = a.r > 0;
-  const int G = (ngroups - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
-  int* slots = reinterpret_cast<int*>(lds + a.M * XS);   // [G][main, residual][token block][lane] v4i
+  const int ngroups = (a.N + 15) / 16;
+  const int b = static_cast<int>(blockIdx.x) % sp.nb, ks = static_cast<int>(blockIdx.x) / sp.nb;
+  const int gbase = b * sp.G;
+  const int Gb = min(sp.G, ngroups - gbase);          // groups of this workgroup
+  const int C = (a.K + 255) / 256;
+  const int c0 = ks * sp.seg;                         // first chunk of the slice
+  const int Cs = min(sp.seg, C - c0);                 // main items per group
+  const bool res_here = has_res && ks == 0;
+  const int Ts = Cs + (res_here ? 1 : 0);             // items per group
+  const int NI = Gb * Ts;                             // items of the workgroup
+  const int XS = sp.seg * CXB + 16;                   // LDS row stride of the activation slice
+  const int xoff = c0 * CXB;                          // slice start within an activation row
+  const int xlen = min(Cs * CXB, Xrow - xoff);        // slice bytes per row
+  v4i* slots = reinterpret_cast<v4i*>(lds + a.M * XS);   // [Gb][main, residual][token block][lane]
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  auto group_n0 = [&](int j) { return (static_cast<int>(blockIdx.x) + j * static_cast<int>(gridDim.x)) * 16; };
-  // Segment s: main chunks [s seg, s seg + mains(s)), plus the residual item
-  // in segment 0. Only the first and the last segment differ from the rest.
-  auto rounds_of = [&](int n) { return SEG ? ((n + kSkxWaves - 1) / kSkxWaves + IPW - 1) / IPW : 1; };
-  const int m_last = C - (S - 1) * seg;
-  const int i_first = (S == 1 ? m_last : seg) + (has_res ? 1 : 0);
-  const int i_last = S == 1 ? i_first : m_last;
-  const int r_first = rounds_of(i_first), r_mid = rounds_of(seg), r_last = rounds_of(i_last);
-  auto mains = [&](int s) { return s == S - 1 ? m_last : seg; };
-  auto items = [&](int s) { return s == 0 ? i_first : (s == S - 1 ? i_last : seg); };
-  auto rounds = [&](int s) { return s == 0 ? r_first : (s == S - 1 ? r_last : r_mid); };
 
-  // Activation segment s into LDS (direct loads; this wave's share).
-  auto load_x = [&](int s) {
-    const int off = s * seg * CXB;
-    const int len = min(seg * CXB, Xrow - off);
-    const int per_row = (len + 1023) / 1024;
-    for (int q = wv; q < a.M * per_row; q += kSkxWaves) {
-      const int t = q / per_row, c = q - t * per_row;
-      if (1024 * c + 16 * lane < len)
-        dma16(a.Xq + static_cast<size_t>(t) * Xrow + off, 1024 * c + 16 * lane, lds_base + t * XS + 1024 * c);
-    }
-  };
-
-  // Scales of the group this wave writes at the end (group wv), then
-  // segment 0 of the activations; both are older than every weight load.
+  // Scales of the group this wave writes at the end (group wv), then the
+  // activation slice into LDS (direct loads); both are older than every
+  // weight load.
   float wsc[4], rsc[4], sxv[MG];
   {
-    const int nb = group_n0(min(wv, G - 1));
+    const int nb = (gbase + min(wv, Gb - 1)) * 16;
     const float* srp = has_res ? a.sr : a.sw;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -874,67 +875,52 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
 #pragma unroll
     for (int t = 0; t < MG; ++t) sxv[t] = a.sx[min(t * 16 + l16, a.M - 1)];
   }
-  load_x(0);
-  for (int i = threadIdx.x; i < G * skx_slot_bytes<MG>() / 4; i += 64 * kSkxWaves) slots[i] = 0;
+  {
+    const int per_row = (xlen + 1023) / 1024;
+    for (int q = wv; q < a.M * per_row; q += kSkxWaves) {
+      const int t = q / per_row, c = q - t * per_row;
+      if (1024 * c + 16 * lane < xlen)
+        dma16(a.Xq + static_cast<size_t>(t) * Xrow + xoff, 1024 * c + 16 * lane, lds_base + t * XS + 1024 * c);
+    }
+  }
+  for (int i = threadIdx.x; i < Gb * SLOT; i += 64 * kSkxWaves) slots[i] = v4i{0, 0, 0, 0};
 
-  // A unit is (segment s, group j, round q): items t = wv + 8 (q IPW + k),
-  // k < IPW, of that segment and group. Past the end of the list the cursor
-  // stays on valid bytes; slots past a segment's items are computed against
-  // zero activations.
-  struct Unit {
-    int s, j, q;
-  };
-  auto advance = [&](Unit& u) {
-    if constexpr (!SEG) {
-      ++u.j;
-      return;
-    }
-    if (++u.q == rounds(u.s)) {
-      u.q = 0;
-      if (++u.j == G) {
-        u.j = 0;
-        ++u.s;
-      }
-    }
-  };
+  // Item f (group f / Ts, item f % Ts of it). Past the list the loads read
+  // the last item's bytes and the item is computed against zero
+  // activations. The group and item index travel with the loaded data.
   struct Buf {
     uint4 w[IPW][LW];
+    int j[IPW], t[IPW];
   };
-  auto issue = [&](const Unit& u, Buf& b) {
-    const int s = SEG ? min(u.s, S - 1) : 0, j = min(u.j, G - 1);
-    const int nrow = min(group_n0(j) + l16, a.N - 1);
-    const int ms = mains(s), ts = items(s);
+  auto issue = [&](int u, Buf& bf) {
     static_for<IPW>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      const int t = min(wv + kSkxWaves * (u.q * IPW + k), ts - 1);
-      const bool res = t >= ms;
+      const int f = min(wv + kSkxWaves * (u * IPW + k), NI - 1);
+      const int j = f / Ts, t = f - j * Ts;
+      bf.j[k] = j;
+      bf.t[k] = t;
+      const bool res = t >= Cs;
+      const int nrow = min((gbase + j) * 16 + l16, a.N - 1);
       const uint8_t* wp = res ? a.Rq + static_cast<size_t>(nrow) * Rb : a.Wq + static_cast<size_t>(nrow) * Kb;
       const int wlim = res ? Rb : Kb;
-      const int c = res ? 0 : s * seg + t;
+      const int c = res ? 0 : c0 + t;
 #pragma unroll
       for (int l = 0; l < LW; ++l) {
         const int o = c * CWB + g * (CWB / 4) + 16 * l;
-        b.w[k][l] = *reinterpret_cast<const uint4*>(wp + min(o, wlim - 16));
+        bf.w[k][l] = *reinterpret_cast<const uint4*>(wp + min(o, wlim - 16));
       }
     });
   };
-  auto consume = [&](const Unit& u, const Buf& b) {
-    const bool live = SEG ? u.s < S : u.j < G;
-    const int s = min(u.s, S - 1);
-    const int ms = mains(s), ts = items(s);
-    v4i acc[MG], accr[MG];
-#pragma unroll
-    for (int t = 0; t < MG; ++t) acc[t] = accr[t] = v4i{0, 0, 0, 0};
+  auto consume = [&](int u, const Buf& bf) {
     static_for<IPW>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      const int ti = wv + kSkxWaves * (u.q * IPW + k);
-      const bool used = live && ti < ts;
-      const int t = min(ti, ts - 1);
-      const bool res = t >= ms;
-      // Activation bytes of this item: offset within the segment row, and
-      // the bytes that take part (the row's end, or the residual's codes).
+      const bool used = wv + kSkxWaves * (u * IPW + k) < NI;
+      const int j = bf.j[k], t = bf.t[k];
+      const bool res = t >= Cs;
+      // Activation bytes of the item within the slice row, and the bytes
+      // that take part (the row's end, or the residual's codes).
       const int xo = res ? 0 : t * CXB;
-      const int xlim = !used ? 0 : (res ? Rb * A_BITS / 4 : Xrow - s * seg * CXB);
+      const int xlim = !used ? 0 : (res ? Rb * A_BITS / 4 : xlen);
       uint4 xs[MG][LX];
 #pragma unroll
       for (int tb = 0; tb < MG; ++tb)
@@ -950,7 +936,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
       for (int tb = 0; tb < MG; ++tb) p[tb] = v4i{0, 0, 0, 0};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const uint4 ww = b.w[k][st >> 1];
+        const uint4 ww = bf.w[k][st >> 1];
         const v4i wa = (st & 1) ? widen16(ww.z, ww.w) : widen16(ww.x, ww.y);
 #pragma unroll
         for (int tb = 0; tb < MG; ++tb) {
@@ -964,78 +950,93 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
           p[tb] = mfma(wa, xv, p[tb]);
         }
       }
-      if (res) {
-#pragma unroll
-        for (int tb = 0; tb < MG; ++tb) accr[tb] += p[tb];
-      } else {
-#pragma unroll
-        for (int tb = 0; tb < MG; ++tb) acc[tb] += p[tb];
-      }
-    });
-    if (live && wv < ts) {
-      int* sp = slots + u.j * (skx_slot_bytes<MG>() / 4);
-#pragma unroll
-      for (int tb = 0; tb < MG; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) atomicAdd(sp + (tb * 64 + lane) * 4 + e, acc[tb][e]);
-      if (has_res && s == 0) {
+      if (used) {
+        int* dst = reinterpret_cast<int*>(slots + j * SLOT + (res ? MG : 0) * 64 + lane);
 #pragma unroll
         for (int tb = 0; tb < MG; ++tb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) atomicAdd(sp + ((MG + tb) * 64 + lane) * 4 + e, accr[tb][e]);
+          for (int e = 0; e < 4; ++e) atomicAdd(dst + tb * 256 + e, p[tb][e]);
       }
-    }
-    // After the last unit of a segment: every wave is done with it, then the
-    // next segment replaces it (this wave's loads all land, including the
-    // unit already issued) and a barrier publishes it.
-    if (SEG && live && u.s + 1 < S && u.j == G - 1 && u.q == rounds(u.s) - 1) {
-      lds_barrier();
-      load_x(u.s + 1);
-      wait_vmcnt<0>();
-      lds_barrier();
-    }
+    });
   };
 
-  // The first unit's loads go out first; then this wave's scale and direct
-  // loads (older) are waited for and one barrier publishes the activation
-  // rows and the cleared slots. Unit n + 1 is issued before unit n is
-  // computed, the loop unrolled by two so each buffer keeps its registers.
-  const int total = G * (S == 1 ? r_first : r_first + r_last + (S - 2) * r_mid);
-  Unit uc{0, 0, 0}, ui{0, 0, 0};
+  // Unit 0's loads go out first; then this wave's scale and direct loads
+  // (older) are waited for and one barrier publishes the activation slice
+  // and the cleared slots. Unit u + 1 is issued before unit u is computed,
+  // the loop unrolled by two so each buffer keeps its registers.
+  const int units = ((NI + kSkxWaves - 1) / kSkxWaves + IPW - 1) / IPW;
   Buf A, B;
-  issue(ui, A);
-  advance(ui);
+  issue(0, A);
   wait_vmcnt<IPW * LW>();
   lds_barrier();
-  int n = 0;
-  for (; n + 2 <= total; n += 2) {
-    issue(ui, B);
-    advance(ui);
-    consume(uc, A);
-    advance(uc);
-    issue(ui, A);
-    advance(ui);
-    consume(uc, B);
-    advance(uc);
+  int u = 0;
+  for (; u + 2 <= units; u += 2) {
+    issue(u + 1, B);
+    consume(u, A);
+    issue(u + 2, A);
+    consume(u + 1, B);
   }
-  if (n < total) consume(uc, A);
+  if (u < units) consume(u, A);
   wait_vmcnt<0>();                           // the last issue, past the end, unused
   lds_barrier();
-  if (wv >= G) return;
-  const int* sp = slots + wv * (skx_slot_bytes<MG>() / 4);
+
+  if (sp.KS > 1) {
+    // Partial sums out with agent-scope stores (written through to the
+    // point of coherence of all XCDs, so no whole-L2 write-back is needed),
+    // waited for before the counter is bumped; the group set's last
+    // workgroup then reads them with agent-scope loads. Slice 0 alone holds
+    // residual sums.
+    if (wv < Gb) {
+      long long* dst = reinterpret_cast<long long*>(sp.part + (static_cast<size_t>(ks) * ngroups + gbase + wv) * SLOT);
+      const long long* src = reinterpret_cast<const long long*>(slots + wv * SLOT);
+      const int hn = ks == 0 && has_res ? 2 * MG : MG;
+      for (int h = 0; h < hn; ++h)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          __hip_atomic_store(dst + (h * 64 + lane) * 2 + e, src[(h * 64 + lane) * 2 + e], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(sp.cnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.KS - 1;
+    lds_barrier();
+    if (!s_last) return;
+    if (threadIdx.x == 0) __hip_atomic_store(sp.cnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (wv >= Gb) return;
+  v4i sm[MG], sr[MG];
+  if (sp.KS == 1) {
+#pragma unroll
+    for (int t = 0; t < MG; ++t) {
+      sm[t] = slots[wv * SLOT + t * 64 + lane];
+      sr[t] = slots[wv * SLOT + (MG + t) * 64 + lane];
+    }
+  } else {
+    auto ld = [&](int q, int h) {
+      const long long* src = reinterpret_cast<const long long*>(sp.part + (static_cast<size_t>(q) * ngroups + gbase + wv) * SLOT);
+      const long long lo = __hip_atomic_load(src + (h * 64 + lane) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const long long hi = __hip_atomic_load(src + (h * 64 + lane) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return v4i{static_cast<int>(lo), static_cast<int>(lo >> 32), static_cast<int>(hi), static_cast<int>(hi >> 32)};
+    };
+#pragma unroll
+    for (int t = 0; t < MG; ++t) {
+      sm[t] = v4i{0, 0, 0, 0};
+      sr[t] = has_res ? ld(0, MG + t) : v4i{0, 0, 0, 0};
+    }
+    for (int q = 0; q < sp.KS; ++q)
+#pragma unroll
+      for (int t = 0; t < MG; ++t) sm[t] += ld(q, t);
+  }
   const float4 w4 = make_float4(wsc[0], wsc[1], wsc[2], wsc[3]);
   const float4 r4 = has_res ? make_float4(rsc[0], rsc[1], rsc[2], rsc[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
-  const int nb = group_n0(wv);
+  const int nb = (gbase + wv) * 16;
 #pragma unroll
-  for (int t = 0; t < MG; ++t) {
-    const v4i sm = *reinterpret_cast<const v4i*>(sp + (t * 64 + lane) * 4);
-    const v4i sr = *reinterpret_cast<const v4i*>(sp + ((MG + t) * 64 + lane) * 4);
-    store4<SHIFT>(a, sm, sr, t * 16 + l16, nb + 4 * g, sxv[t], w4, r4);
-  }
+  for (int t = 0; t < MG; ++t) store4<SHIFT>(a, sm[t], sr[t], t * 16 + l16, nb + 4 * g, sxv[t], w4, r4);
 }
 
 // ---------------------------------------------------------------------------
-// GEMV kernel (W4A4, M <= 4 tokens): v_dot8c_i32_i4 multiplies eight packed
+// GEMV kernel (W4A4, M <= 3 tokens): v_dot8c_i32_i4 multiplies eight packed
 // int4 codes of each operand and adds to an int32, in the canonical nibble
 // order of both Q(W^) and the activation codes, so the packed bytes are used
 // as loaded -- no widening, and no matrix-core work thrown away on missing
@@ -1056,7 +1057,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
 
 constexpr int kGemvRing = 8;                // load instructions in flight per wave
 constexpr int kGemvMaxX = 64 * 1024;        // LDS bytes for the activation rows
-constexpr int kGemvMaxTokens = 4;
+constexpr int kGemvMaxTokens = 3;          // from four tokens the skinny kernel measured faster
 
 template <int MT, int KP>
 __global__ __launch_bounds__(kThreads) void serq_gemv_kernel(LinearArgs a) {
@@ -1244,43 +1245,113 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Groups per workgroup G <= 8; the activation segment takes what LDS has
-// left after the group slots; IPW items per wave and unit (up to 8).
-template <int MG, int A_BITS, int IPW, bool SEG>
-hipError_t launch_skinny_ipw(const LinearArgs& a, int grid, int ngroups, int seg, hipStream_t st) {
+// The split workspace (counters, then partial sums), one per device, grown
+// on demand and zeroed when allocated; the kernel leaves the counters at
+// zero. Calls that take the split path share it, so they must not overlap
+// on one device.
+std::mutex g_ws_mutex;
+void* g_ws_ptr[64] = {};
+size_t g_ws_bytes[64] = {};
+
+hipError_t skinny_workspace(size_t part_bytes, int** cnt, v4i** part) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const size_t cnt_bytes = kSkxCounters * sizeof(int);
+  const size_t need = cnt_bytes + part_bytes;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if (g_ws_bytes[dev] < need) {
+    if (g_ws_ptr[dev]) {
+      e = hipDeviceSynchronize();           // earlier calls may still use it
+      if (e != hipSuccess) return e;
+      (void)hipFree(g_ws_ptr[dev]);
+      g_ws_ptr[dev] = nullptr;
+      g_ws_bytes[dev] = 0;
+    }
+    const size_t bytes = (need + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
+    e = hipMalloc(&g_ws_ptr[dev], bytes);
+    if (e != hipSuccess) return e;
+    e = hipMemset(g_ws_ptr[dev], 0, bytes);
+    if (e != hipSuccess) return e;
+    g_ws_bytes[dev] = bytes;
+  }
+  *cnt = static_cast<int*>(g_ws_ptr[dev]);
+  *part = reinterpret_cast<v4i*>(static_cast<uint8_t*>(g_ws_ptr[dev]) + cnt_bytes);
+  return hipSuccess;
+}
+
+// G and KS: about one workgroup per CU, the slice fitting LDS beside the
+// group slots; one slice if the activations fit, else the choice with the
+// least activation traffic (every workgroup loads its slice of the M rows)
+// plus partial-sum traffic (KS x the outputs, written and read back).
+template <int MG, int A_BITS>
+SkinnySplit plan_skinny(const LinearArgs& a) {
   constexpr int CXB = 2 * A_BITS * 16;
-  const int G = (ngroups + grid - 1) / grid;
-  const int lds = a.M * (seg * CXB + 16) + G * skx_slot_bytes<MG>();
+  const int ngroups = (a.N + 15) / 16;
+  const int C = (a.K + 255) / 256;
+  SkinnySplit best{0, 0, 0, 0, nullptr, nullptr};
+  double best_cost = 0.0;
+  for (int G = 1; G <= kSkxMaxGroups; ++G) {
+    const int nb = (ngroups + G - 1) / G;
+    if (G > 1 && (ngroups + G - 2) / (G - 1) == nb) continue;   // same group sets as G - 1
+    int KS = max(1, min(C, (kCUs + nb - 1) / nb));
+    if (ngroups > kCUs * kSkxMaxGroups) KS = 1;
+    for (;; ++KS) {
+      const int seg = (C + KS - 1) / KS;
+      if (static_cast<long>(a.M) * (seg * CXB + 16) + G * skx_slot_bytes<MG>() <= kSkxLds || KS >= C) break;
+    }
+    const int seg = (C + KS - 1) / KS;
+    if (static_cast<long>(a.M) * (seg * CXB + 16) + G * skx_slot_bytes<MG>() > kSkxLds) continue;
+    if (KS > 1 && nb > kSkxCounters) continue;
+    const int ks_used = (C + seg - 1) / seg;
+    const double xbytes = static_cast<double>(nb) * a.M * (a.K * A_BITS / 8);
+    const double pbytes = ks_used > 1 ? 2.0 * ks_used * ngroups * skx_slot_bytes<MG>() : 0.0;
+    const double cost = xbytes + pbytes;
+    // One slice whenever the activations fit: the split's tail (partial sums
+    // out, counter, the last workgroup's reads) measured several us.
+    const bool better = best.G == 0 || (ks_used == 1 && best.KS > 1) ||
+                        (cost < best_cost && !(ks_used > 1 && best.KS == 1));
+    if (better) {
+      best = SkinnySplit{G, nb, ks_used, seg, nullptr, nullptr};
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int MG, int A_BITS, int IPW>
+hipError_t launch_skinny_ipw(const LinearArgs& a, const SkinnySplit& sp, hipStream_t st) {
+  constexpr int CXB = 2 * A_BITS * 16;
+  const int lds = a.M * (sp.seg * CXB + 16) + sp.G * skx_slot_bytes<MG>();
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_skinny_kernel<MG, A_BITS, IPW, SEG>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_skinny_kernel<MG, A_BITS, IPW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSkxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  serq_skinny_kernel<MG, A_BITS, IPW, SEG><<<dim3(grid), dim3(64 * kSkxWaves), lds, st>>>(a, ngroups, seg);
+  serq_skinny_kernel<MG, A_BITS, IPW><<<dim3(sp.nb * sp.KS), dim3(64 * kSkxWaves), lds, st>>>(a, sp);
   return hipGetLastError();
 }
 
 template <int MG, int A_BITS>
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t st) {
-  constexpr int CXB = 2 * A_BITS * 16;
-  const int ngroups = (a.N + 15) / 16;
-  const int grid = max(min(ngroups, kCUs), (ngroups + kSkxMaxGroups - 1) / kSkxMaxGroups);
-  const int G = (ngroups + grid - 1) / grid;
-  const int C = (a.K + 255) / 256;
-  const int row_budget = (kSkxLds - G * skx_slot_bytes<MG>()) / a.M - 16;
-  int seg = min(C, row_budget / CXB);
-  if (seg < 1) return hipErrorInvalidValue;
-  const int S = (C + seg - 1) / seg;
-  seg = (C + S - 1) / S;                      // equal segments
-  const int per = (seg + (a.r > 0 ? 1 : 0) + kSkxWaves - 1) / kSkxWaves;   // items of the busiest wave
-  if (S > 1 || per > 8) return launch_skinny_ipw<MG, A_BITS, 8, true>(a, grid, ngroups, seg, st);
-  if (per <= 2) return launch_skinny_ipw<MG, A_BITS, 2, false>(a, grid, ngroups, seg, st);
-  if (per <= 3) return launch_skinny_ipw<MG, A_BITS, 3, false>(a, grid, ngroups, seg, st);
-  if (per <= 4) return launch_skinny_ipw<MG, A_BITS, 4, false>(a, grid, ngroups, seg, st);
-  if (per <= 5) return launch_skinny_ipw<MG, A_BITS, 5, false>(a, grid, ngroups, seg, st);
-  return launch_skinny_ipw<MG, A_BITS, 8, false>(a, grid, ngroups, seg, st);
+  SkinnySplit sp = plan_skinny<MG, A_BITS>(a);
+  if (sp.G == 0) return hipErrorInvalidValue;
+  if (sp.KS > 1) {
+    const int ngroups = (a.N + 15) / 16;
+    hipError_t e = skinny_workspace(static_cast<size_t>(sp.KS) * ngroups * skx_slot_bytes<MG>(), &sp.cnt, &sp.part);
+    if (e != hipSuccess) return e;
+  }
+  // About one group's items per unit and wave: the CU's loads in flight then
+  // stay within one or two groups' rows.
+  const int per = max(2, (sp.seg + (a.r > 0 ? 1 : 0) + kSkxWaves - 1) / kSkxWaves);
+  if (per <= 2) return launch_skinny_ipw<MG, A_BITS, 2>(a, sp, st);
+  if (per <= 3) return launch_skinny_ipw<MG, A_BITS, 3>(a, sp, st);
+  if (per <= 4) return launch_skinny_ipw<MG, A_BITS, 4>(a, sp, st);
+  if (per <= 6) return launch_skinny_ipw<MG, A_BITS, 6>(a, sp, st);
+  return launch_skinny_ipw<MG, A_BITS, 8>(a, sp, st);
 }
 
 template <int MT, int KP>
@@ -1345,8 +1416,7 @@ hipError_t launch_linear(const LinearArgs& a, const LinearPlan& p, hipStream_t s
       switch (a.M) {
         case 1: return launch_gemv<1>(a, st);
         case 2: return launch_gemv<2>(a, st);
-        case 3: return launch_gemv<3>(a, st);
-        default: return launch_gemv<4>(a, st);
+        default: return launch_gemv<3>(a, st);
       }
     case LinearKernel::kDecode16:
       return a.a_bits == 4 ? launch_skinny<1, 4>(a, st) : launch_skinny<1, 8>(a, st);
