@@ -174,6 +174,12 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
  *              NULL on the hot path; when non-NULL, device M x N int32
  *              buffers that receive the exact integer accumulators (both
  *              must then be given).
+ * Workspace: for 4..32 tokens whose activation rows exceed the kernel's LDS
+ * budget (long K), the K range is split across workgroups and their int32
+ * partial sums meet in a per-device workspace that the library allocates
+ * (hipMalloc, zeroed) on the first such call and grows when a later call
+ * needs more; such calls on one device must not overlap (they share it), and
+ * the first one must not run under stream capture.
  * Errors: SERQ_EINVAL (NULL pointer, bad sizes, bad a_bits or dtype, only one
  * debug buffer), SERQ_EALIGN (pointer not 16-byte aligned), SERQ_EHIP.
  */
