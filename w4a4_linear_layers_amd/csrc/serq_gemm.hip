@@ -1044,7 +1044,8 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
 //
 // A wave streams 8 weight rows over a K range: each load instruction takes
 // 128 contiguous bytes (one cache line) of each of the 8 rows, lane (row
-// l / 8, part l % 8) 16 of them, with kGemvRing instructions in flight. A
+// l / 8, part l % 8) 16 of them, with two units of kGemvUnit instructions
+// in flight. A
 // four-wave workgroup covers 4 / KP row octets, each split into KP K ranges
 // (KP from N, so that small layers still spread over every CU). The
 // activation rows (M x K/2 bytes) are loaded into LDS once per workgroup and
@@ -1055,7 +1056,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
 // first activation codes.
 // ---------------------------------------------------------------------------
 
-constexpr int kGemvRing = 8;                // load instructions in flight per wave
+constexpr int kGemvUnit = 4;                // load instructions per unit (two units in flight per wave)
 constexpr int kGemvMaxX = 64 * 1024;        // LDS bytes for the activation rows
 constexpr int kGemvMaxTokens = 3;          // from four tokens the skinny kernel measured faster
 
@@ -1094,59 +1095,87 @@ __global__ __launch_bounds__(kThreads) void serq_gemv_kernel(LinearArgs a) {
   const int l0 = min(kp * per, lines), l1 = min(l0 + per, lines);
   const bool res_here = a.r > 0 && kp == KP - 1;
   const int total = (l1 - l0) + (res_here ? 1 : 0);
-  const uint8_t* wrow = a.Wq + static_cast<size_t>(nrow) * Kb + 16 * part;
-  const uint8_t* rrow = a.r > 0 ? a.Rq + static_cast<size_t>(nrow) * Rb + 16 * part : nullptr;
+  const uint8_t* wrow = a.Wq + static_cast<size_t>(nrow) * Kb;
+  const uint8_t* rrow = a.Rq + static_cast<size_t>(nrow) * Rb;   // read only when r > 0
+  // Item i of this wave: line l0 + i, or the residual line after the last.
+  // Every load is issued (items past the end reload the last one, pieces
+  // past a row's end read its last 16 bytes) and every item is computed,
+  // with the activation side zeroed where the weight bytes do not count:
+  // the compiler's load counters then stay exact and the ring never drains.
   auto load = [&](int i, uint4& w) {
-    if (l0 + i < l1) {
-      const int off = 128 * (l0 + i) + 16 * part;
-      w = off < Kb ? *reinterpret_cast<const uint4*>(wrow + 128 * (l0 + i)) : make_uint4(0, 0, 0, 0);
-    } else {
-      w = 16 * part < Rb ? *reinterpret_cast<const uint4*>(rrow) : make_uint4(0, 0, 0, 0);
-    }
+    const int ii = min(i, max(total - 1, 0));
+    const bool res = res_here && l0 + ii >= l1;
+    const uint8_t* p = res ? rrow : wrow;
+    const int lim = res ? Rb : Kb;
+    const int off = (res ? 0 : 128 * (l0 + ii)) + 16 * part;
+    w = *reinterpret_cast<const uint4*>(p + min(off, lim - 16));
   };
-  uint4 buf[kGemvRing];
-  static_for<kGemvRing>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    if (k < total) load(k, buf[k]);
-  });
+  // Units of kGemvUnit items, double-buffered: unit u + 1 is issued before
+  // unit u is computed; the loop is unrolled by two so each buffer keeps its
+  // registers (a single rotating ring got its loads hoisted into fresh
+  // registers and copied back at the loop end, which waits for them).
+  struct Unit {
+    uint4 w[kGemvUnit];
+  };
+  auto issue = [&](int u, Unit& b) {
+    static_for<kGemvUnit>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      load(u * kGemvUnit + k, b.w[k]);
+    });
+  };
+  Unit A, B;
+  issue(0, A);
   // This wave's activation loads are older than its weight loads: once at
   // most the weight loads are outstanding, its part of LDS is written.
-  const int issued = min(total, kGemvRing);
-  static_for<kGemvRing + 1>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    if (issued == k) wait_vmcnt<k>();
-  });
+  wait_vmcnt<kGemvUnit>();
   lds_barrier();
 
   int acc[MT], accr[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = accr[t] = 0;
-  auto consume = [&](int i, const uint4& w) {
-    const bool res = l0 + i >= l1;
-    const int off = (res ? 0 : 128 * (l0 + i)) + 16 * part;
-    const bool inx = off < Kb;                        // (Q(R)'s padding is zero)
+  auto consume1 = [&](int i, const uint4& w) {
+    const bool used = i < total;
+    const int ii = min(i, max(total - 1, 0));
+    const bool res = res_here && l0 + ii >= l1;
+    const int off = (res ? 0 : 128 * (l0 + ii)) + 16 * part;
+    const bool inx = used && off < (res ? Rb : Kb);   // (Q(R)'s padding is zero)
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const uint4 x = inx ? *reinterpret_cast<const uint4*>(lds + t * Kb + off) : make_uint4(0, 0, 0, 0);
-      int d = res ? accr[t] : acc[t];
+      int d = 0;
       d = __builtin_amdgcn_sdot8(static_cast<int>(w.x), static_cast<int>(x.x), d, false);
       d = __builtin_amdgcn_sdot8(static_cast<int>(w.y), static_cast<int>(x.y), d, false);
       d = __builtin_amdgcn_sdot8(static_cast<int>(w.z), static_cast<int>(x.z), d, false);
       d = __builtin_amdgcn_sdot8(static_cast<int>(w.w), static_cast<int>(x.w), d, false);
-      if (res) accr[t] = d; else acc[t] = d;
+      if (res) accr[t] += d; else acc[t] += d;
     }
   };
-  for (int base = 0; base < total; base += kGemvRing) {
-    static_for<kGemvRing>([&](auto kc) {
+  auto consume = [&](int u, const Unit& b) {
+    static_for<kGemvUnit>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      const int i = base + k;
-      if (i < total) {
-        const uint4 w = buf[k];
-        if (i + kGemvRing < total) load(i + kGemvRing, buf[k]);
-        consume(i, w);
-      }
+      consume1(u * kGemvUnit + k, b.w[k]);
     });
+  };
+  // fence_sums: an empty asm that takes the sums, so a unit's dot products
+  // are done before the next issue into its registers (the compiler would
+  // otherwise sink them, load into fresh registers and copy back at the loop
+  // end, waiting for the loads).
+  auto fence_sums = [&]() {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) asm volatile("" : "+v"(acc[t]), "+v"(accr[t]) :: "memory");
+  };
+  const int units = (total + kGemvUnit - 1) / kGemvUnit;
+  int u = 0;
+  for (; u + 2 <= units; u += 2) {
+    issue(u + 1, B);
+    consume(u, A);
+    fence_sums();
+    issue(u + 2, A);
+    consume(u + 1, B);
+    fence_sums();
   }
+  if (u < units) consume(u, A);
+  wait_vmcnt<0>();                               // the last issue, past the end, unused
 
   // Sum over the row's 8 lanes, then over the KP waves of the row octet.
 #pragma unroll
