@@ -1045,9 +1045,9 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
 // A wave streams 8 weight rows over a K range: each load instruction takes
 // 128 contiguous bytes (one cache line) of each of the 8 rows, lane (row
 // l / 8, part l % 8) 16 of them, with two units of kGemvUnit instructions
-// in flight. A
-// four-wave workgroup covers 4 / KP row octets, each split into KP K ranges
-// (KP from N, so that small layers still spread over every CU). The
+// in flight. A workgroup of KP waves covers one row octet split into KP K
+// ranges (KP = 8 for narrow layers, so that they still keep about sixteen
+// waves per CU loading, else 4). The
 // activation rows (M x K/2 bytes) are loaded into LDS once per workgroup and
 // read back in broadcast. At the end each row's partial sums are added over
 // its 8 lanes, then over the KP waves through LDS, and the K range 0 wave
@@ -1061,10 +1061,10 @@ constexpr int kGemvMaxX = 64 * 1024;        // LDS bytes for the activation rows
 constexpr int kGemvMaxTokens = 3;          // from four tokens the skinny kernel measured faster
 
 template <int MT, int KP>
-__global__ __launch_bounds__(kThreads) void serq_gemv_kernel(LinearArgs a) {
-  constexpr int OCT = 4 / KP;                         // row octets per workgroup
+__global__ __launch_bounds__(64 * KP) void serq_gemv_kernel(LinearArgs a) {
+  constexpr int OCT = 1;                              // row octets per workgroup
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];   // [MT][Kb] activation codes
-  __shared__ int red[4][2][MT][64];                   // [wave][main, residual][token][lane]
+  __shared__ int red[KP][2][MT][64];                  // [wave][main, residual][token][lane]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int oct = wv / KP, kp = wv % KP;
@@ -1083,7 +1083,7 @@ __global__ __launch_bounds__(kThreads) void serq_gemv_kernel(LinearArgs a) {
   for (int t = 0; t < MT; ++t) sxv[t] = a.sx[t];
   // Activation rows into LDS, 1 KB per load instruction over the four waves.
   const int nx = (MT * Kb + 1023) / 1024;
-  for (int q = wv; q < nx; q += 4) {
+  for (int q = wv; q < nx; q += KP) {
     const int off = 1024 * q + 16 * lane;
     if (off < MT * Kb) dma16(a.Xq, static_cast<uint32_t>(off), lds_base + 1024 * q);
   }
@@ -1386,7 +1386,7 @@ hipError_t launch_skinny(const LinearArgs& a, hipStream_t st) {
 template <int MT, int KP>
 hipError_t launch_gemv_kp(const LinearArgs& a, hipStream_t st) {
   const int octets = (a.N + 7) / 8;
-  const int grid = (octets + (4 / KP) - 1) / (4 / KP);
+  const int grid = octets;
   const int lds = (MT * (a.K / 2) + 15) / 16 * 16;
   static bool attr_set = false;
   if (!attr_set) {
@@ -1395,15 +1395,16 @@ hipError_t launch_gemv_kp(const LinearArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  serq_gemv_kernel<MT, KP><<<dim3(grid), dim3(kThreads), lds, st>>>(a);
+  serq_gemv_kernel<MT, KP><<<dim3(grid), dim3(64 * KP), lds, st>>>(a);
   return hipGetLastError();
 }
 
-// Four K ranges per row octet: short-lived waves with a shallow ring
-// measured faster than longer ones on every LLaMA shape (more resident
-// workgroups per CU, more lines in flight).
+// Four K ranges per row octet, eight when there are few octets (so that
+// narrow layers still keep about sixteen waves per CU loading).
 template <int MT>
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t st) {
+  const int octets = (a.N + 7) / 8;
+  if (octets < 4 * kCUs) return launch_gemv_kp<MT, 8>(a, st);
   return launch_gemv_kp<MT, 4>(a, st);
 }
 
