@@ -780,7 +780,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
 
 // ---------------------------------------------------------------------------
 // Skinny kernel (4..32 tokens, and W4A8 from one token): eight-wave
-// workgroups, each owning G <= 8 consecutive 16-channel groups and one K
+// workgroups, each owning G <= 8 16-channel groups and one K
 // slice of `seg` 256-code chunks (KS slices in all). The workgroup's slice of
 // the activation rows is loaded into LDS once and shared by its G groups.
 // Few groups per workgroup with the whole of K would reload the activations
@@ -845,8 +845,10 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
   const bool has_res = a.r > 0;
   const int ngroups = (a.N + 15) / 16;
   const int b = static_cast<int>(blockIdx.x) % sp.nb, ks = static_cast<int>(blockIdx.x) / sp.nb;
-  const int gbase = b * sp.G;
-  const int Gb = min(sp.G, ngroups - gbase);          // groups of this workgroup
+  // Group j of this workgroup is b + nb j: at any moment the CUs stream rows
+  // spread over the whole matrix rather than each its own contiguous block.
+  auto grp = [&](int j) { return b + sp.nb * j; };
+  const int Gb = (ngroups - b + sp.nb - 1) / sp.nb;   // groups of this workgroup
   const int C = (a.K + 255) / 256;
   const int c0 = ks * sp.seg;                         // first chunk of the slice
   const int Cs = min(sp.seg, C - c0);                 // main items per group
@@ -864,7 +866,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
   // weight load.
   float wsc[4], rsc[4], sxv[MG];
   {
-    const int nb = (gbase + min(wv, Gb - 1)) * 16;
+    const int nb = grp(min(wv, Gb - 1)) * 16;
     const float* srp = has_res ? a.sr : a.sw;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -900,7 +902,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
       bf.j[k] = j;
       bf.t[k] = t;
       const bool res = t >= Cs;
-      const int nrow = min((gbase + j) * 16 + l16, a.N - 1);
+      const int nrow = min(grp(j) * 16 + l16, a.N - 1);
       const uint8_t* wp = res ? a.Rq + static_cast<size_t>(nrow) * Rb : a.Wq + static_cast<size_t>(nrow) * Kb;
       const int wlim = res ? Rb : Kb;
       const int c = res ? 0 : c0 + t;
@@ -987,7 +989,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
     // workgroup then reads them with agent-scope loads. Slice 0 alone holds
     // residual sums.
     if (wv < Gb) {
-      long long* dst = reinterpret_cast<long long*>(sp.part + (static_cast<size_t>(ks) * ngroups + gbase + wv) * SLOT);
+      long long* dst = reinterpret_cast<long long*>(sp.part + (static_cast<size_t>(ks) * ngroups + grp(wv)) * SLOT);
       const long long* src = reinterpret_cast<const long long*>(slots + wv * SLOT);
       const int hn = ks == 0 && has_res ? 2 * MG : MG;
       for (int h = 0; h < hn; ++h)
@@ -1014,7 +1016,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
     }
   } else {
     auto ld = [&](int q, int h) {
-      const long long* src = reinterpret_cast<const long long*>(sp.part + (static_cast<size_t>(q) * ngroups + gbase + wv) * SLOT);
+      const long long* src = reinterpret_cast<const long long*>(sp.part + (static_cast<size_t>(q) * ngroups + grp(wv)) * SLOT);
       const long long lo = __hip_atomic_load(src + (h * 64 + lane) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const long long hi = __hip_atomic_load(src + (h * 64 + lane) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return v4i{static_cast<int>(lo), static_cast<int>(lo >> 32), static_cast<int>(hi), static_cast<int>(hi >> 32)};
@@ -1030,7 +1032,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
   }
   const float4 w4 = make_float4(wsc[0], wsc[1], wsc[2], wsc[3]);
   const float4 r4 = has_res ? make_float4(rsc[0], rsc[1], rsc[2], rsc[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
-  const int nb = (gbase + wv) * 16;
+  const int nb = grp(wv) * 16;
 #pragma unroll
   for (int t = 0; t < MG; ++t) store4<SHIFT>(a, sm[t], sr[t], t * 16 + l16, nb + 4 * g, sxv[t], w4, r4);
 }
