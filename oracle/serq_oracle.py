@@ -392,3 +392,59 @@ def linear_float_residual(Xq: dict, layer: dict) -> np.ndarray:
     main = xd @ (layer["Wq_codes"].astype(np.float64) * layer["sw"].astype(np.float64)[None, :])
     res = xd[:, :r] @ layer["R"].astype(np.float64)
     return main + res
+
+
+# ---------------------------------------------------------------------------
+# The MLP activation between gate/up and down, fused with down's activation
+# quantization. [N] 关键设计 3: the down projection's input permutation is
+# pushed offline into the gate/up output channels, so h = silu(g) * u leaves
+# the elementwise step already in down's saliency order and goes straight
+# into the per-token quantizer, with no gather. The pages do not spell out
+# the MLP nonlinearity; the reading is the LLaMA MLP, silu(g) = g * sigma(g)
+# = g / (1 + e^-g). For bit-exact parity both implementations evaluate it
+# with one fixed fp32 recipe (no fused multiply-add, IEEE division):
+#     e  = exp32(-g)            (argument clamped to [-80, 80])
+#     sg = fl32(g / fl32(1 + e))
+#     h  = fl32(sg * u)
+# exp32 follows Cody and Waite's argument reduction: e^x = 2^n e^r with
+# n = rne(fl32(x log2 e)) and r = fl32(fl32(x - n c_hi) - n c_lo), where
+# c_hi + c_lo = ln 2 and c_hi has 12 significant bits so that n c_hi is
+# exact for |n| < 2^11; e^r (|r| <= ln2 / 2) is its Taylor polynomial to
+# degree 7 in Horner form (truncation below 2^-27 relative), then scaled by
+# 2^n exactly. The clamp keeps every intermediate a normal number.
+# ---------------------------------------------------------------------------
+
+LOG2E_F32 = np.float32(1.0 / math.log(2.0))
+LN2_HI_F32 = np.float32(0.693145751953125)                  # 12 significant bits
+LN2_LO_F32 = np.float32(math.log(2.0) - 0.693145751953125)
+EXP_TAYLOR_F32 = [np.float32(1.0 / math.factorial(k)) for k in range(8)]   # 1/k!
+EXP_ARG_CLAMP = np.float32(80.0)
+
+
+def exp32(x: np.ndarray) -> np.ndarray:
+    """e^x for float32 x by the fixed recipe above (elementwise, float32)."""
+    x = np.clip(np.asarray(x, dtype=np.float32), -EXP_ARG_CLAMP, EXP_ARG_CLAMP).astype(np.float32)
+    n = np.rint((x * LOG2E_F32).astype(np.float32)).astype(np.float32)
+    r = (x - (n * LN2_HI_F32).astype(np.float32)).astype(np.float32)
+    r = (r - (n * LN2_LO_F32).astype(np.float32)).astype(np.float32)
+    p = np.full(x.shape, EXP_TAYLOR_F32[7], np.float32)
+    for k in range(6, -1, -1):
+        p = (p * r).astype(np.float32)
+        p = (p + EXP_TAYLOR_F32[k]).astype(np.float32)
+    return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+
+
+def silu_mul(G: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u elementwise in fp32 by the recipe above."""
+    g = np.asarray(G, dtype=np.float32)
+    u = np.asarray(U, dtype=np.float32)
+    e = exp32(-g)
+    s = (np.float32(1.0) + e).astype(np.float32)
+    sg = (g / s).astype(np.float32)
+    return (sg * u).astype(np.float32)
+
+
+def silu_mul_quant_act(G: np.ndarray, U: np.ndarray, s_hat_inv: np.ndarray, a_bits: int) -> dict:
+    """down's quantized input from the gate and up outputs (both M x K, in
+    down's saliency order): quant_act(silu(G) * U)."""
+    return quant_act(silu_mul(G, U), s_hat_inv, a_bits)

@@ -382,7 +382,55 @@ def check_rank_trend(O):
     assert np.linalg.norm(O.linear(q1, L1, out="f32")["y64"] - Y) > errs[0]
 
 
+# ------------------------------------------------- MLP activation (silu * up)
+# Closed forms only: the oracle's fp32 recipe for e^x and silu(g) * u against
+# the fp64 definitions, a special value, the clamp, an odd-symmetry identity
+# and the composition with the per-token quantizer the step is defined as.
+
+def check_exp32(O):
+    x = np.linspace(-80.0, 80.0, 400001).astype(np.float32)
+    truth = np.exp(x.astype(np.float64))
+    got = O.exp32(x).astype(np.float64)
+    ulp = np.spacing(truth.astype(np.float32)).astype(np.float64)
+    assert (np.abs(got - truth) <= 2.0 * ulp).all(), float((np.abs(got - truth) / ulp).max())
+    assert O.exp32(np.float32(0.0)) == np.float32(1.0)
+    assert O.exp32(np.float32(500.0)) == O.exp32(np.float32(80.0))
+    assert O.exp32(np.float32(-500.0)) == O.exp32(np.float32(-80.0))
+
+
+def check_silu_mul(O):
+    rng = np.random.default_rng(11)
+    g = np.concatenate([rng.standard_normal(20000) * 4.0, np.linspace(-30.0, 30.0, 6001)]).astype(np.float32)
+    u = (rng.standard_normal(g.size) * 2.0).astype(np.float32)
+    h = O.silu_mul(g, u).astype(np.float64)
+    g64, u64 = g.astype(np.float64), u.astype(np.float64)
+    truth = g64 * u64 / (1.0 + np.exp(-g64))
+    tol = 4.0 * np.spacing(np.abs(truth).astype(np.float32)).astype(np.float64) + 1e-30
+    assert (np.abs(h - truth) <= tol).all(), float((np.abs(h - truth) / tol).max())
+    # silu(0) = 0; for g >= 20, e^-g < 2^-25 so 1 + e rounds to 1: h = fl32(g u)
+    assert (O.silu_mul(np.zeros(5, np.float32), u[:5]) == 0).all()
+    big = np.float32([20.0, 33.5, 79.0])
+    assert np.array_equal(O.silu_mul(big, u[:3]), (big * u[:3]).astype(np.float32))
+    # odd symmetry: silu(g) - silu(-g) = g (sigma(g) + sigma(-g) = 1)
+    gs = np.linspace(-12.0, 12.0, 2001).astype(np.float32)
+    one = np.ones_like(gs)
+    d = O.silu_mul(gs, one).astype(np.float64) - O.silu_mul(-gs, one).astype(np.float64)
+    assert np.allclose(d, gs.astype(np.float64), rtol=0, atol=8 * np.spacing(np.float32(12.0)))
+    # the fused step is the quantizer applied to silu(G) * U (same codes and scales)
+    G = (rng.standard_normal((5, 96)) * 3).astype(np.float32)
+    U = rng.standard_normal((5, 96)).astype(np.float32)
+    sinv = (rng.random(96) + 0.5).astype(np.float32)
+    for bits in (4, 8):
+        a = O.silu_mul_quant_act(G, U, sinv, bits)
+        hh = (G.astype(np.float64) * U / (1.0 + np.exp(-G.astype(np.float64)))).astype(np.float32)
+        b = O.quant_act(hh, sinv, bits)
+        # codes agree except where the fp64 and fp32-recipe values straddle a rounding edge
+        assert (np.abs(a["codes"].astype(int) - b["codes"].astype(int)) <= 1).all()
+        assert np.mean(a["codes"] == b["codes"]) > 0.99
+        assert np.allclose(a["sx"], b["sx"], rtol=1e-6, atol=0)
+
+
 ALL_CHECKS = [check_pack, check_quantizer_golden, check_quantizer_bruteforce, check_smoothing,
               check_perm, check_fold_identity, check_compensator, check_int_gemm,
               check_dequant_identity, check_special_cases, check_worked_layer, check_bf16,
-              check_permute_outputs, check_rank_trend]
+              check_permute_outputs, check_rank_trend, check_exp32, check_silu_mul]

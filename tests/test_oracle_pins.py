@@ -118,6 +118,30 @@ def _mut_bf16_via_f32(orig):
     return f
 
 
+def _mut_exp_drops_ln2_lo(orig):
+    def f(x):
+        x = np.clip(np.asarray(x, np.float32), -O.EXP_ARG_CLAMP, O.EXP_ARG_CLAMP).astype(np.float32)
+        n = np.rint((x * O.LOG2E_F32).astype(np.float32)).astype(np.float32)
+        r = (x - (n * O.LN2_HI_F32).astype(np.float32)).astype(np.float32)
+        p = np.full(x.shape, O.EXP_TAYLOR_F32[7], np.float32)
+        for k in range(6, -1, -1):
+            p = ((p * r).astype(np.float32) + O.EXP_TAYLOR_F32[k]).astype(np.float32)
+        return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+    return f
+
+
+def _mut_silu_sign(orig):
+    def f(G, U):
+        g = np.asarray(G, np.float32)
+        s = (np.float32(1.0) + O.exp32(g)).astype(np.float32)
+        return ((g / s).astype(np.float32) * np.asarray(U, np.float32)).astype(np.float32)
+    return f
+
+
+def _mut_fused_skips_silu(orig):
+    return lambda G, U, s_hat_inv, a_bits: O.quant_act((np.asarray(G, np.float32) * np.asarray(U, np.float32)).astype(np.float32), s_hat_inv, a_bits)
+
+
 MUTANTS = {
     "compensator_sign": ("compensator", _mut_compensator_sign),
     "saliency_ascending": ("saliency_order", _mut_saliency_ascending),
@@ -132,6 +156,9 @@ MUTANTS = {
     "per_tensor_weights": ("quantize_columns", _mut_per_tensor_weights),
     "alpha_swapped": ("smoothing_factors", _mut_alpha_swapped),
     "bf16_double_rounding": ("round_f64_to_bf16", _mut_bf16_via_f32),
+    "exp_drops_ln2_lo": ("exp32", _mut_exp_drops_ln2_lo),
+    "silu_sign": ("silu_mul", _mut_silu_sign),
+    "fused_skips_silu": ("silu_mul_quant_act", _mut_fused_skips_silu),
 }
 
 
