@@ -60,6 +60,11 @@ def quant_bytes(M, K, a_bits):
     return M * K * 2 + 4 * K + M * K * a_bits // 8 + 4 * M
 
 
+def act_bytes(M, K, a_bits):
+    """serq_silu_mul_quant_act: g and u (bf16), s_hat_inv, codes, scales."""
+    return M * K * 4 + 4 * K + M * K * a_bits // 8 + 4 * M
+
+
 def linear_ops(M, K, N, r):
     return 2 * M * N * (K + r)
 
@@ -158,6 +163,53 @@ class Setup:
             torch.cuda.synchronize()
             out.append(e0.elapsed_time(e1) * 1e3 / n)
         return tuple(out)
+
+
+def time_mlp_act(K, Ms, n=100, a_bits=4, seed=0):
+    """The MLP step before down, alone: silu(g) * u -> down's codes and
+    scales, reading g and u in place from a gate/up output (bf16, M x 2K,
+    ld = 2K) as serq_silu_mul_quant_act does in a LLaMA MLP with the
+    intermediate width K. Each launch reads its own copy of the output (the
+    copies span >= 768 MiB, beyond the last-level cache); n launches are
+    captured in one graph and timed with events on the replay stream."""
+    import torch
+
+    import w4a4_linear_layers_amd as S
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    sinv = torch.exp(torch.rand(K, device=dev, generator=gen) * 3 - 2)
+    out = []
+    for M in Ms:
+        per = M * 2 * K * 2
+        copies = max(2, math.ceil(ROTATE_BYTES / per))
+        y = torch.randn((copies, M, 2 * K), device=dev, generator=gen).mul_(2).to(torch.bfloat16)
+        xq = torch.empty((M, K // 2 if a_bits == 4 else K), dtype=torch.uint8 if a_bits == 4 else torch.int8,
+                         device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def act(i):
+            yc = y[i % copies]
+            S.silu_mul_quant_act(yc[:, :K], yc[:, K:], sinv, a_bits=a_bits, out=(xq, sx))
+
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                act(i)
+        g.replay()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        gbs = act_bytes(M, K, a_bits) / (us * 1e-6) / 1e9
+        out.append(dict(K=K, M=M, us=round(us, 2), HBM_GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 3)))
+        del g, y
+    return out
 
 
 def cpu_baseline(setup, M, rows=None, budget_s=20.0):
@@ -294,6 +346,14 @@ def main(argv=None):
             print(f"# M={m}: linear {lu:.2f} us {tops:.1f} TOP/s {hbm:.0f} GB/s ({e['bound']} frac "
                   f"{e['frac']:.3f}); quant_act {qu:.2f} us", file=sys.stderr, flush=True)
 
+    mlp_act = []
+    if not args.no_sweep:
+        for k_int in (14336, 28672):
+            for e in time_mlp_act(k_int, (1, 16, 256, 4096)):
+                mlp_act.append(e)
+                print(f"# silu_mul_quant_act K={e['K']} M={e['M']}: {e['us']:.2f} us {e['HBM_GBs']:.0f} GB/s",
+                      file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(setup, M)
@@ -312,6 +372,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "mlp_activation": mlp_act,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -150,6 +150,40 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
                    void* Xq, float* sx, void* stream);
 
 /*
+ * serq_silu_mul_quant_act -- online, device memory, asynchronous on `stream`.
+ *
+ * The MLP step between gate/up and down, fused with down's activation
+ * quantization: h = silu(g) * u elementwise, then exactly serq_quant_act on
+ * h (per token: x^ = h * s_hat_inv, absmax, codes, sx). The gate and up
+ * outputs arrive already in down's saliency order, the permutation having
+ * been pushed into their output channels offline with serq_permute_outputs
+ * (papernotes.org SERQ notes, 关键设计 3), so no gather is needed. The pages
+ * do not spell out the nonlinearity; silu(g) = g / (1 + e^-g) as in the
+ * LLaMA MLP, evaluated by a fixed fp32 recipe so results are reproducible
+ * bit for bit: e = exp(-g) with the argument clamped to [-80, 80], by
+ * Cody-Waite reduction (e^x = 2^n e^r, n = rne(x log2 e), ln 2 split in a
+ * 12-bit head and a tail) and the degree-7 Taylor polynomial of e^r; then
+ * fl32(fl32(g / fl32(1 + e)) * u) with IEEE division; no fused multiply-add.
+ *
+ *   G, U       device, row m of gate at G + m * ld, of up at U + m * ld, K
+ *              elements each, of x_dtype (a gate/up output stored as one
+ *              M x 2K buffer is G = Y, U = Y + K, ld = 2K).
+ *   ld         row stride in elements, ld >= K. G and U need only be
+ *              aligned to their element; rows that are all 16-byte aligned
+ *              (and K % 8 == 0) take the vector path, others a scalar one
+ *              with the same results.
+ *   s_hat_inv  K floats, device (down's, from serq_calibrate).
+ *   a_bits, Xq, sx as for serq_quant_act.
+ * M == 0 is a no-op. Errors: SERQ_EINVAL (NULL pointer, M < 0, K <= 0, odd
+ * K, ld < K, bad a_bits or dtype), SERQ_EALIGN (G or U not aligned to its
+ * element, Xq or sx not 16-byte aligned), SERQ_EHIP. Subnormal inputs are
+ * outside the contract.
+ */
+int serq_silu_mul_quant_act(const void* G, const void* U, int ld, serq_dtype x_dtype,
+                            int M, int K, const float* s_hat_inv, int a_bits,
+                            void* Xq, float* sx, void* stream);
+
+/*
  * serq_linear -- online, device memory, asynchronous on `stream`.
  *
  * The SERQ linear: acc_main = Xq . Q(W^) over all K, acc_res = Xq[:, :r] . Q(R)

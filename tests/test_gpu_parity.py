@@ -74,6 +74,80 @@ def test_quant_act_empty_is_noop():
     _sync()
 
 
+# ------------------------------------------------- silu(g) * u -> quant_act
+
+def _gate_up_input(M, K, dtype, layout, seed):
+    """Gate and up outputs in down's order: g of a few units spread, u with
+    a few outlier channels, planted values at the exp clamp, the saturation
+    of silu, zero, and a zero row; returned as host fp32 arrays (the values
+    the device holds) and as device views of the requested layout."""
+    rng = np.random.default_rng(seed)
+    G = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+    U = rng.standard_normal((M, K)).astype(np.float32)
+    U[:, rng.choice(K, max(1, K // 64), replace=False)] *= 30
+    planted = np.array([-200.0, -88.7, -80.0, -79.9, -30.0, -0.0, 0.0, 1e-3, 20.0, 37.5, 90.0, 1e4], np.float32)
+    G[0, :min(K, planted.size)] = planted[:K]
+    if M > 1:
+        U[1] = 0.0                              # h = 0 row -> scale 0, zero codes
+    if M > 2:
+        G[2] = -60.0                            # h tiny (silu(-60) ~ -5e-25), codes still full range
+    if dtype == "bf16":
+        gb = round_to_bf16_bits(G).reshape(M, K)
+        ub = round_to_bf16_bits(U).reshape(M, K)
+        G = (gb.astype(np.uint32) << 16).view(np.float32)
+        U = (ub.astype(np.uint32) << 16).view(np.float32)
+        pack = lambda a: bf16_tensor(a)         # noqa: E731
+        raw_g, raw_u = gb, ub
+    else:
+        pack = dev
+        raw_g, raw_u = G, U
+    if layout == "split":
+        return G, U, pack(raw_g), pack(raw_u)
+    pad = 0 if layout == "cat" else 24
+    Y = np.zeros((M, 2 * K + pad), raw_g.dtype)
+    Y[:, :K] = raw_g
+    Y[:, K + pad:] = raw_u
+    Yt = pack(Y)
+    return G, U, Yt[:, :K], Yt[:, K + pad:]
+
+
+@pytest.mark.parametrize("M,K,layout", [(16, 14336, "cat"), (5, 28672, "cat"), (33, 4096, "split"),
+                                        (3, 1000, "split"), (4, 1002, "cat"), (2, 40000, "split"),
+                                        (9, 2048, "padded"), (1, 2, "split"), (600, 1000, "padded"),
+                                        (1030, 4096, "cat")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_silu_mul_quant_act_bit_exact(M, K, layout, dtype, bits):
+    G, U, g, u = _gate_up_input(M, K, dtype, layout, seed=M * 13 + K)
+    rng = np.random.default_rng(K)
+    sinv = np.exp(rng.uniform(-2, 1, K)).astype(np.float32)
+    xq, sx = S.silu_mul_quant_act(g, u, dev(sinv), a_bits=bits)
+    _sync()
+    ref = O.silu_mul_quant_act(G, U, sinv, bits)
+    assert np.array_equal(host(sx).view(np.uint32), ref["sx"].view(np.uint32))
+    got = host(xq).view(np.uint8)
+    assert np.array_equal(got, ref["packed"].view(np.uint8)), np.argwhere(got != ref["packed"].view(np.uint8))[:5]
+
+
+def test_silu_mul_quant_act_empty_and_bad_arguments():
+    sinv = torch.ones(64, device="cuda")
+    xq = torch.full((0, 32), 7, dtype=torch.uint8, device="cuda")
+    sx = torch.empty(0, device="cuda")
+    z = torch.empty((0, 64), device="cuda")
+    S.silu_mul_quant_act(z, z, sinv, a_bits=4, out=(xq, sx))
+    g = torch.zeros((4, 64), device="cuda")
+    vp = lambda t: t.data_ptr()                 # noqa: E731
+    xq = torch.empty((4, 32), dtype=torch.uint8, device="cuda")
+    sx = torch.empty(4, device="cuda")
+    f = S.lib.serq_silu_mul_quant_act
+    st = torch.cuda.current_stream().cuda_stream
+    assert f(vp(g), vp(g), 32, S._lib.SERQ_F32, 4, 64, vp(sinv), 4, vp(xq), vp(sx), st) == S._lib.SERQ_EINVAL   # ld < K
+    assert f(vp(g), vp(g), 64, S._lib.SERQ_F32, 4, 63, vp(sinv), 4, vp(xq), vp(sx), st) == S._lib.SERQ_EINVAL   # odd K
+    assert f(vp(g), vp(g), 64, S._lib.SERQ_F32, 4, 64, vp(sinv), 5, vp(xq), vp(sx), st) == S._lib.SERQ_EINVAL   # a_bits
+    assert f(vp(g) + 2, vp(g), 64, S._lib.SERQ_F32, 4, 62, vp(sinv), 4, vp(xq), vp(sx), st) == S._lib.SERQ_EALIGN
+    _sync()
+
+
 # ------------------------------------------------------- linear on raw codes
 
 def _codes_case(M, K, N, r, bits, seed, zero_scales=True):
@@ -306,3 +380,45 @@ def test_mlp8b_p4_propagation():
     am_ref, ar_ref = O.linear_int(q["codes"], R["Wq_codes"], R["Rq_codes"], 128)
     assert np.array_equal(host(am)[:, cols], am_ref) and np.array_equal(host(ar)[:, cols], ar_ref)
     check_y(host(y)[:, cols], am_ref, ar_ref, q["sx"], R["sw"], R["sr"], "bf16")
+
+
+@pytest.mark.slow
+def test_mlp8b_fused_activation_chain():
+    """gate and up as one layer of 2 x 14336 outputs whose channels carry
+    down's order P4 (serq_permute_outputs), its bf16 output M x 28672 read
+    in place by serq_silu_mul_quant_act (g = left half, u = right half,
+    ld = 28672), then down: codes, scales and accumulators against the
+    oracle's silu_mul_quant_act and linear."""
+    M = 32
+    gu = workload_layer("mlp8b", "gate_up", M_max=M)
+    dn = workload_layer("mlp8b", "down", M_max=1, draw_x=False)
+    N = gu.N
+    Wcat = np.concatenate([gu.W_bits, gu.meta["W_up_bits"]], axis=1)
+    Lgu = S.calibrate(Wcat, gu.act_absmax, r=128)
+    Ld = S.calibrate(dn.W_bits, dn.act_absmax, r=128)
+    p4 = Ld.perm
+    Lp = S.permute_outputs(S.SerqLayer(K=Lgu.K, N=2 * N, r=128, perm=Lgu.perm, s_hat_inv=Lgu.s_hat_inv,
+                                       Wq=Lgu.Wq.copy(), sw=Lgu.sw.copy(), Rq=Lgu.Rq.copy(), sr=Lgu.sr.copy()),
+                           np.concatenate([p4, N + p4]))
+    xq, sx = S.quant_act(bf16_tensor(gu.X_bits[:, Lgu.perm]), dev(Lgu.s_hat_inv), a_bits=4)
+    y0 = S.linear(xq, sx, Lgu.to("cuda"), a_bits=4, out_dtype=torch.bfloat16)
+    y = S.linear(xq, sx, Lp.to("cuda"), a_bits=4, out_dtype=torch.bfloat16)
+    D = Ld.to("cuda")
+    xq_d, sx_d = S.silu_mul_quant_act(y[:, :N], y[:, N:], D, a_bits=4)
+    yd, am, ar = S.linear(xq_d, sx_d, D, a_bits=4, out_dtype=torch.bfloat16, debug=True)
+    _sync()
+    yb, y0b = host(y), host(y0)
+    assert np.array_equal(yb[:, :N], y0b[:, :N][:, p4]) and np.array_equal(yb[:, N:], y0b[:, N:][:, p4])
+    f32 = lambda b: (b.astype(np.uint32) << 16).view(np.float32)     # noqa: E731
+    cols = sample(dn.N, 192, 5)
+    R = O.calibrate_columns(dn.W, dn.act_absmax, cols, r=128)
+    assert np.array_equal(R["perm"], p4)
+    q = O.silu_mul_quant_act(f32(yb[:, :N]), f32(yb[:, N:]), R["s_hat_inv"], 4)
+    # the same codes from the unpermuted outputs, gathered on the host
+    q0 = O.silu_mul_quant_act(f32(y0b[:, :N])[:, p4], f32(y0b[:, N:])[:, p4], R["s_hat_inv"], 4)
+    assert np.array_equal(q["packed"], q0["packed"]) and np.array_equal(q["sx"], q0["sx"])
+    assert np.array_equal(host(xq_d).view(np.uint8), q["packed"].view(np.uint8))
+    assert np.array_equal(host(sx_d).view(np.uint32), q["sx"].view(np.uint32))
+    am_ref, ar_ref = O.linear_int(q["codes"], R["Wq_codes"], R["Rq_codes"], 128)
+    assert np.array_equal(host(am)[:, cols], am_ref) and np.array_equal(host(ar)[:, cols], ar_ref)
+    check_y(host(yd)[:, cols], am_ref, ar_ref, q["sx"], R["sw"], R["sr"], "bf16")

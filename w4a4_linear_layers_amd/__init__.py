@@ -22,8 +22,8 @@ from ._lib import SERQ_BF16, SERQ_F32, SerqError, check
 
 lib = _lib.lib
 
-__all__ = ["SerqLayer", "DeviceLayer", "calibrate", "permute_outputs", "quant_act", "linear",
-           "kernel_name", "rq_row_bytes", "SerqError"]
+__all__ = ["SerqLayer", "DeviceLayer", "calibrate", "permute_outputs", "quant_act", "silu_mul_quant_act",
+           "linear", "kernel_name", "rq_row_bytes", "SerqError"]
 
 
 def _ptr(a: np.ndarray):
@@ -169,6 +169,37 @@ def quant_act(x, layer_or_sinv, *, a_bits: int = 4, out=None):
         xq, sx = out
     check("serq_quant_act", lib.serq_quant_act(x.data_ptr(), dt, M, K, sinv.data_ptr(), a_bits,
                                                xq.data_ptr(), sx.data_ptr(), _stream()))
+    return xq, sx
+
+
+def silu_mul_quant_act(g, u, layer_or_sinv, *, a_bits: int = 4, out=None):
+    """The MLP step before down (serq_silu_mul_quant_act) on the current
+    stream: quant_act(silu(g) * u). ``g`` and ``u`` are M x K float32 or
+    bfloat16 views with the same row stride (e.g. the two halves of a gate/up
+    output M x 2K), already in down's saliency order; ``layer_or_sinv`` is the
+    down layer (or its s_hat_inv). Returns (xq, sx) as quant_act does."""
+    import torch
+    sinv = layer_or_sinv.s_hat_inv if isinstance(layer_or_sinv, DeviceLayer) else layer_or_sinv
+    if g.shape != u.shape or g.dtype != u.dtype or g.stride() != u.stride() or g.dim() != 2:
+        raise ValueError("g and u must be M x K views of one dtype and row stride")
+    if g.stride(1) != 1 or not g.is_cuda or not u.is_cuda or not sinv.is_cuda or not sinv.is_contiguous():
+        raise ValueError("g and u must be CUDA tensors with unit column stride")
+    M, K = g.shape
+    if g.dtype == torch.bfloat16:
+        dt = SERQ_BF16
+    elif g.dtype == torch.float32:
+        dt = SERQ_F32
+    else:
+        raise ValueError("g and u must be float32 or bfloat16")
+    if out is None:
+        xq = torch.empty((M, K // 2 if a_bits == 4 else K), dtype=torch.uint8 if a_bits == 4 else torch.int8,
+                         device=g.device)
+        sx = torch.empty(M, dtype=torch.float32, device=g.device)
+    else:
+        xq, sx = out
+    ld = g.stride(0) if M > 1 else K
+    check("serq_silu_mul_quant_act", lib.serq_silu_mul_quant_act(
+        g.data_ptr(), u.data_ptr(), ld, dt, M, K, sinv.data_ptr(), a_bits, xq.data_ptr(), sx.data_ptr(), _stream()))
     return xq, sx
 
 

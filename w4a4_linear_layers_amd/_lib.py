@@ -19,7 +19,8 @@ SERQ_F32, SERQ_BF16 = 0, 1
 
 # every symbol include/serq.h declares
 EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_permute_outputs",
-           "serq_quant_act", "serq_linear", "serq_linear_kernel_name", "serq_rq_row_bytes")
+           "serq_quant_act", "serq_silu_mul_quant_act", "serq_linear", "serq_linear_kernel_name",
+           "serq_rq_row_bytes")
 
 
 class SerqError(RuntimeError):
@@ -52,6 +53,8 @@ def _load() -> ctypes.CDLL:
     lib.serq_permute_outputs.restype = ip
     lib.serq_quant_act.argtypes = [vp, i32, ip, ip, vp, ip, vp, vp, vp]
     lib.serq_quant_act.restype = ip
+    lib.serq_silu_mul_quant_act.argtypes = [vp, vp, ip, i32, ip, ip, vp, ip, vp, vp, vp]
+    lib.serq_silu_mul_quant_act.restype = ip
     lib.serq_linear.argtypes = [vp, vp, ip, vp, vp, vp, vp, ip, ip, ip, ip, vp, i32, vp, vp, vp]
     lib.serq_linear.restype = ip
     lib.serq_linear_kernel_name.argtypes = [ip, ip, ip, ip, ip]

@@ -65,16 +65,81 @@ __device__ __forceinline__ int qcode(float v, float inv) {
   return static_cast<int>(q);
 }
 
+// The MLP activation h = silu(g) * u, evaluated by one fixed fp32 recipe so
+// that the codes it feeds the quantizer are reproducible bit for bit (the
+// LLaMA MLP's silu(g) = g / (1 + e^-g); its input order is already down's
+// saliency order, the permutation having been pushed into gate and up
+// offline -- papernotes.org SERQ notes, 关键设计 3). e^x by Cody and Waite's
+// reduction: e^x = 2^n e^r, n = rne(x log2 e), r = (x - n c_hi) - n c_lo
+// with c_hi + c_lo = ln 2 and c_hi of 12 significant bits (n c_hi exact),
+// then the degree-7 Taylor polynomial of e^r in Horner form and an exact
+// scaling by 2^n; the argument is clamped to [-80, 80] so every step stays a
+// normal number. Every operation is one fp32 op (the build disables
+// contraction into fused multiply-adds); the division is IEEE.
+constexpr double kLn2 = 0.6931471805599453;
+constexpr float kLog2e = static_cast<float>(1.0 / kLn2);
+constexpr float kLn2Hi = 0.693145751953125f;
+constexpr float kLn2Lo = static_cast<float>(kLn2 - 0.693145751953125);
+constexpr float kInvFact[8] = {1.0f, 1.0f, static_cast<float>(1.0 / 2), static_cast<float>(1.0 / 6),
+                               static_cast<float>(1.0 / 24), static_cast<float>(1.0 / 120),
+                               static_cast<float>(1.0 / 720), static_cast<float>(1.0 / 5040)};
+
+__device__ __forceinline__ float exp32(float x) {
+#pragma clang fp contract(off)
+  x = fminf(fmaxf(x, -80.0f), 80.0f);
+  const float n = __builtin_rintf(x * kLog2e);
+  float r = x - n * kLn2Hi;
+  r = r - n * kLn2Lo;
+  float p = kInvFact[7];
+#pragma unroll
+  for (int k = 6; k >= 0; --k) {
+    p = p * r;
+    p = p + kInvFact[k];
+  }
+  return __builtin_ldexpf(p, static_cast<int>(n));
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+#pragma clang fp contract(off)
+  const float s = 1.0f + exp32(-g);
+  const float sg = g / s;
+  return sg * u;
+}
+
+// Where a row's values come from: the activations themselves (ACT false:
+// row m of x at a + m * ld), or h = silu(g) * u (ACT true: g at a, u at b,
+// both with row stride ld).
+template <typename T, bool ACT>
+struct RowSrc {
+  const T* a;
+  const T* b;
+  int ld;
+  __device__ __forceinline__ void load8(size_t row, int c, float (&v)[8]) const {
+    if constexpr (!ACT) {
+      serq::load8(a + row * ld + c, v);
+    } else {
+      float g[8], u[8];
+      serq::load8(a + row * ld + c, g);
+      serq::load8(b + row * ld + c, u);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = silu_mul(g[i], u[i]);
+    }
+  }
+  __device__ __forceinline__ float load1(size_t row, int k) const {
+    if constexpr (!ACT) return serq::load1(a + row * ld + k);
+    else return silu_mul(serq::load1(a + row * ld + k), serq::load1(b + row * ld + k));
+  }
+};
+
 // Fast path: K % 8 == 0, K <= NP * 2048, 16-byte aligned rows.
-template <typename T, int A_BITS, int NP>
-__global__ __launch_bounds__(kThreads) void quant_act_rows(const T* __restrict__ X,
+template <typename T, int A_BITS, int NP, bool ACT>
+__global__ __launch_bounds__(kThreads) void quant_act_rows(RowSrc<T, ACT> src,
                                                            const float* __restrict__ sinv, int K,
                                                            uint8_t* __restrict__ Xq,
                                                            float* __restrict__ sx) {
   constexpr int QMAX = A_BITS == 4 ? 7 : 127;
   __shared__ float red[kThreads / 64];
   const size_t row = blockIdx.x;
-  const T* xr = X + row * static_cast<size_t>(K);
   float v[NP][kVec];
   float amax = 0.0f;
 #pragma unroll
@@ -82,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_rows(const T* __restrict__
     const int c = (p * kThreads + static_cast<int>(threadIdx.x)) * kVec;
     if (c < K) {
       float s[kVec];
-      load8(xr + c, v[p]);
+      src.load8(row, c, v[p]);
       load8(sinv + c, s);
 #pragma unroll
       for (int i = 0; i < kVec; ++i) {
@@ -119,25 +184,24 @@ __global__ __launch_bounds__(kThreads) void quant_act_rows(const T* __restrict__
 }
 
 // General path: any even K, any alignment; two reads of the row.
-template <typename T, int A_BITS>
-__global__ __launch_bounds__(kThreads) void quant_act_rows_generic(const T* __restrict__ X,
+template <typename T, int A_BITS, bool ACT>
+__global__ __launch_bounds__(kThreads) void quant_act_rows_generic(RowSrc<T, ACT> src,
                                                                    const float* __restrict__ sinv,
                                                                    int K, uint8_t* __restrict__ Xq,
                                                                    float* __restrict__ sx) {
   constexpr int QMAX = A_BITS == 4 ? 7 : 127;
   __shared__ float red[kThreads / 64];
   const size_t row = blockIdx.x;
-  const T* xr = X + row * static_cast<size_t>(K);
   float amax = 0.0f;
-  for (int k = threadIdx.x; k < K; k += kThreads) amax = fmaxf(amax, fabsf(load1(xr + k) * sinv[k]));
+  for (int k = threadIdx.x; k < K; k += kThreads) amax = fmaxf(amax, fabsf(src.load1(row, k) * sinv[k]));
   amax = block_max(amax, red);
   float inv = static_cast<float>(QMAX) / amax;
   const bool zero = !(inv <= FLT_MAX);
   if (zero) inv = 0.0f;
   if (threadIdx.x == 0) sx[row] = zero ? 0.0f : amax / static_cast<float>(QMAX);
   for (int k2 = 2 * threadIdx.x; k2 < K; k2 += 2 * kThreads) {
-    const int q0 = qcode<QMAX>(load1(xr + k2) * sinv[k2], inv);
-    const int q1 = qcode<QMAX>(load1(xr + k2 + 1) * sinv[k2 + 1], inv);
+    const int q0 = qcode<QMAX>(src.load1(row, k2) * sinv[k2], inv);
+    const int q1 = qcode<QMAX>(src.load1(row, k2 + 1) * sinv[k2 + 1], inv);
     if (A_BITS == 4) {
       Xq[row * static_cast<size_t>(K / 2) + k2 / 2] = static_cast<uint8_t>((q0 & 0xF) | ((q1 & 0xF) << 4));
     } else {
@@ -147,43 +211,55 @@ __global__ __launch_bounds__(kThreads) void quant_act_rows_generic(const T* __re
   }
 }
 
-template <typename T, int A_BITS>
-hipError_t launch_typed(const T* X, int M, int K, const float* sinv, uint8_t* Xq, float* sx,
+template <typename T, int A_BITS, bool ACT>
+hipError_t launch_typed(RowSrc<T, ACT> src, int M, int K, const float* sinv, uint8_t* Xq, float* sx,
                         hipStream_t st) {
   const dim3 grid(M), block(kThreads);
-  const bool aligned = (K % kVec == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
-                       ((reinterpret_cast<uintptr_t>(sinv) & 15) == 0) &&
-                       ((reinterpret_cast<uintptr_t>(Xq) & 15) == 0);
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool aligned = (K % kVec == 0) && (src.ld % kVec == 0) && al16(src.a) && (!ACT || al16(src.b)) &&
+                       al16(sinv) && al16(Xq);
   const int passes = (K + kPassElems - 1) / kPassElems;
   if (!aligned || passes > 16) {
-    quant_act_rows_generic<T, A_BITS><<<grid, block, 0, st>>>(X, sinv, K, Xq, sx);
+    quant_act_rows_generic<T, A_BITS, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   } else if (passes <= 1) {
-    quant_act_rows<T, A_BITS, 1><<<grid, block, 0, st>>>(X, sinv, K, Xq, sx);
+    quant_act_rows<T, A_BITS, 1, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   } else if (passes <= 2) {
-    quant_act_rows<T, A_BITS, 2><<<grid, block, 0, st>>>(X, sinv, K, Xq, sx);
+    quant_act_rows<T, A_BITS, 2, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   } else if (passes <= 4) {
-    quant_act_rows<T, A_BITS, 4><<<grid, block, 0, st>>>(X, sinv, K, Xq, sx);
+    quant_act_rows<T, A_BITS, 4, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   } else if (passes <= 8) {
-    quant_act_rows<T, A_BITS, 8><<<grid, block, 0, st>>>(X, sinv, K, Xq, sx);
+    quant_act_rows<T, A_BITS, 8, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   } else {
-    quant_act_rows<T, A_BITS, 16><<<grid, block, 0, st>>>(X, sinv, K, Xq, sx);
+    quant_act_rows<T, A_BITS, 16, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   }
   return hipGetLastError();
+}
+
+template <bool ACT>
+hipError_t launch_any(const void* A, const void* B, int ld, int x_bf16, int M, int K, const float* sinv,
+                      int a_bits, void* Xq, float* sx, hipStream_t st) {
+  uint8_t* q = static_cast<uint8_t*>(Xq);
+  if (x_bf16) {
+    const RowSrc<uint16_t, ACT> src{static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), ld};
+    return a_bits == 4 ? launch_typed<uint16_t, 4, ACT>(src, M, K, sinv, q, sx, st)
+                       : launch_typed<uint16_t, 8, ACT>(src, M, K, sinv, q, sx, st);
+  }
+  const RowSrc<float, ACT> src{static_cast<const float*>(A), static_cast<const float*>(B), ld};
+  return a_bits == 4 ? launch_typed<float, 4, ACT>(src, M, K, sinv, q, sx, st)
+                     : launch_typed<float, 8, ACT>(src, M, K, sinv, q, sx, st);
 }
 
 }  // namespace
 
 hipError_t launch_quant_act(const void* X, int x_bf16, int M, int K, const float* s_hat_inv,
                             int a_bits, void* Xq, float* sx, hipStream_t stream) {
-  uint8_t* q = static_cast<uint8_t*>(Xq);
-  if (x_bf16) {
-    const uint16_t* x = static_cast<const uint16_t*>(X);
-    return a_bits == 4 ? launch_typed<uint16_t, 4>(x, M, K, s_hat_inv, q, sx, stream)
-                       : launch_typed<uint16_t, 8>(x, M, K, s_hat_inv, q, sx, stream);
-  }
-  const float* x = static_cast<const float*>(X);
-  return a_bits == 4 ? launch_typed<float, 4>(x, M, K, s_hat_inv, q, sx, stream)
-                     : launch_typed<float, 8>(x, M, K, s_hat_inv, q, sx, stream);
+  return launch_any<false>(X, nullptr, K, x_bf16, M, K, s_hat_inv, a_bits, Xq, sx, stream);
+}
+
+hipError_t launch_silu_mul_quant_act(const void* G, const void* U, int ld, int x_bf16, int M, int K,
+                                     const float* s_hat_inv, int a_bits, void* Xq, float* sx,
+                                     hipStream_t stream) {
+  return launch_any<true>(G, U, ld, x_bf16, M, K, s_hat_inv, a_bits, Xq, sx, stream);
 }
 
 }  // namespace serq

@@ -48,6 +48,25 @@ extern "C" int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
   return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
 }
 
+extern "C" int serq_silu_mul_quant_act(const void* G, const void* U, int ld, serq_dtype x_dtype, int M,
+                                       int K, const float* s_hat_inv, int a_bits, void* Xq, float* sx,
+                                       void* stream) {
+  if (x_dtype != SERQ_F32 && x_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (a_bits != 4 && a_bits != 8) return SERQ_EINVAL;
+  if (M < 0 || K <= 0 || (K % 2) != 0 || ld < K) return SERQ_EINVAL;
+  if (!s_hat_inv) return SERQ_EINVAL;
+  if (!aligned16(s_hat_inv)) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;  // the M-sized buffers may then be empty (NULL)
+  if (!G || !U || !Xq || !sx) return SERQ_EINVAL;
+  const uintptr_t eb = x_dtype == SERQ_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(G) % eb) != 0 || (reinterpret_cast<uintptr_t>(U) % eb) != 0 ||
+      !aligned16(Xq) || !aligned16(sx))
+    return SERQ_EALIGN;
+  hipError_t e = serq::launch_silu_mul_quant_act(G, U, ld, x_dtype == SERQ_BF16, M, K, s_hat_inv, a_bits, Xq,
+                                                 sx, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
+}
+
 extern "C" int serq_linear(const void* Xq, const float* sx, int a_bits, const uint8_t* Wq,
                            const float* sw, const uint8_t* Rq, const float* sr, int M, int K, int N,
                            int r, void* Y, serq_dtype y_dtype, int32_t* acc_main_dbg,

@@ -42,5 +42,8 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits);
 hipError_t launch_quant_act(const void* X, int x_bf16, int M, int K, const float* s_hat_inv,
                             int a_bits, void* Xq, float* sx, hipStream_t stream);
 hipError_t launch_linear(const LinearArgs& a, const LinearPlan& plan, hipStream_t stream);
+hipError_t launch_silu_mul_quant_act(const void* G, const void* U, int ld, int x_bf16, int M, int K,
+                                     const float* s_hat_inv, int a_bits, void* Xq, float* sx,
+                                     hipStream_t stream);
 
 }  // namespace serq
