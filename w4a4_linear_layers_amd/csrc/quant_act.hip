@@ -211,6 +211,125 @@ __global__ __launch_bounds__(kThreads) void quant_act_rows_generic(RowSrc<T, ACT
   }
 }
 
+// Few long rows: one workgroup per row would leave most CUs idle while each
+// works through K elements alone, so each row is cut into C chunks of
+// 512 * NP elements, one wave each, in two launches. The first writes every
+// chunk's max |x^|; the second reduces the row's C maxima, recomputes its
+// chunk's x^ (the same operations, so the same values) and writes the codes;
+// chunk 0 writes the scale. Codes and scales equal the one-pass kernels' bit
+// for bit (a max does not depend on the order it is taken in). The chunk
+// maxima sit in a library-held device array (each device has its own copy),
+// fully written by the first launch before the second reads it: calls that
+// overlap on one device must not both take this path.
+constexpr int kSplitMaxRows = 128;
+constexpr int kSplitMaxChunks = 64;
+constexpr int kChunkElems = 64 * kVec;        // one wave, 8 elements per lane
+
+__device__ float g_chunk_max[kSplitMaxRows * kSplitMaxChunks];
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+template <typename T, int NP, bool ACT>
+__device__ __forceinline__ float chunk_values(const RowSrc<T, ACT>& src, const float* __restrict__ sinv,
+                                              size_t row, int c0, int K, float (&v)[NP][kVec]) {
+  const int lane = static_cast<int>(threadIdx.x);
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c = c0 + (p * 64 + lane) * kVec;
+    if (c < K) {
+      float s[kVec];
+      src.load8(row, c, v[p]);
+      load8(sinv + c, s);
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        v[p][i] = v[p][i] * s[i];
+        amax = fmaxf(amax, fabsf(v[p][i]));
+      }
+    }
+  }
+  return amax;
+}
+
+template <typename T, int NP, bool ACT>
+__global__ __launch_bounds__(64) void chunk_max_kernel(RowSrc<T, ACT> src, const float* __restrict__ sinv,
+                                                       int K, int C) {
+  const int chunk = blockIdx.x;
+  const size_t row = blockIdx.y;
+  float v[NP][kVec];
+  const float amax = wave_max(chunk_values<T, NP, ACT>(src, sinv, row, chunk * kChunkElems * NP, K, v));
+  if (threadIdx.x == 0) g_chunk_max[row * C + chunk] = amax;
+}
+
+template <typename T, int A_BITS, int NP, bool ACT>
+__global__ __launch_bounds__(64) void chunk_quant_kernel(RowSrc<T, ACT> src, const float* __restrict__ sinv,
+                                                         int K, int C, uint8_t* __restrict__ Xq,
+                                                         float* __restrict__ sx) {
+  constexpr int QMAX = A_BITS == 4 ? 7 : 127;
+  const int lane = static_cast<int>(threadIdx.x);
+  const int chunk = blockIdx.x;
+  const size_t row = blockIdx.y;
+  const int c0 = chunk * kChunkElems * NP;
+  float v[NP][kVec];
+  chunk_values<T, NP, ACT>(src, sinv, row, c0, K, v);
+  const float amax = wave_max(lane < C ? g_chunk_max[row * C + lane] : 0.0f);
+  float inv = static_cast<float>(QMAX) / amax;
+  const bool zero = !(inv <= FLT_MAX);
+  if (zero) inv = 0.0f;
+  if (chunk == 0 && lane == 0) sx[row] = zero ? 0.0f : amax / static_cast<float>(QMAX);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c = c0 + (p * 64 + lane) * kVec;
+    if (c < K) {
+      int q[kVec];
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) q[i] = qcode<QMAX>(v[p][i], inv);
+      if (A_BITS == 4) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) w |= static_cast<uint32_t>(q[i] & 0xF) << (4 * i);
+        *reinterpret_cast<uint32_t*>(Xq + row * static_cast<size_t>(K / 2) + c / 2) = w;
+      } else {
+        uint2 w;
+        w.x = (q[0] & 0xFF) | ((q[1] & 0xFF) << 8) | ((q[2] & 0xFF) << 16) | (static_cast<uint32_t>(q[3] & 0xFF) << 24);
+        w.y = (q[4] & 0xFF) | ((q[5] & 0xFF) << 8) | ((q[6] & 0xFF) << 16) | (static_cast<uint32_t>(q[7] & 0xFF) << 24);
+        *reinterpret_cast<uint2*>(Xq + row * static_cast<size_t>(K) + c) = w;
+      }
+    }
+  }
+}
+
+template <typename T, int A_BITS, int NP, bool ACT>
+hipError_t launch_split_np(RowSrc<T, ACT> src, int M, int K, const float* sinv, uint8_t* Xq, float* sx,
+                           hipStream_t st) {
+  const int C = (K + kChunkElems * NP - 1) / (kChunkElems * NP);
+  const dim3 grid(C, M), block(64);
+  chunk_max_kernel<T, NP, ACT><<<grid, block, 0, st>>>(src, sinv, K, C);
+  chunk_quant_kernel<T, A_BITS, NP, ACT><<<grid, block, 0, st>>>(src, sinv, K, C, Xq, sx);
+  return hipGetLastError();
+}
+
+// The split path's share: at most kSplitMaxRows rows, chunks of up to 2048
+// elements, at most kSplitMaxChunks of them; rows short enough for one
+// workgroup's pass gain nothing from it.
+template <bool ACT>
+bool use_split(int M, int K) {
+  return M <= kSplitMaxRows && K > (ACT ? 2 : 4) * kPassElems && K <= kSplitMaxChunks * 4 * kChunkElems;
+}
+
+template <typename T, int A_BITS, bool ACT>
+hipError_t launch_split(RowSrc<T, ACT> src, int M, int K, const float* sinv, uint8_t* Xq, float* sx,
+                        hipStream_t st) {
+  if (K <= kSplitMaxChunks * kChunkElems) return launch_split_np<T, A_BITS, 1, ACT>(src, M, K, sinv, Xq, sx, st);
+  if (K <= kSplitMaxChunks * 2 * kChunkElems)
+    return launch_split_np<T, A_BITS, 2, ACT>(src, M, K, sinv, Xq, sx, st);
+  return launch_split_np<T, A_BITS, 4, ACT>(src, M, K, sinv, Xq, sx, st);
+}
+
 template <typename T, int A_BITS, bool ACT>
 hipError_t launch_typed(RowSrc<T, ACT> src, int M, int K, const float* sinv, uint8_t* Xq, float* sx,
                         hipStream_t st) {
@@ -219,6 +338,7 @@ hipError_t launch_typed(RowSrc<T, ACT> src, int M, int K, const float* sinv, uin
   const bool aligned = (K % kVec == 0) && (src.ld % kVec == 0) && al16(src.a) && (!ACT || al16(src.b)) &&
                        al16(sinv) && al16(Xq);
   const int passes = (K + kPassElems - 1) / kPassElems;
+  if (aligned && use_split<ACT>(M, K)) return launch_split<T, A_BITS, ACT>(src, M, K, sinv, Xq, sx, st);
   if (!aligned || passes > 16) {
     quant_act_rows_generic<T, A_BITS, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   } else if (passes <= 1) {
