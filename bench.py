@@ -171,7 +171,10 @@ def time_mlp_act(K, Ms, n=100, a_bits=4, seed=0):
     ld = 2K) as serq_silu_mul_quant_act does in a LLaMA MLP with the
     intermediate width K. Each launch reads its own copy of the output (the
     copies span >= 768 MiB, beyond the last-level cache); n launches are
-    captured in one graph and timed with events on the replay stream."""
+    captured in one graph and timed with events on the replay stream.
+    For comparison, the same step unfused: torch's silu(g) * u written to
+    HBM as bf16 (two elementwise kernels), then serq_quant_act on it (timing
+    only; torch's silu is not the fixed recipe)."""
     import torch
 
     import w4a4_linear_layers_amd as S
@@ -188,27 +191,40 @@ def time_mlp_act(K, Ms, n=100, a_bits=4, seed=0):
                          device=dev)
         sx = torch.empty(M, dtype=torch.float32, device=dev)
 
+        h = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+
         def act(i):
             yc = y[i % copies]
             S.silu_mul_quant_act(yc[:, :K], yc[:, K:], sinv, a_bits=a_bits, out=(xq, sx))
 
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                act(i)
-        g.replay()
-        torch.cuda.synchronize()
-        st = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        g.replay()
-        e1.record(st)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n
+        def unfused(i):
+            yc = y[i % copies]
+            torch.mul(torch.nn.functional.silu(yc[:, :K]), yc[:, K:], out=h)
+            S.quant_act(h, sinv, a_bits=a_bits, out=(xq, sx))
+
+        times = []
+        for fn in (act, unfused):
+            fn(0)                      # outside the capture: first-call set-up
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            g.replay()
+            e1.record(st)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / n)
+            del g
+        us = times[0]
         gbs = act_bytes(M, K, a_bits) / (us * 1e-6) / 1e9
-        out.append(dict(K=K, M=M, us=round(us, 2), HBM_GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 3)))
-        del g, y
+        out.append(dict(K=K, M=M, us=round(us, 2), HBM_GBs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 3),
+                        unfused_us=round(times[1], 2)))
+        del y, h
     return out
 
 
@@ -292,9 +308,17 @@ def main(argv=None):
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (a reference kernel of known "
                          "traffic for scaling HBM byte counters), then exit")
+    ap.add_argument("--mlp-act", default=None, metavar="K:M[,M...]",
+                    help="only time serq_silu_mul_quant_act at intermediate width K for the given token "
+                         "counts (one JSON line each), then exit")
     args = ap.parse_args(argv)
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.mlp_act:
+        k_s, m_s = args.mlp_act.split(":")
+        for e in time_mlp_act(int(k_s), [int(m) for m in m_s.split(",")], n=max(args.steps, 20)):
+            print(json.dumps(dict(kernel="serq_silu_mul_quant_act", **e)), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path)", file=sys.stderr)
@@ -351,8 +375,8 @@ def main(argv=None):
         for k_int in (14336, 28672):
             for e in time_mlp_act(k_int, (1, 16, 256, 4096)):
                 mlp_act.append(e)
-                print(f"# silu_mul_quant_act K={e['K']} M={e['M']}: {e['us']:.2f} us {e['HBM_GBs']:.0f} GB/s",
-                      file=sys.stderr, flush=True)
+                print(f"# silu_mul_quant_act K={e['K']} M={e['M']}: {e['us']:.2f} us {e['HBM_GBs']:.0f} GB/s "
+                      f"(unfused {e['unfused_us']:.2f} us)", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:

@@ -27,8 +27,10 @@
  *     m the group's absolute maximum, qmax 7 (int4) or 127 (int8), rne round
  *     half to even. A group whose fl32(qmax / m) overflows (an all-zero group
  *     in particular) gets scale 0 and zero codes.
- *   - The caller owns every buffer. The library keeps no global state,
- *     allocates no memory and creates no streams.
+ *   - The caller owns every input and output. The library creates no
+ *     streams; the only device memory it holds is scratch for two paths
+ *     (serq_linear's K split, chunked activation quantization), described
+ *     at those calls: calls that take them must not overlap on one device.
  *   - Argument errors are detected on the host and returned before anything
  *     is launched; the output buffers are then untouched.
  *   - Online calls only enqueue work on `stream` (a hipStream_t; NULL is the
@@ -141,6 +143,9 @@ int serq_permute_outputs(const int32_t* perm_next, int N, int K, int r,
  *   a_bits     4 (W4A4) or 8 (W4A8).
  *   Xq         device, M x K/2 bytes (a_bits 4, packed) or M x K int8.
  *   sx         device, M floats: per-token scale.
+ * Scratch: up to 128 rows with K > 8192 are cut into chunks over two
+ * launches whose chunk maxima meet in a 32 KB device array the library holds
+ * per device (no allocation call); such calls on one device must not overlap.
  * M == 0 is a no-op; X, Xq and sx may then be NULL. Errors: SERQ_EINVAL
  * (NULL pointer, M < 0, K <= 0, odd K, bad a_bits or dtype), SERQ_EALIGN
  * (pointer not 16-byte aligned), SERQ_EHIP.
@@ -173,7 +178,8 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
  *              (and K % 8 == 0) take the vector path, others a scalar one
  *              with the same results.
  *   s_hat_inv  K floats, device (down's, from serq_calibrate).
- *   a_bits, Xq, sx as for serq_quant_act.
+ *   a_bits, Xq, sx as for serq_quant_act (so is the scratch rule, here for
+ *              up to 128 rows with K > 4096).
  * M == 0 is a no-op. Errors: SERQ_EINVAL (NULL pointer, M < 0, K <= 0, odd
  * K, ld < K, bad a_bits or dtype), SERQ_EALIGN (G or U not aligned to its
  * element, Xq or sx not 16-byte aligned), SERQ_EHIP. Subnormal inputs are

@@ -38,7 +38,7 @@ def test_header_declarations_are_exported():
 
 
 def test_strerror_and_version():
-    assert _lib.lib.serq_abi_version() == 200
+    assert _lib.lib.serq_abi_version() == 201
     for code in (0, -1, -2, -3, -4, 7):
         assert _lib.lib.serq_strerror(code)
 
@@ -64,6 +64,27 @@ A_BAD = 0x10004        # a misaligned one
 
 def quant(X=A16, dt=_lib.SERQ_BF16, M=4, K=64, sinv=A16, bits=4, xq=A16, sx=A16):
     return _lib.lib.serq_quant_act(X, dt, M, K, sinv, bits, xq, sx, None)
+
+
+def act(G=A16, U=A16 + 128, ld=64, dt=_lib.SERQ_BF16, M=4, K=64, sinv=A16, bits=4, xq=A16, sx=A16):
+    return _lib.lib.serq_silu_mul_quant_act(G, U, ld, dt, M, K, sinv, bits, xq, sx, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=5), _lib.SERQ_EINVAL), (dict(bits=2), _lib.SERQ_EINVAL), (dict(M=-1), _lib.SERQ_EINVAL),
+    (dict(K=0), _lib.SERQ_EINVAL), (dict(K=63, ld=64), _lib.SERQ_EINVAL), (dict(ld=62), _lib.SERQ_EINVAL),
+    (dict(G=None), _lib.SERQ_EINVAL), (dict(U=None), _lib.SERQ_EINVAL), (dict(sinv=None), _lib.SERQ_EINVAL),
+    (dict(xq=None), _lib.SERQ_EINVAL), (dict(sx=None), _lib.SERQ_EINVAL),
+    (dict(G=A16 + 1), _lib.SERQ_EALIGN), (dict(U=A16 + 3), _lib.SERQ_EALIGN),
+    (dict(dt=_lib.SERQ_F32, U=A16 + 2), _lib.SERQ_EALIGN), (dict(sinv=A_BAD), _lib.SERQ_EALIGN),
+    (dict(xq=A_BAD), _lib.SERQ_EALIGN), (dict(sx=A_BAD), _lib.SERQ_EALIGN),
+    (dict(M=0), _lib.SERQ_OK), (dict(M=0, G=None, U=None, xq=None, sx=None), _lib.SERQ_OK),
+    (dict(M=0, sinv=None), _lib.SERQ_EINVAL),
+])
+def test_silu_mul_quant_act_argument_errors(kw, code):
+    """G and U need only element alignment (U = G + K for a gate/up output);
+    Xq, sx and s_hat_inv 16 bytes; ld >= K."""
+    assert act(**kw) == code
 
 
 def lin(xq=A16, sx=A16, bits=4, wq=A16, sw=A16, rq=A16, sr=A16, M=4, K=64, N=32, r=8, y=A16,

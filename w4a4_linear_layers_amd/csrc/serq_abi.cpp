@@ -28,7 +28,7 @@ extern "C" const char* serq_strerror(int status) {
   }
 }
 
-extern "C" int serq_abi_version(void) { return 200; }
+extern "C" int serq_abi_version(void) { return 201; }
 
 extern "C" int serq_rq_row_bytes(int r) { return r < 0 ? -1 : SERQ_RQ_ROW_BYTES(r); }
 
