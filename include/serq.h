@@ -167,8 +167,9 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
  * LLaMA MLP, evaluated by a fixed fp32 recipe so results are reproducible
  * bit for bit: e = exp(-g) with the argument clamped to [-80, 80], by
  * Cody-Waite reduction (e^x = 2^n e^r, n = rne(x log2 e), ln 2 split in a
- * 12-bit head and a tail) and the degree-7 Taylor polynomial of e^r; then
- * fl32(fl32(g / fl32(1 + e)) * u) with IEEE division; no fused multiply-add.
+ * 12-bit head and a tail, r by two fused multiply-adds) and the degree-7
+ * Taylor polynomial of e^r (Horner, one fused multiply-add per degree); then
+ * fl32(fl32(g / fl32(1 + e)) * u) with IEEE division and no other fused op.
  *
  *   G, U       device, row m of gate at G + m * ld, of up at U + m * ld, K
  *              elements each, of x_dtype (a gate/up output stored as one

@@ -25,7 +25,8 @@ compensator.
 Arithmetic rules of this oracle (the pages fix none of them; these are the
 readings the library must reproduce bit for bit):
   * every fp32 step below is one IEEE binary32 operation, round to nearest
-    even, no fused multiply-add;
+    even, no fused multiply-add except the exactly rounded ones written out
+    as fma32 (the MLP activation's exponential);
   * ``rne`` is round-half-to-even;
   * bf16 inputs widen exactly to fp32;
   * the final output y is evaluated in fp64 from exact integer accumulators
@@ -402,16 +403,18 @@ def linear_float_residual(Xq: dict, layer: dict) -> np.ndarray:
 # into the per-token quantizer, with no gather. The pages do not spell out
 # the MLP nonlinearity; the reading is the LLaMA MLP, silu(g) = g * sigma(g)
 # = g / (1 + e^-g). For bit-exact parity both implementations evaluate it
-# with one fixed fp32 recipe (no fused multiply-add, IEEE division):
+# with one fixed fp32 recipe (IEEE division; fused multiply-adds, each one
+# exactly rounded, where written, and nowhere else):
 #     e  = exp32(-g)            (argument clamped to [-80, 80])
 #     sg = fl32(g / fl32(1 + e))
 #     h  = fl32(sg * u)
 # exp32 follows Cody and Waite's argument reduction: e^x = 2^n e^r with
-# n = rne(fl32(x log2 e)) and r = fl32(fl32(x - n c_hi) - n c_lo), where
-# c_hi + c_lo = ln 2 and c_hi has 12 significant bits so that n c_hi is
-# exact for |n| < 2^11; e^r (|r| <= ln2 / 2) is its Taylor polynomial to
-# degree 7 in Horner form (truncation below 2^-27 relative), then scaled by
-# 2^n exactly. The clamp keeps every intermediate a normal number.
+# n = rne(fl32(x log2 e)) and r = fma(-n, c_lo, fma(-n, c_hi, x)), where
+# c_hi + c_lo = ln 2 and c_hi has 12 significant bits (so n c_hi, |n| < 2^11,
+# is exact and the first fma is exact too); e^r (|r| <= ln2 / 2) is its
+# Taylor polynomial to degree 7 in Horner form, p <- fma(p, r, 1/k!)
+# (truncation below 2^-27 relative), then scaled by 2^n exactly. The clamp
+# keeps every intermediate a normal number.
 # ---------------------------------------------------------------------------
 
 LOG2E_F32 = np.float32(1.0 / math.log(2.0))
@@ -421,16 +424,36 @@ EXP_TAYLOR_F32 = [np.float32(1.0 / math.factorial(k)) for k in range(8)]   # 1/k
 EXP_ARG_CLAMP = np.float32(80.0)
 
 
+def fma32(a, b, c) -> np.ndarray:
+    """fl32(a * b + c) with one rounding (round to nearest even), for float32
+    operands whose result is a normal number or zero. a * b is exact in
+    binary64 (48 significant bits); the sum is rounded to odd in binary64
+    (round to nearest, then, if inexact, the neighbour with an odd last bit
+    toward the exact value -- the error comes from Knuth's two-sum), and
+    that rounds correctly to binary32 since 53 >= 24 + 2 (Boldo and
+    Melquiond, "Emulation of FMA and correctly rounded sums: proved
+    algorithms using rounding to odd", IEEE Trans. Computers 2008)."""
+    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p = a64 * b64
+    s = p + c64
+    bv = s - p
+    t = (p - (s - bv)) + (c64 - bv)              # two-sum: p + c = s + t exactly
+    even = (s.view(np.int64) & 1) == 0
+    s = np.where((t != 0) & even, np.nextafter(s, np.where(t > 0, np.inf, -np.inf)), s)
+    return s.astype(np.float32)
+
+
 def exp32(x: np.ndarray) -> np.ndarray:
     """e^x for float32 x by the fixed recipe above (elementwise, float32)."""
     x = np.clip(np.asarray(x, dtype=np.float32), -EXP_ARG_CLAMP, EXP_ARG_CLAMP).astype(np.float32)
     n = np.rint((x * LOG2E_F32).astype(np.float32)).astype(np.float32)
-    r = (x - (n * LN2_HI_F32).astype(np.float32)).astype(np.float32)
-    r = (r - (n * LN2_LO_F32).astype(np.float32)).astype(np.float32)
+    r = fma32(-n, LN2_HI_F32, x)
+    r = fma32(-n, LN2_LO_F32, r)
     p = np.full(x.shape, EXP_TAYLOR_F32[7], np.float32)
     for k in range(6, -1, -1):
-        p = (p * r).astype(np.float32)
-        p = (p + EXP_TAYLOR_F32[k]).astype(np.float32)
+        p = fma32(p, r, EXP_TAYLOR_F32[k])
     return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
 
 

@@ -387,12 +387,62 @@ def check_rank_trend(O):
 # the fp64 definitions, a special value, the clamp, an odd-symmetry identity
 # and the composition with the per-token quantizer the step is defined as.
 
+def _f32_nearest(q: Fraction) -> np.float32:
+    """The binary32 value nearest to the rational q (ties to even), for q
+    zero or in the normal range: exact integer arithmetic throughout."""
+    if q == 0:
+        return np.float32(0.0)
+    neg, q = q < 0, abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= q:
+        e += 1
+    m = q / Fraction(2) ** (e - 23)              # in [2^23, 2^24)
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = math.ldexp(float(fl), e - 23)            # exact: fl has at most 25 bits
+    return np.float32(-v if neg else v)
+
+
+def check_fma32(O):
+    """fma32 against exact rational arithmetic rounded once, including the
+    double-rounding cases a plain binary64 sum gets wrong."""
+    rng = np.random.default_rng(17)
+    n = 3000
+    a = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
+    b = (rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n))).astype(np.float32)
+    c = (rng.standard_normal(n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
+    c[: n // 3] = -(a[: n // 3] * b[: n // 3]).astype(np.float32)            # cancellation
+    c[n // 3: n // 2] = np.nextafter(c[: n // 6], np.float32(np.inf))
+    # a * b exactly halfway between two binary32 values, then nudged by a c
+    # far below the binary64 spacing: only a single rounding gets these right
+    h = np.float32(1.0 + 2.0 ** -12)
+    hard_a = np.array([h, h, h, -h, np.float32(3.0 * (1.0 + 2.0 ** -12))], np.float32)
+    hard_b = np.array([h, h, h, h, h], np.float32)
+    hard_c = np.array([0.0, 2.0 ** -60, -2.0 ** -60, 2.0 ** -70, -2.0 ** -58], np.float32)
+    A, B, C = (np.concatenate([x, y]) for x, y in ((a, hard_a), (b, hard_b), (c, hard_c)))
+    got = O.fma32(A, B, C)
+    for i in range(A.size):
+        want = _f32_nearest(Fraction(float(A[i])) * Fraction(float(B[i])) + Fraction(float(C[i])))
+        if abs(float(want)) >= 2.0 ** -126 or want == 0:
+            assert got[i].view(np.uint32) == want.view(np.uint32), (i, A[i], B[i], C[i], got[i], want)
+    # the tie itself rounds to even, and the nudges decide it
+    assert O.fma32(h, h, np.float32(0.0)) == np.float32(1.0 + 2.0 ** -11)
+    assert O.fma32(h, h, np.float32(2.0 ** -60)) == np.float32(1.0 + 2.0 ** -11 + 2.0 ** -23)
+    # no addend: the binary32 product; unit factor: the binary32 sum
+    assert np.array_equal(O.fma32(a, b, np.zeros_like(a)), (a * b).astype(np.float32))
+    assert np.array_equal(O.fma32(a, np.ones_like(a), c), (a + c).astype(np.float32))
+
+
 def check_exp32(O):
     x = np.linspace(-80.0, 80.0, 400001).astype(np.float32)
     truth = np.exp(x.astype(np.float64))
     got = O.exp32(x).astype(np.float64)
     ulp = np.spacing(truth.astype(np.float32)).astype(np.float64)
-    assert (np.abs(got - truth) <= 2.0 * ulp).all(), float((np.abs(got - truth) / ulp).max())
+    assert (np.abs(got - truth) <= 1.0 * ulp).all(), float((np.abs(got - truth) / ulp).max())
     assert O.exp32(np.float32(0.0)) == np.float32(1.0)
     assert O.exp32(np.float32(500.0)) == O.exp32(np.float32(80.0))
     assert O.exp32(np.float32(-500.0)) == O.exp32(np.float32(-80.0))
@@ -433,4 +483,4 @@ def check_silu_mul(O):
 ALL_CHECKS = [check_pack, check_quantizer_golden, check_quantizer_bruteforce, check_smoothing,
               check_perm, check_fold_identity, check_compensator, check_int_gemm,
               check_dequant_identity, check_special_cases, check_worked_layer, check_bf16,
-              check_permute_outputs, check_rank_trend, check_exp32, check_silu_mul]
+              check_permute_outputs, check_rank_trend, check_fma32, check_exp32, check_silu_mul]

@@ -122,11 +122,18 @@ def _mut_exp_drops_ln2_lo(orig):
     def f(x):
         x = np.clip(np.asarray(x, np.float32), -O.EXP_ARG_CLAMP, O.EXP_ARG_CLAMP).astype(np.float32)
         n = np.rint((x * O.LOG2E_F32).astype(np.float32)).astype(np.float32)
-        r = (x - (n * O.LN2_HI_F32).astype(np.float32)).astype(np.float32)
+        r = O.fma32(-n, O.LN2_HI_F32, x)
         p = np.full(x.shape, O.EXP_TAYLOR_F32[7], np.float32)
         for k in range(6, -1, -1):
-            p = ((p * r).astype(np.float32) + O.EXP_TAYLOR_F32[k]).astype(np.float32)
+            p = O.fma32(p, r, O.EXP_TAYLOR_F32[k])
         return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+    return f
+
+
+def _mut_fma_double_rounding(orig):
+    def f(a, b, c):
+        a64, b64, c64 = (np.asarray(v, np.float32).astype(np.float64) for v in (a, b, c))
+        return (a64 * b64 + c64).astype(np.float32)
     return f
 
 
@@ -157,6 +164,7 @@ MUTANTS = {
     "alpha_swapped": ("smoothing_factors", _mut_alpha_swapped),
     "bf16_double_rounding": ("round_f64_to_bf16", _mut_bf16_via_f32),
     "exp_drops_ln2_lo": ("exp32", _mut_exp_drops_ln2_lo),
+    "fma_double_rounding": ("fma32", _mut_fma_double_rounding),
     "silu_sign": ("silu_mul", _mut_silu_sign),
     "fused_skips_silu": ("silu_mul_quant_act", _mut_fused_skips_silu),
 }

@@ -70,12 +70,14 @@ __device__ __forceinline__ int qcode(float v, float inv) {
 // LLaMA MLP's silu(g) = g / (1 + e^-g); its input order is already down's
 // saliency order, the permutation having been pushed into gate and up
 // offline -- papernotes.org SERQ notes, 关键设计 3). e^x by Cody and Waite's
-// reduction: e^x = 2^n e^r, n = rne(x log2 e), r = (x - n c_hi) - n c_lo
-// with c_hi + c_lo = ln 2 and c_hi of 12 significant bits (n c_hi exact),
-// then the degree-7 Taylor polynomial of e^r in Horner form and an exact
-// scaling by 2^n; the argument is clamped to [-80, 80] so every step stays a
-// normal number. Every operation is one fp32 op (the build disables
-// contraction into fused multiply-adds); the division is IEEE.
+// reduction: e^x = 2^n e^r, n = rne(x log2 e), r = fma(-n, c_lo,
+// fma(-n, c_hi, x)) with c_hi + c_lo = ln 2 and c_hi of 12 significant bits
+// (n c_hi exact), then the degree-7 Taylor polynomial of e^r in Horner form,
+// one fused multiply-add per degree, and an exact scaling by 2^n; the
+// argument is clamped to [-80, 80] so every step stays a normal number.
+// Every other operation is one fp32 op (the build disables contraction into
+// fused multiply-adds, so only the ones written here exist); the division is
+// IEEE.
 constexpr double kLn2 = 0.6931471805599453;
 constexpr float kLog2e = static_cast<float>(1.0 / kLn2);
 constexpr float kLn2Hi = 0.693145751953125f;
@@ -88,14 +90,11 @@ __device__ __forceinline__ float exp32(float x) {
 #pragma clang fp contract(off)
   x = fminf(fmaxf(x, -80.0f), 80.0f);
   const float n = __builtin_rintf(x * kLog2e);
-  float r = x - n * kLn2Hi;
-  r = r - n * kLn2Lo;
+  float r = __builtin_fmaf(-n, kLn2Hi, x);
+  r = __builtin_fmaf(-n, kLn2Lo, r);
   float p = kInvFact[7];
 #pragma unroll
-  for (int k = 6; k >= 0; --k) {
-    p = p * r;
-    p = p + kInvFact[k];
-  }
+  for (int k = 6; k >= 0; --k) p = __builtin_fmaf(p, r, kInvFact[k]);
   return __builtin_ldexpf(p, static_cast<int>(n));
 }
 
