@@ -143,7 +143,7 @@ int serq_permute_outputs(const int32_t* perm_next, int N, int K, int r,
  *   a_bits     4 (W4A4) or 8 (W4A8).
  *   Xq         device, M x K/2 bytes (a_bits 4, packed) or M x K int8.
  *   sx         device, M floats: per-token scale.
- * Scratch: up to 128 rows with K > 8192 are cut into chunks over two
+ * Scratch: up to 64 rows with K > 8192 are cut into chunks over two
  * launches whose chunk maxima meet in a 32 KB device array the library holds
  * per device (no allocation call); such calls on one device must not overlap.
  * M == 0 is a no-op; X, Xq and sx may then be NULL. Errors: SERQ_EINVAL
@@ -180,7 +180,7 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
  *              with the same results.
  *   s_hat_inv  K floats, device (down's, from serq_calibrate).
  *   a_bits, Xq, sx as for serq_quant_act (so is the scratch rule, here for
- *              up to 128 rows with K > 4096).
+ *              up to 64 rows with K > 4096, or 128 with K > 16384).
  * M == 0 is a no-op. Errors: SERQ_EINVAL (NULL pointer, M < 0, K <= 0, odd
  * K, ld < K, bad a_bits or dtype), SERQ_EALIGN (G or U not aligned to its
  * element, Xq or sx not 16-byte aligned), SERQ_EHIP. Subnormal inputs are

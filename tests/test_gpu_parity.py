@@ -55,7 +55,8 @@ def _act_input(M, K, dtype, seed):
 @pytest.mark.parametrize("M,K", [(16, 256), (7, 4096), (33, 14336), (5, 28672), (9, 1000), (4, 1002), (11, 8192), (6, 2048),
                                  (3, 40000), (1, 2), (64, 8),
                                  (600, 1000), (1030, 4096), (520, 8192),     # several rows per workgroup
-                                 (2, 70000), (128, 14336), (129, 14336)])    # chunked rows (few rows, long K)
+                                 (2, 70000), (128, 14336), (129, 14336),     # chunked rows (few rows, long K)
+                                 (520, 40000), (513, 4096), (512, 4104)])    # 512 or 256 lanes per row
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_quant_act_bit_exact(M, K, dtype, bits):
@@ -116,7 +117,8 @@ def _gate_up_input(M, K, dtype, layout, seed):
                                         (3, 1000, "split"), (4, 1002, "cat"), (2, 40000, "split"),
                                         (9, 2048, "padded"), (1, 2, "split"), (600, 1000, "padded"),
                                         (1030, 4096, "cat"), (2, 70000, "split"), (128, 14336, "padded"),
-                                        (129, 8200, "padded"), (7, 4104, "cat")])
+                                        (129, 8200, "padded"), (7, 4104, "cat"), (513, 36000, "split"),
+                                        (100, 28672, "cat"), (65, 14336, "split")])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_silu_mul_quant_act_bit_exact(M, K, layout, dtype, bits):

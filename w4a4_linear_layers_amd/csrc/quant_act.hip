@@ -9,9 +9,9 @@
 // with qmax = 7 (int4, packed two codes per byte) or 127 (int8). A row whose
 // reciprocal overflows (all-zero row) gets scale 0 and zero codes.
 //
-// This is a streaming scan, bound by HBM: one workgroup of 256 lanes per row,
-// 16-byte loads, the flattened row kept in registers between the absmax
-// reduction (wave shuffles, then LDS across the four waves) and the
+// This is a streaming scan, bound by HBM: one workgroup of 256 or 512 lanes
+// per row, 16-byte loads, the flattened row kept in registers between the
+// absmax reduction (wave shuffles, then LDS across the waves) and the
 // quantization, so X is read exactly once.
 
 #include <cfloat>
@@ -21,9 +21,9 @@
 namespace serq {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;                 // lanes of the generic kernel
 constexpr int kVec = 8;                       // elements per lane per pass
-constexpr int kPassElems = kThreads * kVec;   // 2048 elements per pass
+constexpr int kPassElems = kThreads * kVec;   // 2048: the split path's row-length unit
 
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
@@ -46,6 +46,7 @@ __device__ __forceinline__ float load1(const uint16_t* p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);
 }
 
+template <int NT>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -54,7 +55,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   __syncthreads();
   float m = red[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
   return m;
 }
 
@@ -130,20 +131,21 @@ struct RowSrc {
   }
 };
 
-// Fast path: K % 8 == 0, K <= NP * 2048, 16-byte aligned rows.
-template <typename T, int A_BITS, int NP, bool ACT>
-__global__ __launch_bounds__(kThreads) void quant_act_rows(RowSrc<T, ACT> src,
+// Fast path: K % 8 == 0, K <= NP * NT * 8, 16-byte aligned rows; NT lanes
+// per row.
+template <typename T, int A_BITS, int NP, bool ACT, int NT>
+__global__ __launch_bounds__(NT) void quant_act_rows(RowSrc<T, ACT> src,
                                                            const float* __restrict__ sinv, int K,
                                                            uint8_t* __restrict__ Xq,
                                                            float* __restrict__ sx) {
   constexpr int QMAX = A_BITS == 4 ? 7 : 127;
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[NT / 64];
   const size_t row = blockIdx.x;
   float v[NP][kVec];
   float amax = 0.0f;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int c = (p * kThreads + static_cast<int>(threadIdx.x)) * kVec;
+    const int c = (p * NT + static_cast<int>(threadIdx.x)) * kVec;
     if (c < K) {
       float s[kVec];
       src.load8(row, c, v[p]);
@@ -155,14 +157,14 @@ __global__ __launch_bounds__(kThreads) void quant_act_rows(RowSrc<T, ACT> src,
       }
     }
   }
-  amax = block_max(amax, red);
+  amax = block_max<NT>(amax, red);
   float inv = static_cast<float>(QMAX) / amax;
   const bool zero = !(inv <= FLT_MAX);
   if (zero) inv = 0.0f;
   if (threadIdx.x == 0) sx[row] = zero ? 0.0f : amax / static_cast<float>(QMAX);
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int c = (p * kThreads + static_cast<int>(threadIdx.x)) * kVec;
+    const int c = (p * NT + static_cast<int>(threadIdx.x)) * kVec;
     if (c < K) {
       int q[kVec];
 #pragma unroll
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_rows_generic(RowSrc<T, ACT
   const size_t row = blockIdx.x;
   float amax = 0.0f;
   for (int k = threadIdx.x; k < K; k += kThreads) amax = fmaxf(amax, fabsf(src.load1(row, k) * sinv[k]));
-  amax = block_max(amax, red);
+  amax = block_max<kThreads>(amax, red);
   float inv = static_cast<float>(QMAX) / amax;
   const bool zero = !(inv <= FLT_MAX);
   if (zero) inv = 0.0f;
@@ -312,12 +314,14 @@ hipError_t launch_split_np(RowSrc<T, ACT> src, int M, int K, const float* sinv, 
   return hipGetLastError();
 }
 
-// The split path's share: at most kSplitMaxRows rows, chunks of up to 2048
-// elements, at most kSplitMaxChunks of them; rows short enough for one
-// workgroup's pass gain nothing from it.
+// The split path's share (measured against the one-pass kernel): up to 64
+// rows, or kSplitMaxRows rows of the fused activation beyond 16384 elements,
+// chunks of up to 2048 elements, at most kSplitMaxChunks of them; rows short
+// enough for one workgroup's pass gain nothing from it.
 template <bool ACT>
 bool use_split(int M, int K) {
-  return M <= kSplitMaxRows && K > (ACT ? 2 : 4) * kPassElems && K <= kSplitMaxChunks * 4 * kChunkElems;
+  const int max_rows = ACT && K > 16384 ? kSplitMaxRows : 64;
+  return M <= max_rows && K > (ACT ? 2 : 4) * kPassElems && K <= kSplitMaxChunks * 4 * kChunkElems;
 }
 
 template <typename T, int A_BITS, bool ACT>
@@ -329,28 +333,39 @@ hipError_t launch_split(RowSrc<T, ACT> src, int M, int K, const float* sinv, uin
   return launch_split_np<T, A_BITS, 4, ACT>(src, M, K, sinv, Xq, sx, st);
 }
 
+template <typename T, int A_BITS, bool ACT, int NT>
+hipError_t launch_rows(RowSrc<T, ACT> src, int M, int K, const float* sinv, uint8_t* Xq, float* sx,
+                       hipStream_t st) {
+  const dim3 grid(M), block(NT);
+  const int passes = (K + NT * kVec - 1) / (NT * kVec);
+  if (passes <= 1) {
+    quant_act_rows<T, A_BITS, 1, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
+  } else if (passes <= 2) {
+    quant_act_rows<T, A_BITS, 2, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
+  } else if (passes <= 4) {
+    quant_act_rows<T, A_BITS, 4, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
+  } else if (passes <= 8) {
+    quant_act_rows<T, A_BITS, 8, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
+  } else {
+    quant_act_rows<T, A_BITS, 16, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int A_BITS, bool ACT>
 hipError_t launch_typed(RowSrc<T, ACT> src, int M, int K, const float* sinv, uint8_t* Xq, float* sx,
                         hipStream_t st) {
-  const dim3 grid(M), block(kThreads);
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   const bool aligned = (K % kVec == 0) && (src.ld % kVec == 0) && al16(src.a) && (!ACT || al16(src.b)) &&
                        al16(sinv) && al16(Xq);
-  const int passes = (K + kPassElems - 1) / kPassElems;
   if (aligned && use_split<ACT>(M, K)) return launch_split<T, A_BITS, ACT>(src, M, K, sinv, Xq, sx, st);
-  if (!aligned || passes > 16) {
-    quant_act_rows_generic<T, A_BITS, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
-  } else if (passes <= 1) {
-    quant_act_rows<T, A_BITS, 1, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
-  } else if (passes <= 2) {
-    quant_act_rows<T, A_BITS, 2, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
-  } else if (passes <= 4) {
-    quant_act_rows<T, A_BITS, 4, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
-  } else if (passes <= 8) {
-    quant_act_rows<T, A_BITS, 8, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
-  } else {
-    quant_act_rows<T, A_BITS, 16, ACT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
-  }
+  // 512 lanes per row while the rows are few or long (more waves in flight
+  // per row, fewer values per lane; measured 1.3x at 256 rows of 14336),
+  // 256 for many short rows (more rows resident per CU).
+  if (aligned && K <= 16 * 512 * kVec && (M <= 512 || K > 8192))
+    return launch_rows<T, A_BITS, ACT, 512>(src, M, K, sinv, Xq, sx, st);
+  if (aligned && K <= 16 * kThreads * kVec) return launch_rows<T, A_BITS, ACT, kThreads>(src, M, K, sinv, Xq, sx, st);
+  quant_act_rows_generic<T, A_BITS, ACT><<<dim3(M), dim3(kThreads), 0, st>>>(src, sinv, K, Xq, sx);
   return hipGetLastError();
 }
 
