@@ -152,6 +152,34 @@ def test_silu_mul_quant_act_empty_and_bad_arguments():
     _sync()
 
 
+def test_binding_rejects_wrong_buffer_sizes():
+    """The binding checks caller-supplied buffers against the sizes the
+    kernels write or read (the C ABI cannot), before anything is launched."""
+    x = torch.zeros((4, 64), device="cuda")
+    sinv = torch.ones(64, device="cuda")
+    with pytest.raises(ValueError):
+        S.quant_act(x, sinv, out=(torch.empty((4, 16), dtype=torch.uint8, device="cuda"),
+                                  torch.empty(4, device="cuda")))
+    with pytest.raises(ValueError):
+        S.quant_act(x, sinv, out=(torch.empty((4, 32), dtype=torch.uint8, device="cuda"),
+                                  torch.empty(3, device="cuda")))
+    with pytest.raises(ValueError):
+        S.quant_act(x, torch.ones(32, device="cuda"))
+    with pytest.raises(ValueError):
+        S.silu_mul_quant_act(x, x, sinv, a_bits=8, out=(torch.empty((4, 32), dtype=torch.int8, device="cuda"),
+                                                        torch.empty(4, device="cuda")))
+    li = workload_layer("tiny", "tiny")
+    D = S.calibrate(li.W, li.act_absmax, r=8).to("cuda")
+    xq, sx = S.quant_act(torch.zeros((4, 256), device="cuda"), D)
+    with pytest.raises(ValueError):
+        S.linear(xq[:, :64], sx, D)
+    with pytest.raises(ValueError):
+        S.linear(xq, sx, D, out=torch.empty((4, 255), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        S.linear(xq, sx, D, out_dtype=torch.float32, out=torch.empty((4, 256), dtype=torch.bfloat16, device="cuda"))
+    _sync()
+
+
 # ------------------------------------------------------- linear on raw codes
 
 def _codes_case(M, K, N, r, bits, seed, zero_scales=True):

@@ -147,6 +147,21 @@ def _need_cuda(*ts):
             raise ValueError("device tensors must be contiguous CUDA tensors")
 
 
+def _act_out(out, M, K, a_bits, device):
+    """The (xq, sx) buffers: new ones, or the caller's after checking that
+    they are device tensors of exactly the sizes the kernels write."""
+    import torch
+    shape = (M, K // 2 if a_bits == 4 else K)
+    if out is None:
+        xq = torch.empty(shape, dtype=torch.uint8 if a_bits == 4 else torch.int8, device=device)
+        return xq, torch.empty(M, dtype=torch.float32, device=device)
+    xq, sx = out
+    _need_cuda(xq, sx)
+    if tuple(xq.shape) != shape or xq.element_size() != 1 or tuple(sx.shape) != (M,) or sx.dtype != torch.float32:
+        raise ValueError(f"out must be (xq {shape} of 1-byte codes, sx ({M},) float32)")
+    return xq, sx
+
+
 def quant_act(x, layer_or_sinv, *, a_bits: int = 4, out=None):
     """Per-token activation quantization (serq_quant_act) on the current
     stream. ``x`` is M x K float32 or bfloat16, already in saliency order.
@@ -161,12 +176,9 @@ def quant_act(x, layer_or_sinv, *, a_bits: int = 4, out=None):
         dt = SERQ_F32
     else:
         raise ValueError("x must be float32 or bfloat16")
-    if out is None:
-        xq = torch.empty((M, K // 2 if a_bits == 4 else K), dtype=torch.uint8 if a_bits == 4 else torch.int8,
-                         device=x.device)
-        sx = torch.empty(M, dtype=torch.float32, device=x.device)
-    else:
-        xq, sx = out
+    if sinv.numel() != K:
+        raise ValueError(f"s_hat_inv has {sinv.numel()} entries for K = {K}")
+    xq, sx = _act_out(out, M, K, a_bits, x.device)
     check("serq_quant_act", lib.serq_quant_act(x.data_ptr(), dt, M, K, sinv.data_ptr(), a_bits,
                                                xq.data_ptr(), sx.data_ptr(), _stream()))
     return xq, sx
@@ -180,24 +192,25 @@ def silu_mul_quant_act(g, u, layer_or_sinv, *, a_bits: int = 4, out=None):
     down layer (or its s_hat_inv). Returns (xq, sx) as quant_act does."""
     import torch
     sinv = layer_or_sinv.s_hat_inv if isinstance(layer_or_sinv, DeviceLayer) else layer_or_sinv
-    if g.shape != u.shape or g.dtype != u.dtype or g.stride() != u.stride() or g.dim() != 2:
-        raise ValueError("g and u must be M x K views of one dtype and row stride")
-    if g.stride(1) != 1 or not g.is_cuda or not u.is_cuda or not sinv.is_cuda or not sinv.is_contiguous():
-        raise ValueError("g and u must be CUDA tensors with unit column stride")
+    if g.dim() != 2 or g.shape != u.shape or g.dtype != u.dtype:
+        raise ValueError("g and u must be M x K tensors of one dtype")
     M, K = g.shape
+    if M > 1 and g.stride(0) != u.stride(0):
+        raise ValueError("g and u must share their row stride")
+    if (K > 1 and (g.stride(1) != 1 or u.stride(1) != 1)) or not g.is_cuda or not u.is_cuda:
+        raise ValueError("g and u must be CUDA tensors with unit column stride")
+    if not sinv.is_cuda or not sinv.is_contiguous():
+        raise ValueError("s_hat_inv must be a contiguous CUDA tensor")
     if g.dtype == torch.bfloat16:
         dt = SERQ_BF16
     elif g.dtype == torch.float32:
         dt = SERQ_F32
     else:
         raise ValueError("g and u must be float32 or bfloat16")
-    if out is None:
-        xq = torch.empty((M, K // 2 if a_bits == 4 else K), dtype=torch.uint8 if a_bits == 4 else torch.int8,
-                         device=g.device)
-        sx = torch.empty(M, dtype=torch.float32, device=g.device)
-    else:
-        xq, sx = out
-    ld = g.stride(0) if M > 1 else K
+    if sinv.numel() != K:
+        raise ValueError(f"s_hat_inv has {sinv.numel()} entries for K = {K}")
+    xq, sx = _act_out(out, M, K, a_bits, g.device)
+    ld = g.stride(0) if M > 1 else K             # one row: the stride is never used
     check("serq_silu_mul_quant_act", lib.serq_silu_mul_quant_act(
         g.data_ptr(), u.data_ptr(), ld, dt, M, K, sinv.data_ptr(), a_bits, xq.data_ptr(), sx.data_ptr(), _stream()))
     return xq, sx
@@ -211,13 +224,23 @@ def linear(xq, sx, layer: DeviceLayer, *, a_bits: int = 4, out_dtype=None, out=N
     _need_cuda(xq, sx, layer.Wq, layer.sw, layer.Rq if layer.r else None, layer.sr if layer.r else None)
     M = xq.shape[0]
     K, N, r = layer.K, layer.N, layer.r
+    if xq.dim() != 2 or xq.shape[1] != (K // 2 if a_bits == 4 else K) or xq.element_size() != 1:
+        raise ValueError(f"xq must be M x {K // 2 if a_bits == 4 else K} codes of one byte for this layer")
+    if tuple(sx.shape) != (M,) or sx.dtype != torch.float32:
+        raise ValueError(f"sx must be ({M},) float32")
     if out_dtype == torch.bfloat16:
         dt = SERQ_BF16
     elif out_dtype == torch.float32:
         dt = SERQ_F32
     else:
         raise ValueError("out_dtype must be float32 or bfloat16")
-    y = torch.empty((M, N), dtype=out_dtype, device=xq.device) if out is None else out
+    if out is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    else:
+        y = out
+        _need_cuda(y)
+        if tuple(y.shape) != (M, N) or y.dtype != out_dtype:
+            raise ValueError(f"out must be a ({M}, {N}) {out_dtype} tensor")
     am = ar = None
     if debug:
         am = torch.empty((M, N), dtype=torch.int32, device=xq.device)

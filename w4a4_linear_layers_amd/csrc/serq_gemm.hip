@@ -29,6 +29,7 @@
 // operands holds codes [32 g, 32 g + 32) (16 packed bytes); MFMA step 0 uses
 // its first 16 codes and step 1 the next 16.
 
+#include <atomic>
 #include <mutex>
 #include <utility>
 
@@ -1260,16 +1261,27 @@ __global__ __launch_bounds__(kThreads) void serq_generic_kernel(LinearArgs a) {
     static_cast<float*>(a.Y)[idx] = y;
 }
 
+// Raise a kernel's dynamic-LDS limit once per device (the attribute is set
+// with the device current; `done` holds one bit per device).
+hipError_t ensure_max_lds(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = uint64_t{1} << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 template <int TN, int TM, int A_BITS, int WGM>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
   using C = TileCfg<TN, TM, A_BITS, WGM>;
-  static bool attr_set = false;  // idempotent; the attribute is per function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_tile_kernel<TN, TM, A_BITS, WGM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_tile_kernel<TN, TM, A_BITS, WGM>),
+                                C::LDS_BYTES, lds_set);
+  if (e != hipSuccess) return e;
   const int n_tiles = (a.N + C::BN - 1) / C::BN;
   const int m_tiles = (a.M + C::BM - 1) / C::BM;
   serq_tile_kernel<TN, TM, A_BITS, WGM><<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS_BYTES, st>>>(a, n_tiles);
@@ -1355,13 +1367,10 @@ template <int MG, int A_BITS, int IPW>
 hipError_t launch_skinny_ipw(const LinearArgs& a, const SkinnySplit& sp, hipStream_t st) {
   constexpr int CXB = 2 * A_BITS * 16;
   const int lds = a.M * (sp.seg * CXB + 16) + sp.G * skx_slot_bytes<MG>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_skinny_kernel<MG, A_BITS, IPW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSkxLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_skinny_kernel<MG, A_BITS, IPW>), kSkxLds,
+                                lds_set);
+  if (e != hipSuccess) return e;
   serq_skinny_kernel<MG, A_BITS, IPW><<<dim3(sp.nb * sp.KS), dim3(64 * kSkxWaves), lds, st>>>(a, sp);
   return hipGetLastError();
 }
@@ -1390,13 +1399,9 @@ hipError_t launch_gemv_kp(const LinearArgs& a, hipStream_t st) {
   const int octets = (a.N + 7) / 8;
   const int grid = octets;
   const int lds = (MT * (a.K / 2) + 15) / 16 * 16;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&serq_gemv_kernel<MT, KP>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kGemvMaxX);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_gemv_kernel<MT, KP>), kGemvMaxX, lds_set);
+  if (e != hipSuccess) return e;
   serq_gemv_kernel<MT, KP><<<dim3(grid), dim3(64 * KP), lds, st>>>(a);
   return hipGetLastError();
 }
