@@ -70,9 +70,11 @@ def linear_ops(M, K, N, r):
 
 
 def kernel_src_sha():
+    """Hash of serq_linear's kernel sources: stored HBM-traffic counters are
+    used only while it matches the sources they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a4_linear_layers_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("serq_gemm.hip", "serq_internal.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -303,7 +305,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="q_proj", choices=sorted(WORKLOADS))
     ap.add_argument("--M", type=int, default=None, help="tokens per step (default: the workload's)")
-    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the other token counts and the MLP activation")
+    ap.add_argument("--no-mlp-act", action="store_true", help="skip the MLP activation timing")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (a reference kernel of known "
@@ -371,7 +374,7 @@ def main(argv=None):
                   f"{e['frac']:.3f}); quant_act {qu:.2f} us", file=sys.stderr, flush=True)
 
     mlp_act = []
-    if not args.no_sweep:
+    if not args.no_sweep and not args.no_mlp_act:
         for k_int in (14336, 28672):
             for e in time_mlp_act(k_int, (1, 16, 256, 4096)):
                 mlp_act.append(e)
