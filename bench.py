@@ -131,6 +131,8 @@ class Setup:
         torch's capture stream), so that replays are not bound by Python
         launch overhead."""
         import torch
+        fn(0)                 # outside the capture: the library's first-call set-up (workspaces)
+        torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
