@@ -250,15 +250,15 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(32, 4096, 14336, 128) == "decode32"
     assert S.kernel_name(4096, 4096, 14336, 128) == "tile128x128"
     assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x128"
-    assert S.kernel_name(65, 4096, 4096, 64) == "tile32x64"          # 128 tiles of 64 x 64: half the CUs
-    assert S.kernel_name(128, 14336, 4096, 128) == "tile32x64"
+    assert S.kernel_name(65, 4096, 4096, 64) == "tile32x64k4"          # 128 tiles of 64 x 64: half the CUs
+    assert S.kernel_name(128, 14336, 4096, 128) == "tile32x64k4"
     assert S.kernel_name(129, 4096, 4096, 64) == "tile64x64"         # 192 tiles of 64 x 64
     assert S.kernel_name(256, 4096, 4096, 64) == "tile64x64"         # 256 tiles of 64 x 64
     assert S.kernel_name(40, 4096, 28672, 128) == "tile64x64"        # 448 tiles of 64 x 64
     assert S.kernel_name(64, 4096, 32768, 64) == "tile64x128"        # 256 tiles of 64 x 128
     assert S.kernel_name(768, 4096, 4096, 64) == "tile64x128"        # 192 tiles of 128 x 128 would be too few
     assert S.kernel_name(1024, 4096, 4096, 64) == "tile128x128"
-    assert S.kernel_name(64, 4096, 4096, 64) == "tile32x64"
+    assert S.kernel_name(64, 4096, 4096, 64) == "tile32x64k4"
     assert S.kernel_name(16, 4100, 64, 8) == "generic"      # K % 32 != 0
     assert S.kernel_name(16, 4096, 64, 6) == "generic"      # r % 8 != 0
     assert S.kernel_name(16, 4096, 64, 512) == "generic"    # r > 256

@@ -232,11 +232,11 @@ LINEAR_CASES = [
     (12, 28672, 48, 256, "decode16"),     # long rows: several rounds of loads per wave
     (32, 28672, 40, 32, "decode32"),      # long rows, two token blocks, r <= 32 (16-byte Q(R) rows)
     (20, 4128, 80, 16, "decode32"),
-    (40, 1056, 130, 72, "tile32x64"),
-    (64, 96, 256, 96, "tile32x64"),       # K shorter than one k-tile, r = K
-    (100, 512, 300, 64, "tile32x64"),
-    (129, 800, 258, 8, "tile32x64"),
-    (128, 4096, 4096, 64, "tile32x64"),       # deep pipeline, 32-token tiles
+    (40, 1056, 130, 72, "tile32x64k4"),
+    (64, 96, 256, 96, "tile32x64k4"),       # K shorter than one k-tile, r = K
+    (100, 512, 300, 64, "tile32x64k4"),
+    (129, 800, 258, 8, "tile32x64k4"),
+    (128, 4096, 4096, 64, "tile32x64k4"),       # deep pipeline, 32-token tiles
     (256, 4096, 4096, 64, "tile64x64"),       # deep pipeline, one workgroup per CU
     (200, 1056, 2600, 72, "tile64x64"),       # ragged M and N
     (60, 1056, 32800, 72, "tile64x128"),      # ragged M and N

@@ -264,46 +264,61 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
 }
 #pragma clang diagnostic pop
 
-// Tile shape: each wave owns TN x TM blocks of 32 x 32; the workgroup is a
-// 2 (channels) x WGM (tokens) grid of waves; OCC workgroups share a CU (two
-// four-wave or four two-wave ones: two waves per SIMD either way).
-template <int TN, int TM, int A_BITS, int WGM>
+// Tile shape: each wave owns TN x TM blocks of 32 x 32; a k-group is a
+// 2 (channels) x WGM (tokens) grid of waves, and the workgroup holds KG
+// k-groups, group g taking k-tile g of every KG-k-tile stage (their sums are
+// added through LDS at the end). OCC workgroups share a CU: two waves per
+// SIMD in every shape.
+template <int TN, int TM, int A_BITS, int WGM, int KG>
 struct TileCfg {
-  static constexpr int NW = 2 * WGM;                     // waves per workgroup
+  static constexpr int NWG = 2 * WGM;                    // waves per k-group
+  static constexpr int NW = NWG * KG;                    // waves per workgroup
   static constexpr int NT = 64 * NW;                     // lanes per workgroup
-  static constexpr int OCC = WGM == 2 ? 2 : 4;           // workgroups per CU
+  static constexpr int OCC = 8 / NW;                     // workgroups per CU
   static constexpr int WN = 32 * TN, WM = 32 * TM;       // wave tile
   static constexpr int BN = 2 * WN, BM = WGM * WM;       // workgroup tile
   static constexpr int XB = kKTileCodes * A_BITS / 8;    // activation bytes / row / k-tile
   static constexpr int W_BYTES = BN * kKTileW;
-  static constexpr int STAGE = W_BYTES + BM * XB;        // bytes per LDS stage
-  static constexpr int W_CHUNKS = W_BYTES / 1024;        // 1 KB wave chunks per stage
+  static constexpr int SUB = W_BYTES + BM * XB;          // one k-tile of the tile in LDS
+  static constexpr int STAGE = KG * SUB;                 // bytes per LDS stage (KG k-tiles)
+  static constexpr int W_CHUNKS = W_BYTES / 1024;        // 1 KB wave chunks per k-tile
   static constexpr int X_CHUNKS = BM * XB / 1024;
-  static constexpr int CW = W_CHUNKS / NW;               // weight chunks per wave and stage
-  static constexpr int CX = X_CHUNKS / NW;               // activation chunks per wave and stage
+  static constexpr int CW = KG * W_CHUNKS / NW;          // weight chunks per wave and stage
+  static constexpr int CX = KG * X_CHUNKS / NW;          // activation chunks per wave and stage
   static constexpr int CHUNKS_PER_WAVE = CW + CX;
   static constexpr int SCALE_BYTES = 4 * (2 * BN + BM);  // sw, sr, sx of the tile
+  static constexpr int TRASH_BYTES = KG > 1 ? 1024 : 0;  // sink of the loads that only keep counts even
   static constexpr int kLdsCap = 160 * 1024 / OCC;       // the CU's LDS split between its workgroups
   static constexpr int kMaxStages = 8;
   static constexpr int stages() {
     int st = kMaxStages;
-    while (st > 2 && st * STAGE + SCALE_BYTES > kLdsCap) --st;
+    while (st > 2 && st * STAGE + SCALE_BYTES + TRASH_BYTES > kLdsCap) --st;
     return st;
   }
   static constexpr int STAGES = stages();
   static constexpr int SCALE_OFF = STAGES * STAGE;
+  static constexpr int TRASH_OFF = SCALE_OFF + SCALE_BYTES;
   static constexpr int OUT_BYTES = BM * BN * 4;          // fp32 output tile (bf16 takes half)
-  static constexpr int LDS_BYTES = SCALE_OFF + SCALE_BYTES > OUT_BYTES ? SCALE_OFF + SCALE_BYTES : OUT_BYTES;
+  static constexpr int RED_BYTES = (KG - 1) * NWG * 64 * TN * TM * 2 * 64;   // other groups' sums
+  static constexpr int lds_bytes() {
+    int b = TRASH_OFF + TRASH_BYTES;
+    if (OUT_BYTES > b) b = OUT_BYTES;
+    if (RED_BYTES > b) b = RED_BYTES;
+    return b;
+  }
+  static constexpr int LDS_BYTES = lds_bytes();
   static constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
   // Output-tile chunk swizzle mask for rows of `eb`-byte elements: XOR with
   // the row's low bits, within the row's 16-byte chunks.
   static constexpr int out_swz(int eb) { return BN * eb / 16 >= 16 ? 15 : BN * eb / 16 - 1; }
-  static_assert(W_CHUNKS % NW == 0 && X_CHUNKS % NW == 0, "stage must split over the waves");
+  static_assert((KG * W_CHUNKS) % NW == 0 && (KG * X_CHUNKS) % NW == 0, "stage must split over the waves");
+  static_assert(RED_BYTES <= SCALE_OFF, "group sums fit in the stages");
   static_assert(BN % 64 == 0 && (BM % 64 == 0 || BM == 32), "scale rows are loaded 64 at a time");
   static_assert(CHUNKS_PER_WAVE * (STAGES - 1) < 64, "vmcnt range");
   // The residual k-tiles (at most two) stay in their buffers while the last
   // main k-tile is computed from another one.
-  static_assert(STAGES >= (kMaxResidual / 2 + kKTileW - 1) / kKTileW + 1, "residual k-tiles need free stages");
+  static_assert(STAGES >= ((kMaxResidual / 2 + kKTileW - 1) / kKTileW + KG - 1) / KG + 1,
+                "residual k-tiles need free stages");
   static_assert(LDS_BYTES <= kLdsCap, "LDS");
 };
 
@@ -313,17 +328,18 @@ struct TileCfg {
 // consecutive rows at one column on distinct banks.
 __device__ __forceinline__ int half_swap(int row) { return ((row >> 3) ^ (row >> 4)) & 1; }
 
-template <int TN, int TM, int A_BITS, int WGM>
-__global__ __launch_bounds__(128 * WGM, 2)   // NT lanes; two waves per SIMD (OCC workgroups per CU)
+template <int TN, int TM, int A_BITS, int WGM, int KG>
+__global__ __launch_bounds__(128 * WGM * KG, 2)   // NT lanes; two waves per SIMD (OCC workgroups per CU)
 void serq_tile_kernel(LinearArgs a, int n_tiles) {
-  using C = TileCfg<TN, TM, A_BITS, WGM>;
-  static_assert(C::NT == 128 * WGM && C::OCC * C::NW == 8, "launch bounds");
+  using C = TileCfg<TN, TM, A_BITS, WGM, KG>;
+  static_assert(C::NT == 128 * WGM * KG && C::OCC * C::NW == 8, "launch bounds");
   constexpr int STAGES = C::STAGES;
   constexpr int CPW = C::CHUNKS_PER_WAVE;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave / WGM, wm = wave % WGM;
+  const int kg = wave / C::NWG, wl = wave % C::NWG;     // k-group, and wave within it
+  const int wn = wl / WGM, wm = wl % WGM;
   const int l32 = lane & 31, h = lane >> 5;
   int tile_n, tile_m;
   tile_coords(blockIdx.x, gridDim.x, n_tiles, tile_n, tile_m);
@@ -332,8 +348,9 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   const int Kb = a.K / 2;                      // packed weight bytes per row
   const int Xrow = a.K * A_BITS / 8;           // activation bytes per row
   const int Rb = rq_row_bytes(a.r);            // Q(R) bytes per row (zero-padded)
-  const int nkt = (Kb + kKTileW - 1) / kKTileW;  // main k-tiles
-  const int ntot = nkt + (Rb + kKTileW - 1) / kKTileW;   // plus residual k-tiles
+  // Stages of KG k-tiles: main ones, then the residual ones.
+  const int nkt = ((Kb + kKTileW - 1) / kKTileW + KG - 1) / KG;
+  const int ntot = nkt + ((Rb + kKTileW - 1) / kKTileW + KG - 1) / KG;
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // The operand bases, held in registers: selecting between fields of the
@@ -374,67 +391,86 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
 
   // Wave w loads weight chunks [w CW, (w + 1) CW) and activation chunks
   // [w CX, (w + 1) CX) of every stage: 16 rows x 64 bytes per chunk (8 rows x
-  // 128 bytes for int8 activations). Per lane: the byte offset of its row and
-  // swizzled part at k-tile 0; the k-tile advances the (scalar) base pointer.
+  // 128 bytes for int8 activations) of one of the stage's KG k-tiles. Per
+  // lane: the byte offset of its row and swizzled part at stage 0, and the
+  // chunk's place in the stage; the stage advances the (scalar) base pointer.
   const int part64 = (lane & 3) ^ swz64(lane >> 2);    // 16-row chunks: row & 15 = lane >> 2
-  uint32_t woff[C::CW], roff[C::CW], xoff[C::CX];
+  uint32_t woff[C::CW], roff[C::CW], xoff[C::CX], wdst[C::CW], xdst[C::CX];
   int xpart[C::CX];                                     // this lane's 16-byte part of each activation chunk
+  int wsub[C::CW], xsub[C::CX], wrow[C::CW], xrow[C::CX];   // k-tile within the stage, source row
 #pragma unroll
   for (int i = 0; i < C::CW; ++i) {
-    const int row = min(n0 + (wv * C::CW + i) * 16 + (lane >> 2), a.N - 1);
-    woff[i] = static_cast<uint32_t>(row) * Kb + part64 * 16;
-    roff[i] = static_cast<uint32_t>(row) * Rb + part64 * 16;
+    const int c = wv * C::CW + i, sub = c / C::W_CHUNKS, cc = c % C::W_CHUNKS;
+    const int row = min(n0 + cc * 16 + (lane >> 2), a.N - 1);
+    wsub[i] = sub;
+    wrow[i] = row;
+    wdst[i] = sub * C::SUB + cc * 1024;
+    woff[i] = static_cast<uint32_t>(row) * Kb + part64 * 16 + sub * kKTileW;
+    roff[i] = static_cast<uint32_t>(row) * Rb + part64 * 16 + sub * kKTileW;
   }
 #pragma unroll
   for (int i = 0; i < C::CX; ++i) {
+    const int c = wv * C::CX + i, sub = c / C::X_CHUNKS, cc = c % C::X_CHUNKS;
+    xsub[i] = sub;
+    xdst[i] = sub * C::SUB + C::W_BYTES + cc * 1024;
     if constexpr (A_BITS == 4) {
-      const int row = (wv * C::CX + i) * 16 + (lane >> 2);
+      const int row = cc * 16 + (lane >> 2);
       xpart[i] = part64;
-      xoff[i] = static_cast<uint32_t>(min(m0 + row, a.M - 1)) * Xrow + part64 * 16;
+      xrow[i] = min(m0 + row, a.M - 1);
     } else {
-      const int row = (wv * C::CX + i) * 8 + (lane >> 3);
+      const int row = cc * 8 + (lane >> 3);
       xpart[i] = (lane & 7) ^ swz128(row);
-      xoff[i] = static_cast<uint32_t>(min(m0 + row, a.M - 1)) * Xrow + xpart[i] * 16;
+      xrow[i] = min(m0 + row, a.M - 1);
     }
+    xoff[i] = static_cast<uint32_t>(xrow[i]) * Xrow + xpart[i] * 16 + sub * C::XB;
   }
-  // Issue the loads of k-tile kt (main k-tiles, then residual ones) into LDS
+  // Issue the loads of stage kt (main stages, then residual ones) into LDS
   // stage `stage`. A k-tile that runs past the end of its rows (the last
   // main one when K % 128 != 0, the last residual one) zero-fills its missing
-  // 16-byte slots with an ordinary LDS store instead; every instruction still
-  // has at least one loading lane, so the per-wave load count is the same
-  // for every k-tile.
+  // 16-byte slots with an ordinary LDS store instead. Every load instruction
+  // keeps at least one loading lane, and a chunk wholly past the end (a
+  // stage's trailing k-tiles) still issues one load, of valid bytes into a
+  // scratch kilobyte of LDS, so the per-wave load count is the same for every
+  // stage.
   auto issue = [&](int kt, int stage) {
     const uint32_t sbase = lds_base + stage * C::STAGE;
     const bool res = kt >= nkt;
-    const int kx = res ? kt - nkt : kt;        // k-tile index within its source rows
-    const uint8_t* wsrc = (res ? Rq : Wq) + kx * kKTileW;
-    const uint8_t* xsrc = Xq + kx * C::XB;
-    const int wleft = (res ? Rb : Kb) - kx * kKTileW;     // row bytes left from the k-tile start
-    const int xleft = Xrow - kx * C::XB;
-    // Full main k-tiles take a path with no per-lane masks.
-    if (!res && wleft >= kKTileW && xleft >= C::XB) {
+    const int kx = res ? kt - nkt : kt;        // stage index within its source rows
+    const uint8_t* wsrc = (res ? Rq : Wq) + kx * KG * kKTileW;
+    const uint8_t* xsrc = Xq + kx * KG * C::XB;
+    const int wleft = (res ? Rb : Kb) - kx * KG * kKTileW;     // row bytes left from the stage start
+    const int xleft = Xrow - kx * KG * C::XB;
+    // Full main stages take a path with no per-lane masks.
+    if (!res && wleft >= KG * kKTileW && xleft >= KG * C::XB) {
 #pragma unroll
-      for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + (wv * C::CW + i) * 1024);
+      for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + wdst[i]);
 #pragma unroll
-      for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + C::W_BYTES + (wv * C::CX + i) * 1024);
+      for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + xdst[i]);
       return;
     }
 #pragma unroll
     for (int i = 0; i < C::CW; ++i) {
-      const uint32_t chunk = sbase + (wv * C::CW + i) * 1024;
+      const uint32_t chunk = sbase + wdst[i];
       const uint32_t off = res ? roff[i] : woff[i];
-      if (wleft >= kKTileW || part64 * 16 < wleft)
+      const int wl = wleft - wsub[i] * kKTileW;             // bytes of this k-tile's rows left
+      if (wl > 0 && (wl >= kKTileW || part64 * 16 < wl)) {
         dma16(wsrc, off, chunk);
-      else
+      } else {
+        if (KG > 1 && wl <= 0)
+          dma16(res ? Rq : Wq, static_cast<uint32_t>(wrow[i]) * (res ? Rb : Kb), lds_base + C::TRASH_OFF);
         *reinterpret_cast<uint4*>(lds + (chunk - lds_base) + lane * 16) = make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::CX; ++i) {
-      const uint32_t chunk = sbase + C::W_BYTES + (wv * C::CX + i) * 1024;
-      if (xleft >= C::XB || xpart[i] * 16 < xleft)
+      const uint32_t chunk = sbase + xdst[i];
+      const int xl = xleft - xsub[i] * C::XB;
+      if (xl > 0 && (xl >= C::XB || xpart[i] * 16 < xl)) {
         dma16(xsrc, xoff[i], chunk);
-      else
+      } else {
+        if (KG > 1 && xl <= 0) dma16(Xq, static_cast<uint32_t>(xrow[i]) * Xrow, lds_base + C::TRASH_OFF);
         *reinterpret_cast<uint4*>(lds + (chunk - lds_base) + lane * 16) = make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
@@ -455,13 +491,13 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   int wrd[2], xrd[XP];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
-    wrd[p] = (wn * C::WN + l32) * kKTileW + (((2 * h + p) ^ swz64(l32)) * 16);
+    wrd[p] = kg * C::SUB + (wn * C::WN + l32) * kKTileW + (((2 * h + p) ^ swz64(l32)) * 16);
 #pragma unroll
   for (int p = 0; p < XP; ++p) {
     if constexpr (A_BITS == 4)
-      xrd[p] = C::W_BYTES + (wm * C::WM + l32) * C::XB + (((2 * h + p) ^ swz64(l32)) * 16);
+      xrd[p] = kg * C::SUB + C::W_BYTES + (wm * C::WM + l32) * C::XB + (((2 * h + p) ^ swz64(l32)) * 16);
     else
-      xrd[p] = C::W_BYTES + (wm * C::WM + l32) * C::XB + (((4 * h + p) ^ swz128(l32)) * 16);
+      xrd[p] = kg * C::SUB + C::W_BYTES + (wm * C::WM + l32) * C::XB + (((4 * h + p) ^ swz128(l32)) * 16);
   }
 
   // This lane's packed fragments of one k-tile: two 16-byte parts per weight
@@ -577,12 +613,12 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
     wait_vmcnt<CPW * (STAGES - 2)>();
     asm volatile("s_barrier" ::: "memory");
     const uint32_t sbase = lds_base + st * C::STAGE;
-    const uint8_t* wsrc = Wq + (kt + STAGES) * kKTileW;
-    const uint8_t* xsrc = Xq + (kt + STAGES) * C::XB;
+    const uint8_t* wsrc = Wq + (kt + STAGES) * KG * kKTileW;
+    const uint8_t* xsrc = Xq + (kt + STAGES) * KG * C::XB;
 #pragma unroll
-    for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + (wv * C::CW + i) * 1024);
+    for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + wdst[i]);
 #pragma unroll
-    for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + C::W_BYTES + (wv * C::CX + i) * 1024);
+    for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + xdst[i]);
     read_frags((st + 1) % STAGES, next);
     compute(cur, accs);
   };
@@ -592,7 +628,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   Frags f0, f1;
   read_frags(0, f0);
   constexpr int UNR = STAGES % 2 ? 2 * STAGES : STAGES;
-  const int nfull = min(Kb / kKTileW, Xrow / C::XB);   // main k-tiles with no ragged end
+  const int nfull = min(Kb / kKTileW, Xrow / C::XB) / KG;   // main stages with no ragged end
   int kt0 = 0;
   for (; kt0 + UNR <= nfull - STAGES; kt0 += UNR) {
     static_for<UNR>([&](auto ic) {
@@ -647,7 +683,42 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
         acc[i][j] += accs[k][i][j];
         ar[i][j] += ars[k][i][j];
       }
-  if (a.dbg_main) {                            // exact accumulators, for tests
+  if constexpr (KG > 1) {
+    // The other k-groups' sums through LDS (the stages are free once every
+    // wave is here; lane-contiguous words, no bank conflicts), added up by
+    // group 0, which runs the epilogue.
+    constexpr int PL = TN * TM * 16;
+    lds_barrier();
+    int* red = reinterpret_cast<int*>(lds);
+    if (kg > 0) {
+      int* dst = red + ((kg - 1) * C::NWG + wl) * 2 * PL * 64 + lane;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            dst[((i * TM + j) * 16 + e) * 64] = acc[i][j][e];
+            dst[(PL + (i * TM + j) * 16 + e) * 64] = ar[i][j][e];
+          }
+    }
+    lds_barrier();
+    if (kg == 0) {
+      for (int g = 1; g < KG; ++g) {
+        const int* src = red + ((g - 1) * C::NWG + wl) * 2 * PL * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              acc[i][j][e] += src[((i * TM + j) * 16 + e) * 64];
+              ar[i][j][e] += src[(PL + (i * TM + j) * 16 + e) * 64];
+            }
+      }
+    }
+  }
+  if (a.dbg_main && kg == 0) {                 // exact accumulators, for tests
     static_for<TM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int m = m0 + wm * C::WM + j * 32 + l32;
@@ -675,7 +746,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   float sxm[TM];
 #pragma unroll
   for (int j = 0; j < TM; ++j) sxm[j] = s_sx[wm * C::WM + j * 32 + l32] * (1.0f / (1 << C::SHIFT));
-  static_for<TN>([&](auto ic) {
+  if (kg == 0) static_for<TN>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int nt = wn * C::WN + i * 32 + 4 * h;   // first channel (within the tile) of group q = 0
     float4 w4[4], r4[4];
@@ -702,7 +773,9 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   __syncthreads();                              // residual buffers and scales no longer read
 
   // Output tile into LDS, row = token, swizzled 16-byte chunks.
-  if (a.y_bf16) {
+  if (kg > 0) {
+    // the other k-groups only help with the copy-out
+  } else if (a.y_bf16) {
     constexpr int RB = C::BN * 2, SWZ = C::out_swz(2);
     static_for<TM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
@@ -747,20 +820,20 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
     constexpr int CPR = C::BN * EB / 16;      // chunks per tile row
     constexpr int EPC = 16 / EB;              // elements per chunk
     constexpr int RPP = C::NT / CPR;          // rows per pass
-    constexpr int PASSES = C::BM / RPP;
+    constexpr int PASSES = (C::BM + RPP - 1) / RPP;
     const int c = tid % CPR;
     const int n = n0 + c * EPC;
     const bool vec = (a.N % EPC) == 0 && n + EPC <= a.N;
     uint4 v[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const int row = p * RPP + tid / CPR;
+      const int row = min(p * RPP + tid / CPR, C::BM - 1);
       v[p] = *reinterpret_cast<const uint4*>(lds + row * C::BN * EB + 16 * (c ^ (row & C::out_swz(EB))));
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = p * RPP + tid / CPR;
-      if (m0 + row >= a.M) break;
+      if (row >= C::BM || m0 + row >= a.M) break;
       uint4 w = v[p];
       if (EB == 2 && half_swap(row)) w = make_uint4(w.z, w.w, w.x, w.y);
       uint8_t* dst = static_cast<uint8_t*>(a.Y) + (static_cast<size_t>(m0 + row) * a.N + n) * EB;
@@ -1279,16 +1352,16 @@ hipError_t ensure_max_lds(const void* fn, int bytes, std::atomic<uint64_t>& done
   return e;
 }
 
-template <int TN, int TM, int A_BITS, int WGM>
+template <int TN, int TM, int A_BITS, int WGM, int KG>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
-  using C = TileCfg<TN, TM, A_BITS, WGM>;
+  using C = TileCfg<TN, TM, A_BITS, WGM, KG>;
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_tile_kernel<TN, TM, A_BITS, WGM>),
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_tile_kernel<TN, TM, A_BITS, WGM, KG>),
                                 C::LDS_BYTES, lds_set);
   if (e != hipSuccess) return e;
   const int n_tiles = (a.N + C::BN - 1) / C::BN;
   const int m_tiles = (a.M + C::BM - 1) / C::BM;
-  serq_tile_kernel<TN, TM, A_BITS, WGM><<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS_BYTES, st>>>(a, n_tiles);
+  serq_tile_kernel<TN, TM, A_BITS, WGM, KG><<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS_BYTES, st>>>(a, n_tiles);
   return hipGetLastError();
 }
 
@@ -1421,10 +1494,10 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t st) {
 
 template <int A_BITS>
 hipError_t launch_tile_bits(const LinearArgs& a, const LinearPlan& p, hipStream_t st) {
-  if (p.tn == 2 && p.tm == 2 && p.wgm == 2) return launch_tile<2, 2, A_BITS, 2>(a, st);
-  if (p.tn == 2 && p.tm == 1 && p.wgm == 2) return launch_tile<2, 1, A_BITS, 2>(a, st);
-  if (p.tn == 1 && p.tm == 1 && p.wgm == 2) return launch_tile<1, 1, A_BITS, 2>(a, st);
-  if (p.tn == 1 && p.tm == 1 && p.wgm == 1) return launch_tile<1, 1, A_BITS, 1>(a, st);
+  if (p.tn == 2 && p.tm == 2 && p.wgm == 2 && p.kg == 1) return launch_tile<2, 2, A_BITS, 2, 1>(a, st);
+  if (p.tn == 2 && p.tm == 1 && p.wgm == 2 && p.kg == 1) return launch_tile<2, 1, A_BITS, 2, 1>(a, st);
+  if (p.tn == 1 && p.tm == 1 && p.wgm == 2 && p.kg == 1) return launch_tile<1, 1, A_BITS, 2, 1>(a, st);
+  if (p.tn == 1 && p.tm == 1 && p.wgm == 1 && p.kg == 4) return launch_tile<1, 1, A_BITS, 1, 4>(a, st);
   return hipErrorInvalidValue;
 }
 
@@ -1435,26 +1508,31 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   const bool small = static_cast<uint64_t>(N) * (K / 2) < (1ull << 32) &&
                      static_cast<uint64_t>(M) * K * a_bits / 8 < (1ull << 32);
   const bool fast = (K % 32 == 0) && (r % 8 == 0) && r <= kMaxResidual && small;
-  if (!fast) return {LinearKernel::kGeneric, 0, 0, 0, "generic"};
+  if (!fast) return {LinearKernel::kGeneric, 0, 0, 0, 1, "generic"};
   // A few tokens of W4A4 whose activation rows fit in LDS: int4 dot products.
   if (a_bits == 4 && M <= kGemvMaxTokens && static_cast<long>(M) * (K / 2) <= kGemvMaxX)
-    return {LinearKernel::kGemv, 0, 0, 0, "gemv"};
-  if (M <= 16) return {LinearKernel::kDecode16, 0, 0, 0, "decode16"};
-  if (M <= 32) return {LinearKernel::kDecode32, 0, 0, 0, "decode32"};
+    return {LinearKernel::kGemv, 0, 0, 0, 1, "gemv"};
+  if (M <= 16) return {LinearKernel::kDecode16, 0, 0, 0, 1, "decode16"};
+  if (M <= 32) return {LinearKernel::kDecode32, 0, 0, 0, 1, "decode32"};
   // Macro tiles, two four-wave workgroups per CU: the two run independently,
   // so one's barrier and load waits are covered by the other's MFMAs. (One
   // eight-wave 256 x 128 workgroup per CU, lockstep at every k-tile barrier,
   // measured 12-20 % slower on the LLaMA shapes.) The largest tile that still
   // gives every CU a workgroup; smaller tiles keep more k-tiles in flight.
   auto tiles = [&](int bm, int bn) { return static_cast<long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (M > 64 && tiles(128, 128) >= kCUs) return {LinearKernel::kTile, 2, 2, 2, "tile128x128"};
-  if (tiles(64, 128) >= kCUs) return {LinearKernel::kTile, 2, 1, 2, "tile64x128"};
-  // When 64 x 64 tiles would leave half the CUs idle, 32 x 64 tiles of two
-  // waves (up to four per CU): every CU gets work, at twice the weight
-  // traffic into LDS (measured 1.1-1.15x faster at 128 tokens of 4096 x 4096
-  // and 14336 x 4096, slower from 192 tokens on).
-  if (tiles(64, 64) <= kCUs / 2) return {LinearKernel::kTile, 1, 1, 1, "tile32x64"};
-  return {LinearKernel::kTile, 1, 1, 2, "tile64x64"};
+  if (M > 64 && tiles(128, 128) >= kCUs) return {LinearKernel::kTile, 2, 2, 2, 1, "tile128x128"};
+  if (tiles(64, 128) >= kCUs) return {LinearKernel::kTile, 2, 1, 2, 1, "tile64x128"};
+  // When 64 x 64 tiles would leave half the CUs idle, 32 x 64 tiles whose
+  // eight waves form four k-groups (each a k-tile of every four-k-tile
+  // stage): every CU gets work and all four SIMDs of a CU share one tile's
+  // k-loop, at twice the weight traffic into LDS (measured 1.1x faster than
+  // 64 x 64 at 40-128 tokens of 4096 x 4096, 1.25x on 14336 x 4096; four
+  // k-groups beat one two-wave group per tile by the same margins). Two
+  // k-groups of 64 x 64 tiles measured slower than one wherever 64 x 64
+  // tiles fill the CUs (one eight-wave workgroup per CU against two
+  // four-wave ones).
+  if (tiles(64, 64) <= kCUs / 2) return {LinearKernel::kTile, 1, 1, 1, 4, "tile32x64k4"};
+  return {LinearKernel::kTile, 1, 1, 2, 1, "tile64x64"};
 }
 
 hipError_t launch_linear(const LinearArgs& a, const LinearPlan& p, hipStream_t st) {

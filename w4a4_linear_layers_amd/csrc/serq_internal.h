@@ -33,7 +33,8 @@ enum class LinearKernel { kGemv, kDecode16, kDecode32, kTile, kGeneric };
 struct LinearPlan {
   LinearKernel kind;
   int tn, tm;          // per-wave 32x32 block counts (kTile only)
-  int wgm;             // wave rows (token direction) per workgroup (kTile only)
+  int wgm;             // wave rows (token direction) per k-group (kTile only)
+  int kg;              // k-groups per workgroup, each a k-tile of every stage (kTile only)
   const char* name;
 };
 
