@@ -257,7 +257,7 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(384, 4096, 4096, 64) == "tile64x64"         # 384 tiles of 64 x 64
     assert S.kernel_name(40, 4096, 28672, 128) == "tile64x64"        # 448 tiles of 64 x 64
     assert S.kernel_name(64, 4096, 32768, 64) == "tile64x128"        # 256 tiles of 64 x 128
-    assert S.kernel_name(768, 4096, 4096, 64) == "tile64x128"        # 192 tiles of 128 x 128 would be too few
+    assert S.kernel_name(768, 4096, 4096, 64) == "tile128x128k2"     # 192 tiles of 128 x 128: two k-groups
     assert S.kernel_name(1024, 4096, 4096, 64) == "tile128x128"
     assert S.kernel_name(64, 4096, 4096, 64) == "tile32x64k4"
     assert S.kernel_name(16, 4100, 64, 8) == "generic"      # K % 32 != 0

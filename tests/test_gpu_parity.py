@@ -242,6 +242,8 @@ LINEAR_CASES = [
     (300, 544, 4000, 40, "tile64x64"),        # ragged M, N and K
     (60, 1056, 32800, 72, "tile64x128"),      # ragged M and N
     (100, 288, 16400, 128, "tile64x128"),
+    (100, 288, 24600, 128, "tile128x128k2"),  # two k-groups of 128 x 128, a ragged stage
+    (130, 4160, 12400, 256, "tile128x128k2"), # an odd number of k-tiles, two residual k-tiles
     (200, 256, 32768, 64, "tile128x128"),     # many workgroups
     (300, 288, 32768, 128, "tile128x128"),    # K not a multiple of the k-tile, ragged M
     (520, 1056, 16400, 72, "tile128x128"),    # ragged M and N, r % 32 != 0

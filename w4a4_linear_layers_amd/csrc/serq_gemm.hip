@@ -1495,6 +1495,7 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t st) {
 template <int A_BITS>
 hipError_t launch_tile_bits(const LinearArgs& a, const LinearPlan& p, hipStream_t st) {
   if (p.tn == 2 && p.tm == 2 && p.wgm == 2 && p.kg == 1) return launch_tile<2, 2, A_BITS, 2, 1>(a, st);
+  if (p.tn == 2 && p.tm == 2 && p.wgm == 2 && p.kg == 2) return launch_tile<2, 2, A_BITS, 2, 2>(a, st);
   if (p.tn == 2 && p.tm == 1 && p.wgm == 2 && p.kg == 1) return launch_tile<2, 1, A_BITS, 2, 1>(a, st);
   if (p.tn == 1 && p.tm == 1 && p.wgm == 2 && p.kg == 1) return launch_tile<1, 1, A_BITS, 2, 1>(a, st);
   if (p.tn == 1 && p.tm == 1 && p.wgm == 1 && p.kg == 4) return launch_tile<1, 1, A_BITS, 1, 4>(a, st);
@@ -1522,6 +1523,11 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   // gives every CU a workgroup; smaller tiles keep more k-tiles in flight.
   auto tiles = [&](int bm, int bn) { return static_cast<long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (M > 64 && tiles(128, 128) >= kCUs) return {LinearKernel::kTile, 2, 2, 2, 1, "tile128x128"};
+  // Three quarters of the CUs or more with one 128 x 128 tile each: two
+  // k-groups of four waves per tile, one eight-wave workgroup per CU
+  // (1.1-1.2x on 4096 x 28672, 8192 x 28672 at 65-128 tokens and on
+  // 4096 x 4096 at 768; with half the CUs it lost to the 64-row tiles).
+  if (M > 64 && tiles(128, 128) >= 3 * kCUs / 4) return {LinearKernel::kTile, 2, 2, 2, 2, "tile128x128k2"};
   if (tiles(64, 128) >= kCUs) return {LinearKernel::kTile, 2, 1, 2, 1, "tile64x128"};
   // When 64 x 64 tiles would leave half the CUs idle, 32 x 64 tiles whose
   // eight waves form four k-groups (each a k-tile of every four-k-tile
