@@ -232,6 +232,84 @@ def time_mlp_act(K, Ms, n=100, a_bits=4, seed=0):
     return out
 
 
+def time_mlp_step(Ms, n=50, seed=0):
+    """The whole LLaMA-3-8B MLP on the path, per step: quant_act of x ->
+    gate/up as one 4096 -> 2 x 14336 layer whose output channels carry
+    down's input order (serq_permute_outputs) -> serq_silu_mul_quant_act on
+    its bf16 output read in place -> down 14336 -> 4096. W4A4, r = 128,
+    seeded synthetic weights, the layer pair rotated over >= 768 MiB of
+    copies; n steps captured in one graph, timed with events."""
+    import numpy as np
+    import torch
+
+    import w4a4_linear_layers_amd as S
+    from synth import workload_layer
+
+    M_max = max(Ms)
+    gu = workload_layer("mlp8b", "gate_up", M_max=M_max, seed=seed)
+    dn = workload_layer("mlp8b", "down", M_max=1, seed=seed, draw_x=False)
+    Ni = gu.N
+    Lg = S.calibrate(np.concatenate([gu.W_bits, gu.meta["W_up_bits"]], axis=1), gu.act_absmax, r=128)
+    Ld = S.calibrate(dn.W_bits, dn.act_absmax, r=128)
+    S.permute_outputs(Lg, np.concatenate([Ld.perm, Ni + Ld.perm]))
+    dev = torch.device("cuda")
+    per = Lg.Wq.nbytes + Lg.Rq.nbytes + Ld.Wq.nbytes + Ld.Rq.nbytes
+    copies = max(2, math.ceil(ROTATE_BYTES / per))
+    G0, D0 = Lg.to(dev), Ld.to(dev)
+
+    def clone(L):
+        return S.DeviceLayer(K=L.K, N=L.N, r=L.r, perm=L.perm, s_hat_inv=L.s_hat_inv, Wq=L.Wq.clone(),
+                             sw=L.sw.clone(), Rq=L.Rq.clone(), sr=L.sr.clone())
+
+    pairs = [(clone(G0), clone(D0)) for _ in range(copies)]
+    x = torch.from_numpy(np.ascontiguousarray(gu.X_bits[:, Lg.perm]).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = []
+    for M in Ms:
+        xq = torch.empty((M, gu.K // 2), dtype=torch.uint8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        y = torch.empty((M, 2 * Ni), dtype=torch.bfloat16, device=dev)
+        hq = torch.empty((M, Ni // 2), dtype=torch.uint8, device=dev)
+        hs = torch.empty(M, dtype=torch.float32, device=dev)
+        yd = torch.empty((M, dn.N), dtype=torch.bfloat16, device=dev)
+        parts = {
+            "quant_act": lambda i: S.quant_act(x[:M], pairs[i % copies][0], out=(xq, sx)),
+            "gate_up": lambda i: S.linear(xq, sx, pairs[i % copies][0], out=y),
+            "silu_mul_quant_act": lambda i: S.silu_mul_quant_act(y[:, :Ni], y[:, Ni:], pairs[i % copies][1],
+                                                                 out=(hq, hs)),
+            "down": lambda i: S.linear(hq, hs, pairs[i % copies][1], out=yd),
+        }
+
+        def step(i):
+            for f in parts.values():
+                f(i)
+
+        def timed(fn):
+            fn(0)                      # outside the capture: first-call set-up
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            g.replay()
+            e1.record(st)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        step_us = timed(step)
+        e = dict(M=M, step_us=round(step_us, 2))
+        for k, f in parts.items():
+            step(0)                    # the buffers every part reads hold one real step's data
+            e[k + "_us"] = round(timed(f), 2)
+        e["kernels"] = [S.kernel_name(M, gu.K, 2 * Ni, 128), S.kernel_name(M, Ni, dn.N, 128)]
+        out.append(e)
+    return out
+
+
 def cpu_baseline(setup, M, rows=None, budget_s=20.0):
     """The CPU oracle as it stands, on a bounded row sample of the workload:
     activation quantization + int64 matmuls + fp64 epilogue. Rows are
@@ -383,6 +461,14 @@ def main(argv=None):
                 print(f"# silu_mul_quant_act K={e['K']} M={e['M']}: {e['us']:.2f} us {e['HBM_GBs']:.0f} GB/s "
                       f"(unfused {e['unfused_us']:.2f} us)", file=sys.stderr, flush=True)
 
+    mlp_step = []
+    if not args.no_sweep and not args.no_mlp_act:
+        mlp_step = time_mlp_step((1, 16, 256, 4096))
+        for e in mlp_step:
+            print(f"# mlp step M={e['M']}: {e['step_us']:.1f} us (quant_act {e['quant_act_us']:.1f}, gate/up "
+                  f"{e['gate_up_us']:.1f}, silu_mul_quant_act {e['silu_mul_quant_act_us']:.1f}, down "
+                  f"{e['down_us']:.1f})", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(setup, M)
@@ -402,6 +488,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "sweep": sweep,
         "mlp_activation": mlp_act,
+        "mlp_step": mlp_step,
     }
     print(json.dumps(out), flush=True)
     return 0
