@@ -252,8 +252,9 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x128"
     assert S.kernel_name(65, 4096, 4096, 64) == "tile32x64k4"          # 128 tiles of 64 x 64: half the CUs
     assert S.kernel_name(128, 14336, 4096, 128) == "tile32x64k4"
-    assert S.kernel_name(129, 4096, 4096, 64) == "tile64x64k4"       # 192 tiles of 64 x 64
-    assert S.kernel_name(256, 4096, 4096, 64) == "tile64x64k4"       # 256 tiles of 64 x 64
+    assert S.kernel_name(129, 14336, 4096, 64) == "tile64x64k4"      # 192 tiles of 64 x 64, long K
+    assert S.kernel_name(256, 14336, 4096, 64) == "tile64x64k4"      # 256 tiles of 64 x 64, long K
+    assert S.kernel_name(256, 4096, 4096, 64) == "tile64x64"         # 32 k-tiles: one group
     assert S.kernel_name(384, 4096, 4096, 64) == "tile64x64"         # 384 tiles of 64 x 64
     assert S.kernel_name(40, 4096, 28672, 128) == "tile64x64"        # 448 tiles of 64 x 64
     assert S.kernel_name(64, 4096, 32768, 64) == "tile64x128"        # 256 tiles of 64 x 128

@@ -237,8 +237,10 @@ LINEAR_CASES = [
     (100, 512, 300, 64, "tile32x64k4"),
     (129, 800, 258, 8, "tile32x64k4"),
     (128, 4096, 4096, 64, "tile32x64k4"),       # deep pipeline, 32-token tiles
-    (256, 4096, 4096, 64, "tile64x64k4"),     # deep pipeline, one workgroup per CU
-    (200, 1056, 2600, 72, "tile64x64k4"),     # ragged M and N
+    (256, 4096, 4096, 64, "tile64x64"),       # deep pipeline, one workgroup per CU
+    (256, 8192, 4096, 64, "tile64x64k4"),     # four k-groups of two 32 x 64 waves
+    (200, 8224, 2600, 72, "tile64x64k4"),     # ragged M, N and K
+    (200, 1056, 2600, 72, "tile64x64"),       # ragged M and N
     (300, 544, 4000, 40, "tile64x64"),        # ragged M, N and K
     (60, 1056, 32800, 72, "tile64x128"),      # ragged M and N
     (100, 288, 16400, 128, "tile64x128"),

@@ -1539,9 +1539,12 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   // tiles fill the CUs (one eight-wave workgroup per CU against two
   // four-wave ones).
   if (tiles(64, 64) <= kCUs / 2) return {LinearKernel::kTile, 1, 1, 1, 4, "tile32x64k4"};
-  // Up to one 64 x 64 tile per CU: two waves of 32 x 64 per k-group, four
-  // k-groups (1.12x on 14336 x 4096 at 192-256 tokens, even on 4096 x 4096).
-  if (tiles(64, 64) <= kCUs) return {LinearKernel::kTile, 1, 2, 1, 4, "tile64x64k4"};
+  // Up to one 64 x 64 tile per CU and K of 64 k-tiles or more: two waves of
+  // 32 x 64 per k-group, four k-groups (1.12x on 14336 x 4096 at 192-256
+  // tokens; with K = 4096 its eight four-k-tile stages left it even or a
+  // few % behind the single group).
+  if (tiles(64, 64) <= kCUs && K >= 64 * kKTileCodes)
+    return {LinearKernel::kTile, 1, 2, 1, 4, "tile64x64k4"};
   return {LinearKernel::kTile, 1, 1, 2, 1, "tile64x64"};
 }
 
