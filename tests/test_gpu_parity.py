@@ -133,6 +133,22 @@ def test_silu_mul_quant_act_bit_exact(M, K, layout, dtype, bits):
     assert np.array_equal(got, ref["packed"].view(np.uint8)), np.argwhere(got != ref["packed"].view(np.uint8))[:5]
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("M,K", [(4096, 14336), (16, 28672)])
+def test_silu_mul_quant_act_full_size(M, K):
+    """The benchmark's launch configuration (a bf16 gate/up output M x 2K read
+    in place), codes and scales of sampled rows (always the first and last;
+    rows are independent) against the oracle."""
+    G, U, g, u = _gate_up_input(M, K, "bf16", "cat", seed=K + M)
+    sinv = np.exp(np.random.default_rng(5).uniform(-2, 1, K)).astype(np.float32)
+    xq, sx = S.silu_mul_quant_act(g, u, dev(sinv), a_bits=4)
+    _sync()
+    rows = sample(M, 48, 7)
+    ref = O.silu_mul_quant_act(G[rows], U[rows], sinv, 4)
+    assert np.array_equal(host(sx)[rows].view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(host(xq)[rows].view(np.uint8), ref["packed"].view(np.uint8))
+
+
 def test_silu_mul_quant_act_empty_and_bad_arguments():
     sinv = torch.ones(64, device="cuda")
     xq = torch.full((0, 32), 7, dtype=torch.uint8, device="cuda")
