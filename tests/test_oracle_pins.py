@@ -6,6 +6,8 @@ least one pin must then fail: a dropped term, a wrong sign, a wrong index, a
 transposed or inverted permutation, a wrong rounding rule or a wrong scale.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -182,3 +184,22 @@ def test_mutant_is_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught.append(check.__name__)
     assert caught, f"no pin catches mutant {name}"
+
+
+def test_worked_layer_fixture_is_the_exact_derivation():
+    """The worked 4 x 2 layer fixture equals its exact-rational derivation
+    (tests/golden/derive_worked_layer.py, independent of the oracle), value
+    for value."""
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "derive_worked_layer.py")
+    spec = importlib.util.spec_from_file_location("derive_worked_layer", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    fx = mod.load_fixture()
+    got = mod.derive(fx["inputs"])
+
+    def flat(v):
+        return [float(x) for x in np.ravel(np.array(v, dtype=object))]
+
+    for k, v in got.items():
+        assert flat(v) == flat(fx["expected"][k]), k
