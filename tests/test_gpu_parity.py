@@ -56,7 +56,8 @@ def _act_input(M, K, dtype, seed):
                                  (3, 40000), (1, 2), (64, 8),
                                  (600, 1000), (1030, 4096), (520, 8192),     # several rows per workgroup
                                  (2, 70000), (128, 14336), (129, 14336),     # chunked rows (few rows, long K)
-                                 (520, 40000), (513, 4096), (512, 4104)])    # 512 or 256 lanes per row
+                                 (520, 40000), (513, 4096), (512, 4104),     # 1024, 256 or 512 lanes per row
+                                 (600, 20000)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_quant_act_bit_exact(M, K, dtype, bits):

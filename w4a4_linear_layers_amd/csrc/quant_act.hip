@@ -346,8 +346,10 @@ hipError_t launch_rows(RowSrc<T, ACT> src, int M, int K, const float* sinv, uint
     quant_act_rows<T, A_BITS, 4, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
   } else if (passes <= 8) {
     quant_act_rows<T, A_BITS, 8, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
-  } else {
+  } else if constexpr (NT < 1024) {       // 1024 lanes hold at most 8 passes in their registers
     quant_act_rows<T, A_BITS, 16, ACT, NT><<<grid, block, 0, st>>>(src, sinv, K, Xq, sx);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -361,7 +363,11 @@ hipError_t launch_typed(RowSrc<T, ACT> src, int M, int K, const float* sinv, uin
   if (aligned && use_split<ACT>(M, K)) return launch_split<T, A_BITS, ACT>(src, M, K, sinv, Xq, sx, st);
   // 512 lanes per row while the rows are few or long (more waves in flight
   // per row, fewer values per lane; measured 1.3x at 256 rows of 14336),
-  // 256 for many short rows (more rows resident per CU).
+  // 1024 for many rows beyond 16384 (1.05-1.15x at 1024-4096 rows of 28672;
+  // at 14336 it was slower), 256 for many short rows (more rows resident
+  // per CU).
+  if (aligned && M > 512 && K > 16384 && K <= 8 * 1024 * kVec)
+    return launch_rows<T, A_BITS, ACT, 1024>(src, M, K, sinv, Xq, sx, st);
   if (aligned && K <= 16 * 512 * kVec && (M <= 512 || K > 8192))
     return launch_rows<T, A_BITS, ACT, 512>(src, M, K, sinv, Xq, sx, st);
   if (aligned && K <= 16 * kThreads * kVec) return launch_rows<T, A_BITS, ACT, kThreads>(src, M, K, sinv, Xq, sx, st);
