@@ -20,6 +20,13 @@ synchronizations, so the measurement is not bound by Python launch overhead.
 
 Prints one JSON line. `value` is whole-job throughput in TOP/s:
 2 * M * N * (K + r) integer operations per step / measured step time.
+`roofline` is the dominant kernel (serq_linear) against the dense int8 MFMA
+or the HBM peak, with the counter-measured bytes per launch when they were
+taken on the current kernel sources. Beside the headline: "mlp_activation"
+(serq_silu_mul_quant_act on bf16 gate/up outputs of the 8B and 70B MLP
+widths, with the unfused pair for comparison), "mlp_step" (the whole 8B MLP:
+quant_act, gate/up, the fused activation, down) and "cpu_baseline" (the
+oracle on a bounded row sample).
 """
 
 from __future__ import annotations
