@@ -544,10 +544,14 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   };
   // The four MFMA steps of one k-tile, software-pipelined: the widening for
   // step s + 1 is issued between the MFMAs of step s, so the VALU work runs
-  // while the matrix core is busy.
+  // while the matrix core is busy. With one k-group the wave raises its issue
+  // priority for the k-tile's MFMA sequence, so that of the two waves on a
+  // SIMD the one feeding the matrix core goes first (2-3 % on the prefill
+  // shapes; it did not help the four-k-group tiles).
   auto compute = [&](const Frags& f, v16i (&acc)[AS][TN][TM]) {
     v4i wa[TN], xb[TM];
     unpack(f, 0, wa, xb);
+    if constexpr (KG == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v4i wn2[TN], xn2[TM];
@@ -569,6 +573,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
         for (int j = 0; j < TM; ++j) xb[j] = xn2[j];
       }
     }
+    if constexpr (KG == 1) __builtin_amdgcn_s_setprio(0);
   };
   // One k-tile: publish k-tile kt + 1 (own loads done, then a barrier), reuse
   // the buffer of k-tile kt -- its fragments are already in registers -- for
