@@ -544,14 +544,16 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   };
   // The four MFMA steps of one k-tile, software-pipelined: the widening for
   // step s + 1 is issued between the MFMAs of step s, so the VALU work runs
-  // while the matrix core is busy. With one k-group the wave raises its issue
-  // priority for the k-tile's MFMA sequence, so that of the two waves on a
-  // SIMD the one feeding the matrix core goes first (2-3 % on the prefill
-  // shapes; it did not help the four-k-group tiles).
+  // while the matrix core is busy. The wave raises its issue priority for the
+  // k-tile's MFMA sequence, so that of the two waves on a SIMD the one feeding
+  // the matrix core goes first: 2-3 % on the one-k-group prefill tiles, 3-7 %
+  // on the 64x64 four-k-group tile; on the 32x64 four-k-group tile and the
+  // two-k-group 128x128 tile it cost 1-2 %, so those leave it alone.
+  static constexpr bool kRaisePrio = KG == 1 || (KG == 4 && TM == 2);
   auto compute = [&](const Frags& f, v16i (&acc)[AS][TN][TM]) {
     v4i wa[TN], xb[TM];
     unpack(f, 0, wa, xb);
-    if constexpr (KG == 1) __builtin_amdgcn_s_setprio(1);
+    if constexpr (kRaisePrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       v4i wn2[TN], xn2[TM];
@@ -573,7 +575,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
         for (int j = 0; j < TM; ++j) xb[j] = xn2[j];
       }
     }
-    if constexpr (KG == 1) __builtin_amdgcn_s_setprio(0);
+    if constexpr (kRaisePrio) __builtin_amdgcn_s_setprio(0);
   };
   // One k-tile: publish k-tile kt + 1 (own loads done, then a barrier), reuse
   // the buffer of k-tile kt -- its fragments are already in registers -- for
