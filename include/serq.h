@@ -40,6 +40,7 @@
 #ifndef SERQ_H_
 #define SERQ_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -238,6 +239,90 @@ int serq_linear(const void* Xq, const float* sx, int a_bits,
  * for invalid sizes. Host only; launches nothing. For profiling and tests.
  */
 const char* serq_linear_kernel_name(int M, int K, int N, int r, int a_bits);
+
+/*
+ * The same linear on gfx950's scaled FP6 matrix instruction (bf6 route).
+ *
+ * The pages run SERQ on integer or microscaling-FP4 matrix hardware alike
+ * (gist.science/de/paper/2603.08185, "3. Wichtige Beiträge": the method is
+ * compatible with INT4 and MXFP4 formats; "4. Ergebnisse", Performance &
+ * Latenz: the fast path is the hardware FP4 product, the residual adding
+ * about 1 %). CDNA4 has no int4 matrix instruction, but every int4 code in
+ * [-8, 7] is exactly a bf6 (E3M2) value, and a product of two such codes
+ * summed in fp32 stays an exact integer while |sum| <= 2^24, i.e. for K up to
+ * 2^18. So this route computes bit for bit the accumulators of serq_linear
+ * (W4A4 only) at the FP6 instruction rate, on operands re-encoded as bf6:
+ *
+ * bf6 tile layout of a matrix of `rows` x `k` int4 codes. Rows are padded
+ * with zero codes to a multiple of 128 (Rp) and k to a multiple of 128 (Kp).
+ * The buffer is a sequence of 3072-byte fragment blocks, block (kt, rb) at
+ * byte ((kt * Rp / 32) + rb) * 3072 for k-tile kt (codes [128 kt, +128)) and
+ * 32-row block rb; inside a block, step s (0, 1) at +1536 s and lane l
+ * (0..63) at +24 l hold the 32 codes of row 32 rb + l % 32 at
+ * k = 128 kt + 64 s + 32 (l / 32) + f, f = 0..31, each as the 6-bit E3M2
+ * pattern (sign bit 5, exponent bits 4..2 with bias 3, mantissa bits 1..0)
+ * in bits [6 f, 6 f + 6) of the 24 bytes read as one little-endian 192-bit
+ * integer. Code -> pattern: 0 -> 0x00, 1 -> 0x0C, 2 -> 0x10, 3 -> 0x12,
+ * 4 -> 0x14, 5 -> 0x15, 6 -> 0x16, 7 -> 0x17, and -v -> 0x20 | pattern(v),
+ * -8 -> 0x38. Size: SERQ_BF6_BYTES(rows, k) bytes.
+ */
+#define SERQ_BF6_BYTES(rows, k) ((size_t)(((k) + 127) / 128) * (size_t)(((rows) + 127) / 128) * 12288u)
+
+/* SERQ_BF6_BYTES as a function; returns -1 for rows < 0 or k < 0. */
+int64_t serq_bf6_bytes(int rows, int k);
+
+/*
+ * serq_prepack_bf6 -- offline, host memory, synchronous.
+ *
+ * Re-encodes a packed int4 matrix (serq_calibrate's Q(W^) with k = K and
+ * pitch = K/2, or Q(R) with k = r and pitch = SERQ_RQ_ROW_BYTES(r)) into the
+ * bf6 tile layout, writing every byte of `out` (padding included).
+ *   codes  rows x pitch bytes, canonical nibble order (host).
+ *   rows, k, pitch  rows > 0, 0 < k <= 2 * pitch, k even.
+ *   out    SERQ_BF6_BYTES(rows, k) bytes (host), caller-owned.
+ * Errors: SERQ_EINVAL (NULL pointer, bad sizes).
+ */
+int serq_prepack_bf6(const uint8_t* codes, int rows, int k, int pitch, uint8_t* out);
+
+/*
+ * serq_act_bf6 -- online, device memory, asynchronous on `stream`.
+ *
+ * Re-encodes W4A4 activation codes (serq_quant_act's Xq, M x K/2 bytes) into
+ * the bf6 tile layout, padding included, for serq_linear_bf6. The token
+ * scales sx are used as they are.
+ *   Xq   device, M x K/2 bytes, 16-byte aligned.
+ *   M, K M >= 0 (0: no-op), K > 0 even, K <= 262144.
+ *   X6   device, SERQ_BF6_BYTES(M, K) bytes, 16-byte aligned.
+ * Errors: SERQ_EINVAL, SERQ_EALIGN, SERQ_EHIP.
+ */
+int serq_act_bf6(const void* Xq, int M, int K, void* X6, void* stream);
+
+/*
+ * serq_linear_bf6 -- online, device memory, asynchronous on `stream`.
+ *
+ * serq_linear (W4A4) on bf6 operands: the same acc_main, acc_res (exact
+ * integers) and the same fp32 epilogue, so Y and the debug accumulators are
+ * bit-identical to serq_linear's on the same codes.
+ *   X6         SERQ_BF6_BYTES(M, K) bytes from serq_act_bf6 (device).
+ *   sx         M floats from serq_quant_act (device).
+ *   W6, sw     SERQ_BF6_BYTES(N, K) bytes from serq_prepack_bf6 of Q(W^),
+ *              and N floats (device).
+ *   R6, sr     SERQ_BF6_BYTES(N, r) bytes from serq_prepack_bf6 of Q(R),
+ *              and N floats (device); may be NULL when r == 0.
+ *   M, K, N, r M >= 0 (0: no-op), K > 0 even, K <= 262144, N > 0,
+ *              0 <= r <= min(K, 256), r even.
+ *   Y, y_dtype, acc_main_dbg, acc_res_dbg  as for serq_linear.
+ * Uses no scratch memory. Errors: SERQ_EINVAL (NULL pointer, bad sizes or
+ * dtype, only one debug buffer), SERQ_EALIGN (pointer not 16-byte aligned),
+ * SERQ_EHIP.
+ */
+int serq_linear_bf6(const void* X6, const float* sx,
+                    const uint8_t* W6, const float* sw,
+                    const uint8_t* R6, const float* sr,
+                    int M, int K, int N, int r,
+                    void* Y, serq_dtype y_dtype,
+                    int32_t* acc_main_dbg, int32_t* acc_res_dbg,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ import torch
 
 import w4a4_linear_layers_amd as S
 from gpu_helpers import bf16_tensor, check_y, dev, host, sample
-from layouts import pack_rq, pad_rq
+from layouts import bf6_decode, pack_rq, pad_rq, rq_row_bytes
 from oracle import serq_oracle as O
 from synth import random_codes, round_to_bf16_bits, workload_layer
 
@@ -478,3 +478,112 @@ def test_mlp8b_fused_activation_chain():
     am_ref, ar_ref = O.linear_int(q["codes"], R["Wq_codes"], R["Rq_codes"], 128)
     assert np.array_equal(host(am)[:, cols], am_ref) and np.array_equal(host(ar)[:, cols], ar_ref)
     check_y(host(yd)[:, cols], am_ref, ar_ref, q["sx"], R["sw"], R["sr"], "bf16")
+
+
+# ------------------------------------------------------------- the bf6 route
+
+@pytest.mark.parametrize("M,K", [(1, 2), (5, 30), (37, 320), (130, 1000), (129, 256), (300, 4096), (64, 96)])
+def test_act_bf6_layout(M, K):
+    """serq_act_bf6 against the header's layout (independent reader) and
+    against the host prepack of the same codes, byte for byte."""
+    rng = np.random.default_rng(M * 3 + K)
+    c = random_codes(rng, (M, K), 4)
+    c.flat[:16] = np.arange(-8, 8)[: min(16, c.size)]
+    packed = O.pack_int4(c)
+    x6 = S.act_bf6(dev(packed), K)
+    _sync()
+    got = host(x6)
+    assert got.size == S.bf6_bytes(M, K)
+    assert np.array_equal(got, S._prepack(packed, M, K, K // 2))
+    full, codes = bf6_decode(got, M, K)
+    assert np.array_equal(codes, c)
+    full[:M, :K] = 0
+    assert not full.any()
+
+
+def _bf6_layer(Wc, Rc, sw, sr, K, N, r):
+    W6 = S._prepack(O.pack_int4(Wc.T), N, K, K // 2)
+    R6 = S._prepack(pack_rq(Rc), N, r, rq_row_bytes(r)) if r else np.zeros(0, np.uint8)
+    return S.Bf6Layer(K=K, N=N, r=r, W6=dev(W6), sw=dev(sw), R6=dev(R6), sr=dev(sr))
+
+
+BF6_CASES = [
+    # M, K, N, r
+    (1, 256, 128, 64),
+    (37, 320, 200, 72),        # K % 128 != 0, ragged M and N, r % 32 != 0
+    (130, 1000, 260, 40),      # K % 32 != 0 (the element-wise activation path)
+    (64, 96, 256, 96),         # K shorter than one k-tile, r = K
+    (200, 4160, 1000, 256),    # an odd number of k-tiles, two residual k-tiles
+    (256, 1056, 300, 0),       # r = 0
+    (513, 2048, 640, 130),     # two residual k-tiles, the second nearly empty
+    (128, 4096, 4096, 64),
+    (300, 8192, 1000, 128),
+]
+
+
+@pytest.mark.parametrize("M,K,N,r", BF6_CASES, ids=[f"{c[0]}x{c[1]}x{c[2]}r{c[3]}" for c in BF6_CASES])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_linear_bf6_bit_exact(M, K, N, r, out):
+    """The bf6 route: exact integer accumulators against the oracle, Y within
+    the epilogue tolerance, and Y bit-identical to serq_linear's."""
+    Xc, Wc, Rc, sx, sw, sr, Xq, layer = _codes_case(M, K, N, r, 4, seed=M + K + N + r + 6)
+    L6 = _bf6_layer(Wc, Rc, sw, sr, K, N, r)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    xq_d, sx_d = dev(Xq), dev(sx)
+    x6 = S.act_bf6(xq_d, K)
+    y, am, ar = S.linear_bf6(x6, sx_d, L6, out_dtype=odt, debug=True)
+    y_int = S.linear(xq_d, sx_d, layer, a_bits=4, out_dtype=odt)
+    _sync()
+    cols = np.arange(N) if N <= 2048 else sample(N, 512, M)
+    am_ref, ar_ref = O.linear_int(Xc, Wc[:, cols], Rc[:, cols], r)
+    am_g, ar_g = host(am)[:, cols], host(ar)[:, cols]
+    assert np.array_equal(am_g, am_ref), np.argwhere(am_g != am_ref)[:5]
+    assert np.array_equal(ar_g, ar_ref), np.argwhere(ar_g != ar_ref)[:5]
+    check_y(host(y)[:, cols], am_ref, ar_ref, sx, sw[cols], sr[cols], out)
+    assert np.array_equal(host(y), host(y_int))
+
+
+def test_linear_bf6_extreme_codes_and_empty():
+    """All codes -8 over K = 4096 (+ r = 256): the largest sums, exact in fp32."""
+    M, K, N, r = 48, 4096, 64, 256
+    Xc = np.full((M, K), -8, np.int8)
+    Wc = np.full((K, N), -8, np.int8)
+    Rc = np.full((r, N), -8, np.int8)
+    sx = np.ones(M, np.float32)
+    sw = np.full(N, 2.0 ** -10, np.float32)
+    sr = np.full(N, 2.0 ** -12, np.float32)
+    L6 = _bf6_layer(Wc, Rc, sw, sr, K, N, r)
+    x6 = S.act_bf6(dev(O.pack_int4(Xc)), K)
+    y, am, ar = S.linear_bf6(x6, dev(sx), L6, out_dtype=torch.float32, debug=True)
+    _sync()
+    am_ref, ar_ref = O.linear_int(Xc, Wc, Rc, r)
+    assert np.array_equal(host(am), am_ref) and np.array_equal(host(ar), ar_ref)
+    check_y(host(y), am_ref, ar_ref, sx, sw, sr, "f32")
+    e6 = S.act_bf6(torch.empty((0, K // 2), dtype=torch.uint8, device="cuda"), K)
+    y0 = S.linear_bf6(e6, torch.empty(0, dtype=torch.float32, device="cuda"), L6)
+    _sync()
+    assert e6.numel() == 0 and y0.shape == (0, N)
+
+
+@pytest.mark.slow
+def test_workload_q_proj_bf6():
+    """q_proj at 2048 tokens (the benchmark's launch): calibrated layer, GPU
+    quant_act, then the bf6 route against serq_linear bit for bit and the
+    oracle's accumulators on sampled columns."""
+    li = workload_layer("q_proj", "q_proj")
+    L = S.calibrate(li.W_bits, li.act_absmax, r=64)
+    D = L.to("cuda")
+    B = S.prepack_bf6(L).to("cuda")
+    M = 2048
+    xq, sx = S.quant_act(bf16_tensor(li.X_bits[:M][:, L.perm]), D, a_bits=4)
+    x6 = S.act_bf6(xq, L.K)
+    y6, am, ar = S.linear_bf6(x6, sx, B, debug=True)
+    y = S.linear(xq, sx, D, a_bits=4)
+    _sync()
+    assert np.array_equal(host(y6), host(y))
+    cols = sample(L.N, 128, 3)
+    Xc = O.unpack_int4(host(xq))
+    Wc = O.unpack_int4(L.Wq[cols]).T
+    Rc = O.unpack_int4(np.ascontiguousarray(L.Rq[cols, : L.r // 2])).T
+    am_ref, ar_ref = O.linear_int(Xc, Wc, Rc, L.r)
+    assert np.array_equal(host(am)[:, cols], am_ref) and np.array_equal(host(ar)[:, cols], ar_ref)

@@ -23,7 +23,8 @@ from ._lib import SERQ_BF16, SERQ_F32, SerqError, check
 lib = _lib.lib
 
 __all__ = ["SerqLayer", "DeviceLayer", "calibrate", "permute_outputs", "quant_act", "silu_mul_quant_act",
-           "linear", "kernel_name", "rq_row_bytes", "SerqError"]
+           "linear", "kernel_name", "rq_row_bytes", "SerqError", "Bf6Layer", "bf6_bytes", "prepack_bf6", "act_bf6",
+           "linear_bf6"]
 
 
 def _ptr(a: np.ndarray):
@@ -255,3 +256,108 @@ def linear(xq, sx, layer: DeviceLayer, *, a_bits: int = 4, out_dtype=None, out=N
 def kernel_name(M: int, K: int, N: int, r: int, a_bits: int = 4) -> str | None:
     s = lib.serq_linear_kernel_name(M, K, N, r, a_bits)
     return s.decode() if s else None
+
+
+# ------------------------------------------------------------------ bf6 route
+
+def bf6_bytes(rows: int, k: int) -> int:
+    """Bytes of a rows x k matrix in the bf6 tile layout (serq_bf6_bytes)."""
+    b = lib.serq_bf6_bytes(int(rows), int(k))
+    if b < 0:
+        raise ValueError("rows and k must be >= 0")
+    return b
+
+
+@dataclass
+class Bf6Layer:
+    """A calibrated layer's weights in the bf6 tile layout (serq_prepack_bf6),
+    host numpy arrays or, after ``to``, device tensors."""
+
+    K: int
+    N: int
+    r: int
+    W6: "object"            # bf6_bytes(N, K) uint8
+    sw: "object"            # N float32
+    R6: "object"            # bf6_bytes(N, r) uint8 (empty when r == 0)
+    sr: "object"            # N float32
+
+    def to(self, device="cuda") -> "Bf6Layer":
+        import torch
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+        return Bf6Layer(K=self.K, N=self.N, r=self.r, W6=t(self.W6), sw=t(self.sw), R6=t(self.R6), sr=t(self.sr))
+
+
+def _prepack(codes: np.ndarray, rows: int, k: int, pitch: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    if codes.shape != (rows, pitch):
+        raise ValueError(f"packed codes must be {rows} x {pitch} bytes")
+    out = np.empty(bf6_bytes(rows, k), np.uint8)
+    check("serq_prepack_bf6", lib.serq_prepack_bf6(_ptr(codes), rows, k, pitch, _ptr(out)))
+    return out
+
+
+def prepack_bf6(layer: SerqLayer) -> Bf6Layer:
+    """Offline: Q(W^) and Q(R) of a host layer re-encoded as bf6 (host)."""
+    W6 = _prepack(layer.Wq, layer.N, layer.K, layer.K // 2)
+    R6 = _prepack(layer.Rq, layer.N, layer.r, rq_row_bytes(layer.r)) if layer.r else np.zeros(0, np.uint8)
+    return Bf6Layer(K=layer.K, N=layer.N, r=layer.r, W6=W6, sw=np.asarray(layer.sw, np.float32), R6=R6,
+                    sr=np.asarray(layer.sr, np.float32))
+
+
+def act_bf6(xq, K: int, *, out=None):
+    """W4A4 activation codes (quant_act's xq, M x K/2) re-encoded in the bf6
+    tile layout on the current stream (serq_act_bf6). Returns a uint8 tensor
+    of bf6_bytes(M, K) bytes."""
+    import torch
+    _need_cuda(xq)
+    if xq.dim() != 2 or xq.shape[1] != K // 2 or xq.element_size() != 1:
+        raise ValueError(f"xq must be M x {K // 2} packed int4 codes")
+    M = xq.shape[0]
+    n = bf6_bytes(M, K)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=xq.device)
+    else:
+        _need_cuda(out)
+        if out.numel() != n or out.element_size() != 1:
+            raise ValueError(f"out must hold {n} bytes")
+    check("serq_act_bf6", lib.serq_act_bf6(xq.data_ptr(), M, K, out.data_ptr(), _stream()))
+    return out
+
+
+def linear_bf6(x6, sx, layer: Bf6Layer, *, out_dtype=None, out=None, debug: bool = False):
+    """serq_linear_bf6 on the current stream: the W4A4 linear on bf6 operands
+    (``x6`` from act_bf6, ``sx`` from quant_act). Returns Y (M x N) or, with
+    ``debug=True``, (Y, acc_main, acc_res); bit-identical to ``linear``."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    K, N, r = layer.K, layer.N, layer.r
+    _need_cuda(x6, sx, layer.W6, layer.sw, layer.R6 if r else None, layer.sr if r else None)
+    M = sx.shape[0]
+    if sx.dim() != 1 or sx.dtype != torch.float32:
+        raise ValueError("sx must be a float32 vector")
+    if x6.numel() != bf6_bytes(M, K) or x6.element_size() != 1:
+        raise ValueError(f"x6 must hold bf6_bytes({M}, {K}) bytes")
+    if layer.W6.numel() != bf6_bytes(N, K) or (r and layer.R6.numel() != bf6_bytes(N, r)):
+        raise ValueError("layer buffers do not match its sizes")
+    if out_dtype == torch.bfloat16:
+        dt = SERQ_BF16
+    elif out_dtype == torch.float32:
+        dt = SERQ_F32
+    else:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=x6.device)
+    else:
+        y = out
+        _need_cuda(y)
+        if tuple(y.shape) != (M, N) or y.dtype != out_dtype:
+            raise ValueError(f"out must be a ({M}, {N}) {out_dtype} tensor")
+    am = ar = None
+    if debug:
+        am = torch.empty((M, N), dtype=torch.int32, device=x6.device)
+        ar = torch.empty((M, N), dtype=torch.int32, device=x6.device)
+    check("serq_linear_bf6", lib.serq_linear_bf6(
+        x6.data_ptr(), sx.data_ptr(), layer.W6.data_ptr(), layer.sw.data_ptr(),
+        layer.R6.data_ptr() if r else None, layer.sr.data_ptr() if r else None, M, K, N, r,
+        y.data_ptr(), dt, am.data_ptr() if debug else None, ar.data_ptr() if debug else None, _stream()))
+    return (y, am, ar) if debug else y

@@ -20,7 +20,7 @@ SERQ_F32, SERQ_BF16 = 0, 1
 # every symbol include/serq.h declares
 EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_permute_outputs",
            "serq_quant_act", "serq_silu_mul_quant_act", "serq_linear", "serq_linear_kernel_name",
-           "serq_rq_row_bytes")
+           "serq_rq_row_bytes", "serq_bf6_bytes", "serq_prepack_bf6", "serq_act_bf6", "serq_linear_bf6")
 
 
 class SerqError(RuntimeError):
@@ -61,6 +61,14 @@ def _load() -> ctypes.CDLL:
     lib.serq_linear_kernel_name.restype = ctypes.c_char_p
     lib.serq_rq_row_bytes.argtypes = [ip]
     lib.serq_rq_row_bytes.restype = ip
+    lib.serq_bf6_bytes.argtypes = [ip, ip]
+    lib.serq_bf6_bytes.restype = ctypes.c_int64
+    lib.serq_prepack_bf6.argtypes = [vp, ip, ip, ip, vp]
+    lib.serq_prepack_bf6.restype = ip
+    lib.serq_act_bf6.argtypes = [vp, ip, ip, vp, vp]
+    lib.serq_act_bf6.restype = ip
+    lib.serq_linear_bf6.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, vp, i32, vp, vp, vp]
+    lib.serq_linear_bf6.restype = ip
     return lib
 
 

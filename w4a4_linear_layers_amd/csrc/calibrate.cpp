@@ -225,3 +225,50 @@ extern "C" int serq_permute_outputs(const int32_t* perm_next, int N, int K, int 
   }
   return SERQ_OK;
 }
+
+// bf6 tile layout of a packed int4 matrix (the layout and the E3M2 patterns
+// are stated with serq_prepack_bf6 in serq.h): each 24-byte fragment holds
+// 32 codes of one row as six-bit fields, low field first.
+namespace {
+
+constexpr int kBf6Tile = 128;
+
+// E3M2 pattern of a 4-bit two's complement code (the nibble as stored).
+inline uint32_t bf6_pattern(uint32_t nib) {
+  static const uint8_t kMag[9] = {0x00, 0x0C, 0x10, 0x12, 0x14, 0x15, 0x16, 0x17, 0x18};   // |v| = 0..8
+  const int v = nib < 8 ? static_cast<int>(nib) : static_cast<int>(nib) - 16;
+  return v < 0 ? (0x20u | kMag[-v]) : kMag[v];
+}
+
+}  // namespace
+
+extern "C" int64_t serq_bf6_bytes(int rows, int k) {
+  if (rows < 0 || k < 0) return -1;
+  return static_cast<int64_t>(SERQ_BF6_BYTES(rows, k));
+}
+
+extern "C" int serq_prepack_bf6(const uint8_t* codes, int rows, int k, int pitch, uint8_t* out) {
+  if (!codes || !out) return SERQ_EINVAL;
+  if (rows <= 0 || k <= 0 || (k & 1) || pitch <= 0 || k > 2 * pitch) return SERQ_EINVAL;
+  const int rp = (rows + kBf6Tile - 1) / kBf6Tile * kBf6Tile;
+  const int nkt = (k + kBf6Tile - 1) / kBf6Tile, nrb = rp / 32;
+  for (int kt = 0; kt < nkt; ++kt)
+    for (int rb = 0; rb < nrb; ++rb)
+      for (int s = 0; s < 2; ++s)
+        for (int l = 0; l < 64; ++l) {
+          const int row = rb * 32 + l % 32;
+          const int k0 = kt * kBf6Tile + 64 * s + 32 * (l / 32);
+          uint8_t frag[24] = {0};
+          for (int f = 0; f < 32 && row < rows; ++f) {
+            const int kk = k0 + f;
+            if (kk >= k) break;
+            const uint8_t byte = codes[static_cast<size_t>(row) * pitch + kk / 2];
+            const uint32_t pat = bf6_pattern((kk & 1) ? (byte >> 4) : (byte & 15u));
+            for (int b = 0; b < 6; ++b)
+              if (pat >> b & 1u) frag[(6 * f + b) / 8] |= static_cast<uint8_t>(1u << ((6 * f + b) % 8));
+          }
+          const size_t off = ((static_cast<size_t>(kt) * nrb + rb) * 2 + s) * 1536 + static_cast<size_t>(l) * 24;
+          std::memcpy(out + off, frag, sizeof frag);
+        }
+  return SERQ_OK;
+}

@@ -28,7 +28,7 @@ extern "C" const char* serq_strerror(int status) {
   }
 }
 
-extern "C" int serq_abi_version(void) { return 201; }
+extern "C" int serq_abi_version(void) { return 202; }
 
 extern "C" int serq_rq_row_bytes(int r) { return r < 0 ? -1 : SERQ_RQ_ROW_BYTES(r); }
 
@@ -107,4 +107,53 @@ extern "C" int serq_linear(const void* Xq, const float* sx, int a_bits, const ui
 extern "C" const char* serq_linear_kernel_name(int M, int K, int N, int r, int a_bits) {
   if ((a_bits != 4 && a_bits != 8) || !valid_sizes(M, K, N, r)) return nullptr;
   return serq::plan_linear(M, K, N, r, a_bits).name;
+}
+
+namespace {
+constexpr int kBf6MaxK = 1 << 18;       // |acc| <= 64 K stays an exact fp32 integer
+constexpr int kBf6MaxResidual = 256;
+}  // namespace
+
+extern "C" int serq_act_bf6(const void* Xq, int M, int K, void* X6, void* stream) {
+  if (M < 0 || K <= 0 || (K % 2) != 0 || K > kBf6MaxK) return SERQ_EINVAL;
+  if (M == 0) return SERQ_OK;
+  if (!Xq || !X6) return SERQ_EINVAL;
+  if (!aligned16(Xq) || !aligned16(X6)) return SERQ_EALIGN;
+  hipError_t e = serq::launch_act_bf6(Xq, M, K, X6, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
+}
+
+extern "C" int serq_linear_bf6(const void* X6, const float* sx, const uint8_t* W6, const float* sw,
+                               const uint8_t* R6, const float* sr, int M, int K, int N, int r, void* Y,
+                               serq_dtype y_dtype, int32_t* acc_main_dbg, int32_t* acc_res_dbg,
+                               void* stream) {
+  if (y_dtype != SERQ_F32 && y_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (!valid_sizes(M, K, N, r) || K > kBf6MaxK || r > kBf6MaxResidual) return SERQ_EINVAL;
+  if (!W6 || !sw) return SERQ_EINVAL;
+  if (r > 0 && (!R6 || !sr)) return SERQ_EINVAL;
+  if ((acc_main_dbg == nullptr) != (acc_res_dbg == nullptr)) return SERQ_EINVAL;
+  if (!aligned16(W6) || !aligned16(sw)) return SERQ_EALIGN;
+  if (r > 0 && (!aligned16(R6) || !aligned16(sr))) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;
+  if (!X6 || !sx || !Y) return SERQ_EINVAL;
+  if (!aligned16(X6) || !aligned16(sx) || !aligned16(Y)) return SERQ_EALIGN;
+  if (acc_main_dbg && (!aligned16(acc_main_dbg) || !aligned16(acc_res_dbg))) return SERQ_EALIGN;
+  serq::LinearArgs a{};
+  a.Xq = static_cast<const uint8_t*>(X6);
+  a.sx = sx;
+  a.Wq = W6;
+  a.sw = sw;
+  a.Rq = r > 0 ? R6 : nullptr;
+  a.sr = r > 0 ? sr : nullptr;
+  a.Y = Y;
+  a.dbg_main = acc_main_dbg;
+  a.dbg_res = acc_res_dbg;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.r = r;
+  a.a_bits = 4;
+  a.y_bf16 = y_dtype == SERQ_BF16;
+  hipError_t e = serq::launch_linear_bf6(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
 }

@@ -1510,6 +1510,203 @@ hipError_t launch_tile_bits(const LinearArgs& a, const LinearPlan& p, hipStream_
   return hipErrorInvalidValue;
 }
 
+
+// ---------------------------------------------------------------------------
+// bf6 route: the same linear on v_mfma_scale_f32_32x32x64_f8f6f4 with both
+// operands as E3M2 six-bit values and unit block scales (E8M0 127 = 2^0).
+// Every int4 code is exactly such a value, a product of two codes is at most
+// 64 in magnitude and every partial sum an integer of magnitude <= 64 K <=
+// 2^24, so the fp32 accumulators hold the exact integer dot products and the
+// epilogue is serq_linear's on those integers.
+//
+// Operands come in the bf6 tile layout (weights prepacked on the host,
+// activations re-encoded by serq_act_bf6): for one 128-code k-tile the 128
+// rows of a tile are 12 KB of contiguous 24-byte lane fragments, in the
+// order the MFMA takes them. So the direct global->LDS loads move contiguous
+// 1 KB chunks, and each fragment read is three 8-byte LDS reads at a 24-byte
+// lane stride (16 lanes cover the 32 banks once: no conflicts).
+//
+// Workgroup: 128 x 128 outputs, four waves of 64 x 64 (2 x 2 blocks of
+// 32 x 32; A = weight rows, B = tokens, the output layout of the integer
+// 32 x 32 MFMA). Three LDS stages of one k-tile (12 KB of weights, then 12 KB
+// of activations); waves 0-1 load the weight half, 2-3 the activation half,
+// six 1 KB chunks each per stage, so every wave counts the same loads per
+// k-tile. The k-tile pipeline is the integer tile kernel's: wait until only
+// the next k-tile's loads are outstanding, one barrier publishes k-tile t and
+// frees the buffer of t - 1, which the loads of t + 2 go into. The residual
+// k-tiles (Q(R) against the first activation k-tiles) follow the main ones
+// in the same pipeline, into a second set of accumulators.
+// ---------------------------------------------------------------------------
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kB6Tile = 128;                        // rows (and codes) of a tile side
+constexpr int kB6Frag = 24;                         // bytes of one lane fragment (32 codes)
+constexpr int kB6Step = 64 * kB6Frag;               // one MFMA operand of a 32-row block
+constexpr int kB6Block = 2 * kB6Step;               // 32 rows x 128 codes
+constexpr int kB6Half = kB6Tile / 32 * kB6Block;    // one operand of a stage (12 KB)
+constexpr int kB6Stage = 2 * kB6Half;
+constexpr int kB6Stages = 3;
+constexpr int kB6Chunks = kB6Stage / 1024 / 4;      // 1 KB chunks per wave and stage
+constexpr int kB6Lds = kB6Stages * kB6Stage;
+static_assert(kB6Chunks * 4 * 1024 == kB6Stage && 2 * kB6Chunks * 1024 == kB6Half, "chunk split");
+
+__device__ __forceinline__ v16f mfma_bf6(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 3, 3, 0, 127, 0, 127);
+}
+
+// One lane fragment from LDS: 32 six-bit fields in the low six dwords.
+__device__ __forceinline__ v8i ld_frag(const uint8_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  const uint2 v = *reinterpret_cast<const uint2*>(p + 8);
+  const uint2 w = *reinterpret_cast<const uint2*>(p + 16);
+  return v8i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(v.x), static_cast<int>(v.y),
+             static_cast<int>(w.x), static_cast<int>(w.y), 0, 0};
+}
+
+__global__ __launch_bounds__(256, 2) void serq_bf6_tile_kernel(LinearArgs a, int n_tiles) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int wn = wv >> 1, wm = wv & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  int tile_n, tile_m;
+  tile_coords(blockIdx.x, gridDim.x, n_tiles, tile_n, tile_m);
+  const int n0 = __builtin_amdgcn_readfirstlane(tile_n * kB6Tile);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile_m * kB6Tile);
+  const int rbn = (a.N + kB6Tile - 1) / kB6Tile * (kB6Tile / 32);   // 32-row blocks per k-tile
+  const int rbm = (a.M + kB6Tile - 1) / kB6Tile * (kB6Tile / 32);
+  const int nk = (a.K + kB6Tile - 1) / kB6Tile;
+  const int ntot = nk + (a.r + kB6Tile - 1) / kB6Tile;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const uint8_t* const W6 = a.Wq;
+  const uint8_t* const R6 = a.Rq;
+  const uint8_t* const X6 = a.Xq;
+
+  // k-tile t (main for t < nk, else residual t - nk) into buffer t % 3.
+  auto issue = [&](int t) {
+    const int kt = t < nk ? t : t - nk;
+    const uint8_t* src =
+        wv < 2 ? (t < nk ? W6 : R6) + (static_cast<size_t>(kt) * rbn + n0 / 32) * kB6Block + wv * kB6Chunks * 1024
+               : X6 + (static_cast<size_t>(kt) * rbm + m0 / 32) * kB6Block + (wv - 2) * kB6Chunks * 1024;
+    const uint32_t dst = lds_base + (t % kB6Stages) * kB6Stage + wv * kB6Chunks * 1024;
+#pragma unroll
+    for (int c = 0; c < kB6Chunks; ++c) dma16(src + c * 1024, 16 * lane, dst + c * 1024);
+  };
+  auto compute = [&](int buf, v16f (&acc)[2][2]) {
+    const uint8_t* wb = lds + buf * kB6Stage + wn * 2 * kB6Block + lane * kB6Frag;
+    const uint8_t* xb = lds + buf * kB6Stage + kB6Half + wm * 2 * kB6Block + lane * kB6Frag;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      v8i wf[2], xf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) wf[i] = ld_frag(wb + i * kB6Block + s * kB6Step);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) xf[j] = ld_frag(xb + j * kB6Block + s * kB6Step);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf6(wf[i], xf[j], acc[i][j]);
+    }
+  };
+
+  v16f acc[2][2], accr[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = accr[i][j][e] = 0.0f;
+
+  for (int p = 0; p < kB6Stages - 1; ++p)
+    if (p < ntot) issue(p);
+  for (int t = 0; t < ntot; ++t) {
+    if (t + 2 <= ntot)
+      wait_vmcnt<kB6Chunks>();                 // k-tile t + 1 may still be in flight
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (t + 2 < ntot) issue(t + 2);
+    if (t < nk)
+      compute(t % kB6Stages, acc);
+    else
+      compute(t % kB6Stages, accr);
+  }
+
+  // The accumulators are exact integers: serq_linear's epilogue on them.
+  const int nw = n0 + wn * 64, mw = m0 + wm * 64;
+  const bool has_res = a.r > 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = mw + 32 * j + l32;
+    const float sxm = a.sx[min(m, a.M - 1)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nw + 32 * i + 8 * q + 4 * h;
+        float wv4[4], rv4[4];
+        v4i am, ar;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int nc = min(n + c, a.N - 1);
+          wv4[c] = a.sw[nc];
+          rv4[c] = has_res ? a.sr[nc] : 0.0f;
+          am[c] = static_cast<int>(acc[i][j][4 * q + c]);
+          ar[c] = static_cast<int>(accr[i][j][4 * q + c]);
+        }
+        store4<0>(a, am, ar, m, n, sxm, make_float4(wv4[0], wv4[1], wv4[2], wv4[3]),
+                  make_float4(rv4[0], rv4[1], rv4[2], rv4[3]));
+      }
+  }
+}
+
+// E3M2 pattern of a stored nibble (4-bit two's complement code): byte c of
+// the first constant for codes 0..7, of the second for nibbles 8..15 (codes
+// -8..-1).
+__device__ __forceinline__ uint64_t bf6_of_nibble(uint32_t nib) {
+  constexpr uint64_t kPos = 0x1716151412100C00ull;
+  constexpr uint64_t kNeg = 0x2C30323435363738ull;
+  return (((nib & 8u) ? kNeg : kPos) >> (8 * (nib & 7u))) & 0x3Full;
+}
+
+// serq_act_bf6: lane f writes fragment f of the bf6 tile layout (32 codes of
+// one row, zero past the M x K codes).
+__global__ __launch_bounds__(256) void serq_act_bf6_kernel(const uint8_t* Xq, int M, int K, uint8_t* X6, int rbm,
+                                                           int nfrag) {
+  const int f = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+  if (f >= nfrag) return;
+  const int l = f & 63, s = (f >> 6) & 1, blk = f >> 7;
+  const int rb = blk % rbm, kt = blk / rbm;
+  const int row = rb * 32 + (l & 31);
+  const int k0 = kt * kB6Tile + 64 * s + 32 * (l >> 5);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (row < M && k0 < K) {
+    const uint8_t* src = Xq + static_cast<size_t>(row) * (K / 2) + k0 / 2;
+    if ((K & 31) == 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      w[0] = v.x;
+      w[1] = v.y;
+      w[2] = v.z;
+      w[3] = v.w;
+    } else {
+      for (int b = 0; b < 16 && k0 + 2 * b < K; ++b) w[b >> 2] |= static_cast<uint32_t>(src[b]) << (8 * (b & 3));
+    }
+  }
+  uint64_t o[3] = {0ull, 0ull, 0ull};
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    const uint64_t p = bf6_of_nibble((w[c >> 3] >> (4 * (c & 7))) & 15u);
+    const int bit = 6 * c;
+    o[bit >> 6] |= p << (bit & 63);
+    if ((bit & 63) > 58) o[(bit >> 6) + 1] |= p >> (64 - (bit & 63));
+  }
+  uint2* dst = reinterpret_cast<uint2*>(X6 + static_cast<size_t>(f) * kB6Frag);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) dst[q] = make_uint2(static_cast<uint32_t>(o[q]), static_cast<uint32_t>(o[q] >> 32));
+}
+
 }  // namespace
 
 LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
@@ -1577,6 +1774,26 @@ hipError_t launch_linear(const LinearArgs& a, const LinearPlan& p, hipStream_t s
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_act_bf6(const void* Xq, int M, int K, void* X6, hipStream_t st) {
+  const int rbm = (M + kB6Tile - 1) / kB6Tile * (kB6Tile / 32);
+  const long long nfrag = static_cast<long long>((K + kB6Tile - 1) / kB6Tile) * rbm * 128;
+  if (nfrag > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const int nf = static_cast<int>(nfrag);
+  serq_act_bf6_kernel<<<dim3((nf + 255) / 256), dim3(256), 0, st>>>(static_cast<const uint8_t*>(Xq), M, K,
+                                                                   static_cast<uint8_t*>(X6), rbm, nf);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_bf6(const LinearArgs& a, hipStream_t st) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_bf6_tile_kernel), kB6Lds, lds_set);
+  if (e != hipSuccess) return e;
+  const int n_tiles = (a.N + kB6Tile - 1) / kB6Tile;
+  const int m_tiles = (a.M + kB6Tile - 1) / kB6Tile;
+  serq_bf6_tile_kernel<<<dim3(n_tiles * m_tiles), dim3(256), kB6Lds, st>>>(a, n_tiles);
+  return hipGetLastError();
 }
 
 }  // namespace serq

@@ -47,4 +47,9 @@ hipError_t launch_silu_mul_quant_act(const void* G, const void* U, int ld, int x
                                      const float* s_hat_inv, int a_bits, void* Xq, float* sx,
                                      hipStream_t stream);
 
+// The bf6 route (serq_act_bf6, serq_linear_bf6): operands in the bf6 tile
+// layout; LinearArgs carries X6 / W6 / R6 in place of Xq / Wq / Rq.
+hipError_t launch_act_bf6(const void* Xq, int M, int K, void* X6, hipStream_t stream);
+hipError_t launch_linear_bf6(const LinearArgs& a, hipStream_t stream);
+
 }  // namespace serq
