@@ -532,8 +532,10 @@ def test_linear_bf6_bit_exact(M, K, N, r, out):
     xq_d, sx_d = dev(Xq), dev(sx)
     x6 = S.act_bf6(xq_d, K)
     y, am, ar = S.linear_bf6(x6, sx_d, L6, out_dtype=odt, debug=True)
+    y_fast = S.linear_bf6(x6, sx_d, L6, out_dtype=odt)            # the epilogue without debug outputs
     y_int = S.linear(xq_d, sx_d, layer, a_bits=4, out_dtype=odt)
     _sync()
+    assert np.array_equal(host(y_fast), host(y_int))
     cols = np.arange(N) if N <= 2048 else sample(N, 512, M)
     am_ref, ar_ref = O.linear_int(Xc, Wc[:, cols], Rc[:, cols], r)
     am_g, ar_g = host(am)[:, cols], host(ar)[:, cols]
@@ -559,6 +561,7 @@ def test_linear_bf6_extreme_codes_and_empty():
     am_ref, ar_ref = O.linear_int(Xc, Wc, Rc, r)
     assert np.array_equal(host(am), am_ref) and np.array_equal(host(ar), ar_ref)
     check_y(host(y), am_ref, ar_ref, sx, sw, sr, "f32")
+    assert np.array_equal(host(S.linear_bf6(x6, dev(sx), L6, out_dtype=torch.float32)), host(y))
     e6 = S.act_bf6(torch.empty((0, K // 2), dtype=torch.uint8, device="cuda"), K)
     y0 = S.linear_bf6(e6, torch.empty(0, dtype=torch.float32, device="cuda"), L6)
     _sync()
@@ -578,9 +581,10 @@ def test_workload_q_proj_bf6():
     xq, sx = S.quant_act(bf16_tensor(li.X_bits[:M][:, L.perm]), D, a_bits=4)
     x6 = S.act_bf6(xq, L.K)
     y6, am, ar = S.linear_bf6(x6, sx, B, debug=True)
+    y6f = S.linear_bf6(x6, sx, B)
     y = S.linear(xq, sx, D, a_bits=4)
     _sync()
-    assert np.array_equal(host(y6), host(y))
+    assert np.array_equal(host(y6), host(y)) and np.array_equal(host(y6f), host(y))
     cols = sample(L.N, 128, 3)
     Xc = O.unpack_int4(host(xq))
     Wc = O.unpack_int4(L.Wq[cols]).T

@@ -1548,9 +1548,12 @@ constexpr int kB6Block = 2 * kB6Step;               // 32 rows x 128 codes
 constexpr int kB6Half = kB6Tile / 32 * kB6Block;    // one operand of a stage (12 KB)
 constexpr int kB6Stage = 2 * kB6Half;
 constexpr int kB6Stages = 3;
+constexpr int kB6Occ = 2;                           // workgroups per CU
 constexpr int kB6Chunks = kB6Stage / 1024 / 4;      // 1 KB chunks per wave and stage
 constexpr int kB6Lds = kB6Stages * kB6Stage;
 static_assert(kB6Chunks * 4 * 1024 == kB6Stage && 2 * kB6Chunks * 1024 == kB6Half, "chunk split");
+static_assert(kB6Occ * kB6Lds <= 160 * 1024 && (kB6Stages - 1) * kB6Chunks < 64, "LDS, vmcnt range");
+static_assert(kB6Stages >= 256 / kB6Tile + 1, "the residual k-tiles and the last main k-tile need distinct buffers");
 
 __device__ __forceinline__ v16f mfma_bf6(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 3, 3, 0, 127, 0, 127);
@@ -1565,7 +1568,7 @@ __device__ __forceinline__ v8i ld_frag(const uint8_t* p) {
              static_cast<int>(w.x), static_cast<int>(w.y), 0, 0};
 }
 
-__global__ __launch_bounds__(256, 2) void serq_bf6_tile_kernel(LinearArgs a, int n_tiles) {
+__global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a, int n_tiles) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -1584,82 +1587,222 @@ __global__ __launch_bounds__(256, 2) void serq_bf6_tile_kernel(LinearArgs a, int
   const uint8_t* const R6 = a.Rq;
   const uint8_t* const X6 = a.Xq;
 
-  // k-tile t (main for t < nk, else residual t - nk) into buffer t % 3.
+  // k-tile t (main for t < nk, else residual t - nk) into buffer t % STAGES.
+  // Past the last k-tile the loads repeat the last one into a buffer that is
+  // never read again, so every wave issues the same loads per k-tile and the
+  // wait counts below hold without branches.
   auto issue = [&](int t) {
-    const int kt = t < nk ? t : t - nk;
+    const int tl = min(t, ntot - 1);
+    const int kt = tl < nk ? tl : tl - nk;
     const uint8_t* src =
-        wv < 2 ? (t < nk ? W6 : R6) + (static_cast<size_t>(kt) * rbn + n0 / 32) * kB6Block + wv * kB6Chunks * 1024
+        wv < 2 ? (tl < nk ? W6 : R6) + (static_cast<size_t>(kt) * rbn + n0 / 32) * kB6Block + wv * kB6Chunks * 1024
                : X6 + (static_cast<size_t>(kt) * rbm + m0 / 32) * kB6Block + (wv - 2) * kB6Chunks * 1024;
     const uint32_t dst = lds_base + (t % kB6Stages) * kB6Stage + wv * kB6Chunks * 1024;
 #pragma unroll
     for (int c = 0; c < kB6Chunks; ++c) dma16(src + c * 1024, 16 * lane, dst + c * 1024);
   };
-  auto compute = [&](int buf, v16f (&acc)[2][2]) {
-    const uint8_t* wb = lds + buf * kB6Stage + wn * 2 * kB6Block + lane * kB6Frag;
-    const uint8_t* xb = lds + buf * kB6Stage + kB6Half + wm * 2 * kB6Block + lane * kB6Frag;
+  // One MFMA step (64 codes) of a k-tile: the wave's two weight and two
+  // activation fragments, then its four MFMAs.
+  auto read = [&](int buf, int st, v8i (&wf)[2], v8i (&xf)[2]) {
+    const uint8_t* wb = lds + buf * kB6Stage + wn * 2 * kB6Block + st * kB6Step + lane * kB6Frag;
+    const uint8_t* xb = lds + buf * kB6Stage + kB6Half + wm * 2 * kB6Block + st * kB6Step + lane * kB6Frag;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8i wf[2], xf[2];
+    for (int i = 0; i < 2; ++i) wf[i] = ld_frag(wb + i * kB6Block);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) wf[i] = ld_frag(wb + i * kB6Block + s * kB6Step);
+    for (int j = 0; j < 2; ++j) xf[j] = ld_frag(xb + j * kB6Block);
+  };
+  auto mm = [&](const v8i (&wf)[2], const v8i (&xf)[2], v16f (&acc)[2][2]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) xf[j] = ld_frag(xb + j * kB6Block + s * kB6Step);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf6(wf[i], xf[j], acc[i][j]);
-    }
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf6(wf[i], xf[j], acc[i][j]);
   };
 
-  v16f acc[2][2], accr[2][2];
+  v16f acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = accr[i][j][e] = 0.0f;
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  for (int p = 0; p < kB6Stages - 1; ++p)
-    if (p < ntot) issue(p);
-  for (int t = 0; t < ntot; ++t) {
-    if (t + 2 <= ntot)
-      wait_vmcnt<kB6Chunks>();                 // k-tile t + 1 may still be in flight
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    if (t + 2 < ntot) issue(t + 2);
-    if (t < nk)
-      compute(t % kB6Stages, acc);
-    else
-      compute(t % kB6Stages, accr);
-  }
-
-  // The accumulators are exact integers: serq_linear's epilogue on them.
-  const int nw = n0 + wn * 64, mw = m0 + wm * 64;
-  const bool has_res = a.r > 0;
+  // Every buffer starts loading; step 0 of k-tile 0 goes into registers.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = mw + 32 * j + l32;
-    const float sxm = a.sx[min(m, a.M - 1)];
+  for (int p = 0; p < kB6Stages; ++p) issue(p);
+  wait_vmcnt<(kB6Stages - 1) * kB6Chunks>();
+  lds_barrier();
+  v8i w0[2], x0[2], w1[2], x1[2];
+  read(0, 0, w0, x0);
+  // Main k-tile t: step 1's fragments are read while step 0's MFMAs run;
+  // then (this wave's k-tile t + 1 loads done, one barrier) k-tile t + 1 is
+  // published and buffer t, fully read by every wave, takes k-tile
+  // t + STAGES; step 0 of k-tile t + 1 is read while step 1's MFMAs run.
+  // The MFMAs are pure values that the compiler would otherwise move past
+  // the barrier: empty asm statements that take the accumulators (after step
+  // 0) and step 1's fragments (after the barrier) pin them in program order,
+  // so the matrix core has step 0's work while the wave waits.
+  auto pin = [&](v16f (&ac)[2][2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nw + 32 * i + 8 * q + 4 * h;
-        float wv4[4], rv4[4];
-        v4i am, ar;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int nc = min(n + c, a.N - 1);
-          wv4[c] = a.sw[nc];
-          rv4[c] = has_res ? a.sr[nc] : 0.0f;
-          am[c] = static_cast<int>(acc[i][j][4 * q + c]);
-          ar[c] = static_cast<int>(accr[i][j][4 * q + c]);
-        }
-        store4<0>(a, am, ar, m, n, sxm, make_float4(wv4[0], wv4[1], wv4[2], wv4[3]),
-                  make_float4(rv4[0], rv4[1], rv4[2], rv4[3]));
-      }
+      for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(ac[i][j]));
+  };
+  auto pin_frags = [&](v8i (&wf)[2], v8i (&xf)[2]) {
+    asm volatile("" : "+v"(wf[0]), "+v"(wf[1]), "+v"(xf[0]), "+v"(xf[1]));
+  };
+  for (int t = 0; t < nk - 1; ++t) {
+    read(t % kB6Stages, 1, w1, x1);
+    mm(w0, x0, acc);
+    pin(acc);
+    wait_vmcnt<(kB6Stages - 2) * kB6Chunks>();
+    lds_barrier();
+    issue(t + kB6Stages);
+    pin_frags(w1, x1);
+    read((t + 1) % kB6Stages, 0, w0, x0);
+    mm(w1, x1, acc);
   }
+  read((nk - 1) % kB6Stages, 1, w1, x1);
+  mm(w0, x0, acc);
+  mm(w1, x1, acc);
+  // The residual k-tiles (at most two, in buffers the last main k-tile does
+  // not use) are complete and published; each block's residual MFMAs run in
+  // the epilogue into one temporary accumulator.
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  // The accumulators are exact integers: serq_linear's epilogue on them,
+  // one weight block row at a time: its two blocks' residual MFMAs into two
+  // temporaries (independent chains), then
+  //   y = sx (sw acc_main + sr acc_res)
+  // in fp32 in place of the main accumulator (already the fp32 value of the
+  // integer sum), or element-wise stores with the exact sums for tests.
+  const int nw = n0 + wn * 64, mw = m0 + wm * 64;
+  const int nr = ntot - nk;
+  const bool dbg = a.dbg_main != nullptr;
+  float sxm[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sxm[j] = a.sx[min(mw + 32 * j + l32, a.M - 1)];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    v16f res[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) res[j][e] = 0.0f;
+    for (int q = 0; q < nr; ++q) {
+      const uint8_t* bp = lds + ((nk + q) % kB6Stages) * kB6Stage + lane * kB6Frag;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const v8i wf = ld_frag(bp + (wn * 2 + i) * kB6Block + st * kB6Step);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          res[j] = mfma_bf6(wf, ld_frag(bp + kB6Half + (wm * 2 + j) * kB6Block + st * kB6Step), res[j]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = nw + 32 * i + 8 * q + 4 * h;
+      float wv4[4], rv4[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int nc = min(n + c, a.N - 1);
+        wv4[c] = a.sw[nc];
+        rv4[c] = nr > 0 ? a.sr[nc] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (dbg) {
+          v4i am, ar;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            am[c] = static_cast<int>(acc[i][j][4 * q + c]);
+            ar[c] = static_cast<int>(res[j][4 * q + c]);
+          }
+          store4<0>(a, am, ar, mw + 32 * j + l32, n, sxm[j], make_float4(wv4[0], wv4[1], wv4[2], wv4[3]),
+                    make_float4(rv4[0], rv4[1], rv4[2], rv4[3]));
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[i][j][4 * q + c] =
+                sxm[j] * __builtin_fmaf(rv4[c], res[j][4 * q + c], wv4[c] * acc[i][j][4 * q + c]);
+        }
+      }
+    }
+  }
+  if (dbg) return;
+  // Output tile into LDS (the stages are free once every wave is here), row =
+  // token, 16-byte chunks swizzled as in the integer tile kernel; then 16-byte
+  // stores along the rows of Y.
+  lds_barrier();
+  const bool bf = a.y_bf16;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = wm * 64 + 32 * j + l32;
+    if (bf) {
+      uint8_t* rp = lds + row * (kB6Tile * 2);
+      const int hs = (h ^ half_swap(row)) * 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (wn * 64 + 32 * i) / 8 + q;
+          const uint2 o = make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          *reinterpret_cast<uint2*>(rp + 16 * (c ^ (row & 15)) + hs) = o;
+        }
+    } else {
+      uint8_t* rp = lds + row * (kB6Tile * 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (wn * 64 + 32 * i + 8 * q + 4 * h) / 4;
+          *reinterpret_cast<float4*>(rp + 16 * (c ^ (row & 15))) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+    }
+  }
+  __syncthreads();
+  auto copy_out = [&](auto ebc) {
+    constexpr int EB = decltype(ebc)::value;   // bytes per element
+    constexpr int CPR = kB6Tile * EB / 16;     // chunks per tile row
+    constexpr int EPC = 16 / EB;               // elements per chunk
+    constexpr int RPP = 256 / CPR;             // rows per pass
+    constexpr int PASSES = kB6Tile / RPP;
+    const int tid = threadIdx.x;
+    const int c = tid % CPR;
+    const int n = n0 + c * EPC;
+    const bool vec = (a.N % EPC) == 0 && n + EPC <= a.N;
+    uint4 v[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = p * RPP + tid / CPR;
+      v[p] = *reinterpret_cast<const uint4*>(lds + row * kB6Tile * EB + 16 * (c ^ (row & 15)));
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = p * RPP + tid / CPR;
+      if (m0 + row >= a.M) break;
+      uint4 w = v[p];
+      if (EB == 2 && half_swap(row)) w = make_uint4(w.z, w.w, w.x, w.y);
+      uint8_t* dst = static_cast<uint8_t*>(a.Y) + (static_cast<size_t>(m0 + row) * a.N + n) * EB;
+      if (vec) {
+        *reinterpret_cast<uint4*>(dst) = w;
+      } else {
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+        for (int e = 0; e < EPC && n + e < a.N; ++e) {
+          if (EB == 2)
+            reinterpret_cast<uint16_t*>(dst)[e] = static_cast<uint16_t>(d[e >> 1] >> (16 * (e & 1)));
+          else
+            reinterpret_cast<uint32_t*>(dst)[e] = d[e];
+        }
+      }
+    }
+  };
+  if (bf)
+    copy_out(std::integral_constant<int, 2>{});
+  else
+    copy_out(std::integral_constant<int, 4>{});
 }
 
 // E3M2 pattern of a stored nibble (4-bit two's complement code): byte c of
