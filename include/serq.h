@@ -324,6 +324,14 @@ int serq_linear_bf6(const void* X6, const float* sx,
                     int32_t* acc_main_dbg, int32_t* acc_res_dbg,
                     void* stream);
 
+/*
+ * serq_linear_bf6_kernel_name -- which tile serq_linear_bf6 launches for M
+ * tokens and N outputs (static string "bf6_tile128x128" or
+ * "bf6_tile256x256"), or NULL for M <= 0 or N <= 0. Host only; launches
+ * nothing. For profiling and tests.
+ */
+const char* serq_linear_bf6_kernel_name(int M, int N);
+
 #ifdef __cplusplus
 }
 #endif

@@ -518,6 +518,9 @@ BF6_CASES = [
     (513, 2048, 640, 130),     # two residual k-tiles, the second nearly empty
     (128, 4096, 4096, 64),
     (300, 8192, 1000, 128),
+    (1024, 256, 16384, 64),    # 256 x 256 tiles
+    (1000, 300, 16284, 130),   # 256 x 256 tiles, ragged M, N and K, two residual k-tiles
+    (2048, 1024, 8192, 0),     # 256 x 256 tiles, r = 0
 ]
 
 
@@ -526,6 +529,8 @@ BF6_CASES = [
 def test_linear_bf6_bit_exact(M, K, N, r, out):
     """The bf6 route: exact integer accumulators against the oracle, Y within
     the epilogue tolerance, and Y bit-identical to serq_linear's."""
+    wide = (-(-M // 128) % 2 == 0) and (-(-N // 128) % 2 == 0) and (-(-M // 256)) * (-(-N // 256)) >= 256
+    assert S.bf6_kernel_name(M, N) == ("bf6_tile256x256" if wide else "bf6_tile128x128")
     Xc, Wc, Rc, sx, sw, sr, Xq, layer = _codes_case(M, K, N, r, 4, seed=M + K + N + r + 6)
     L6 = _bf6_layer(Wc, Rc, sw, sr, K, N, r)
     odt = torch.float32 if out == "f32" else torch.bfloat16

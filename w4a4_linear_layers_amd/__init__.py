@@ -24,7 +24,7 @@ lib = _lib.lib
 
 __all__ = ["SerqLayer", "DeviceLayer", "calibrate", "permute_outputs", "quant_act", "silu_mul_quant_act",
            "linear", "kernel_name", "rq_row_bytes", "SerqError", "Bf6Layer", "bf6_bytes", "prepack_bf6", "act_bf6",
-           "linear_bf6"]
+           "linear_bf6", "bf6_kernel_name"]
 
 
 def _ptr(a: np.ndarray):
@@ -361,3 +361,9 @@ def linear_bf6(x6, sx, layer: Bf6Layer, *, out_dtype=None, out=None, debug: bool
         layer.R6.data_ptr() if r else None, layer.sr.data_ptr() if r else None, M, K, N, r,
         y.data_ptr(), dt, am.data_ptr() if debug else None, ar.data_ptr() if debug else None, _stream()))
     return (y, am, ar) if debug else y
+
+
+def bf6_kernel_name(M: int, N: int) -> str | None:
+    """The tile serq_linear_bf6 launches for these sizes."""
+    s = lib.serq_linear_bf6_kernel_name(M, N)
+    return s.decode() if s else None

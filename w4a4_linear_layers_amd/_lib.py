@@ -20,7 +20,8 @@ SERQ_F32, SERQ_BF16 = 0, 1
 # every symbol include/serq.h declares
 EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_permute_outputs",
            "serq_quant_act", "serq_silu_mul_quant_act", "serq_linear", "serq_linear_kernel_name",
-           "serq_rq_row_bytes", "serq_bf6_bytes", "serq_prepack_bf6", "serq_act_bf6", "serq_linear_bf6")
+           "serq_rq_row_bytes", "serq_bf6_bytes", "serq_prepack_bf6", "serq_act_bf6", "serq_linear_bf6",
+           "serq_linear_bf6_kernel_name")
 
 
 class SerqError(RuntimeError):
@@ -69,6 +70,8 @@ def _load() -> ctypes.CDLL:
     lib.serq_act_bf6.restype = ip
     lib.serq_linear_bf6.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, vp, i32, vp, vp, vp]
     lib.serq_linear_bf6.restype = ip
+    lib.serq_linear_bf6_kernel_name.argtypes = [ip, ip]
+    lib.serq_linear_bf6_kernel_name.restype = ctypes.c_char_p
     return lib
 
 

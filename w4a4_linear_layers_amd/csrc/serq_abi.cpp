@@ -157,3 +157,8 @@ extern "C" int serq_linear_bf6(const void* X6, const float* sx, const uint8_t* W
   hipError_t e = serq::launch_linear_bf6(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
 }
+
+extern "C" const char* serq_linear_bf6_kernel_name(int M, int N) {
+  if (M <= 0 || N <= 0) return nullptr;
+  return serq::bf6_wide_tiles(M, N) ? "bf6_tile256x256" : "bf6_tile128x128";
+}

@@ -1541,19 +1541,30 @@ hipError_t launch_tile_bits(const LinearArgs& a, const LinearPlan& p, hipStream_
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kB6Tile = 128;                        // rows (and codes) of a tile side
+constexpr int kB6Tile = 128;                        // row padding of the layout, codes per k-tile
 constexpr int kB6Frag = 24;                         // bytes of one lane fragment (32 codes)
 constexpr int kB6Step = 64 * kB6Frag;               // one MFMA operand of a 32-row block
 constexpr int kB6Block = 2 * kB6Step;               // 32 rows x 128 codes
-constexpr int kB6Half = kB6Tile / 32 * kB6Block;    // one operand of a stage (12 KB)
-constexpr int kB6Stage = 2 * kB6Half;
-constexpr int kB6Stages = 3;
-constexpr int kB6Occ = 2;                           // workgroups per CU
-constexpr int kB6Chunks = kB6Stage / 1024 / 4;      // 1 KB chunks per wave and stage
-constexpr int kB6Lds = kB6Stages * kB6Stage;
-static_assert(kB6Chunks * 4 * 1024 == kB6Stage && 2 * kB6Chunks * 1024 == kB6Half, "chunk split");
-static_assert(kB6Occ * kB6Lds <= 160 * 1024 && (kB6Stages - 1) * kB6Chunks < 64, "LDS, vmcnt range");
-static_assert(kB6Stages >= 256 / kB6Tile + 1, "the residual k-tiles and the last main k-tile need distinct buffers");
+
+// Tile shape: each wave owns TN x TM blocks of 32 x 32, the workgroup a
+// WNW x WMW grid of waves; STAGES LDS buffers of one k-tile each, OCC
+// workgroups per CU. The first waves load the weight half of a stage, the
+// others the activation half, CHUNKS 1 KB chunks each.
+template <int TN, int TM, int WNW, int WMW, int STAGES, int OCC>
+struct B6Cfg {
+  static constexpr int NW = WNW * WMW, NT = 64 * NW;
+  static constexpr int BN = 32 * TN * WNW, BM = 32 * TM * WMW;
+  static constexpr int W_HALF = BN / 32 * kB6Block, X_HALF = BM / 32 * kB6Block;
+  static constexpr int STAGE = W_HALF + X_HALF;
+  static constexpr int CHUNKS = STAGE / 1024 / NW;
+  static constexpr int NW_W = W_HALF / (CHUNKS * 1024);       // waves that load weights
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr bool F32_VIA_LDS = BM * BN * 4 <= LDS;     // else fp32 outputs are stored element-wise
+  static_assert(CHUNKS * 1024 * NW == STAGE && NW_W * CHUNKS * 1024 == W_HALF, "chunk split");
+  static_assert(OCC * LDS <= 160 * 1024 && (STAGES - 1) * CHUNKS < 64, "LDS, vmcnt range");
+  static_assert(STAGES >= 256 / kB6Tile + 1, "the residual k-tiles and the last main k-tile need distinct buffers");
+  static_assert(BM * BN * 2 <= LDS && BN * 2 / 16 >= 16, "bf16 output tile in LDS");
+};
 
 __device__ __forceinline__ v16f mfma_bf6(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 3, 3, 0, 127, 0, 127);
@@ -1568,16 +1579,20 @@ __device__ __forceinline__ v8i ld_frag(const uint8_t* p) {
              static_cast<int>(w.x), static_cast<int>(w.y), 0, 0};
 }
 
-__global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a, int n_tiles) {
+// The layout pads rows to 128 only: a launch needs BN | Np and BM | Mp (the
+// host picks the shape accordingly), so every load stays inside the buffers.
+template <int TN, int TM, int WNW, int WMW, int STAGES, int OCC>
+__global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_bf6_tile_kernel(LinearArgs a, int n_tiles) {
+  using C = B6Cfg<TN, TM, WNW, WMW, STAGES, OCC>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int wn = wv >> 1, wm = wv & 1;
+  const int wn = wv / WMW, wm = wv % WMW;
   const int l32 = lane & 31, h = lane >> 5;
   int tile_n, tile_m;
   tile_coords(blockIdx.x, gridDim.x, n_tiles, tile_n, tile_m);
-  const int n0 = __builtin_amdgcn_readfirstlane(tile_n * kB6Tile);
-  const int m0 = __builtin_amdgcn_readfirstlane(tile_m * kB6Tile);
+  const int n0 = __builtin_amdgcn_readfirstlane(tile_n * C::BN);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile_m * C::BM);
   const int rbn = (a.N + kB6Tile - 1) / kB6Tile * (kB6Tile / 32);   // 32-row blocks per k-tile
   const int rbm = (a.M + kB6Tile - 1) / kB6Tile * (kB6Tile / 32);
   const int nk = (a.K + kB6Tile - 1) / kB6Tile;
@@ -1595,43 +1610,44 @@ __global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a
     const int tl = min(t, ntot - 1);
     const int kt = tl < nk ? tl : tl - nk;
     const uint8_t* src =
-        wv < 2 ? (tl < nk ? W6 : R6) + (static_cast<size_t>(kt) * rbn + n0 / 32) * kB6Block + wv * kB6Chunks * 1024
-               : X6 + (static_cast<size_t>(kt) * rbm + m0 / 32) * kB6Block + (wv - 2) * kB6Chunks * 1024;
-    const uint32_t dst = lds_base + (t % kB6Stages) * kB6Stage + wv * kB6Chunks * 1024;
+        wv < C::NW_W
+            ? (tl < nk ? W6 : R6) + (static_cast<size_t>(kt) * rbn + n0 / 32) * kB6Block + wv * C::CHUNKS * 1024
+            : X6 + (static_cast<size_t>(kt) * rbm + m0 / 32) * kB6Block + (wv - C::NW_W) * C::CHUNKS * 1024;
+    const uint32_t dst = lds_base + (t % STAGES) * C::STAGE + wv * C::CHUNKS * 1024;
 #pragma unroll
-    for (int c = 0; c < kB6Chunks; ++c) dma16(src + c * 1024, 16 * lane, dst + c * 1024);
+    for (int c = 0; c < C::CHUNKS; ++c) dma16(src + c * 1024, 16 * lane, dst + c * 1024);
   };
-  // One MFMA step (64 codes) of a k-tile: the wave's two weight and two
-  // activation fragments, then its four MFMAs.
-  auto read = [&](int buf, int st, v8i (&wf)[2], v8i (&xf)[2]) {
-    const uint8_t* wb = lds + buf * kB6Stage + wn * 2 * kB6Block + st * kB6Step + lane * kB6Frag;
-    const uint8_t* xb = lds + buf * kB6Stage + kB6Half + wm * 2 * kB6Block + st * kB6Step + lane * kB6Frag;
+  // One MFMA step (64 codes) of a k-tile: the wave's TN weight and TM
+  // activation fragments, then its TN x TM MFMAs.
+  auto read = [&](int buf, int st, v8i (&wf)[TN], v8i (&xf)[TM]) {
+    const uint8_t* wb = lds + buf * C::STAGE + wn * TN * kB6Block + st * kB6Step + lane * kB6Frag;
+    const uint8_t* xb = lds + buf * C::STAGE + C::W_HALF + wm * TM * kB6Block + st * kB6Step + lane * kB6Frag;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wf[i] = ld_frag(wb + i * kB6Block);
+    for (int i = 0; i < TN; ++i) wf[i] = ld_frag(wb + i * kB6Block);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) xf[j] = ld_frag(xb + j * kB6Block);
+    for (int j = 0; j < TM; ++j) xf[j] = ld_frag(xb + j * kB6Block);
   };
-  auto mm = [&](const v8i (&wf)[2], const v8i (&xf)[2], v16f (&acc)[2][2]) {
+  auto mm = [&](const v8i (&wf)[TN], const v8i (&xf)[TM], v16f (&acc)[TN][TM]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf6(wf[i], xf[j], acc[i][j]);
+      for (int j = 0; j < TM; ++j) acc[i][j] = mfma_bf6(wf[i], xf[j], acc[i][j]);
   };
 
-  v16f acc[2][2];
+  v16f acc[TN][TM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TM; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   // Every buffer starts loading; step 0 of k-tile 0 goes into registers.
 #pragma unroll
-  for (int p = 0; p < kB6Stages; ++p) issue(p);
-  wait_vmcnt<(kB6Stages - 1) * kB6Chunks>();
+  for (int p = 0; p < STAGES; ++p) issue(p);
+  wait_vmcnt<(STAGES - 1) * C::CHUNKS>();
   lds_barrier();
-  v8i w0[2], x0[2], w1[2], x1[2];
+  v8i w0[TN], x0[TM], w1[TN], x1[TM];
   read(0, 0, w0, x0);
   // Main k-tile t: step 1's fragments are read while step 0's MFMAs run;
   // then (this wave's k-tile t + 1 loads done, one barrier) k-tile t + 1 is
@@ -1641,62 +1657,65 @@ __global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a
   // the barrier: empty asm statements that take the accumulators (after step
   // 0) and step 1's fragments (after the barrier) pin them in program order,
   // so the matrix core has step 0's work while the wave waits.
-  auto pin = [&](v16f (&ac)[2][2]) {
+  auto pin = [&](v16f (&ac)[TN][TM]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(ac[i][j]));
+      for (int j = 0; j < TM; ++j) asm volatile("" : "+v"(ac[i][j]));
   };
-  auto pin_frags = [&](v8i (&wf)[2], v8i (&xf)[2]) {
-    asm volatile("" : "+v"(wf[0]), "+v"(wf[1]), "+v"(xf[0]), "+v"(xf[1]));
+  auto pin_frags = [&](v8i (&wf)[TN], v8i (&xf)[TM]) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) asm volatile("" : "+v"(wf[i]));
+#pragma unroll
+    for (int j = 0; j < TM; ++j) asm volatile("" : "+v"(xf[j]));
   };
   for (int t = 0; t < nk - 1; ++t) {
-    read(t % kB6Stages, 1, w1, x1);
+    read(t % STAGES, 1, w1, x1);
     mm(w0, x0, acc);
     pin(acc);
-    wait_vmcnt<(kB6Stages - 2) * kB6Chunks>();
+    wait_vmcnt<(STAGES - 2) * C::CHUNKS>();
     lds_barrier();
-    issue(t + kB6Stages);
+    issue(t + STAGES);
     pin_frags(w1, x1);
-    read((t + 1) % kB6Stages, 0, w0, x0);
+    read((t + 1) % STAGES, 0, w0, x0);
     mm(w1, x1, acc);
   }
-  read((nk - 1) % kB6Stages, 1, w1, x1);
+  read((nk - 1) % STAGES, 1, w1, x1);
   mm(w0, x0, acc);
   mm(w1, x1, acc);
   // The residual k-tiles (at most two, in buffers the last main k-tile does
-  // not use) are complete and published; each block's residual MFMAs run in
-  // the epilogue into one temporary accumulator.
+  // not use) are complete and published.
   wait_vmcnt<0>();
   lds_barrier();
 
   // The accumulators are exact integers: serq_linear's epilogue on them,
-  // one weight block row at a time: its two blocks' residual MFMAs into two
+  // one weight block row at a time: its blocks' residual MFMAs into TM
   // temporaries (independent chains), then
   //   y = sx (sw acc_main + sr acc_res)
   // in fp32 in place of the main accumulator (already the fp32 value of the
-  // integer sum), or element-wise stores with the exact sums for tests.
-  const int nw = n0 + wn * 64, mw = m0 + wm * 64;
+  // integer sum), or element-wise stores (with the exact sums for tests, or
+  // fp32 outputs too large for LDS).
+  const int nw = n0 + wn * 32 * TN, mw = m0 + wm * 32 * TM;
   const int nr = ntot - nk;
-  const bool dbg = a.dbg_main != nullptr;
-  float sxm[2];
+  const bool direct = a.dbg_main != nullptr || (!a.y_bf16 && !C::F32_VIA_LDS);
+  float sxm[TM];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) sxm[j] = a.sx[min(mw + 32 * j + l32, a.M - 1)];
+  for (int j = 0; j < TM; ++j) sxm[j] = a.sx[min(mw + 32 * j + l32, a.M - 1)];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    v16f res[2];
+  for (int i = 0; i < TN; ++i) {
+    v16f res[TM];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TM; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) res[j][e] = 0.0f;
     for (int q = 0; q < nr; ++q) {
-      const uint8_t* bp = lds + ((nk + q) % kB6Stages) * kB6Stage + lane * kB6Frag;
+      const uint8_t* bp = lds + ((nk + q) % STAGES) * C::STAGE + lane * kB6Frag;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const v8i wf = ld_frag(bp + (wn * 2 + i) * kB6Block + st * kB6Step);
+        const v8i wf = ld_frag(bp + (wn * TN + i) * kB6Block + st * kB6Step);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          res[j] = mfma_bf6(wf, ld_frag(bp + kB6Half + (wm * 2 + j) * kB6Block + st * kB6Step), res[j]);
+        for (int j = 0; j < TM; ++j)
+          res[j] = mfma_bf6(wf, ld_frag(bp + C::W_HALF + (wm * TM + j) * kB6Block + st * kB6Step), res[j]);
       }
     }
 #pragma unroll
@@ -1710,8 +1729,8 @@ __global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a
         rv4[c] = nr > 0 ? a.sr[nc] : 0.0f;
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (dbg) {
+      for (int j = 0; j < TM; ++j) {
+        if (direct) {
           v4i am, ar;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
@@ -1729,34 +1748,34 @@ __global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a
       }
     }
   }
-  if (dbg) return;
+  if (direct) return;
   // Output tile into LDS (the stages are free once every wave is here), row =
   // token, 16-byte chunks swizzled as in the integer tile kernel; then 16-byte
   // stores along the rows of Y.
   lds_barrier();
   const bool bf = a.y_bf16;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = wm * 64 + 32 * j + l32;
+  for (int j = 0; j < TM; ++j) {
+    const int row = wm * 32 * TM + 32 * j + l32;
     if (bf) {
-      uint8_t* rp = lds + row * (kB6Tile * 2);
+      uint8_t* rp = lds + row * (C::BN * 2);
       const int hs = (h ^ half_swap(row)) * 8;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = (wn * 64 + 32 * i) / 8 + q;
+          const int c = (wn * 32 * TN + 32 * i) / 8 + q;
           const uint2 o = make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                                      pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
           *reinterpret_cast<uint2*>(rp + 16 * (c ^ (row & 15)) + hs) = o;
         }
-    } else {
-      uint8_t* rp = lds + row * (kB6Tile * 4);
+    } else if constexpr (C::F32_VIA_LDS) {
+      uint8_t* rp = lds + row * (C::BN * 4);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = (wn * 64 + 32 * i + 8 * q + 4 * h) / 4;
+          const int c = (wn * 32 * TN + 32 * i + 8 * q + 4 * h) / 4;
           *reinterpret_cast<float4*>(rp + 16 * (c ^ (row & 15))) =
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
@@ -1765,10 +1784,10 @@ __global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a
   __syncthreads();
   auto copy_out = [&](auto ebc) {
     constexpr int EB = decltype(ebc)::value;   // bytes per element
-    constexpr int CPR = kB6Tile * EB / 16;     // chunks per tile row
+    constexpr int CPR = C::BN * EB / 16;       // chunks per tile row
     constexpr int EPC = 16 / EB;               // elements per chunk
-    constexpr int RPP = 256 / CPR;             // rows per pass
-    constexpr int PASSES = kB6Tile / RPP;
+    constexpr int RPP = C::NT / CPR;           // rows per pass
+    constexpr int PASSES = C::BM / RPP;
     const int tid = threadIdx.x;
     const int c = tid % CPR;
     const int n = n0 + c * EPC;
@@ -1777,7 +1796,7 @@ __global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = p * RPP + tid / CPR;
-      v[p] = *reinterpret_cast<const uint4*>(lds + row * kB6Tile * EB + 16 * (c ^ (row & 15)));
+      v[p] = *reinterpret_cast<const uint4*>(lds + row * C::BN * EB + 16 * (c ^ (row & 15)));
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
@@ -1799,10 +1818,11 @@ __global__ __launch_bounds__(256, kB6Occ) void serq_bf6_tile_kernel(LinearArgs a
       }
     }
   };
-  if (bf)
+  if (bf) {
     copy_out(std::integral_constant<int, 2>{});
-  else
+  } else if constexpr (C::F32_VIA_LDS) {
     copy_out(std::integral_constant<int, 4>{});
+  }
 }
 
 // E3M2 pattern of a stored nibble (4-bit two's complement code): byte c of
@@ -1929,14 +1949,35 @@ hipError_t launch_act_bf6(const void* Xq, int M, int K, void* X6, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_linear_bf6(const LinearArgs& a, hipStream_t st) {
+namespace {
+
+template <int TN, int TM, int WNW, int WMW, int STAGES, int OCC>
+hipError_t launch_bf6_tile(const LinearArgs& a, hipStream_t st) {
+  using C = B6Cfg<TN, TM, WNW, WMW, STAGES, OCC>;
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_bf6_tile_kernel), kB6Lds, lds_set);
+  auto* fn = &serq_bf6_tile_kernel<TN, TM, WNW, WMW, STAGES, OCC>;
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(fn), C::LDS, lds_set);
   if (e != hipSuccess) return e;
-  const int n_tiles = (a.N + kB6Tile - 1) / kB6Tile;
-  const int m_tiles = (a.M + kB6Tile - 1) / kB6Tile;
-  serq_bf6_tile_kernel<<<dim3(n_tiles * m_tiles), dim3(256), kB6Lds, st>>>(a, n_tiles);
+  const int n_tiles = (a.N + C::BN - 1) / C::BN;
+  const int m_tiles = (a.M + C::BM - 1) / C::BM;
+  fn<<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS, st>>>(a, n_tiles);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// 256 x 256 tiles (eight waves, one workgroup per CU: half the L2->LDS bytes
+// per output of 128 x 128 and twice the MFMA work per barrier) when the
+// padded sizes split into them and they still give every CU a tile;
+// otherwise 128 x 128 tiles, two workgroups per CU.
+bool bf6_wide_tiles(int M, int N) {
+  const int mp = (M + kB6Tile - 1) / kB6Tile * kB6Tile, np = (N + kB6Tile - 1) / kB6Tile * kB6Tile;
+  return mp % 256 == 0 && np % 256 == 0 && static_cast<long>(mp / 256) * (np / 256) >= kCUs;
+}
+
+hipError_t launch_linear_bf6(const LinearArgs& a, hipStream_t st) {
+  if (bf6_wide_tiles(a.M, a.N)) return launch_bf6_tile<4, 2, 2, 4, 3, 1>(a, st);
+  return launch_bf6_tile<2, 2, 2, 2, 3, 2>(a, st);
 }
 
 }  // namespace serq
