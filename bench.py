@@ -25,8 +25,10 @@ or the HBM peak, with the counter-measured bytes per launch when they were
 taken on the current kernel sources. Beside the headline: "mlp_activation"
 (serq_silu_mul_quant_act on bf16 gate/up outputs of the 8B and 70B MLP
 widths, with the unfused pair for comparison), "mlp_step" (the whole 8B MLP:
-quant_act, gate/up, the fused activation, down) and "cpu_baseline" (the
-oracle on a bounded row sample).
+quant_act, gate/up, the fused activation, down), "bf6_route" (the same
+linear on the scaled FP6 MFMA with int4 codes re-encoded as E3M2, against
+serq_linear on the same codes, for prefill-sized layers) and "cpu_baseline"
+(the oracle on a bounded row sample).
 """
 
 from __future__ import annotations
@@ -385,6 +387,82 @@ def copy_probe(mib, reps=10):
     return 0
 
 
+FP6_PEAK_TOPS = 10100.0        # MI355X dense FP6/FP4 MFMA (no sparsity)
+BF6_SHAPES = (                 # (M, K, N, r): q_proj, 8B gate/up and down, 70B up and down
+    (2048, 4096, 4096, 64), (4096, 4096, 28672, 128), (4096, 14336, 4096, 128),
+    (8192, 8192, 28672, 256), (8192, 28672, 8192, 256))
+
+
+def time_bf6_route(shapes=BF6_SHAPES, reps=20):
+    """The bf6 route (serq_act_bf6 + serq_linear_bf6) against serq_linear on
+    the same random W4A4 codes: per-kernel times from graph replays, weights
+    rotated over copies beyond the last-level cache, and whether the outputs
+    are bit-identical."""
+    import numpy as np
+    import torch
+    import w4a4_linear_layers_amd as S
+    out = []
+    for (M, K, N, r) in shapes:
+        rng = np.random.default_rng(M + K + N + r)
+        Wp = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        Rp = np.zeros((N, S.rq_row_bytes(r)), np.uint8)
+        Rp[:, : r // 2] = rng.integers(0, 256, (N, r // 2), dtype=np.uint8)
+        W6 = torch.from_numpy(S._prepack(Wp, N, K, K // 2)).cuda()
+        R6 = torch.from_numpy(S._prepack(Rp, N, r, S.rq_row_bytes(r))).cuda()
+        copies = int(min(8, max(2, ROTATE_BYTES // (W6.numel() + M * K))))
+        sw = torch.rand(N, device="cuda") * 0.01
+        sr = torch.rand(N, device="cuda") * 0.001
+        sx = torch.rand(M, device="cuda")
+        L6 = [S.Bf6Layer(K=K, N=N, r=r, W6=W6.clone() if c else W6, sw=sw, R6=R6, sr=sr) for c in range(copies)]
+        Wd, Rd = torch.from_numpy(Wp).cuda(), torch.from_numpy(Rp).cuda()
+        L4 = [S.DeviceLayer(K=K, N=N, r=r, perm=None, s_hat_inv=None, Wq=Wd.clone() if c else Wd, sw=sw, Rq=Rd,
+                            sr=sr) for c in range(copies)]
+        Xs = [torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        X6s = [S.act_bf6(x, K) for x in Xs]
+        y6 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        y4 = torch.empty_like(y6)
+        S.linear_bf6(X6s[0], sx, L6[0], out=y6)
+        S.linear(Xs[0], sx, L4[0], a_bits=4, out=y4)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y6.view(torch.int16), y4.view(torch.int16)))
+
+        def timed(fn):
+            g = _graph_of(fn, reps)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        t6 = timed(lambda i: S.linear_bf6(X6s[i % copies], sx, L6[i % copies], out=y6))
+        t4 = timed(lambda i: S.linear(Xs[i % copies], sx, L4[i % copies], a_bits=4, out=y4))
+        x6o = torch.empty_like(X6s[0])
+        ta = timed(lambda i: S.act_bf6(Xs[i % copies], K, out=x6o))
+        ops = linear_ops(M, K, N, r)
+        out.append(dict(M=M, K=K, N=N, r=r, kernel=S.bf6_kernel_name(M, N), bit_identical=same,
+                        linear_bf6_us=round(t6, 2), act_bf6_us=round(ta, 2), serq_linear_us=round(t4, 2),
+                        TOPS=round(ops / t6 / 1e6, 1), frac_fp6_peak=round(ops / t6 / 1e6 / FP6_PEAK_TOPS, 4),
+                        speedup_vs_int8_path=round(t4 / t6, 3)))
+        del L6, L4, Xs, X6s, W6, R6, Wd, Rd
+        torch.cuda.empty_cache()
+    return out
+
+
+def _graph_of(fn, reps):
+    import torch
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,6 +473,7 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true", help="skip the other token counts and the MLP activation")
     ap.add_argument("--no-mlp-act", action="store_true", help="skip the MLP activation timing")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-bf6", action="store_true", help="skip the bf6 route timings")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (a reference kernel of known "
                          "traffic for scaling HBM byte counters), then exit")
@@ -476,6 +555,15 @@ def main(argv=None):
                   f"{e['gate_up_us']:.1f}, silu_mul_quant_act {e['silu_mul_quant_act_us']:.1f}, down "
                   f"{e['down_us']:.1f})", file=sys.stderr, flush=True)
 
+    bf6 = []
+    if not args.no_sweep and not args.no_bf6:
+        bf6 = time_bf6_route()
+        for e in bf6:
+            print(f"# bf6 route M={e['M']} K={e['K']} N={e['N']}: linear_bf6 {e['linear_bf6_us']:.1f} us "
+                  f"({e['kernel']}, {e['TOPS']:.0f} TOP/s) vs serq_linear {e['serq_linear_us']:.1f} us; "
+                  f"act_bf6 {e['act_bf6_us']:.1f} us; bit-identical {e['bit_identical']}",
+                  file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(setup, M)
@@ -496,6 +584,7 @@ def main(argv=None):
         "sweep": sweep,
         "mlp_activation": mlp_act,
         "mlp_step": mlp_step,
+        "bf6_route": bf6,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -258,15 +258,18 @@ extern "C" int serq_prepack_bf6(const uint8_t* codes, int rows, int k, int pitch
         for (int l = 0; l < 64; ++l) {
           const int row = rb * 32 + l % 32;
           const int k0 = kt * kBf6Tile + 64 * s + 32 * (l / 32);
-          uint8_t frag[24] = {0};
+          uint64_t word[3] = {0, 0, 0};       // the fragment as a little-endian 192-bit integer
           for (int f = 0; f < 32 && row < rows; ++f) {
             const int kk = k0 + f;
             if (kk >= k) break;
             const uint8_t byte = codes[static_cast<size_t>(row) * pitch + kk / 2];
-            const uint32_t pat = bf6_pattern((kk & 1) ? (byte >> 4) : (byte & 15u));
-            for (int b = 0; b < 6; ++b)
-              if (pat >> b & 1u) frag[(6 * f + b) / 8] |= static_cast<uint8_t>(1u << ((6 * f + b) % 8));
+            const uint64_t pat = bf6_pattern((kk & 1) ? (byte >> 4) : (byte & 15u));
+            const int bit = 6 * f;
+            word[bit / 64] |= pat << (bit % 64);
+            if (bit % 64 > 58) word[bit / 64 + 1] |= pat >> (64 - bit % 64);
           }
+          uint8_t frag[24];
+          for (int b = 0; b < 24; ++b) frag[b] = static_cast<uint8_t>(word[b / 8] >> (8 * (b % 8)));
           const size_t off = ((static_cast<size_t>(kt) * nrb + rb) * 2 + s) * 1536 + static_cast<size_t>(l) * 24;
           std::memcpy(out + off, frag, sizeof frag);
         }
