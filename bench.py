@@ -440,7 +440,7 @@ def time_bf6_route(shapes=BF6_SHAPES, reps=20):
         x6o = torch.empty_like(X6s[0])
         ta = timed(lambda i: S.act_bf6(Xs[i % copies], K, out=x6o))
         ops = linear_ops(M, K, N, r)
-        out.append(dict(M=M, K=K, N=N, r=r, kernel=S.bf6_kernel_name(M, N), bit_identical=same,
+        out.append(dict(M=M, K=K, N=N, r=r, kernel=S.bf6_kernel_name(M, N, r), bit_identical=same,
                         linear_bf6_us=round(t6, 2), act_bf6_us=round(ta, 2), serq_linear_us=round(t4, 2),
                         TOPS=round(ops / t6 / 1e6, 1), frac_fp6_peak=round(ops / t6 / 1e6 / FP6_PEAK_TOPS, 4),
                         speedup_vs_int8_path=round(t4 / t6, 3)))

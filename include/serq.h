@@ -326,11 +326,11 @@ int serq_linear_bf6(const void* X6, const float* sx,
 
 /*
  * serq_linear_bf6_kernel_name -- which tile serq_linear_bf6 launches for M
- * tokens and N outputs (static string "bf6_tile128x128" or
- * "bf6_tile256x256"), or NULL for M <= 0 or N <= 0. Host only; launches
- * nothing. For profiling and tests.
+ * tokens, N outputs and r salient rows (static string "bf6_tile128x128" or
+ * "bf6_tile256x256"), or NULL for M <= 0, N <= 0 or r < 0. Host only;
+ * launches nothing. For profiling and tests.
  */
-const char* serq_linear_bf6_kernel_name(int M, int N);
+const char* serq_linear_bf6_kernel_name(int M, int N, int r);
 
 #ifdef __cplusplus
 }

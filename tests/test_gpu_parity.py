@@ -507,6 +507,16 @@ def _bf6_layer(Wc, Rc, sw, sr, K, N, r):
     return S.Bf6Layer(K=K, N=N, r=r, W6=dev(W6), sw=dev(sw), R6=dev(R6), sr=dev(sr))
 
 
+def _bf6_tile(M, N):
+    """The tile rule stated with serq_linear_bf6's host code: a 256 side only
+    where the 128-row padding is a multiple of 256, and only with a tile for
+    every CU."""
+    mp, np_ = -(-M // 128) * 128, -(-N // 128) * 128
+    if mp % 256 == 0 and np_ % 256 == 0 and (mp // 256) * (np_ // 256) >= 256:
+        return "bf6_tile256x256"
+    return "bf6_tile128x128"
+
+
 BF6_CASES = [
     # M, K, N, r
     (1, 256, 128, 64),
@@ -521,6 +531,8 @@ BF6_CASES = [
     (1024, 256, 16384, 64),    # 256 x 256 tiles
     (1000, 300, 16284, 130),   # 256 x 256 tiles, ragged M, N and K, two residual k-tiles
     (2048, 1024, 8192, 0),     # 256 x 256 tiles, r = 0
+    (2048, 1024, 4096, 64),    # 128 x 128 tiles, 512 of them
+    (2000, 520, 4000, 200),    # 128 x 128 tiles, ragged M, N and K, two residual k-tiles
 ]
 
 
@@ -529,8 +541,7 @@ BF6_CASES = [
 def test_linear_bf6_bit_exact(M, K, N, r, out):
     """The bf6 route: exact integer accumulators against the oracle, Y within
     the epilogue tolerance, and Y bit-identical to serq_linear's."""
-    wide = (-(-M // 128) % 2 == 0) and (-(-N // 128) % 2 == 0) and (-(-M // 256)) * (-(-N // 256)) >= 256
-    assert S.bf6_kernel_name(M, N) == ("bf6_tile256x256" if wide else "bf6_tile128x128")
+    assert S.bf6_kernel_name(M, N, r) == _bf6_tile(M, N)
     Xc, Wc, Rc, sx, sw, sr, Xq, layer = _codes_case(M, K, N, r, 4, seed=M + K + N + r + 6)
     L6 = _bf6_layer(Wc, Rc, sw, sr, K, N, r)
     odt = torch.float32 if out == "f32" else torch.bfloat16

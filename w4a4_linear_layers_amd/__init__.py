@@ -363,7 +363,7 @@ def linear_bf6(x6, sx, layer: Bf6Layer, *, out_dtype=None, out=None, debug: bool
     return (y, am, ar) if debug else y
 
 
-def bf6_kernel_name(M: int, N: int) -> str | None:
+def bf6_kernel_name(M: int, N: int, r: int = 0) -> str | None:
     """The tile serq_linear_bf6 launches for these sizes."""
-    s = lib.serq_linear_bf6_kernel_name(M, N)
+    s = lib.serq_linear_bf6_kernel_name(M, N, r)
     return s.decode() if s else None

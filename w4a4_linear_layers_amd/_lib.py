@@ -70,7 +70,7 @@ def _load() -> ctypes.CDLL:
     lib.serq_act_bf6.restype = ip
     lib.serq_linear_bf6.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, vp, i32, vp, vp, vp]
     lib.serq_linear_bf6.restype = ip
-    lib.serq_linear_bf6_kernel_name.argtypes = [ip, ip]
+    lib.serq_linear_bf6_kernel_name.argtypes = [ip, ip, ip]
     lib.serq_linear_bf6_kernel_name.restype = ctypes.c_char_p
     return lib
 

@@ -158,7 +158,7 @@ extern "C" int serq_linear_bf6(const void* X6, const float* sx, const uint8_t* W
   return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
 }
 
-extern "C" const char* serq_linear_bf6_kernel_name(int M, int N) {
-  if (M <= 0 || N <= 0) return nullptr;
-  return serq::bf6_wide_tiles(M, N) ? "bf6_tile256x256" : "bf6_tile128x128";
+extern "C" const char* serq_linear_bf6_kernel_name(int M, int N, int r) {
+  if (M <= 0 || N <= 0 || r < 0) return nullptr;
+  return serq::bf6_tile_kind(M, N, r) == 2 ? "bf6_tile256x256" : "bf6_tile128x128";
 }

@@ -1548,21 +1548,24 @@ constexpr int kB6Block = 2 * kB6Step;               // 32 rows x 128 codes
 
 // Tile shape: each wave owns TN x TM blocks of 32 x 32, the workgroup a
 // WNW x WMW grid of waves; STAGES LDS buffers of one k-tile each, OCC
-// workgroups per CU. The first waves load the weight half of a stage, the
-// others the activation half, CHUNKS 1 KB chunks each.
+// workgroups per CU. Every wave loads an equal share of both halves of a
+// stage (WB weight and XB activation bytes): 1 KB instructions, the last one
+// of a share with 32 lanes when the share ends on a half kilobyte, so each
+// wave issues LOADS instructions per k-tile.
 template <int TN, int TM, int WNW, int WMW, int STAGES, int OCC>
 struct B6Cfg {
   static constexpr int NW = WNW * WMW, NT = 64 * NW;
   static constexpr int BN = 32 * TN * WNW, BM = 32 * TM * WMW;
   static constexpr int W_HALF = BN / 32 * kB6Block, X_HALF = BM / 32 * kB6Block;
   static constexpr int STAGE = W_HALF + X_HALF;
-  static constexpr int CHUNKS = STAGE / 1024 / NW;
-  static constexpr int NW_W = W_HALF / (CHUNKS * 1024);       // waves that load weights
+  static constexpr int WB = W_HALF / NW, XB = X_HALF / NW;
+  static constexpr int WI = (WB + 1023) / 1024, XI = (XB + 1023) / 1024;
+  static constexpr int LOADS = WI + XI;
   static constexpr int LDS = STAGES * STAGE;
   static constexpr bool F32_VIA_LDS = BM * BN * 4 <= LDS;     // else fp32 outputs are stored element-wise
-  static_assert(CHUNKS * 1024 * NW == STAGE && NW_W * CHUNKS * 1024 == W_HALF, "chunk split");
-  static_assert(OCC * LDS <= 160 * 1024 && (STAGES - 1) * CHUNKS < 64, "LDS, vmcnt range");
-  static_assert(STAGES >= 256 / kB6Tile + 1, "the residual k-tiles and the last main k-tile need distinct buffers");
+  static constexpr int MAX_RES = (STAGES - 1) * kB6Tile;      // residual k-tiles must fit beside the last main one
+  static_assert(WB * NW == W_HALF && XB * NW == X_HALF && WB % 512 == 0 && XB % 512 == 0, "load split");
+  static_assert(OCC * LDS <= 160 * 1024 && (STAGES - 1) * LOADS < 64, "LDS, vmcnt range");
   static_assert(BM * BN * 2 <= LDS && BN * 2 / 16 >= 16, "bf16 output tile in LDS");
 };
 
@@ -1609,13 +1612,19 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_bf6_tile_kernel(Line
   auto issue = [&](int t) {
     const int tl = min(t, ntot - 1);
     const int kt = tl < nk ? tl : tl - nk;
-    const uint8_t* src =
-        wv < C::NW_W
-            ? (tl < nk ? W6 : R6) + (static_cast<size_t>(kt) * rbn + n0 / 32) * kB6Block + wv * C::CHUNKS * 1024
-            : X6 + (static_cast<size_t>(kt) * rbm + m0 / 32) * kB6Block + (wv - C::NW_W) * C::CHUNKS * 1024;
-    const uint32_t dst = lds_base + (t % STAGES) * C::STAGE + wv * C::CHUNKS * 1024;
+    const uint8_t* wsrc = (tl < nk ? W6 : R6) + (static_cast<size_t>(kt) * rbn + n0 / 32) * kB6Block + wv * C::WB;
+    const uint8_t* xsrc = X6 + (static_cast<size_t>(kt) * rbm + m0 / 32) * kB6Block + wv * C::XB;
+    const uint32_t dst = lds_base + (t % STAGES) * C::STAGE;
 #pragma unroll
-    for (int c = 0; c < C::CHUNKS; ++c) dma16(src + c * 1024, 16 * lane, dst + c * 1024);
+    for (int c = 0; c < C::WI; ++c) {
+      if (C::WB - 1024 * c >= 1024 || lane < 32)
+        dma16(wsrc + c * 1024, 16 * lane, dst + wv * C::WB + c * 1024);
+    }
+#pragma unroll
+    for (int c = 0; c < C::XI; ++c) {
+      if (C::XB - 1024 * c >= 1024 || lane < 32)
+        dma16(xsrc + c * 1024, 16 * lane, dst + C::W_HALF + wv * C::XB + c * 1024);
+    }
   };
   // One MFMA step (64 codes) of a k-tile: the wave's TN weight and TM
   // activation fragments, then its TN x TM MFMAs.
@@ -1645,7 +1654,7 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_bf6_tile_kernel(Line
   // Every buffer starts loading; step 0 of k-tile 0 goes into registers.
 #pragma unroll
   for (int p = 0; p < STAGES; ++p) issue(p);
-  wait_vmcnt<(STAGES - 1) * C::CHUNKS>();
+  wait_vmcnt<(STAGES - 1) * C::LOADS>();
   lds_barrier();
   v8i w0[TN], x0[TM], w1[TN], x1[TM];
   read(0, 0, w0, x0);
@@ -1673,7 +1682,7 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_bf6_tile_kernel(Line
     read(t % STAGES, 1, w1, x1);
     mm(w0, x0, acc);
     pin(acc);
-    wait_vmcnt<(STAGES - 2) * C::CHUNKS>();
+    wait_vmcnt<(STAGES - 2) * C::LOADS>();
     lds_barrier();
     issue(t + STAGES);
     pin_frags(w1, x1);
@@ -1683,8 +1692,8 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_bf6_tile_kernel(Line
   read((nk - 1) % STAGES, 1, w1, x1);
   mm(w0, x0, acc);
   mm(w1, x1, acc);
-  // The residual k-tiles (at most two, in buffers the last main k-tile does
-  // not use) are complete and published.
+  // The residual k-tiles (at most STAGES - 1, the host checks, in buffers
+  // the last main k-tile does not use) are complete and published.
   wait_vmcnt<0>();
   lds_barrier();
 
@@ -1966,17 +1975,24 @@ hipError_t launch_bf6_tile(const LinearArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// 256 x 256 tiles (eight waves, one workgroup per CU: half the L2->LDS bytes
-// per output of 128 x 128 and twice the MFMA work per barrier) when the
-// padded sizes split into them and they still give every CU a tile;
-// otherwise 128 x 128 tiles, two workgroups per CU.
-bool bf6_wide_tiles(int M, int N) {
+// Tiles: 256 x 256 (eight waves of 4 x 2 blocks, one workgroup per CU:
+// half the L2->LDS bytes per output of 128 x 128 and twice the MFMA work per
+// barrier) when the padded sizes split into them and they give every CU a
+// tile; else 128 x 128, two workgroups per CU (a 256 x 128 tile of eight
+// 2 x 2-block waves, one workgroup per CU, measured 5-10 % slower than it on
+// q_proj at 2048 tokens: with one workgroup per CU nothing overlaps the
+// prologue and the epilogue). The layout pads rows to 128 only, so a 256 side
+// needs the padded size to be a multiple of 256.
+int bf6_tile_kind(int M, int N, int r) {
   const int mp = (M + kB6Tile - 1) / kB6Tile * kB6Tile, np = (N + kB6Tile - 1) / kB6Tile * kB6Tile;
-  return mp % 256 == 0 && np % 256 == 0 && static_cast<long>(mp / 256) * (np / 256) >= kCUs;
+  if (mp % 256 == 0 && np % 256 == 0 && static_cast<long>(mp / 256) * (np / 256) >= kCUs &&
+      r <= B6Cfg<4, 2, 2, 4, 3, 1>::MAX_RES)
+    return 2;
+  return 0;
 }
 
 hipError_t launch_linear_bf6(const LinearArgs& a, hipStream_t st) {
-  if (bf6_wide_tiles(a.M, a.N)) return launch_bf6_tile<4, 2, 2, 4, 3, 1>(a, st);
+  if (bf6_tile_kind(a.M, a.N, a.r) == 2) return launch_bf6_tile<4, 2, 2, 4, 3, 1>(a, st);
   return launch_bf6_tile<2, 2, 2, 2, 3, 2>(a, st);
 }
 

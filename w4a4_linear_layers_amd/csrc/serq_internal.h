@@ -51,6 +51,6 @@ hipError_t launch_silu_mul_quant_act(const void* G, const void* U, int ld, int x
 // layout; LinearArgs carries X6 / W6 / R6 in place of Xq / Wq / Rq.
 hipError_t launch_act_bf6(const void* Xq, int M, int K, void* X6, hipStream_t stream);
 hipError_t launch_linear_bf6(const LinearArgs& a, hipStream_t stream);
-bool bf6_wide_tiles(int M, int N);   // serq_linear_bf6 takes 256 x 256 tiles
+int bf6_tile_kind(int M, int N, int r);   // serq_linear_bf6's tile: 0 128x128, 2 256x256
 
 }  // namespace serq
