@@ -332,9 +332,9 @@ def linear_bf6(x6, sx, layer: Bf6Layer, *, out_dtype=None, out=None, debug: bool
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     K, N, r = layer.K, layer.N, layer.r
     _need_cuda(x6, sx, layer.W6, layer.sw, layer.R6 if r else None, layer.sr if r else None)
-    M = sx.shape[0]
     if sx.dim() != 1 or sx.dtype != torch.float32:
         raise ValueError("sx must be a float32 vector")
+    M = sx.shape[0]
     if x6.numel() != bf6_bytes(M, K) or x6.element_size() != 1:
         raise ValueError(f"x6 must hold bf6_bytes({M}, {K}) bytes")
     if layer.W6.numel() != bf6_bytes(N, K) or (r and layer.R6.numel() != bf6_bytes(N, r)):

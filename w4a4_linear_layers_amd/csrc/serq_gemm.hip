@@ -1969,6 +1969,7 @@ hipError_t launch_bf6_tile(const LinearArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int n_tiles = (a.N + C::BN - 1) / C::BN;
   const int m_tiles = (a.M + C::BM - 1) / C::BM;
+  if (static_cast<long long>(n_tiles) * m_tiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   fn<<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS, st>>>(a, n_tiles);
   return hipGetLastError();
 }
