@@ -474,6 +474,8 @@ def main(argv=None):
     ap.add_argument("--no-mlp-act", action="store_true", help="skip the MLP activation timing")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf6", action="store_true", help="skip the bf6 route timings")
+    ap.add_argument("--bf6", default=None, metavar="M:K:N:r[,...]",
+                    help="only time the bf6 route on the given shapes (one JSON line each), then exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (a reference kernel of known "
                          "traffic for scaling HBM byte counters), then exit")
@@ -487,6 +489,11 @@ def main(argv=None):
         k_s, m_s = args.mlp_act.split(":")
         for e in time_mlp_act(int(k_s), [int(m) for m in m_s.split(",")], n=max(args.steps, 20)):
             print(json.dumps(dict(kernel="serq_silu_mul_quant_act", **e)), flush=True)
+        return 0
+    if args.bf6:
+        shapes = [tuple(int(v) for v in sh.split(":")) for sh in args.bf6.split(",")]
+        for e in time_bf6_route(shapes, reps=max(args.steps, 5) if args.steps != 200 else 20):
+            print(json.dumps(dict(route="bf6", **e)), flush=True)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
