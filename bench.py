@@ -25,7 +25,8 @@ or the HBM peak, with the counter-measured bytes per launch when they were
 taken on the current kernel sources. Beside the headline: "mlp_activation"
 (serq_silu_mul_quant_act on bf16 gate/up outputs of the 8B and 70B MLP
 widths, with the unfused pair for comparison), "mlp_step" (the whole 8B MLP:
-quant_act, gate/up, the fused activation, down), "bf6_route" (the same
+quant_act, gate/up, the fused activation, down; at 4096 tokens also on the
+bf6 route, its output compared bit for bit), "bf6_route" (the same
 linear on the scaled FP6 MFMA with int4 codes re-encoded as E3M2, against
 serq_linear on the same codes, for prefill-sized layers) and "cpu_baseline"
 (the oracle on a bounded row sample).
@@ -271,6 +272,7 @@ def time_mlp_step(Ms, n=50, seed=0):
                              sw=L.sw.clone(), Rq=L.Rq.clone(), sr=L.sr.clone())
 
     pairs = [(clone(G0), clone(D0)) for _ in range(copies)]
+    bf6_pairs = []
     x = torch.from_numpy(np.ascontiguousarray(gu.X_bits[:, Lg.perm]).view(np.int16)).to(dev).view(torch.bfloat16)
     out = []
     for M in Ms:
@@ -315,6 +317,36 @@ def time_mlp_step(Ms, n=50, seed=0):
             step(0)                    # the buffers every part reads hold one real step's data
             e[k + "_us"] = round(timed(f), 2)
         e["kernels"] = [S.kernel_name(M, gu.K, 2 * Ni, 128), S.kernel_name(M, Ni, dn.N, 128)]
+        if M >= 4096:
+            # the same step on the bf6 route: both layers' codes re-encoded
+            # (activations on the device), the output compared bit for bit
+            if not bf6_pairs:
+                Bg, Bd = S.prepack_bf6(Lg).to(dev), S.prepack_bf6(Ld).to(dev)
+                cl6 = lambda B: S.Bf6Layer(K=B.K, N=B.N, r=B.r, W6=B.W6.clone(), sw=B.sw, R6=B.R6, sr=B.sr)  # noqa: E731
+                bf6_pairs.extend((cl6(Bg), cl6(Bd)) for _ in range(copies))
+            x6 = torch.empty(S.bf6_bytes(M, gu.K), dtype=torch.uint8, device=dev)
+            h6 = torch.empty(S.bf6_bytes(M, Ni), dtype=torch.uint8, device=dev)
+            yd6 = torch.empty_like(yd)
+            parts6 = [
+                lambda i: S.quant_act(x[:M], pairs[i % copies][0], out=(xq, sx)),
+                lambda i: S.act_bf6(xq, gu.K, out=x6),
+                lambda i: S.linear_bf6(x6, sx, bf6_pairs[i % copies][0], out=y),
+                lambda i: S.silu_mul_quant_act(y[:, :Ni], y[:, Ni:], pairs[i % copies][1], out=(hq, hs)),
+                lambda i: S.act_bf6(hq, Ni, out=h6),
+                lambda i: S.linear_bf6(h6, hs, bf6_pairs[i % copies][1], out=yd6),
+            ]
+
+            def step6(i):
+                for f in parts6:
+                    f(i)
+            step(0)
+            torch.cuda.synchronize()
+            ref = yd.clone()
+            step6(0)
+            torch.cuda.synchronize()
+            e["bf6_route_step_us"] = round(timed(step6), 2)
+            e["bf6_route_identical"] = bool(torch.equal(yd6.view(torch.int16), ref.view(torch.int16)))
+            e["bf6_route_kernels"] = [S.bf6_kernel_name(M, 2 * Ni, 128), S.bf6_kernel_name(M, dn.N, 128)]
         out.append(e)
     return out
 
@@ -560,7 +592,9 @@ def main(argv=None):
         for e in mlp_step:
             print(f"# mlp step M={e['M']}: {e['step_us']:.1f} us (quant_act {e['quant_act_us']:.1f}, gate/up "
                   f"{e['gate_up_us']:.1f}, silu_mul_quant_act {e['silu_mul_quant_act_us']:.1f}, down "
-                  f"{e['down_us']:.1f})", file=sys.stderr, flush=True)
+                  f"{e['down_us']:.1f})" + (f"; bf6 route {e['bf6_route_step_us']:.1f} us, identical "
+                                            f"{e['bf6_route_identical']}" if "bf6_route_step_us" in e else ""),
+                  file=sys.stderr, flush=True)
 
     bf6 = []
     if not args.no_sweep and not args.no_bf6:
