@@ -201,6 +201,20 @@ def test_prepack_bf6_of_a_calibrated_layer():
     assert np.array_equal(rc, O.unpack_int4(np.ascontiguousarray(L.Rq[:, : L.r // 2])))
 
 
+def test_bf6_tile_choice():
+    """serq_linear_bf6 takes 256 x 256 tiles only where the 128-row padding
+    of both operands is a multiple of 256 and the tiles give every one of the
+    256 CUs one; else 128 x 128."""
+    assert _lib.lib.serq_linear_bf6_kernel_name(0, 4096, 0) is None
+    assert _lib.lib.serq_linear_bf6_kernel_name(16, -1, 0) is None
+    assert _lib.lib.serq_linear_bf6_kernel_name(16, 16, -2) is None
+    for M, N in [(2048, 4096), (4096, 4096), (4000, 4096), (3900, 4096), (4096, 4000), (4096, 3800),
+                 (8192, 28672), (1024, 16384), (1000, 16284), (512, 4096), (1, 1), (2048, 8192)]:
+        mp, np_ = -(-M // 128) * 128, -(-N // 128) * 128
+        wide = mp % 256 == 0 and np_ % 256 == 0 and (mp // 256) * (np_ // 256) >= 256
+        assert S.bf6_kernel_name(M, N, 64) == ("bf6_tile256x256" if wide else "bf6_tile128x128"), (M, N)
+
+
 def test_python_wrapper_raises():
     with pytest.raises(S.SerqError):
         S.calibrate(np.zeros((5, 4), np.float32), np.ones(5, np.float32), r=2)   # odd K
