@@ -168,7 +168,8 @@ int serq_quant_act(const void* X, serq_dtype x_dtype, int M, int K,
  * LLaMA MLP, evaluated by a fixed fp32 recipe so results are reproducible
  * bit for bit: e = exp(-g) with the argument clamped to [-80, 80], by
  * Cody-Waite reduction (e^x = 2^n e^r, n = rne(x log2 e), ln 2 split in a
- * 12-bit head and a tail, r by two fused multiply-adds) and the degree-7
+ * head c_hi = 22713 * 2^-15 of 15 significant bits, so n c_hi is exact for
+ * |n| <= 116, and a tail; r by two fused multiply-adds) and the degree-7
  * Taylor polynomial of e^r (Horner, one fused multiply-add per degree); then
  * fl32(fl32(g / fl32(1 + e)) * u) with IEEE division and no other fused op.
  *

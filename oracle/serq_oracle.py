@@ -410,15 +410,16 @@ def linear_float_residual(Xq: dict, layer: dict) -> np.ndarray:
 #     h  = fl32(sg * u)
 # exp32 follows Cody and Waite's argument reduction: e^x = 2^n e^r with
 # n = rne(fl32(x log2 e)) and r = fma(-n, c_lo, fma(-n, c_hi, x)), where
-# c_hi + c_lo = ln 2 and c_hi has 12 significant bits (so n c_hi, |n| < 2^11,
-# is exact and the first fma is exact too); e^r (|r| <= ln2 / 2) is its
+# c_hi + c_lo = ln 2 and c_hi = 22713 * 2^-15 has 15 significant bits (the
+# clamp keeps |n| <= 116, 7 bits, so n c_hi has at most 22 significant bits
+# and is exact, and the first fma is exact too); e^r (|r| <= ln2 / 2) is its
 # Taylor polynomial to degree 7 in Horner form, p <- fma(p, r, 1/k!)
 # (truncation below 2^-27 relative), then scaled by 2^n exactly. The clamp
 # keeps every intermediate a normal number.
 # ---------------------------------------------------------------------------
 
 LOG2E_F32 = np.float32(1.0 / math.log(2.0))
-LN2_HI_F32 = np.float32(0.693145751953125)                  # 12 significant bits
+LN2_HI_F32 = np.float32(0.693145751953125)                  # 22713 * 2^-15: 15 significant bits
 LN2_LO_F32 = np.float32(math.log(2.0) - 0.693145751953125)
 EXP_TAYLOR_F32 = [np.float32(1.0 / math.factorial(k)) for k in range(8)]   # 1/k!
 EXP_ARG_CLAMP = np.float32(80.0)

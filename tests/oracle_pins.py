@@ -480,7 +480,65 @@ def check_silu_mul(O):
         assert np.allclose(a["sx"], b["sx"], rtol=1e-6, atol=0)
 
 
+# ---------------------------------------------------------------- sampled columns
+
+def check_calibrate_columns(O):
+    """calibrate_columns (the expected values of full-size checks on sampled
+    output columns) equals calibrate restricted to those columns, bit for
+    bit. [N] 关键设计 1: s is per input channel, over the whole weight row,
+    so it (and P) must not depend on which columns are sampled; [N] 关键设计 2
+    and [GDE] 3: the weight and R quantizers are per output column, so a
+    column's codes and scales depend only on that column once s, P are fixed."""
+    rng = np.random.default_rng(21)
+    cases = []
+    # ties and dead channels: equal s on several channels, an all-zero
+    # weight row and a zero activation maximum
+    K, N = 32, 40
+    W = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    a = (rng.random(K) * 3 + 0.5).astype(np.float32)
+    W[5] = W[9]
+    a[5] = a[9]
+    W[12] = W[20]
+    a[12] = a[20]
+    W[17] = 0.0
+    a[3] = 0.0
+    cases.append((W, a, 8, 0.5))
+    W2, a2, _ = _small_layer(seed=7, K=48, N=36)
+    cases.append((W2, a2, 0, 0.5))           # r = 0
+    cases.append((W2, a2, 48, 0.5))          # r = K
+    cases.append((W2, a2, 12, 0.3))          # another alpha
+    for W, a, r, alpha in cases:
+        full = O.calibrate(W, a, alpha=alpha, r=r)
+        N = W.shape[1]
+        for cols in (np.array([0, N - 1]), np.sort(rng.choice(N, N // 3, replace=False)), np.arange(N)):
+            part = O.calibrate_columns(W, a, cols, alpha=alpha, r=r)
+            assert np.array_equal(part["perm"], full["perm"])
+            assert np.array_equal(part["s_hat_inv"].view(np.uint32), full["s_hat_inv"].view(np.uint32))
+            assert np.array_equal(part["Wq_codes"], full["Wq_codes"][:, cols])
+            assert np.array_equal(part["sw"].view(np.uint32), full["sw"][cols].view(np.uint32))
+            assert np.array_equal(part["Wq"], full["Wq"][cols])
+            assert np.array_equal(part["Rq_codes"], full["Rq_codes"][:, cols])
+            assert np.array_equal(part["sr"].view(np.uint32), full["sr"][cols].view(np.uint32))
+            assert np.array_equal(part["Rq"], full["Rq"][cols])
+
+
+def check_exp_split_constant(O):
+    """The exponential's reduction constants: c_hi = 22713 * 2^-15 (15
+    significant bits), c_hi + c_lo within 2^-40 of ln 2, and n * c_hi exact
+    in binary32 for every n the clamp allows (|n| <= 116)."""
+    hi = Fraction(float(O.LN2_HI_F32))
+    assert hi == Fraction(22713, 2 ** 15)
+    assert 22713 % 2 == 1 and 2 ** 14 <= 22713 < 2 ** 15
+    lo = Fraction(float(O.LN2_LO_F32))
+    assert abs(float(hi + lo) - math.log(2.0)) < 2.0 ** -40
+    nmax = int(np.rint(np.float32(O.EXP_ARG_CLAMP) * O.LOG2E_F32))
+    assert nmax <= 116
+    for n in range(-nmax, nmax + 1):
+        assert Fraction(float(np.float32(n) * O.LN2_HI_F32)) == n * hi
+
+
 ALL_CHECKS = [check_pack, check_quantizer_golden, check_quantizer_bruteforce, check_smoothing,
               check_perm, check_fold_identity, check_compensator, check_int_gemm,
               check_dequant_identity, check_special_cases, check_worked_layer, check_bf16,
-              check_permute_outputs, check_rank_trend, check_fma32, check_exp32, check_silu_mul]
+              check_permute_outputs, check_rank_trend, check_fma32, check_exp32, check_silu_mul,
+              check_calibrate_columns, check_exp_split_constant]

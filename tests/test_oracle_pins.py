@@ -151,6 +151,32 @@ def _mut_fused_skips_silu(orig):
     return lambda G, U, s_hat_inv, a_bits: O.quant_act((np.asarray(G, np.float32) * np.asarray(U, np.float32)).astype(np.float32), s_hat_inv, a_bits)
 
 
+def _mut_columns_s_from_sampled(orig):
+    """s formed from the sampled columns' row maxima instead of all of W."""
+    def f(W, act_absmax, cols, *, alpha=O.ALPHA_DEFAULT, r):
+        W = np.asarray(W, np.float32)
+        Wc = W[:, cols]
+        s, s_inv = O.smoothing_factors(act_absmax, np.abs(Wc).max(axis=1), alpha)
+        perm = O.saliency_order(s)
+        W_hat = O.fold_and_permute(Wc, s, perm)
+        Wq_codes, sw = O.quantize_columns(W_hat, 4)
+        R = O.compensator(W_hat, O.dequantize_columns(Wq_codes, sw), r)
+        Rq_codes, sr = O.quantize_columns(R, 4)
+        return dict(s=s, s_inv=s_inv, perm=perm, s_hat_inv=s_inv[perm], cols=np.asarray(cols),
+                    Wq_codes=Wq_codes, sw=sw, Rq_codes=Rq_codes, sr=sr, Wq=O.pack_int4(Wq_codes.T),
+                    Rq=O.pack_int4(Rq_codes.T) if r else np.zeros((len(cols), 0), np.uint8))
+    return f
+
+
+def _mut_columns_codes_shifted(orig):
+    """An off-by-one in the sampled columns (the next column's codes)."""
+    def f(W, act_absmax, cols, **kw):
+        W = np.asarray(W, np.float32)
+        cols = np.asarray(cols)
+        return orig(W, act_absmax, np.minimum(cols + 1, W.shape[1] - 1), **kw)
+    return f
+
+
 MUTANTS = {
     "compensator_sign": ("compensator", _mut_compensator_sign),
     "saliency_ascending": ("saliency_order", _mut_saliency_ascending),
@@ -169,6 +195,8 @@ MUTANTS = {
     "fma_double_rounding": ("fma32", _mut_fma_double_rounding),
     "silu_sign": ("silu_mul", _mut_silu_sign),
     "fused_skips_silu": ("silu_mul_quant_act", _mut_fused_skips_silu),
+    "columns_s_from_sampled": ("calibrate_columns", _mut_columns_s_from_sampled),
+    "columns_codes_shifted": ("calibrate_columns", _mut_columns_codes_shifted),
 }
 
 

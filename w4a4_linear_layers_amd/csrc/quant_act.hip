@@ -72,8 +72,9 @@ __device__ __forceinline__ int qcode(float v, float inv) {
 // saliency order, the permutation having been pushed into gate and up
 // offline -- papernotes.org SERQ notes, 关键设计 3). e^x by Cody and Waite's
 // reduction: e^x = 2^n e^r, n = rne(x log2 e), r = fma(-n, c_lo,
-// fma(-n, c_hi, x)) with c_hi + c_lo = ln 2 and c_hi of 12 significant bits
-// (n c_hi exact), then the degree-7 Taylor polynomial of e^r in Horner form,
+// fma(-n, c_hi, x)) with c_hi + c_lo = ln 2 and c_hi = 22713 * 2^-15 of 15
+// significant bits (|n| <= 116 after the clamp, so n c_hi has at most 22
+// significant bits and is exact), then the degree-7 Taylor polynomial of e^r in Horner form,
 // one fused multiply-add per degree, and an exact scaling by 2^n; the
 // argument is clamped to [-80, 80] so every step stays a normal number.
 // Every other operation is one fp32 op (the build disables contraction into
