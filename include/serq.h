@@ -28,9 +28,10 @@
  *     half to even. A group whose fl32(qmax / m) overflows (an all-zero group
  *     in particular) gets scale 0 and zero codes.
  *   - The caller owns every input and output. The library creates no
- *     streams; the only device memory it holds is scratch for two paths
- *     (serq_linear's K split, chunked activation quantization), described
- *     at those calls: calls that take them must not overlap on one device.
+ *     streams and allocates no memory; the only device memory it holds is
+ *     scratch for two paths (serq_linear's K split, chunked activation
+ *     quantization) in file-scope device arrays, described at those calls:
+ *     calls that take them must not overlap on one device.
  *   - Argument errors are detected on the host and returned before anything
  *     is launched; the output buffers are then untouched.
  *   - Online calls only enqueue work on `stream` (a hipStream_t; NULL is the
@@ -122,12 +123,14 @@ int serq_calibrate(const void* W, serq_dtype w_dtype, int K, int N,
  *
  *   perm_next  N int32, a permutation of 0..N-1: new output channel i is old
  *              channel perm_next[i].
- *   Wq (N x K/2 bytes), sw (N), Rq (N x SERQ_RQ_ROW_BYTES(r)), sr (N) are reordered in
- *   place. Rq and sr may be NULL when r == 0.
+ *   K, N, r    this layer's sizes, in serq_calibrate's order (K inputs, N
+ *              outputs, r salient rows).
+ *   Wq (N x K/2 bytes), sw (N), Rq (N x SERQ_RQ_ROW_BYTES(r)), sr (N) are
+ *   reordered in place. Rq and sr may be NULL when r == 0.
  * Errors: SERQ_EINVAL for NULL pointers, bad sizes, or perm_next not a
  * permutation (detected before anything is modified).
  */
-int serq_permute_outputs(const int32_t* perm_next, int N, int K, int r,
+int serq_permute_outputs(const int32_t* perm_next, int K, int N, int r,
                          uint8_t* Wq, float* sw, uint8_t* Rq, float* sr);
 
 /*
@@ -217,12 +220,16 @@ int serq_silu_mul_quant_act(const void* G, const void* U, int ld, serq_dtype x_d
  *              NULL on the hot path; when non-NULL, device M x N int32
  *              buffers that receive the exact integer accumulators (both
  *              must then be given).
- * Workspace: for 4..32 tokens whose activation rows exceed the kernel's LDS
- * budget (long K), the K range is split across workgroups and their int32
- * partial sums meet in a per-device workspace that the library allocates
- * (hipMalloc, zeroed) on the first such call and grows when a later call
- * needs more; such calls on one device must not overlap (they share it), and
- * the first one must not run under stream capture.
+ * No allocation, no synchronization: the call only enqueues kernels, so it
+ * may be captured into a HIP graph, the first call on a device included.
+ * Scratch: for 4..32 tokens whose activation rows exceed the kernel's LDS
+ * budget (long K), the K range is split across workgroups whose int32
+ * partial sums meet in file-scope device arrays of the library (16 MiB of
+ * partial sums and 64 KiB of counters per device, held from the moment the
+ * library's code is loaded on the device until the process ends). Sizes
+ * whose split would need more take a kernel without a split, so no size is
+ * refused for it. Calls that take the split path on one device share the
+ * arrays, so they must not overlap in time (e.g. on two streams at once).
  * Errors: SERQ_EINVAL (NULL pointer, bad sizes, bad a_bits or dtype, only one
  * debug buffer), SERQ_EALIGN (pointer not 16-byte aligned), SERQ_EHIP.
  */
@@ -236,8 +243,9 @@ int serq_linear(const void* Xq, const float* sx, int a_bits,
 
 /*
  * serq_linear_kernel_name -- which kernel serq_linear would launch for these
- * sizes (static string: "decode", "tile256x256", ..., "generic"), or NULL
- * for invalid sizes. Host only; launches nothing. For profiling and tests.
+ * sizes (static string: "gemv", "decode16", "decode32_ksplit" (the K split
+ * with scratch), "tile128x128", ..., "generic"), or NULL for invalid sizes.
+ * Host only; launches nothing. For profiling and tests.
  */
 const char* serq_linear_kernel_name(int M, int K, int N, int r, int a_bits);
 

@@ -38,7 +38,7 @@ def test_header_declarations_are_exported():
 
 
 def test_strerror_and_version():
-    assert _lib.lib.serq_abi_version() == 202
+    assert _lib.lib.serq_abi_version() == 300
     for code in (0, -1, -2, -3, -4, 7):
         assert _lib.lib.serq_strerror(code)
 
@@ -339,7 +339,7 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(3, 4096, 4096, 64) == "gemv"
     assert S.kernel_name(4, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(4, 4096, 4096, 64, 8) == "decode16"     # W4A8: no int4 dot products
-    assert S.kernel_name(4, 65536, 4096, 64) == "decode16"       # activation rows beyond the LDS budget
+    assert S.kernel_name(4, 65536, 4096, 64) == "decode16"       # activation rows beyond the GEMV's LDS budget
     assert S.kernel_name(5, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(16, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(32, 4096, 14336, 128) == "decode32"
@@ -360,6 +360,24 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(16, 4096, 64, 6) == "generic"      # r % 8 != 0
     assert S.kernel_name(16, 4096, 64, 512) == "generic"    # r > 256
     assert S.kernel_name(16, 63, 64, 8) is None
+
+
+def test_kernel_dispatch_split_scratch_bound():
+    """The K split's partial sums live in 16 MiB of file-scope device scratch:
+    shapes whose split would need more take a tile kernel instead (nothing is
+    allocated and no size is refused). A 32-token split keeps 2 x 32 x 16 x 4
+    bytes per 16 output channels and K slice."""
+    assert S.kernel_name(32, 14336, 4096, 128) == "decode32_ksplit"      # 8B down: 256 groups x 2 slices
+    assert S.kernel_name(32, 28672, 8192, 256) == "decode32_ksplit"      # 70B down: 512 groups x 4 slices
+    assert S.kernel_name(32, 28672, 8192, 256, 8) == "decode32_ksplit"   # W4A8: 512 groups x 8 slices (16 MiB)
+    assert S.kernel_name(20, 14336, 4096, 128) == "decode32"             # fits in LDS: one slice
+    # 2048 groups x 8 slices x 4 KB = 64 MiB of partial sums: no split, no skinny kernel
+    name = S.kernel_name(32, 65536, 32768, 64)
+    assert name.startswith("tile"), name
+    # W4A8 at 16 tokens: 1024 groups x 14 slices x 2 KB = 28 MiB
+    assert S.kernel_name(16, 131072, 16384, 64, 4) == "decode16_ksplit"   # 7 slices: 14 MiB
+    name = S.kernel_name(16, 131072, 16384, 64, 8)
+    assert name.startswith("tile"), name
 
 
 def test_single_hip_runtime_in_process():

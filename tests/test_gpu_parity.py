@@ -277,7 +277,7 @@ LINEAR_CASES = [
 def test_linear_codes_bit_exact(M, K, N, r, kern, bits, out):
     if kern == "gemv" and bits == 8:
         kern = "decode16"                 # the int4 dot-product kernel is W4A4 only
-    assert S.kernel_name(M, K, N, r, bits) == kern
+    assert S.kernel_name(M, K, N, r, bits).removesuffix("_ksplit") == kern
     _run_codes(M, K, N, r, bits, out, seed=M + K + N + r + bits, col_sample=512 if N > 2048 else None)
 
 
@@ -319,18 +319,36 @@ def test_linear_on_side_stream_and_empty():
 
 # ------------------------------------------------ the layer workloads, end to end
 
-def _end_to_end(li, r, bits, out, Ms, *, row_sample=48, col_sample=192, seed=0, layer=None):
-    """Library calibration + GPU quant_act + GPU linear vs the oracle's
-    calibration, activation quantization and linear on sampled rows/columns."""
-    W_in = li.W_bits if li.dtype == "bf16" else li.W
-    L = S.calibrate(W_in, li.act_absmax, r=r) if layer is None else layer
-    D = L.to("cuda")
-    cols = sample(li.N, col_sample, seed + 1)
-    R = O.calibrate_columns(li.W, li.act_absmax, cols, r=r)
+def _end_to_end(li, r, bits, out, Ms, *, row_sample=48, col_sample=192, seed=0, W=None, W_in=None):
+    """Library calibration + GPU quant_act + GPU linear vs the oracle.
+
+    Bit-exact on full tensors: perm, s_hat_inv, Q(W^), Q(R) and their scales
+    for every output column (oracle calibrate on the whole layer), and the
+    activation codes and scales of every token row. The accumulators and Y
+    on sampled rows x columns (always the first and last of each). ``W`` /
+    ``W_in`` replace the layer's weight (fp32 values / the library's input,
+    bf16 bit patterns for bf16 workloads), e.g. gate and up side by side."""
+    W = li.W if W is None else W
+    if W_in is None:
+        W_in = li.W_bits if li.dtype == "bf16" else li.W
+    N = W.shape[1]
+    print(f"calibrate {W.shape[0]} x {N}, r = {r}", flush=True)
+    L = S.calibrate(W_in, li.act_absmax, r=r)
+    R = O.calibrate(W, li.act_absmax, r=r)
     assert np.array_equal(L.perm, R["perm"])
-    assert np.array_equal(L.Wq[cols], R["Wq"]) and np.array_equal(L.Rq[cols], pad_rq(R["Rq"], r))
+    assert np.array_equal(L.s_hat_inv.view(np.uint32), R["s_hat_inv"].view(np.uint32))
+    assert np.array_equal(L.Wq, R["Wq"])
+    assert np.array_equal(L.sw.view(np.uint32), R["sw"].view(np.uint32))
+    assert np.array_equal(L.Rq, pad_rq(R["Rq"], r))
+    assert np.array_equal(L.sr.view(np.uint32), R["sr"].view(np.uint32))
+    D = L.to("cuda")
+    cols = sample(N, col_sample, seed + 1)
+    Wc, Rc = R["Wq_codes"][:, cols], R["Rq_codes"][:, cols]
+    sw, sr = R["sw"][cols], R["sr"][cols]
+    del R
     odt = torch.float32 if out == "f32" else torch.bfloat16
     for M in Ms:
+        print(f"M = {M}: {S.kernel_name(M, W.shape[0], N, r, bits)}", flush=True)
         if li.dtype == "bf16":
             xt = bf16_tensor(li.X_bits[:M][:, L.perm])
         else:
@@ -338,15 +356,24 @@ def _end_to_end(li, r, bits, out, Ms, *, row_sample=48, col_sample=192, seed=0, 
         xq, sx = S.quant_act(xt, D, a_bits=bits)
         y, am, ar = S.linear(xq, sx, D, a_bits=bits, out_dtype=odt, debug=True)
         _sync()
+        q = O.quant_act(li.X[:M][:, L.perm], L.s_hat_inv, bits)
+        assert np.array_equal(host(xq).view(np.uint8), q["packed"].view(np.uint8))
+        assert np.array_equal(host(sx).view(np.uint32), q["sx"].view(np.uint32))
         rows = sample(M, row_sample, seed + M)
-        q = O.quant_act(li.X[rows][:, R["perm"]], R["s_hat_inv"], bits)
-        assert np.array_equal(host(xq)[rows].view(np.uint8), q["packed"].view(np.uint8))
-        assert np.array_equal(host(sx)[rows].view(np.uint32), q["sx"].view(np.uint32))
-        am_ref, ar_ref = O.linear_int(q["codes"], R["Wq_codes"], R["Rq_codes"], r)
+        am_ref, ar_ref = O.linear_int(q["codes"][rows], Wc, Rc, r)
         assert np.array_equal(host(am)[np.ix_(rows, cols)], am_ref)
         assert np.array_equal(host(ar)[np.ix_(rows, cols)], ar_ref)
-        check_y(host(y)[np.ix_(rows, cols)], am_ref, ar_ref, q["sx"], R["sw"], R["sr"], out)
+        check_y(host(y)[np.ix_(rows, cols)], am_ref, ar_ref, q["sx"][rows], sw, sr, out)
+        del xt, xq, sx, y, am, ar, q
     return L
+
+
+def _gate_up_cat(li):
+    """Gate and up side by side, K x 2N: the layer the two share one input
+    as (calibrated together, one s and P for both)."""
+    W = np.concatenate([li.W, li.meta["W_up"]], axis=1)
+    W_in = np.concatenate([li.W_bits, li.meta["W_up_bits"]], axis=1)
+    return W, W_in
 
 
 def test_workload_tiny_full():
@@ -364,15 +391,19 @@ def test_workload_q_proj():
 @pytest.mark.slow
 @pytest.mark.parametrize("layer", ["gate_up", "down"])
 def test_workload_mlp8b(layer):
+    """gate/up as the one 4096 -> 2 x 14336 layer (gate and up share their
+    input, so they are calibrated together), down 14336 -> 4096."""
     li = workload_layer("mlp8b", layer)
-    _end_to_end(li, 128, 4, "bf16", [1, 32, 4096])
+    W, W_in = _gate_up_cat(li) if layer == "gate_up" else (None, None)
+    _end_to_end(li, 128, 4, "bf16", [1, 32, 4096], W=W, W_in=W_in)
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("layer", ["gate_up", "down"])
 def test_workload_mlp8b_w4a8(layer):
     li = workload_layer("mlp8b_w4a8", layer)
-    _end_to_end(li, 128, 8, "bf16", [2048])
+    W, W_in = _gate_up_cat(li) if layer == "gate_up" else (None, None)
+    _end_to_end(li, 128, 8, "bf16", [2048], W=W, W_in=W_in)
 
 
 @pytest.mark.slow

@@ -132,7 +132,7 @@ def permute_outputs(layer: SerqLayer, perm_next) -> SerqLayer:
     (serq_permute_outputs), in place on the host arrays; returns ``layer``."""
     p = np.ascontiguousarray(perm_next, dtype=np.int32)
     check("serq_permute_outputs",
-          lib.serq_permute_outputs(_ptr(p), layer.N, layer.K, layer.r, _ptr(layer.Wq), _ptr(layer.sw),
+          lib.serq_permute_outputs(_ptr(p), layer.K, layer.N, layer.r, _ptr(layer.Wq), _ptr(layer.sw),
                                    _ptr(layer.Rq) if layer.r else None, _ptr(layer.sr) if layer.r else None))
     return layer
 

@@ -50,21 +50,26 @@ def build(verbose: bool = False, asm_dir: str | None = None) -> str:
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    objs, cmds = [], []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc] + common_flags() + lang + ["-c", path, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        cmds.append([cc] + common_flags() + lang + ["-c", path, "-o", obj])
         objs.append(obj)
         if asm_dir and src.endswith(".hip"):
             os.makedirs(asm_dir, exist_ok=True)
             out = os.path.join(asm_dir, os.path.splitext(src)[0] + ".s")
-            subprocess.run([cc] + common_flags() + lang + ["--cuda-device-only", "-S", path, "-o", out],
-                           check=True)
+            cmds.append([cc] + common_flags() + lang + ["--cuda-device-only", "-S", path, "-o", out])
+    # the translation units are independent: compile them side by side
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
+    failed = [cmd for cmd, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp] + objs + ["-lpthread"]
     if verbose:

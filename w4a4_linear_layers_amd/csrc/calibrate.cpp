@@ -196,7 +196,7 @@ extern "C" int serq_calibrate(const void* W, serq_dtype w_dtype, int K, int N,
   return SERQ_OK;
 }
 
-extern "C" int serq_permute_outputs(const int32_t* perm_next, int N, int K, int r,
+extern "C" int serq_permute_outputs(const int32_t* perm_next, int K, int N, int r,
                                     uint8_t* Wq, float* sw, uint8_t* Rq, float* sr) {
   if (!perm_next || !Wq || !sw) return SERQ_EINVAL;
   if (N <= 0 || K <= 0 || (K & 1) || (r & 1) || r < 0 || r > K) return SERQ_EINVAL;

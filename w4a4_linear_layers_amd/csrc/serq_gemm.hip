@@ -30,7 +30,6 @@
 // its first 16 codes and step 1 the next 16.
 
 #include <atomic>
-#include <mutex>
 #include <utility>
 
 #include "serq_internal.h"
@@ -901,15 +900,26 @@ constexpr int kSkxWaves = 8;
 constexpr int kSkxMaxGroups = 8;            // groups per workgroup
 constexpr int kSkxLds = 159 * 1024;         // dynamic LDS bytes: activation slice + group slots
                                             // (the rest of the 160 KB holds the static flag)
-constexpr int kSkxCounters = 16384;         // group-set counters at the start of the workspace
 
 template <int MG>
 constexpr int skx_slot_bytes() { return 2 * MG * 64 * 16; }
 
+// Scratch of the K split (KS > 1): one counter per group set and the slices'
+// int32 partial sums, KS x ngroups x [main, residual][token block][lane].
+// Both are file-scope device arrays, so each device holds its own copy from
+// the moment the code object is loaded, zero-filled, and no call allocates:
+// a plan whose partial sums would not fit takes a tile kernel instead. Every
+// counter is zero when a launch starts (zero at load; the last workgroup of
+// a group set puts its counter back to zero, and the next launch on the
+// stream starts after that one has ended). Launches that take the split
+// path on one device share the arrays, so they must not overlap in time.
+constexpr int kSkxCounters = 16384;                       // group sets per split launch, at most
+constexpr size_t kSkxPartBytes = size_t{16} << 20;        // partial sums per split launch, at most
+__device__ __align__(256) int skx_counters[kSkxCounters];
+__device__ __align__(256) v4i skx_partials[kSkxPartBytes / sizeof(v4i)];
+
 struct SkinnySplit {
   int G, nb, KS, seg;       // groups per workgroup, group sets, K slices, chunks per slice
-  int* cnt;                 // kSkxCounters zeroed counters (KS > 1)
-  v4i* part;                // KS x ngroups x [main, residual][token block][lane] partial sums (KS > 1)
 };
 
 template <int MG, int A_BITS, int IPW>
@@ -1068,13 +1078,25 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
   lds_barrier();
 
   if (sp.KS > 1) {
-    // Partial sums out with agent-scope stores (written through to the
-    // point of coherence of all XCDs, so no whole-L2 write-back is needed),
-    // waited for before the counter is bumped; the group set's last
-    // workgroup then reads them with agent-scope loads. Slice 0 alone holds
-    // residual sums.
+    // Partial sums out, counter, last workgroup reads them back. Every byte
+    // that crosses workgroups (partial sums, counters) is accessed only by
+    // agent-scope atomic operations, never by plain loads or stores. On
+    // gfx950 (the gfx942 memory model) the relaxed agent-scope store and load
+    // are global_store / global_load with sc1, which write through to and
+    // read from the point where all XCDs are coherent, and the counter RMW is
+    // performed there too. The ordering that a release / acquire pair would
+    // give is made by the hardware sequence instead: s_waitcnt vmcnt(0) waits
+    // for every partial-sum store's acknowledgement (the data is at the
+    // coherence point) before the counter RMW is issued; the group set's last
+    // workgroup sees KS - 1 returned only after all KS RMWs, and issues its
+    // loads after that return (vmcnt wait, then barrier), so they observe
+    // every slice's stores. What release / acquire would add -- a write-back
+    // of the whole L2 before the RMW and an invalidation of it after -- only
+    // matters for data moved by plain stores and loads, of which there is
+    // none here (and each costs more than the whole split saves). Slice 0
+    // alone holds residual sums.
     if (wv < Gb) {
-      long long* dst = reinterpret_cast<long long*>(sp.part + (static_cast<size_t>(ks) * ngroups + grp(wv)) * SLOT);
+      long long* dst = reinterpret_cast<long long*>(skx_partials + (static_cast<size_t>(ks) * ngroups + grp(wv)) * SLOT);
       const long long* src = reinterpret_cast<const long long*>(slots + wv * SLOT);
       const int hn = ks == 0 && has_res ? 2 * MG : MG;
       for (int h = 0; h < hn; ++h)
@@ -1086,10 +1108,10 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
     wait_vmcnt<0>();
     lds_barrier();
     if (threadIdx.x == 0)
-      s_last = __hip_atomic_fetch_add(sp.cnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.KS - 1;
+      s_last = __hip_atomic_fetch_add(skx_counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == sp.KS - 1;
     lds_barrier();
     if (!s_last) return;
-    if (threadIdx.x == 0) __hip_atomic_store(sp.cnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(skx_counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (wv >= Gb) return;
   v4i sm[MG], sr[MG];
@@ -1101,7 +1123,7 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
     }
   } else {
     auto ld = [&](int q, int h) {
-      const long long* src = reinterpret_cast<const long long*>(sp.part + (static_cast<size_t>(q) * ngroups + grp(wv)) * SLOT);
+      const long long* src = reinterpret_cast<const long long*>(skx_partials + (static_cast<size_t>(q) * ngroups + grp(wv)) * SLOT);
       const long long lo = __hip_atomic_load(src + (h * 64 + lane) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const long long hi = __hip_atomic_load(src + (h * 64 + lane) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return v4i{static_cast<int>(lo), static_cast<int>(lo >> 32), static_cast<int>(hi), static_cast<int>(hi >> 32)};
@@ -1372,42 +1394,6 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// The split workspace (counters, then partial sums), one per device, grown
-// on demand and zeroed when allocated; the kernel leaves the counters at
-// zero. Calls that take the split path share it, so they must not overlap
-// on one device.
-std::mutex g_ws_mutex;
-void* g_ws_ptr[64] = {};
-size_t g_ws_bytes[64] = {};
-
-hipError_t skinny_workspace(size_t part_bytes, int** cnt, v4i** part) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  const size_t cnt_bytes = kSkxCounters * sizeof(int);
-  const size_t need = cnt_bytes + part_bytes;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  if (g_ws_bytes[dev] < need) {
-    if (g_ws_ptr[dev]) {
-      e = hipDeviceSynchronize();           // earlier calls may still use it
-      if (e != hipSuccess) return e;
-      (void)hipFree(g_ws_ptr[dev]);
-      g_ws_ptr[dev] = nullptr;
-      g_ws_bytes[dev] = 0;
-    }
-    const size_t bytes = (need + (1u << 20) - 1) & ~static_cast<size_t>((1u << 20) - 1);
-    e = hipMalloc(&g_ws_ptr[dev], bytes);
-    if (e != hipSuccess) return e;
-    e = hipMemset(g_ws_ptr[dev], 0, bytes);
-    if (e != hipSuccess) return e;
-    g_ws_bytes[dev] = bytes;
-  }
-  *cnt = static_cast<int*>(g_ws_ptr[dev]);
-  *part = reinterpret_cast<v4i*>(static_cast<uint8_t*>(g_ws_ptr[dev]) + cnt_bytes);
-  return hipSuccess;
-}
-
 // G and KS: about one workgroup per CU, the slice fitting LDS beside the
 // group slots; one slice if the activations fit, else the choice with the
 // least activation traffic (every workgroup loads its slice of the M rows)
@@ -1417,7 +1403,7 @@ SkinnySplit plan_skinny(const LinearArgs& a) {
   constexpr int CXB = 2 * A_BITS * 16;
   const int ngroups = (a.N + 15) / 16;
   const int C = (a.K + 255) / 256;
-  SkinnySplit best{0, 0, 0, 0, nullptr, nullptr};
+  SkinnySplit best{0, 0, 0, 0};
   double best_cost = 0.0;
   for (int G = 1; G <= kSkxMaxGroups; ++G) {
     const int nb = (ngroups + G - 1) / G;
@@ -1430,8 +1416,10 @@ SkinnySplit plan_skinny(const LinearArgs& a) {
     }
     const int seg = (C + KS - 1) / KS;
     if (static_cast<long>(a.M) * (seg * CXB + 16) + G * skx_slot_bytes<MG>() > kSkxLds) continue;
-    if (KS > 1 && nb > kSkxCounters) continue;
     const int ks_used = (C + seg - 1) / seg;
+    if (ks_used > 1 && (nb > kSkxCounters ||
+                        static_cast<size_t>(ks_used) * ngroups * skx_slot_bytes<MG>() > kSkxPartBytes))
+      continue;
     const double xbytes = static_cast<double>(nb) * a.M * (a.K * A_BITS / 8);
     const double pbytes = ks_used > 1 ? 2.0 * ks_used * ngroups * skx_slot_bytes<MG>() : 0.0;
     const double cost = xbytes + pbytes;
@@ -1440,7 +1428,7 @@ SkinnySplit plan_skinny(const LinearArgs& a) {
     const bool better = best.G == 0 || (ks_used == 1 && best.KS > 1) ||
                         (cost < best_cost && !(ks_used > 1 && best.KS == 1));
     if (better) {
-      best = SkinnySplit{G, nb, ks_used, seg, nullptr, nullptr};
+      best = SkinnySplit{G, nb, ks_used, seg};
       best_cost = cost;
     }
   }
@@ -1461,13 +1449,8 @@ hipError_t launch_skinny_ipw(const LinearArgs& a, const SkinnySplit& sp, hipStre
 
 template <int MG, int A_BITS>
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t st) {
-  SkinnySplit sp = plan_skinny<MG, A_BITS>(a);
-  if (sp.G == 0) return hipErrorInvalidValue;
-  if (sp.KS > 1) {
-    const int ngroups = (a.N + 15) / 16;
-    hipError_t e = skinny_workspace(static_cast<size_t>(sp.KS) * ngroups * skx_slot_bytes<MG>(), &sp.cnt, &sp.part);
-    if (e != hipSuccess) return e;
-  }
+  const SkinnySplit sp = plan_skinny<MG, A_BITS>(a);
+  if (sp.G == 0) return hipErrorInvalidValue;   // plan_linear only picks the skinny kernel when a plan exists
   // About one group's items per unit and wave: the CU's loads in flight then
   // stay within one or two groups' rows.
   const int per = max(2, (sp.seg + (a.r > 0 ? 1 : 0) + kSkxWaves - 1) / kSkxWaves);
@@ -1890,8 +1873,23 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   // A few tokens of W4A4 whose activation rows fit in LDS: int4 dot products.
   if (a_bits == 4 && M <= kGemvMaxTokens && static_cast<long>(M) * (K / 2) <= kGemvMaxX)
     return {LinearKernel::kGemv, 0, 0, 0, 1, "gemv"};
-  if (M <= 16) return {LinearKernel::kDecode16, 0, 0, 0, 1, "decode16"};
-  if (M <= 32) return {LinearKernel::kDecode32, 0, 0, 0, 1, "decode32"};
+  // Up to 32 tokens: the skinny kernel, unless its K split would need more
+  // partial-sum scratch than the library holds (then a tile kernel).
+  if (M <= 32) {
+    LinearArgs s{};
+    s.M = M;
+    s.K = K;
+    s.N = N;
+    s.r = r;
+    s.a_bits = a_bits;
+    const SkinnySplit sp = M <= 16 ? (a_bits == 4 ? plan_skinny<1, 4>(s) : plan_skinny<1, 8>(s))
+                                   : (a_bits == 4 ? plan_skinny<2, 4>(s) : plan_skinny<2, 8>(s));
+    if (sp.G > 0) {
+      if (M <= 16)
+        return {LinearKernel::kDecode16, 0, 0, 0, 1, sp.KS > 1 ? "decode16_ksplit" : "decode16"};
+      return {LinearKernel::kDecode32, 0, 0, 0, 1, sp.KS > 1 ? "decode32_ksplit" : "decode32"};
+    }
+  }
   // Macro tiles, two four-wave workgroups per CU: the two run independently,
   // so one's barrier and load waits are covered by the other's MFMAs. (One
   // eight-wave 256 x 128 workgroup per CU, lockstep at every k-tile barrier,
