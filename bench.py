@@ -6,11 +6,13 @@ input: per-token activation quantization (serq_quant_act) followed by the
 fused SERQ linear (serq_linear) -- the pure 4-bit GEMM, the salient-row
 residual and the dequantizing epilogue. Calibration is offline and not timed.
 
-Default workload: the LLaMA-2-7B-shaped q_proj layer (K = N = 4096, r = 64,
-W4A4, bf16 activations and output) at M = 2048 tokens; the other token counts
-of that layer (1, 16, 256) are reported in "sweep". Inputs are seeded
-synthetic data (Gaussian activations with 1 % outlier channels x50, Gaussian
-weights), resident in HBM before the timed region. The weights and
+Headline workload: the LLaMA-3-8B MLP's gate and up projections as the one
+4096 -> 2 x 14336 layer they form (they share their input, so they are
+calibrated together), r = 128, W4A4, bf16 activations and output, at
+M = 4096 tokens: the largest layer of the five layer workloads within the
+metric's 1..4096-token range. Inputs are seeded synthetic data (Gaussian
+activations with 1 % outlier channels x50, Gaussian weights), calibrated by
+the library, resident in HBM before the timed region. The weights and
 activations are rotated through enough copies (>= 768 MiB) that every step
 reads them from HBM rather than from the 256 MB last-level cache.
 
@@ -22,7 +24,10 @@ Prints one JSON line. `value` is whole-job throughput in TOP/s:
 2 * M * N * (K + r) integer operations per step / measured step time.
 `roofline` is the dominant kernel (serq_linear) against the dense int8 MFMA
 or the HBM peak, with the counter-measured bytes per launch when they were
-taken on the current kernel sources. Beside the headline: "mlp_activation"
+taken on the current kernel sources. Beside the headline: "configs" (every
+layer and token count of the five workloads -- tiny, q_proj, the 8B MLP in
+W4A4 and W4A8, the 70B-shaped layers -- each calibrated, with its kernel
+times and its own roofline entry), "mlp_activation"
 (serq_silu_mul_quant_act on bf16 gate/up outputs of the 8B and 70B MLP
 widths, with the unfused pair for comparison), "mlp_step" (the whole 8B MLP:
 quant_act, gate/up, the fused activation, down; at 4096 tokens also on the
@@ -51,23 +56,25 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (no sparsity)
 ROTATE_BYTES = 768 << 20
 
 WORKLOADS = {
-    # name: (synth workload, layer, r, a_bits, default M, sweep Ms)
-    "q_proj": ("q_proj", "q_proj", 64, 4, 2048, (1, 16, 256, 2048)),
-    "gate_up": ("mlp8b", "gate_up", 128, 4, 4096, (1, 32, 4096)),
-    "down": ("mlp8b", "down", 128, 4, 4096, (1, 32, 4096)),
-    "gate_up_w4a8": ("mlp8b_w4a8", "gate_up", 128, 8, 2048, (2048,)),
-    "down_w4a8": ("mlp8b_w4a8", "down", 128, 8, 2048, (2048,)),
-    "up70": ("l70b", "up70", 256, 4, 8192, (1, 8192)),
-    "down70": ("l70b", "down70", 256, 4, 8192, (1, 8192)),
+    # name: (synth workload, layer, r, a_bits, default M, token counts, workload number)
+    "tiny": ("tiny", "tiny", 8, 4, 16, (16,), 1),
+    "q_proj": ("q_proj", "q_proj", 64, 4, 2048, (1, 16, 256, 2048), 2),
+    "gate_up": ("mlp8b", "gate_up", 128, 4, 4096, (1, 32, 4096), 3),
+    "down": ("mlp8b", "down", 128, 4, 4096, (1, 32, 4096), 3),
+    "gate_up_w4a8": ("mlp8b_w4a8", "gate_up", 128, 8, 2048, (2048,), 4),
+    "down_w4a8": ("mlp8b_w4a8", "down", 128, 8, 2048, (2048,), 4),
+    "up70": ("l70b", "up70", 256, 4, 8192, (1, 8192), 5),
+    "down70": ("l70b", "down70", 256, 4, 8192, (1, 8192), 5),
 }
+HEADLINE = "gate_up"
 
 
-def linear_bytes(M, K, N, r, a_bits):
-    return M * K * a_bits // 8 + K * N // 2 + r * N // 2 + 4 * (M + 2 * N) + M * N * 2
+def linear_bytes(M, K, N, r, a_bits, y_bytes=2):
+    return M * K * a_bits // 8 + K * N // 2 + r * N // 2 + 4 * (M + 2 * N) + M * N * y_bytes
 
 
-def quant_bytes(M, K, a_bits):
-    return M * K * 2 + 4 * K + M * K * a_bits // 8 + 4 * M
+def quant_bytes(M, K, a_bits, x_bytes=2):
+    return M * K * x_bytes + 4 * K + M * K * a_bits // 8 + 4 * M
 
 
 def act_bytes(M, K, a_bits):
@@ -100,21 +107,29 @@ class Setup:
         import w4a4_linear_layers_amd as S
         from synth import workload_layer
 
-        wl, layer, r, a_bits, _, _ = WORKLOADS[workload]
+        wl, layer, r, a_bits, _, _, _ = WORKLOADS[workload]
+        t0 = time.time()
         li = workload_layer(wl, layer, M_max=M_max, seed=seed)
+        self.gen_s = time.time() - t0
         self.K, self.N, self.r, self.a_bits = li.K, li.N, r, a_bits
-        W = li.W_bits
-        if "W_up_bits" in li.meta:     # gate and up share the input: calibrate them as one
-            W = np.concatenate([W, li.meta["W_up_bits"]], axis=1)
+        self.bf16 = li.dtype == "bf16"
+        W = li.W_bits if self.bf16 else li.W
+        if "W_up" in li.meta:          # gate and up share the input: calibrate them as one
+            W = np.concatenate([W, li.meta["W_up_bits" if self.bf16 else "W_up"]], axis=1)
             self.N = W.shape[1]
         t0 = time.time()
         L = S.calibrate(W, li.act_absmax, r=r)
         self.calib_s = time.time() - t0
         self.li, self.L = li, L
         dev = torch.device("cuda")
-        x = torch.from_numpy(np.ascontiguousarray(li.X_bits[:, L.perm]).view(np.int16)).to(dev)
-        x = x.view(torch.bfloat16)
-        per = x.numel() * 2 + L.Wq.nbytes + L.Rq.nbytes + 8 * self.N
+        if self.bf16:
+            x = torch.from_numpy(np.ascontiguousarray(li.X_bits[:, L.perm]).view(np.int16)).to(dev)
+            x = x.view(torch.bfloat16)
+        else:
+            x = torch.from_numpy(np.ascontiguousarray(li.X[:, L.perm])).to(dev)
+        self.x_bytes = x.element_size()
+        self.ydt = torch.bfloat16 if self.bf16 else torch.float32
+        per = x.numel() * self.x_bytes + L.Wq.nbytes + L.Rq.nbytes + 8 * self.N
         self.copies = max(2, math.ceil(ROTATE_BYTES / per))
         base = L.to(dev)
         self.layers, self.xs = [], []
@@ -126,22 +141,29 @@ class Setup:
         self.xq = torch.empty((M_max, self.K // 2 if a_bits == 4 else self.K),
                               dtype=torch.uint8 if a_bits == 4 else torch.int8, device=dev)
         self.sx = torch.empty(M_max, dtype=torch.float32, device=dev)
-        self.y = torch.empty((M_max, self.N), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((M_max, self.N), dtype=self.ydt, device=dev)
         torch.cuda.synchronize()
+
+    def free(self):
+        import torch
+        self.layers, self.xs = [], []
+        self.xq = self.sx = self.y = None
+        self.li = None
+        torch.cuda.empty_cache()
 
     def step(self, i, M):
         import w4a4_linear_layers_amd as S
         c = i % self.copies
         L = self.layers[c]
         xq, sx = S.quant_act(self.xs[c][:M], L, a_bits=self.a_bits, out=(self.xq[:M], self.sx[:M]))
-        S.linear(xq, sx, L, a_bits=self.a_bits, out=self.y[:M])
+        S.linear(xq, sx, L, a_bits=self.a_bits, out_dtype=self.ydt, out=self.y[:M])
 
     def graph(self, fn, n):
         """Capture n calls fn(i) into one HIP graph (the kernels are enqueued on
         torch's capture stream), so that replays are not bound by Python
         launch overhead."""
         import torch
-        fn(0)                 # outside the capture: the library's first-call set-up (workspaces)
+        fn(0)                 # one eager call: the kernels' code is loaded before the capture
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -164,7 +186,7 @@ class Setup:
             S.quant_act(self.xs[c][:M], self.layers[c], a_bits=self.a_bits, out=(xq, sx))
 
         def lin(i):
-            S.linear(xq, sx, self.layers[i % self.copies], a_bits=self.a_bits, out=self.y[:M])
+            S.linear(xq, sx, self.layers[i % self.copies], a_bits=self.a_bits, out_dtype=self.ydt, out=self.y[:M])
 
         out = []
         for fn in (q, lin):
@@ -218,7 +240,7 @@ def time_mlp_act(K, Ms, n=100, a_bits=4, seed=0):
 
         times = []
         for fn in (act, unfused):
-            fn(0)                      # outside the capture: first-call set-up
+            fn(0)                      # one eager call before the capture
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -295,7 +317,7 @@ def time_mlp_step(Ms, n=50, seed=0):
                 f(i)
 
         def timed(fn):
-            fn(0)                      # outside the capture: first-call set-up
+            fn(0)                      # one eager call before the capture
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -368,7 +390,7 @@ def cpu_baseline(setup, M, rows=None, budget_s=20.0):
     while True:
         t0 = time.perf_counter()
         q = O.quant_act(X[:n], L.s_hat_inv, setup.a_bits)
-        O.linear(q, layer, out="bf16")
+        O.linear(q, layer, out="bf16" if setup.bf16 else "f32")
         dt = time.perf_counter() - t0
         if rows is not None or dt > budget_s / 4 or n >= M:
             break
@@ -377,12 +399,62 @@ def cpu_baseline(setup, M, rows=None, budget_s=20.0):
     return dict(value=ops / dt / 1e12, unit="TOP/s", cores=1, kind="oracle",
                 sample=f"{n} of {M} rows of the same workload (quant_act + int64 matmuls + fp64 epilogue), "
                        f"{dt:.1f} s; numpy integer matmul runs on one thread",
-                seconds=round(dt, 2), rows=n)
+                seconds=round(dt, 2), rows=n, host_cpu=cpu_model(),
+                affinity_cpus=len(os.sched_getaffinity(0)))
 
 
-def roofline_entry(M, K, N, r, a_bits, us, traffic):
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+WORKLOAD_TITLES = {
+    "tiny": "tiny layer",
+    "q_proj": "LLaMA-2-7B q_proj",
+    "gate_up": "LLaMA-3-8B MLP gate and up as one layer",
+    "down": "LLaMA-3-8B MLP down",
+    "gate_up_w4a8": "LLaMA-3-8B MLP gate and up as one layer, W4A8",
+    "down_w4a8": "LLaMA-3-8B MLP down, W4A8",
+    "up70": "LLaMA-2-70B-shaped up layer",
+    "down70": "LLaMA-2-70B-shaped down layer",
+}
+
+
+def config_lines(setup, name, reps=50):
+    """One entry per token count of a layer workload: kernel times (graph
+    replays, events), throughput and the serq_linear roofline entry."""
+    import w4a4_linear_layers_amd as S
+    _, _, r, a_bits, _, token_counts, number = WORKLOADS[name]
+    K, N = setup.K, setup.N
+    y_bytes = 2 if setup.bf16 else 4
+    out = []
+    for m in token_counts:
+        qu, lu = setup.time_kernels(m, reps)
+        e = roofline_entry(m, K, N, r, a_bits, lu, None, y_bytes)
+        tops = linear_ops(m, K, N, r) / (lu * 1e-6) / 1e12
+        gbs = linear_bytes(m, K, N, r, a_bits, y_bytes) / (lu * 1e-6) / 1e9
+        out.append(dict(workload=number, layer=name, title=WORKLOAD_TITLES[name], M=m, K=K, N=N, r=r,
+                        a_bits=a_bits, kernel=S.kernel_name(m, K, N, r, a_bits), linear_us=round(lu, 2),
+                        quant_act_us=round(qu, 2), step_us=round(qu + lu, 2), TOPS=round(tops, 2),
+                        HBM_GBs=round(gbs, 1),
+                        quant_act_GBs=round(quant_bytes(m, K, a_bits, setup.x_bytes) / (qu * 1e-6) / 1e9, 1),
+                        roofline=dict(bound=e["bound"], achieved=e["achieved"], peak=e["peak"], unit=e["unit"],
+                                      frac=e["frac"])))
+        print(f"# {name} M={m}: linear {lu:.2f} us ({out[-1]['kernel']}) {tops:.1f} TOP/s {gbs:.0f} GB/s "
+              f"({e['bound']} frac {e['frac']:.3f}); quant_act {qu:.2f} us", file=sys.stderr, flush=True)
+    return out
+
+
+def roofline_entry(M, K, N, r, a_bits, us, traffic, y_bytes=2):
     ops = linear_ops(M, K, N, r)
-    byts = linear_bytes(M, K, N, r, a_bits)
+    byts = linear_bytes(M, K, N, r, a_bits, y_bytes)
     if ops / byts > INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         ach = ops / (us * 1e-6) / 1e12
         return dict(bound="mfma", achieved=round(ach, 1), peak=INT8_PEAK_TOPS, unit="TOP/s",
@@ -500,9 +572,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="q_proj", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--M", type=int, default=None, help="tokens per step (default: the workload's)")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the other token counts and the MLP activation")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the other workloads and token counts, the MLP and the bf6 lines")
+    ap.add_argument("--configs", default=None, metavar="NAME[,NAME...]",
+                    help="workloads for the per-config lines besides the headline's (default: all)")
     ap.add_argument("--no-mlp-act", action="store_true", help="skip the MLP activation timing")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf6", action="store_true", help="skip the bf6 route timings")
@@ -536,13 +611,12 @@ def main(argv=None):
     import w4a4_linear_layers_amd as S
 
     torch.cuda.set_device(0)
-    wl, layer, r, a_bits, M_def, sweep_ms = WORKLOADS[args.workload]
+    wl, layer, r, a_bits, M_def, token_counts, _ = WORKLOADS[args.workload]
     M = args.M or M_def
-    M_max = max([M] + ([] if args.no_sweep else list(sweep_ms)))
-    setup = Setup(args.workload, M_max)
+    setup = Setup(args.workload, max([M] + list(token_counts)))
     K, N = setup.K, setup.N
     print(f"# setup: {args.workload} K={K} N={N} r={r} a_bits={a_bits} copies={setup.copies} "
-          f"calibrate {setup.calib_s:.1f}s", file=sys.stderr, flush=True)
+          f"generate {setup.gen_s:.1f}s calibrate {setup.calib_s:.1f}s", file=sys.stderr, flush=True)
 
     for i in range(args.warmup):
         setup.step(i, M)
@@ -554,29 +628,37 @@ def main(argv=None):
     g.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    del g
     ms_per_step = dt * 1e3 / args.steps
     ops = linear_ops(M, K, N, r)
     value = ops * args.steps / dt / 1e12
+    y_bytes = 2 if setup.bf16 else 4
 
     q_us, l_us = setup.time_kernels(M, max(args.steps, 50))
     traffic = load_traffic(args.workload, M)
-    roof = roofline_entry(M, K, N, r, a_bits, l_us, traffic)
+    roof = roofline_entry(M, K, N, r, a_bits, l_us, traffic, y_bytes)
     print(f"# step {ms_per_step * 1e3:.2f} us; quant_act {q_us:.2f} us, serq_linear {l_us:.2f} us "
           f"({S.kernel_name(M, K, N, r, a_bits)})", file=sys.stderr, flush=True)
 
-    sweep = []
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(setup, M)
+        print(f"# cpu oracle: {cpu['value']:.4f} TOP/s on {cpu['rows']} rows", file=sys.stderr, flush=True)
+
+    configs = []
     if not args.no_sweep:
-        for m in sweep_ms:
-            qu, lu = setup.time_kernels(m, 100)
-            e = roofline_entry(m, K, N, r, a_bits, lu, None)
-            hbm = linear_bytes(m, K, N, r, a_bits) / (lu * 1e-6) / 1e9
-            tops = linear_ops(m, K, N, r) / (lu * 1e-6) / 1e12
-            sweep.append(dict(M=m, kernel=S.kernel_name(m, K, N, r, a_bits), linear_us=round(lu, 2),
-                              quant_act_us=round(qu, 2), TOPS=round(tops, 2), HBM_GBs=round(hbm, 1),
-                              bound=e["bound"], frac=e["frac"],
-                              quant_act_GBs=round(quant_bytes(m, K, a_bits) / (qu * 1e-6) / 1e9, 1)))
-            print(f"# M={m}: linear {lu:.2f} us {tops:.1f} TOP/s {hbm:.0f} GB/s ({e['bound']} frac "
-                  f"{e['frac']:.3f}); quant_act {qu:.2f} us", file=sys.stderr, flush=True)
+        names = [n for n in WORKLOADS if n != args.workload] if args.configs is None else args.configs.split(",")
+        configs.extend(config_lines(setup, args.workload))
+        setup.free()
+        for name in names:
+            st = Setup(name, max(WORKLOADS[name][5]))
+            print(f"# setup: {name} generate {st.gen_s:.1f}s calibrate {st.calib_s:.1f}s copies {st.copies}",
+                  file=sys.stderr, flush=True)
+            configs.extend(config_lines(st, name))
+            st.free()
+            del st
+    else:
+        setup.free()
 
     mlp_act = []
     if not args.no_sweep and not args.no_mlp_act:
@@ -605,24 +687,20 @@ def main(argv=None):
                   f"act_bf6 {e['act_bf6_us']:.1f} us; bit-identical {e['bit_identical']}",
                   file=sys.stderr, flush=True)
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(setup, M)
-        print(f"# cpu oracle: {cpu['value']:.4f} TOP/s on {cpu['rows']} rows", file=sys.stderr, flush=True)
-
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int4" if a_bits == 4 else "int8xint4",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: SERQ linear K={K} N={N} r={r} "
-                               f"{'W4A4' if a_bits == 4 else 'W4A8'}, bf16 in/out, M={M} tokens per step",
+        "config": {"workload": f"{WORKLOAD_TITLES[args.workload]}: SERQ linear K={K} N={N} r={r} "
+                               f"{'W4A4' if a_bits == 4 else 'W4A8'}, "
+                               f"{'bf16' if setup.bf16 else 'fp32'} in/out, M={M} tokens per step, calibrated",
                    "M": M, "K": K, "N": N, "r": r, "a_bits": a_bits,
                    "kernel": S.kernel_name(M, K, N, r, a_bits), "rotated_copies": setup.copies},
         "kernels_us": {"serq_quant_act": round(q_us, 3), "serq_linear": round(l_us, 3)},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "sweep": sweep,
+        "configs": configs,
         "mlp_activation": mlp_act,
         "mlp_step": mlp_step,
         "bf6_route": bf6,

@@ -53,10 +53,13 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Input preparation only: a bf16 workload is *defined* as these values.
     Non-finite inputs are not produced by the generators.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return u.astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # in 32 bits: the largest finite pattern 0xFF7FFFFF plus 0x8000 does not wrap
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    lsb += np.uint32(0x7FFF)
+    lsb += u
+    lsb >>= np.uint32(16)
+    return lsb.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
