@@ -205,7 +205,8 @@ int serq_silu_mul_quant_act(const void* G, const void* U, int ld, serq_dtype x_d
  * quantized, no intermediate quantization), and
  *     Y[m, n] = sx[m] * (sw[n] * acc_main[m, n] + sr[n] * acc_res[m, n])
  * evaluated in fp32 and stored as y_dtype (bf16 with round to nearest even).
- * Integer accumulation is exact (int32).
+ * Integer accumulation is exact (int32) for every K the call accepts (the
+ * matrix-core kernels serve K < 2^17, longer rows a plain kernel).
  *
  *   Xq, sx     from serq_quant_act with the same a_bits (device).
  *   Wq, sw     N x K/2 bytes and N floats (device).

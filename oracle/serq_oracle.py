@@ -283,6 +283,146 @@ def calibrate_columns(W: np.ndarray, act_absmax: np.ndarray, cols: np.ndarray, *
 
 
 # ---------------------------------------------------------------------------
+# GPTQ as the weight quantizer: SERQ(GPTQ).
+# [GDE] 3 (Wichtige Beiträge): the method works with round-to-nearest and
+# with GPTQ weight quantization; [N] 实验关键数据: the accuracy rows are
+# SERQ(GPTQ). GPTQ (Frantar, Ashkboos, Hoefler and Alistarh, "GPTQ: Accurate
+# Post-Training Quantization for Generative Pre-trained Transformers", ICLR
+# 2023) quantizes the input rows of W one at a time in a fixed order and,
+# after each row, moves that row's quantization error onto the rows not yet
+# quantized so as to minimise the layer's squared output error on
+# calibration inputs; the weights of the update come from the inverse of
+# H = X^T X (upper Cholesky factor U of H^-1: row i's error e is divided by
+# U[i, i] and subtracted, times U[i, j], from every later row j).
+#
+# Readings (the pages do not spell the combination out):
+#   * the order is the saliency order P, and H is formed from the inputs the
+#     layer sees, X^_cal = fl32(X_cal[:, perm] * s_hat_inv) (flattened,
+#     permuted calibration activations): H[i, j] = sum_t x^[t,i] x^[t,j] in
+#     fp64, summed over t in order (the products are exact in fp64);
+#   * dampening as in GPTQ: lambda = damp * mean(diag H) added to the
+#     diagonal (damp = 0.01); an all-zero H becomes the identity;
+#   * the quantization grid is RTN's: one scale per output column from the
+#     column maximum of W^ before any update, codes clamped to [-8, 7]; a
+#     row's codes quantize its updated values rounded to fp32;
+#   * the r salient rows are quantized first (they lead the order) and their
+#     error is not propagated: the compensator R = W~_s - Q(W~_s) carries it,
+#     so propagating it too would correct it twice. Their codes, R, Q(R) and
+#     its scales are therefore RTN's; GPTQ acts on rows r..K-1 (r = 0: plain
+#     GPTQ on W^);
+#   * every step is one fp64 operation in a fixed order (the factorizations
+#     by outer-product elimination, the update row by row), so that an
+#     independent implementation reproduces the codes bit for bit.
+# ---------------------------------------------------------------------------
+
+GPTQ_DAMP = 0.01
+
+
+def gptq_hessian(X_hat: np.ndarray, damp: float = GPTQ_DAMP) -> np.ndarray:
+    """H = sum_t x^_t x^_t^T (fp64, t in order) plus damp * mean(diag H) on
+    the diagonal; the identity when every input is zero."""
+    X = np.asarray(X_hat, dtype=np.float32).astype(np.float64)
+    K = X.shape[1]
+    H = np.zeros((K, K), np.float64)
+    for t in range(X.shape[0]):
+        H += np.multiply.outer(X[t], X[t])
+    d = 0.0
+    for i in range(K):
+        d += H[i, i]
+    d = d / K
+    if d == 0.0:
+        return np.eye(K)
+    lam = float(np.float32(damp)) * d
+    H[np.arange(K), np.arange(K)] += lam
+    return H
+
+
+def gptq_inverse_factor(H: np.ndarray) -> np.ndarray:
+    """Upper-triangular U with U^T U = H^-1: first V upper with H = V V^T
+    (elimination from the last index), then U = V^-1 by back substitution.
+    Both by outer-product updates, each element updated in a fixed order."""
+    K = H.shape[0]
+    A = np.array(H, dtype=np.float64)
+    V = np.zeros((K, K), np.float64)
+    for k in range(K - 1, -1, -1):
+        if not A[k, k] > 0.0:
+            raise ValueError("Hessian is not positive definite")
+        v = np.sqrt(A[k, k])
+        V[k, k] = v
+        col = A[:k, k] / v
+        V[:k, k] = col
+        A[:k, :k] -= np.multiply.outer(col, col)
+    B = np.eye(K)
+    for k in range(K - 1, -1, -1):
+        B[k, k:] /= V[k, k]
+        B[:k, k:] -= np.multiply.outer(V[:k, k], B[k, k:])
+    return B
+
+
+def gptq_quantize(W_hat: np.ndarray, U: np.ndarray, r: int) -> np.ndarray:
+    """GPTQ codes (K x N int8) of the folded, permuted weight W^ (fp32
+    values), rows in order, on RTN's grid (scale per output column from the
+    column maximum of W^), the first r rows' errors not propagated."""
+    W_hat = np.asarray(W_hat, dtype=np.float32)
+    K, N = W_hat.shape
+    colmax = np.abs(W_hat).max(axis=0) if K else np.zeros(N, np.float32)
+    sw = np.zeros(N, np.float32)
+    inv = np.zeros(N, np.float32)
+    for n in range(N):                      # the quantizer's scale and reciprocal, per column
+        _, sw[n] = quantize_group(np.zeros(0, np.float32), colmax[n], 4)
+        with np.errstate(divide="ignore", over="ignore"):
+            inv[n] = np.float32(np.float32(7.0) / colmax[n])
+    live = np.isfinite(inv) & (sw != 0)
+    inv = np.where(live, inv, np.float32(0.0)).astype(np.float32)
+    Wk = W_hat.astype(np.float64)
+    codes = np.zeros((K, N), np.int8)
+    for i in range(K):
+        v = Wk[i].astype(np.float32)
+        q = np.clip(np.rint((v * inv).astype(np.float32)), -8, 7)
+        q = np.where(live, q, 0).astype(np.int8)
+        codes[i] = q
+        if i < r:
+            continue
+        deq = (q.astype(np.float32) * sw).astype(np.float32).astype(np.float64)
+        err = (Wk[i] - deq) / U[i, i]
+        Wk[i + 1:] -= np.multiply.outer(U[i, i + 1:], err)
+    return codes
+
+
+def calibrate_gptq(W: np.ndarray, act_absmax: np.ndarray, X_cal: np.ndarray, *,
+                   alpha: float = ALPHA_DEFAULT, r: int, damp: float = GPTQ_DAMP) -> dict:
+    """SERQ calibration with GPTQ codes on the non-salient rows.
+
+    ``X_cal`` is T x K calibration activations in the original channel order
+    (fp32 values). Returns calibrate()'s dict with Wq / Wq_codes / W_deq from
+    GPTQ, plus ``H`` and ``U``."""
+    base = calibrate(W, act_absmax, alpha=alpha, r=r)
+    K, N = base["K"], base["N"]
+    perm, shi = base["perm"], base["s_hat_inv"]
+    X_hat = (np.asarray(X_cal, dtype=np.float32)[:, perm] * shi[None, :]).astype(np.float32)
+    H = gptq_hessian(X_hat, damp)
+    U = gptq_inverse_factor(H)
+    codes = gptq_quantize(base["W_hat"], U, r)
+    sw = base["sw"]
+    assert np.array_equal(codes[:r], base["Wq_codes"][:r])
+    out = dict(base)
+    out.update(Wq_codes=codes, W_deq=dequantize_columns(codes, sw), Wq=pack_int4(codes.T), H=H, U=U,
+               X_hat_cal=X_hat)
+    return out
+
+
+def weighted_error(X_hat: np.ndarray, W_hat: np.ndarray, W_deq: np.ndarray, R_deq: np.ndarray | None,
+                   r: int) -> float:
+    """||X^ W^ - (X^ Q(W^) + X^_s deq(Q(R)))||_F in fp64: the layer's output
+    error on the calibration inputs with unquantized activations."""
+    X = np.asarray(X_hat, np.float64)
+    E = X @ (np.asarray(W_hat, np.float64) - np.asarray(W_deq, np.float64))
+    if r and R_deq is not None:
+        E = E - X[:, :r] @ np.asarray(R_deq, np.float64)
+    return float(np.sqrt((E * E).sum()))
+
+
+# ---------------------------------------------------------------------------
 # Offline propagation of a later layer's permutation into this layer's output
 # columns. [N] 关键设计 3: the activation order a layer needs is produced by
 # permuting the previous layer's weight columns offline (the down projection's

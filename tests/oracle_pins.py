@@ -537,8 +537,95 @@ def check_exp_split_constant(O):
         assert Fraction(float(np.float32(n) * O.LN2_HI_F32)) == n * hi
 
 
+# ---------------------------------------------------------------- GPTQ
+
+def _derive_gptq():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("derive_gptq", os.path.join(GOLDEN, "derive_gptq.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _gptq_layer(seed, K, N, T, corr=0.4):
+    rng = np.random.default_rng(seed)
+    A = (rng.standard_normal((K, K)) * corr + np.eye(K)).astype(np.float32)
+    Xc = (rng.standard_normal((T, K)).astype(np.float32) @ A).astype(np.float32)
+    Xc[:, rng.choice(K, 2, replace=False)] *= np.float32(20.0)
+    W = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    return W, np.abs(Xc).max(axis=0).astype(np.float32), Xc
+
+
+def check_gptq_exact(O):
+    """GPTQ codes against the exact-rational optimal-brain-surgeon derivation
+    (tests/golden/derive_gptq.py: trailing-block inverses by Gauss-Jordan, no
+    Cholesky factor): the worked 4 x 2 fixture (r = 0, r = 2, no damping,
+    all rows salient) and random layers, through calibrate_gptq too (the
+    inputs flattened and permuted as the layer sees them). [GDE] 3: SERQ
+    works with GPTQ; GPTQ (Frantar et al., ICLR 2023) is the OBS update."""
+    D = _derive_gptq()
+    fx = golden("gptq_4x2.json")
+    Wh = np.array(fx["inputs"]["W_hat"], np.float32)
+    Xh = np.array(fx["inputs"]["X_hat"], np.float32)
+    for case in fx["inputs"]["cases"]:
+        U = O.gptq_inverse_factor(O.gptq_hessian(Xh, case["damp"]))
+        got = O.gptq_quantize(Wh, U, case["r"])
+        assert got.tolist() == fx["expected"][case["name"]], case["name"]
+    for seed in range(6):
+        K, N, T = 6, 3, 9
+        W, a, Xc = _gptq_layer(100 + seed, K, N, T)
+        for r in (0, 2):
+            damp = (0.01, 0.3)[seed % 2]
+            G = O.calibrate_gptq(W, a, Xc, r=r, damp=damp)
+            Xh = (Xc[:, G["perm"]] * G["s_hat_inv"][None, :]).astype(np.float32)
+            want = D.gptq_codes(G["W_hat"].tolist(), Xh.tolist(), r, Fraction(float(np.float32(damp))))
+            assert G["Wq_codes"].tolist() == want, (seed, r)
+
+
+def check_gptq_special_cases(O):
+    """Where GPTQ has nothing to move, it is RTN bit for bit: a diagonal
+    Hessian (orthogonal calibration inputs: no row's error can be absorbed by
+    another), all-zero inputs (the identity), and r = K (every row salient).
+    The salient rows, R, Q(R) and the permutation are RTN's at any r. The
+    inverse factor satisfies U^T U H = I and is upper triangular."""
+    W, a, Xc = _gptq_layer(7, 24, 10, 64)
+    for r in (0, 8):
+        rtn = O.calibrate(W, a, r=r)
+        diag_x = np.diag(np.linspace(0.5, 3.0, 24)).astype(np.float32)        # orthogonal columns
+        for X in (diag_x, np.zeros((5, 24), np.float32)):
+            g = O.calibrate_gptq(W, a, X, r=r)
+            assert np.array_equal(g["Wq_codes"], rtn["Wq_codes"])
+            assert np.array_equal(g["Wq"], rtn["Wq"])
+        g = O.calibrate_gptq(W, a, Xc, r=r)
+        assert not np.array_equal(g["Wq_codes"], rtn["Wq_codes"])      # correlated inputs: GPTQ moves codes
+        assert np.array_equal(g["Wq_codes"][:r], rtn["Wq_codes"][:r])
+        for k in ("perm", "s_hat_inv", "sw", "Rq", "sr", "Rq_codes"):
+            assert np.array_equal(g[k], rtn[k]), k
+        U, H = g["U"], g["H"]
+        assert np.allclose(U.T @ U @ H, np.eye(24), atol=1e-9)
+        assert np.array_equal(U, np.triu(U)) and (np.diag(U) > 0).all()
+    g = O.calibrate_gptq(W, a, Xc, r=24)
+    assert np.array_equal(g["Wq_codes"], O.calibrate(W, a, r=24)["Wq_codes"])
+
+
+def check_gptq_reduces_error(O):
+    """GPTQ's purpose: a smaller output error on the calibration inputs than
+    round to nearest, with and without the compensator (the pages' accuracy
+    rows use SERQ(GPTQ); [N] 实验关键数据). Statistical, fixed seeds."""
+    for seed in (1, 2):
+        W, a, Xc = _gptq_layer(seed, 96, 48, 256)
+        for r in (0, 16):
+            g = O.calibrate_gptq(W, a, Xc, r=r)
+            t = O.calibrate(W, a, r=r)
+            Xh = g["X_hat_cal"]
+            eg = O.weighted_error(Xh, g["W_hat"], g["W_deq"], O.dequantize_columns(g["Rq_codes"], g["sr"]), r)
+            et = O.weighted_error(Xh, t["W_hat"], t["W_deq"], O.dequantize_columns(t["Rq_codes"], t["sr"]), r)
+            assert eg < 0.9 * et, (seed, r, eg, et)
+
+
 ALL_CHECKS = [check_pack, check_quantizer_golden, check_quantizer_bruteforce, check_smoothing,
               check_perm, check_fold_identity, check_compensator, check_int_gemm,
               check_dequant_identity, check_special_cases, check_worked_layer, check_bf16,
               check_permute_outputs, check_rank_trend, check_fma32, check_exp32, check_silu_mul,
-              check_calibrate_columns, check_exp_split_constant]
+              check_calibrate_columns, check_exp_split_constant, check_gptq_exact,
+              check_gptq_special_cases, check_gptq_reduces_error]

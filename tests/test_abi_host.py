@@ -362,6 +362,16 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(16, 63, 64, 8) is None
 
 
+def test_kernel_dispatch_long_rows():
+    """The MFMA kernels sum widened codes (256x the products for W4A4, 16x for
+    W4A8), exact in int32 for K < 2^17; from 2^17 on only the int4
+    dot-product GEMV (unscaled sums) and the generic kernel serve."""
+    assert S.kernel_name(64, 131040, 64, 8) == "tile32x64k4"
+    assert S.kernel_name(64, 131072, 64, 8) == "generic"
+    assert S.kernel_name(8, 131072, 64, 8, 8) == "generic"
+    assert S.kernel_name(1, 131072, 64, 8) == "gemv"
+
+
 def test_kernel_dispatch_split_scratch_bound():
     """The K split's partial sums live in 16 MiB of file-scope device scratch:
     shapes whose split would need more take a tile kernel instead (nothing is
@@ -375,8 +385,8 @@ def test_kernel_dispatch_split_scratch_bound():
     name = S.kernel_name(32, 65536, 32768, 64)
     assert name.startswith("tile"), name
     # W4A8 at 16 tokens: 1024 groups x 14 slices x 2 KB = 28 MiB
-    assert S.kernel_name(16, 131072, 16384, 64, 4) == "decode16_ksplit"   # 7 slices: 14 MiB
-    name = S.kernel_name(16, 131072, 16384, 64, 8)
+    assert S.kernel_name(16, 131040, 16384, 64, 4) == "decode16_ksplit"   # 7 slices: 14 MiB
+    name = S.kernel_name(16, 131040, 16384, 64, 8)
     assert name.startswith("tile"), name
 
 

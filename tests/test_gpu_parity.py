@@ -302,6 +302,39 @@ def test_linear_extreme_codes():
         check_y(host(y), am_ref, ar_ref, sx, sw, sr, "f32")
 
 
+@pytest.mark.parametrize("M,K,N,kern", [(40, 131040, 64, "tile32x64k4"), (20, 131040, 48, "decode32_ksplit"),
+                                        (4, 131072, 40, "generic"), (1, 131072, 40, "gemv")])
+def test_linear_longest_rows_extreme_codes(M, K, N, kern):
+    """The longest rows at the int4 extremes: just below 2^17, where the
+    widened sums of the MFMA kernels (256 x the products) reach 2^31 - 2^15,
+    and from 2^17 on (generic kernel, int4 dot products). The expected
+    accumulators are the closed forms 64 (K - 1) + x0 w0 over all K and
+    64 (r - 1) + x0 r0 over the r salient columns, with the first code of
+    every row and column varied over [-8, 7]."""
+    r = 64
+    assert S.kernel_name(M, K, N, r, 4) == kern
+    x0 = (np.arange(M) % 16 - 8).astype(np.int8)
+    w0 = ((np.arange(N) * 5) % 16 - 8).astype(np.int8)
+    r0 = ((np.arange(N) * 3 + 1) % 16 - 8).astype(np.int8)
+    Xc = np.full((M, K), -8, np.int8)
+    Xc[:, 0] = x0
+    Wc = np.full((K, N), -8, np.int8)
+    Wc[0] = w0
+    Rc = np.full((r, N), -8, np.int8)
+    Rc[0] = r0
+    sx = np.ones(M, np.float32)
+    sw = np.full(N, 2.0 ** -16, np.float32)
+    sr = np.full(N, 2.0 ** -12, np.float32)
+    layer = S.DeviceLayer(K=K, N=N, r=r, perm=None, s_hat_inv=None, Wq=dev(O.pack_int4(Wc.T)), sw=dev(sw),
+                          Rq=dev(pack_rq(Rc)), sr=dev(sr))
+    y, am, ar = S.linear(dev(O.pack_int4(Xc)), dev(sx), layer, a_bits=4, out_dtype=torch.float32, debug=True)
+    _sync()
+    am_ref = 64 * (K - 1) + x0.astype(np.int64)[:, None] * w0.astype(np.int64)[None, :]
+    ar_ref = 64 * (r - 1) + x0.astype(np.int64)[:, None] * r0.astype(np.int64)[None, :]
+    assert np.array_equal(host(am), am_ref) and np.array_equal(host(ar), ar_ref)
+    check_y(host(y), am_ref, ar_ref, sx, sw, sr, "f32")
+
+
 def test_linear_on_side_stream_and_empty():
     Xc, Wc, Rc, sx, sw, sr, Xq, layer = _codes_case(64, 512, 96, 64, 4, seed=5)
     s = torch.cuda.Stream()
@@ -613,6 +646,39 @@ def test_linear_bf6_extreme_codes_and_empty():
     y0 = S.linear_bf6(e6, torch.empty(0, dtype=torch.float32, device="cuda"), L6)
     _sync()
     assert e6.numel() == 0 and y0.shape == (0, N)
+
+
+@pytest.mark.parametrize("K", [28672, 1 << 18])
+def test_linear_bf6_sums_to_2_24(K):
+    """fp32 accumulation on the FP6 instruction is exact up to 2^24: every
+    code -8 except the first of each row and column (varied over [-8, 7]),
+    so the partial sums are odd or even integers climbing to
+    64 (K - 1) + x0 w0 <= 2^24 (K = 2^18: 24 significant bits in the last
+    steps). Expected values in closed form; K = 28672 is the 70B down
+    layer's length."""
+    M, N, r = 40, 96, 256
+    x0 = (np.arange(M) % 16 - 8).astype(np.int8)
+    w0 = ((np.arange(N) * 5) % 16 - 8).astype(np.int8)
+    r0 = ((np.arange(N) * 3 + 1) % 16 - 8).astype(np.int8)
+    Xc = np.full((M, K), -8, np.int8)
+    Xc[:, 0] = x0
+    Wc = np.full((K, N), -8, np.int8)
+    Wc[0] = w0
+    Rc = np.full((r, N), -8, np.int8)
+    Rc[0] = r0
+    sx = np.ones(M, np.float32)
+    sw = np.full(N, 2.0 ** -20, np.float32)
+    sr = np.full(N, 2.0 ** -12, np.float32)
+    L6 = _bf6_layer(Wc, Rc, sw, sr, K, N, r)
+    x6 = S.act_bf6(dev(O.pack_int4(Xc)), K)
+    y, am, ar = S.linear_bf6(x6, dev(sx), L6, out_dtype=torch.float32, debug=True)
+    _sync()
+    am_ref = 64 * (K - 1) + x0.astype(np.int64)[:, None] * w0.astype(np.int64)[None, :]
+    ar_ref = 64 * (r - 1) + x0.astype(np.int64)[:, None] * r0.astype(np.int64)[None, :]
+    assert am_ref.max() <= 2 ** 24
+    assert np.array_equal(host(am), am_ref), np.argwhere(host(am) != am_ref)[:5]
+    assert np.array_equal(host(ar), ar_ref)
+    check_y(host(y), am_ref, ar_ref, sx, sw, sr, "f32")
 
 
 @pytest.mark.slow

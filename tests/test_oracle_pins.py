@@ -177,6 +177,37 @@ def _mut_columns_codes_shifted(orig):
     return f
 
 
+def _mut_gptq_propagates_salient(orig):
+    """The salient rows' errors moved onto later rows as well (corrected
+    twice: once by R, once by GPTQ)."""
+    return lambda W_hat, U, r: orig(W_hat, U, 0)
+
+
+def _mut_gptq_update_sign(orig):
+    def f(W_hat, U, r):
+        return orig(W_hat, -np.triu(U, 1) + np.diag(np.diag(U)), r)
+    return f
+
+
+def _mut_gptq_no_damping(orig):
+    return lambda X_hat, damp=O.GPTQ_DAMP: orig(X_hat, 0.0)
+
+
+def _mut_gptq_unflattened_inputs(orig):
+    """The Hessian from the calibration inputs in their original order,
+    without the flattening (not what the layer sees)."""
+    def f(W, act_absmax, X_cal, *, alpha=O.ALPHA_DEFAULT, r, damp=O.GPTQ_DAMP):
+        base = O.calibrate(W, act_absmax, alpha=alpha, r=r)
+        U = O.gptq_inverse_factor(O.gptq_hessian(np.asarray(X_cal, np.float32), damp))
+        codes = O.gptq_quantize(base["W_hat"], U, r)
+        out = dict(base)
+        out.update(Wq_codes=codes, W_deq=O.dequantize_columns(codes, base["sw"]), Wq=O.pack_int4(codes.T),
+                   H=None, U=U, X_hat_cal=(np.asarray(X_cal, np.float32)[:, base["perm"]]
+                                           * base["s_hat_inv"][None, :]).astype(np.float32))
+        return out
+    return f
+
+
 MUTANTS = {
     "compensator_sign": ("compensator", _mut_compensator_sign),
     "saliency_ascending": ("saliency_order", _mut_saliency_ascending),
@@ -197,6 +228,10 @@ MUTANTS = {
     "fused_skips_silu": ("silu_mul_quant_act", _mut_fused_skips_silu),
     "columns_s_from_sampled": ("calibrate_columns", _mut_columns_s_from_sampled),
     "columns_codes_shifted": ("calibrate_columns", _mut_columns_codes_shifted),
+    "gptq_propagates_salient": ("gptq_quantize", _mut_gptq_propagates_salient),
+    "gptq_update_sign": ("gptq_quantize", _mut_gptq_update_sign),
+    "gptq_no_damping": ("gptq_hessian", _mut_gptq_no_damping),
+    "gptq_unflattened_inputs": ("calibrate_gptq", _mut_gptq_unflattened_inputs),
 }
 
 

@@ -17,8 +17,9 @@
 // through the same widening, so the k order inside a fragment is the same
 // permutation on both sides and the dot product is unchanged; the int32 sum
 // is exactly 256 * (true sum) for W4A4 (16 * for W4A8, where the int8
-// activations are byte-shuffled into the same order). |acc| stays below
-// 2^31 for K up to 2^17.
+// activations are byte-shuffled into the same order). The scaled sum stays
+// below 2^31 for K < 2^17 (|true sum| <= 64 K for W4A4, 1024 K for W4A8);
+// longer rows take the generic kernel.
 //
 // MFMA operand roles: A = weight rows (16 output channels), B = activation
 // rows (16 tokens), so D[n][m]; lane l of a 16x16 block holds tokens
@@ -44,6 +45,7 @@ constexpr int kCUs = 256;                   // compute units of an MI355X
 constexpr int kKTileCodes = 128;            // codes per k-tile
 constexpr int kKTileW = kKTileCodes / 2;    // packed weight bytes per row per k-tile
 constexpr int kMaxResidual = 256;           // largest r handled by the tile kernels
+constexpr int kWidenMaxK = 1 << 17;         // K bound of the kernels that sum widened codes
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [0, N). Keeps
 // register-array indices static where #pragma unroll may give up.
@@ -1873,6 +1875,9 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   // A few tokens of W4A4 whose activation rows fit in LDS: int4 dot products.
   if (a_bits == 4 && M <= kGemvMaxTokens && static_cast<long>(M) * (K / 2) <= kGemvMaxX)
     return {LinearKernel::kGemv, 0, 0, 0, 1, "gemv"};
+  // The MFMA kernels sum the widened codes, 256 (W4A4) or 16 (W4A8) times the
+  // true products: exact in int32 while |acc| < 2^23, i.e. for K < 2^17.
+  if (K >= kWidenMaxK) return {LinearKernel::kGeneric, 0, 0, 0, 1, "generic"};
   // Up to 32 tokens: the skinny kernel, unless its K split would need more
   // partial-sum scratch than the library holds (then a tile kernel).
   if (M <= 32) {
