@@ -113,6 +113,42 @@ int serq_calibrate(const void* W, serq_dtype w_dtype, int K, int N,
                    uint8_t* Wq, float* sw, uint8_t* Rq, float* sr);
 
 /*
+ * serq_calibrate_gptq -- offline, host memory, synchronous, deterministic.
+ *
+ * serq_calibrate with GPTQ codes for the weights (SERQ(GPTQ); the method
+ * works with RTN and with GPTQ: gist.science/de/paper/2603.08185,
+ * "Technische Zusammenfassung" 3; the pages' accuracy rows use it:
+ * papernotes.org SERQ notes, 实验关键数据). GPTQ (Frantar et al., ICLR 2023)
+ * quantizes the rows of W^ one at a time in the saliency order and moves
+ * each row's error onto the rows not yet quantized, weighted by the upper
+ * Cholesky factor U of H^-1, H = X^^T X^ over calibration inputs. Same
+ * arguments and outputs as serq_calibrate, plus:
+ *   X_cal      T x K calibration activations in the original channel order,
+ *              dtype x_dtype (SERQ_F32 or SERQ_BF16); the Hessian is taken
+ *              over the inputs the layer sees, x^ = fl32(X_cal[t, perm[i]] *
+ *              s_hat_inv[i]), summed over t in order in double.
+ *   T          calibration tokens, T > 0.
+ *   damp       dampening: damp * mean(diag H) is added to the diagonal
+ *              (0.01 in GPTQ); an all-zero H is replaced by the identity.
+ * The r salient rows lead the order and their error is left to the
+ * compensator, so their codes, R, Q(R) and every scale equal
+ * serq_calibrate's; rows r..K-1 get GPTQ codes on the same per-column grid
+ * (scale from the column maximum of W^, codes clamped to [-8, 7]). Every
+ * step is one double operation in a fixed order, so the result does not
+ * depend on the number of host threads. Cost ~ K^3 / 3 + K^2 (T + N) / 2
+ * multiply-adds and 8 (3 K^2 + K N) bytes of host memory.
+ * Errors: as serq_calibrate, plus SERQ_EINVAL for NULL X_cal, T <= 0, bad
+ * x_dtype, damp negative or not finite, and for a Hessian that is not
+ * positive definite (possible only with damp == 0; the outputs then hold
+ * serq_calibrate's results).
+ */
+int serq_calibrate_gptq(const void* W, serq_dtype w_dtype, int K, int N,
+                        const float* act_absmax, float alpha, int r,
+                        const void* X_cal, serq_dtype x_dtype, int T, float damp,
+                        int32_t* perm, float* s_hat_inv,
+                        uint8_t* Wq, float* sw, uint8_t* Rq, float* sr);
+
+/*
  * serq_permute_outputs -- offline, host memory, in place.
  *
  * Pushes the next layer's input order into this layer's output channels so

@@ -17,7 +17,7 @@ import w4a4_linear_layers_amd as S
 from w4a4_linear_layers_amd import _lib
 from layouts import bf6_decode, pad_rq, rq_row_bytes
 from oracle import serq_oracle as O
-from synth import make_layer, workload_layer
+from synth import bf16_bits_to_f32, make_layer, round_to_bf16_bits, workload_layer
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "serq.h")
@@ -303,6 +303,82 @@ def test_calibrate_gate_up_shared_input():
     cols = np.random.default_rng(1).choice(Wf.shape[1], 48, replace=False)
     R = O.calibrate_columns(Wf, li.act_absmax, cols, r=128)
     assert_layer_equal(L, R, cols)
+
+
+# ---------------------------------------------------------------- GPTQ calibration parity
+
+def _gptq_inputs(K, N, T, seed, corr=0.4):
+    rng = np.random.default_rng(seed)
+    A = (rng.standard_normal((K, K)) * corr + np.eye(K)).astype(np.float32)
+    Xc = (rng.standard_normal((T, K)).astype(np.float32) @ A).astype(np.float32)
+    Xc[:, rng.choice(K, max(1, K // 50), replace=False)] *= np.float32(30.0)
+    W = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    return W, Xc
+
+
+@pytest.mark.parametrize("K,N,T,r,wdt,xdt,damp,seed", [
+    (64, 40, 128, 8, "f32", "f32", 0.01, 0), (128, 96, 256, 0, "f32", "f32", 0.01, 1),
+    (96, 33, 50, 96, "bf16", "f32", 0.01, 2), (256, 130, 256, 32, "bf16", "bf16", 0.1, 3),
+    (40, 24, 64, 6, "f32", "bf16", 0.0, 4), (512, 70, 300, 64, "f32", "f32", 0.01, 5),
+    (2, 1, 3, 0, "f32", "f32", 0.01, 6),
+])
+def test_calibrate_gptq_matches_oracle(K, N, T, r, wdt, xdt, damp, seed):
+    """serq_calibrate_gptq bit for bit against the oracle's GPTQ (every output
+    buffer), f32 and bf16 weights and calibration inputs, r = 0 and r = K,
+    with and without dampening."""
+    W, Xc = _gptq_inputs(K, N, T, seed)
+    if wdt == "bf16":
+        Wb = round_to_bf16_bits(W).reshape(K, N)
+        W, W_in = bf16_bits_to_f32(Wb).reshape(K, N), Wb
+    else:
+        W_in = W
+    if xdt == "bf16":
+        Xb = round_to_bf16_bits(Xc).reshape(T, K)
+        Xc, X_in = bf16_bits_to_f32(Xb).reshape(T, K), Xb
+    else:
+        X_in = Xc
+    a = np.abs(Xc).max(axis=0).astype(np.float32)
+    L = S.calibrate_gptq(W_in, a, X_in, r=r, damp=damp)
+    R = O.calibrate_gptq(W, a, Xc, r=r, damp=damp)
+    assert_layer_equal(L, R)
+
+
+def test_calibrate_gptq_dead_channels_and_zero_inputs():
+    """A channel that is zero in every calibration token (zero activation
+    maximum, an all-zero Hessian row, kept positive definite by the
+    dampening), an all-zero weight row, and all-zero calibration inputs (the
+    identity Hessian: RTN's codes)."""
+    W, Xc = _gptq_inputs(48, 20, 96, 9)
+    Xc[:, 7] = 0.0
+    W[11] = 0.0
+    a = np.abs(Xc).max(axis=0).astype(np.float32)
+    assert_layer_equal(S.calibrate_gptq(W, a, Xc, r=6), O.calibrate_gptq(W, a, Xc, r=6))
+    Z = np.zeros_like(Xc)
+    L = S.calibrate_gptq(W, a, Z, r=6)
+    assert_layer_equal(L, O.calibrate_gptq(W, a, Z, r=6))
+    assert_layer_equal(L, O.calibrate(W, a, r=6))
+
+
+def test_calibrate_gptq_argument_errors():
+    W, Xc = _gptq_inputs(8, 4, 16, 1)
+    a = np.abs(Xc).max(axis=0).astype(np.float32)
+    out = [np.zeros(8, np.int32), np.zeros(8, np.float32), np.zeros((4, 4), np.uint8), np.zeros(4, np.float32),
+           np.zeros((4, rq_row_bytes(2)), np.uint8), np.zeros(4, np.float32)]
+    p = [o.ctypes.data for o in out]
+    g = _lib.lib.serq_calibrate_gptq
+    ok = (W.ctypes.data, 0, 8, 4, a.ctypes.data, 0.5, 2, Xc.ctypes.data, 0, 16, 0.01)
+    assert g(*ok, *p) == _lib.SERQ_OK
+    for i, bad in ((7, None), (8, 5), (9, 0), (9, -1), (10, -0.5), (10, float("nan")), (10, float("inf")),
+                   (6, 3), (1, 7)):
+        args = list(ok)
+        args[i] = bad
+        assert g(*args, *p) == _lib.SERQ_EINVAL, (i, bad)
+    # fewer tokens than channels and no dampening: H is singular
+    assert g(W.ctypes.data, 0, 8, 4, a.ctypes.data, 0.5, 2, Xc.ctypes.data, 0, 3, 0.0, *p) == _lib.SERQ_EINVAL
+    with pytest.raises(ValueError):
+        O.calibrate_gptq(W, a, Xc[:3], r=2, damp=0.0)
+    with pytest.raises(ValueError):
+        S.calibrate_gptq(W, a, Xc[:, :6], r=2)
 
 
 def test_permute_outputs_matches_oracle():

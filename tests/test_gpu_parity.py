@@ -409,6 +409,34 @@ def _gate_up_cat(li):
     return W, W_in
 
 
+def test_gptq_layer_end_to_end():
+    """SERQ(GPTQ): a layer calibrated with GPTQ codes (library host code, bit
+    for bit against the oracle's GPTQ), then GPU quant_act + serq_linear on
+    it at 16 and 300 tokens: codes, scales and accumulators bit-exact, Y
+    within tolerance, on every row and column. The kernels are the same;
+    only the weight codes change."""
+    from synth import make_layer
+    li = make_layer(1024, 1536, 300, n_out=10, factor=50.0, seed=0, tag=20, dtype="bf16")
+    r = 64
+    X_cal_bits = round_to_bf16_bits(li.X_cal).reshape(li.X_cal.shape)
+    L = S.calibrate_gptq(li.W_bits, li.act_absmax, X_cal_bits, r=r)
+    R = O.calibrate_gptq(li.W, li.act_absmax, li.X_cal, r=r)
+    assert np.array_equal(L.Wq, R["Wq"]) and np.array_equal(L.perm, R["perm"])
+    assert np.array_equal(L.Rq, pad_rq(R["Rq"], r)) and np.array_equal(L.sw.view(np.uint32), R["sw"].view(np.uint32))
+    assert not np.array_equal(L.Wq, S.calibrate(li.W_bits, li.act_absmax, r=r).Wq)
+    D = L.to("cuda")
+    for M in (16, 300):
+        print(f"M = {M}: {S.kernel_name(M, 1024, 1536, r, 4)}", flush=True)
+        xq, sx = S.quant_act(bf16_tensor(li.X_bits[:M][:, L.perm]), D, a_bits=4)
+        y, am, ar = S.linear(xq, sx, D, a_bits=4, out_dtype=torch.bfloat16, debug=True)
+        _sync()
+        q = O.quant_act(li.X[:M][:, L.perm], L.s_hat_inv, 4)
+        assert np.array_equal(host(xq).view(np.uint8), q["packed"]) and np.array_equal(host(sx), q["sx"])
+        am_ref, ar_ref = O.linear_int(q["codes"], R["Wq_codes"], R["Rq_codes"], r)
+        assert np.array_equal(host(am), am_ref) and np.array_equal(host(ar), ar_ref)
+        check_y(host(y), am_ref, ar_ref, q["sx"], R["sw"], R["sr"], "bf16")
+
+
 def test_workload_tiny_full():
     """256 -> 256, r = 8, M = 16, fp32 in and out: every output checked."""
     li = workload_layer("tiny", "tiny")

@@ -22,7 +22,7 @@ from ._lib import SERQ_BF16, SERQ_F32, SerqError, check
 
 lib = _lib.lib
 
-__all__ = ["SerqLayer", "DeviceLayer", "calibrate", "permute_outputs", "quant_act", "silu_mul_quant_act",
+__all__ = ["SerqLayer", "DeviceLayer", "calibrate", "calibrate_gptq", "permute_outputs", "quant_act", "silu_mul_quant_act",
            "linear", "kernel_name", "rq_row_bytes", "SerqError", "Bf6Layer", "bf6_bytes", "prepack_bf6", "act_bf6",
            "linear_bf6", "bf6_kernel_name"]
 
@@ -124,6 +124,59 @@ def calibrate(W, act_absmax, *, r: int, alpha: float = 0.5, w_dtype: str | None 
     check("serq_calibrate", lib.serq_calibrate(_ptr(W), dt, K, N, _ptr(amax), float(alpha), r, _ptr(perm),
                                                _ptr(shi), _ptr(Wq), _ptr(sw), _ptr(Rq) if r else None,
                                                _ptr(sr) if r else None))
+    return SerqLayer(K=K, N=N, r=r, perm=perm, s_hat_inv=shi, Wq=Wq, sw=sw, Rq=Rq, sr=sr)
+
+
+def _host_matrix(A, dtype_hint):
+    """A float32 array, a uint16 array of bf16 bit patterns, or a CPU torch
+    tensor of dtype float32 / bfloat16 -> (contiguous array, SERQ dtype)."""
+    try:
+        import torch
+        if isinstance(A, torch.Tensor):
+            if A.dtype == torch.bfloat16:
+                A = A.contiguous().view(torch.int16).numpy().view(np.uint16)
+                dtype_hint = "bf16"
+            else:
+                A = A.contiguous().float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    A = np.ascontiguousarray(A)
+    if dtype_hint is None:
+        dtype_hint = "bf16" if A.dtype == np.uint16 else "f32"
+    if dtype_hint == "bf16":
+        return np.ascontiguousarray(A, dtype=np.uint16), SERQ_BF16
+    return np.ascontiguousarray(A, dtype=np.float32), SERQ_F32
+
+
+def calibrate_gptq(W, act_absmax, X_cal, *, r: int, alpha: float = 0.5, damp: float = 0.01,
+                   w_dtype: str | None = None, x_dtype: str | None = None) -> SerqLayer:
+    """Offline calibration with GPTQ weight codes (serq_calibrate_gptq).
+    ``X_cal`` is T x K calibration activations in the original channel
+    order (float32, bf16 bit patterns with ``x_dtype="bf16"``, or a CPU torch
+    tensor); ``W`` and ``act_absmax`` as for ``calibrate``."""
+    W, wdt = _host_matrix(W, w_dtype)
+    X, xdt = _host_matrix(X_cal, x_dtype)
+    K, N = W.shape
+    if X.ndim != 2 or X.shape[1] != K:
+        raise ValueError(f"X_cal must be T x {K}")
+    try:
+        import torch
+        if isinstance(act_absmax, torch.Tensor):
+            act_absmax = act_absmax.float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    amax = np.ascontiguousarray(act_absmax, dtype=np.float32)
+    if amax.shape != (K,):
+        raise ValueError("act_absmax must have K entries")
+    perm = np.empty(K, np.int32)
+    shi = np.empty(K, np.float32)
+    Wq = np.empty((N, K // 2), np.uint8)
+    sw = np.empty(N, np.float32)
+    Rq = np.zeros((N, rq_row_bytes(r)), np.uint8)
+    sr = np.zeros(N, np.float32)
+    check("serq_calibrate_gptq", lib.serq_calibrate_gptq(
+        _ptr(W), wdt, K, N, _ptr(amax), float(alpha), r, _ptr(X), xdt, X.shape[0], float(damp), _ptr(perm),
+        _ptr(shi), _ptr(Wq), _ptr(sw), _ptr(Rq) if r else None, _ptr(sr) if r else None))
     return SerqLayer(K=K, N=N, r=r, perm=perm, s_hat_inv=shi, Wq=Wq, sw=sw, Rq=Rq, sr=sr)
 
 

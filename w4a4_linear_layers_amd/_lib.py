@@ -18,7 +18,7 @@ SERQ_OK, SERQ_EINVAL, SERQ_EALIGN, SERQ_EUNSUPPORTED, SERQ_EHIP = 0, -1, -2, -3,
 SERQ_F32, SERQ_BF16 = 0, 1
 
 # every symbol include/serq.h declares
-EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_permute_outputs",
+EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_calibrate_gptq", "serq_permute_outputs",
            "serq_quant_act", "serq_silu_mul_quant_act", "serq_linear", "serq_linear_kernel_name",
            "serq_rq_row_bytes", "serq_bf6_bytes", "serq_prepack_bf6", "serq_act_bf6", "serq_linear_bf6",
            "serq_linear_bf6_kernel_name")
@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
     lib.serq_abi_version.restype = ip
     lib.serq_calibrate.argtypes = [vp, i32, ip, ip, vp, fp, ip, vp, vp, vp, vp, vp, vp]
     lib.serq_calibrate.restype = ip
+    lib.serq_calibrate_gptq.argtypes = [vp, i32, ip, ip, vp, fp, ip, vp, i32, ip, fp, vp, vp, vp, vp, vp, vp]
+    lib.serq_calibrate_gptq.restype = ip
     lib.serq_permute_outputs.argtypes = [vp, ip, ip, ip, vp, vp, vp, vp]
     lib.serq_permute_outputs.restype = ip
     lib.serq_quant_act.argtypes = [vp, i32, ip, ip, vp, ip, vp, vp, vp]

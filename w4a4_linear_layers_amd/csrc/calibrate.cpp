@@ -17,6 +17,7 @@
 // result does not depend on the thread count.
 
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 #include <cmath>
 #include <cstring>
@@ -141,6 +142,27 @@ void calibrate_columns(const WeightView& W, int K, int r, const float* s, const 
   }
 }
 
+// s_j = fl32(max(a_j, 1e-5)^alpha / max(w_j, 1e-5)^(1 - alpha)) in double
+// (exactly sqrt(a) / sqrt(w) for alpha = 1/2), s_inv_j = fl32(1 / s_j).
+void smoothing_factors(const WeightView& wv, int K, int N, const float* act_absmax, float alpha, float* s,
+                       float* s_inv) {
+  for (int j = 0; j < K; ++j) {
+    float wmax = 0.0f;
+    for (int n = 0; n < N; ++n) wmax = std::max(wmax, std::fabs(wv.at(j, n)));
+    const double a = std::max(static_cast<double>(act_absmax[j]), 1e-5);
+    const double w = std::max(static_cast<double>(wmax), 1e-5);
+    double sv;
+    if (alpha == 0.5f) {
+      sv = std::sqrt(a) / std::sqrt(w);
+    } else {
+      const double al = static_cast<double>(alpha);
+      sv = std::pow(a, al) / std::pow(w, 1.0 - al);
+    }
+    s[j] = static_cast<float>(sv);
+    s_inv[j] = 1.0f / s[j];
+  }
+}
+
 }  // namespace
 
 extern "C" int serq_calibrate(const void* W, serq_dtype w_dtype, int K, int N,
@@ -157,21 +179,7 @@ extern "C" int serq_calibrate(const void* W, serq_dtype w_dtype, int K, int N,
 
   // 1. smoothing factors from the channel maxima (double, rounded once)
   std::vector<float> s(K), s_inv(K);
-  for (int j = 0; j < K; ++j) {
-    float wmax = 0.0f;
-    for (int n = 0; n < N; ++n) wmax = std::max(wmax, std::fabs(wv.at(j, n)));
-    const double a = std::max(static_cast<double>(act_absmax[j]), 1e-5);
-    const double w = std::max(static_cast<double>(wmax), 1e-5);
-    double sv;
-    if (alpha == 0.5f) {
-      sv = std::sqrt(a) / std::sqrt(w);
-    } else {
-      const double al = static_cast<double>(alpha);
-      sv = std::pow(a, al) / std::pow(w, 1.0 - al);
-    }
-    s[j] = static_cast<float>(sv);
-    s_inv[j] = 1.0f / s[j];
-  }
+  smoothing_factors(wv, K, N, act_absmax, alpha, s.data(), s_inv.data());
 
   // 2. saliency order: descending s, ties keep the lower channel first
   std::vector<int32_t> idx(K);
@@ -273,5 +281,216 @@ extern "C" int serq_prepack_bf6(const uint8_t* codes, int rows, int k, int pitch
           const size_t off = ((static_cast<size_t>(kt) * nrb + rb) * 2 + s) * 1536 + static_cast<size_t>(l) * 24;
           std::memcpy(out + off, frag, sizeof frag);
         }
+  return SERQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// SERQ with GPTQ weight codes (serq_calibrate_gptq). GPTQ (Frantar,
+// Ashkboos, Hoefler and Alistarh, ICLR 2023) quantizes the rows of the
+// folded, permuted weight one at a time in the saliency order and moves each
+// row's quantization error onto the rows not yet quantized, weighted by the
+// upper Cholesky factor U of H^-1, H = X^T X over the layer's calibration
+// inputs (gist.science/de "Technische Zusammenfassung" 3: SERQ works with
+// RTN and with GPTQ). The r salient rows come first and their error is left
+// to the compensator R (it would otherwise be corrected twice), so their
+// codes, R, Q(R) and every scale are serq_calibrate's; GPTQ re-quantizes
+// rows r..K-1 on the same per-column grid.
+//
+// All of it is fp64 with every element updated by the same sequence of
+// single operations in the same order as the reference statement of the
+// algorithm (no contraction into fused multiply-adds in this build), so the
+// codes do not depend on the thread count:
+//   H[i][j]  = sum over t in order of x^[t][i] x^[t][j], then damp * mean(diag)
+//              on the diagonal (all-zero H: the identity);
+//   V upper with H = V V^T, eliminating from the last index:
+//              V[k][k] = sqrt(A[k][k]), V[i][k] = A[i][k] / V[k][k],
+//              A[i][j] -= V[i][k] V[j][k] (i <= j < k);
+//   U = V^-1 by back substitution: row k divided by V[k][k], then
+//              B[i][c] -= V[i][k] B[k][c] (i < k <= c);
+//   per row i: codes of fl32(w_i), e = (w_i - deq) / U[i][i] (i >= r),
+//              w_j -= U[i][j] e for j > i.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Spinning barrier for the factorizations' per-step synchronization.
+class StepBarrier {
+ public:
+  explicit StepBarrier(int n) : n_(n) {}
+  void arrive_and_wait() {
+    const int gen = gen_.load(std::memory_order_acquire);
+    if (count_.fetch_add(1, std::memory_order_acq_rel) + 1 == n_) {
+      count_.store(0, std::memory_order_relaxed);
+      gen_.fetch_add(1, std::memory_order_acq_rel);
+    } else {
+      while (gen_.load(std::memory_order_acquire) == gen) std::this_thread::yield();
+    }
+  }
+
+ private:
+  const int n_;
+  std::atomic<int> count_{0};
+  std::atomic<int> gen_{0};
+};
+
+// Run f(t, T) on T threads (t = 0 on the calling thread).
+template <typename Fn>
+void run_threads(int T, Fn f) {
+  std::vector<std::thread> pool;
+  for (int t = 1; t < T; ++t) pool.emplace_back(f, t, T);
+  f(0, T);
+  for (auto& th : pool) th.join();
+}
+
+int gptq_threads(int work) {
+  unsigned hc = std::thread::hardware_concurrency();
+  int t = hc ? static_cast<int>(hc) : 1;
+  return std::max(1, std::min({t, 16, work}));
+}
+
+}  // namespace
+
+extern "C" int serq_calibrate_gptq(const void* W, serq_dtype w_dtype, int K, int N,
+                                   const float* act_absmax, float alpha, int r,
+                                   const void* X_cal, serq_dtype x_dtype, int T, float damp,
+                                   int32_t* perm, float* s_hat_inv,
+                                   uint8_t* Wq, float* sw, uint8_t* Rq, float* sr) {
+  if (!X_cal || T <= 0) return SERQ_EINVAL;
+  if (x_dtype != SERQ_F32 && x_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (!(damp >= 0.0f && damp <= FLT_MAX)) return SERQ_EINVAL;
+  const int st = serq_calibrate(W, w_dtype, K, N, act_absmax, alpha, r, perm, s_hat_inv, Wq, sw, Rq, sr);
+  if (st != SERQ_OK) return st;
+
+  const WeightView wv{W, w_dtype, N};
+  const WeightView xv{X_cal, x_dtype, K};
+  std::vector<float> s(K), s_inv(K);
+  smoothing_factors(wv, K, N, act_absmax, alpha, s.data(), s_inv.data());
+  const size_t KK = static_cast<size_t>(K) * K;
+
+  // the inputs the layer sees: flattened and permuted, x^ = fl32(x[perm] * s^-1)
+  std::vector<double> xh(static_cast<size_t>(T) * K);
+  for (int t = 0; t < T; ++t)
+    for (int i = 0; i < K; ++i) xh[static_cast<size_t>(t) * K + i] = static_cast<double>(xv.at(t, perm[i]) * s_hat_inv[i]);
+
+  // H, upper triangle, rows dealt cyclically (row i holds K - i entries)
+  std::vector<double> A(KK, 0.0);
+  const int TH = gptq_threads(K);
+  run_threads(TH, [&](int tid, int nth) {
+    for (int t = 0; t < T; ++t) {
+      const double* x = &xh[static_cast<size_t>(t) * K];
+      for (int i = tid; i < K; i += nth) {
+        const double xi = x[i];
+        double* row = &A[static_cast<size_t>(i) * K];
+        for (int j = i; j < K; ++j) row[j] += xi * x[j];
+      }
+    }
+  });
+  double d = 0.0;
+  for (int i = 0; i < K; ++i) d += A[static_cast<size_t>(i) * K + i];
+  d = d / K;
+  if (d == 0.0) {
+    std::fill(A.begin(), A.end(), 0.0);
+    for (int i = 0; i < K; ++i) A[static_cast<size_t>(i) * K + i] = 1.0;
+  } else {
+    const double lam = static_cast<double>(damp) * d;
+    for (int i = 0; i < K; ++i) A[static_cast<size_t>(i) * K + i] += lam;
+  }
+
+  // V (upper, H = V V^T) from the last index; then U = V^-1 in B
+  std::vector<double> V(KK, 0.0), B(KK, 0.0);
+  for (int i = 0; i < K; ++i) B[static_cast<size_t>(i) * K + i] = 1.0;
+  std::atomic<int> not_pd{0};
+  {
+    StepBarrier bar(TH);
+    run_threads(TH, [&](int tid, int nth) {
+      std::vector<double> col(K);
+      for (int k = K - 1; k >= 0; --k) {
+        bar.arrive_and_wait();                        // step k + 1's updates are done
+        const double akk = A[static_cast<size_t>(k) * K + k];
+        if (!(akk > 0.0)) {
+          not_pd.store(1, std::memory_order_relaxed);
+          return;                                     // every thread sees the same value
+        }
+        const double v = std::sqrt(akk);
+        for (int i = 0; i < k; ++i) col[i] = A[static_cast<size_t>(i) * K + k] / v;
+        if (tid == 0) V[static_cast<size_t>(k) * K + k] = v;
+        for (int i = tid; i < k; i += nth) {
+          V[static_cast<size_t>(i) * K + k] = col[i];
+          double* row = &A[static_cast<size_t>(i) * K];
+          const double ci = col[i];
+          for (int j = i; j < k; ++j) row[j] -= ci * col[j];
+        }
+      }
+    });
+  }
+  if (not_pd.load()) return SERQ_EINVAL;
+  {
+    StepBarrier bar(TH);
+    run_threads(TH, [&](int tid, int nth) {
+      std::vector<double> rowk(K);
+      for (int k = K - 1; k >= 0; --k) {
+        bar.arrive_and_wait();                        // row k has all its updates
+        const double vkk = V[static_cast<size_t>(k) * K + k];
+        const double* bk = &B[static_cast<size_t>(k) * K];
+        for (int c = k; c < K; ++c) rowk[c] = bk[c] / vkk;
+        bar.arrive_and_wait();                        // every thread has read row k
+        if (k % nth == tid)
+          for (int c = k; c < K; ++c) B[static_cast<size_t>(k) * K + c] = rowk[c];
+        for (int i = tid; i < k; i += nth) {
+          const double vik = V[static_cast<size_t>(i) * K + k];
+          double* bi = &B[static_cast<size_t>(i) * K];
+          for (int c = k; c < K; ++c) bi[c] -= vik * rowk[c];
+        }
+      }
+    });
+  }
+  std::vector<double>().swap(A);
+  std::vector<double>().swap(V);
+
+  // the folded, permuted weight and its per-column grid
+  std::vector<double> Wk(static_cast<size_t>(K) * N);
+  std::vector<float> cmax(N, 0.0f);
+  for (int i = 0; i < K; ++i) {
+    const int j = perm[i];
+    const float sj = s[j];
+    for (int n = 0; n < N; ++n) {
+      const float v = sj * wv.at(j, n);
+      Wk[static_cast<size_t>(i) * N + n] = static_cast<double>(v);
+      cmax[n] = std::max(cmax[n], std::fabs(v));
+    }
+  }
+  std::vector<int8_t> codes(static_cast<size_t>(K) * N);
+  const int TC = gptq_threads(std::max(1, N / 16));
+  run_threads(TC, [&](int tid, int nth) {
+    const int per = (N + nth - 1) / nth, n0 = tid * per, n1 = std::min(N, n0 + per);
+    if (n0 >= n1) return;
+    std::vector<Quantizer> qz;
+    for (int n = n0; n < n1; ++n) qz.emplace_back(cmax[n], 7.0f);
+    std::vector<double> err(n1 - n0);
+    for (int i = 0; i < K; ++i) {
+      double* wi = &Wk[static_cast<size_t>(i) * N];
+      for (int n = n0; n < n1; ++n) {
+        const Quantizer& q = qz[n - n0];
+        const int c = q.code(static_cast<float>(wi[n]), -8, 7);
+        codes[static_cast<size_t>(i) * N + n] = static_cast<int8_t>(c);
+        if (i >= r) {
+          const double deq = static_cast<double>(static_cast<float>(c) * q.scale);
+          err[n - n0] = (wi[n] - deq) / B[static_cast<size_t>(i) * K + i];
+        }
+      }
+      if (i < r) continue;
+      const double* ui = &B[static_cast<size_t>(i) * K];
+      for (int j = i + 1; j < K; ++j) {
+        const double uij = ui[j];
+        double* wj = &Wk[static_cast<size_t>(j) * N];
+        for (int n = n0; n < n1; ++n) wj[n] -= uij * err[n - n0];
+      }
+    }
+  });
+  const size_t Kb = static_cast<size_t>(K) / 2;
+  for (int n = 0; n < N; ++n)
+    for (int i = 0; i < K; i += 2)
+      Wq[static_cast<size_t>(n) * Kb + (i >> 1)] =
+          pack2(codes[static_cast<size_t>(i) * N + n], codes[static_cast<size_t>(i + 1) * N + n]);
   return SERQ_OK;
 }
