@@ -423,6 +423,162 @@ def weighted_error(X_hat: np.ndarray, W_hat: np.ndarray, W_deq: np.ndarray, R_de
 
 
 # ---------------------------------------------------------------------------
+# The MXFP4 variant of the layer.
+# [GDE] 3 (Wichtige Beiträge): SERQ is compatible with the INT4 and MXFP4
+# formats; [GDE] 4 (Performance & Latenz): its speed is measured with MXFP4
+# on hardware FP4 products, the residual adding about 1 %; [N] 实验关键数据
+# sets it beside L2QER-MXFP4. The pages do not define MXFP4; it is the Open
+# Compute Project's "OCP Microscaling Formats (MX) Specification" v1.0:
+# blocks of 32 consecutive elements share one E8M0 scale X = 2^e, e in
+# [-127, 127] (stored as the byte e + 127); each element is FP4 E2M1 (sign,
+# two exponent bits with bias 1, one mantissa bit: magnitudes 0, 0.5, 1,
+# 1.5, 2, 3, 4, 6). The spec's conversion: e = floor(log2(max |v|)) - 2 (2 is
+# E2M1's largest exponent), then every element v / 2^e is rounded to the
+# nearest E2M1 value, ties to the even one (mantissa bit 0), and saturated
+# at +-6.
+#
+# Readings (the layer in MXFP4):
+#   * the blocks run along the reduction dimension: per output column of W^
+#     (32 consecutive rows), per token row of the activations, per output
+#     column of R (32 consecutive salient rows); r and K multiples of 32;
+#   * an all-zero block (and any block whose exponent would fall below the
+#     E8M0 range) takes e = -127; its elements are rounded as above;
+#   * s, P and W^ as in the integer layer; R = W~_s - Q(W~_s) with Q the MX
+#     quantizer of W^ (the main path's own dequantized salient rows), in
+#     fp32; Q(R) in MXFP4; the residual reuses the activation blocks of the
+#     first r channels (no second quantization);
+#   * Y = sum over blocks b of X_b W_b (sum_k x_k w_k) + sum over b < r/32 of
+#     X_b R_b (sum_k x_k rho_k): the block scales are the only scales.
+# FP4 codes are packed two per byte like the int4 codes (element 2t in the
+# low nibble): sign bit 3, exponent bits 2-1, mantissa bit 0.
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])     # magnitude of code c & 7
+E2M1_MAX_EXP = 2
+
+
+def e2m1_round(t: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code (0..15) to each value of t (exact scaled values),
+    ties to the code with mantissa bit 0, magnitudes above 6 saturated; a
+    value that rounds to zero gets code 0 (no negative zero)."""
+    t = np.asarray(t, dtype=np.float64)
+    a = np.minimum(np.abs(t), 6.0)
+    d = np.abs(a[..., None] - E2M1_VALUES)                  # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    even = (np.arange(8) & 1) == 0
+    # among the nearest (two at a tie), the even one; else the only one
+    pick = np.where(cand & even, 1, 0) + np.where(cand & ~even, 0.5, 0)
+    mag = np.argmax(pick, axis=-1)
+    sign = (t < 0) & (mag != 0)
+    return (mag | (sign.astype(np.int64) << 3)).astype(np.uint8)
+
+
+def e2m1_value(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    v = E2M1_VALUES[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def mx_block_exponent(amax: np.ndarray) -> np.ndarray:
+    """e = floor(log2(amax)) - 2 clamped to [-127, 127]; -127 for amax = 0."""
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    # floor(log2 a) through frexp (a = m 2^ex, m in [1/2, 1)), exact for every binary32 value
+    m, ex = np.frexp(np.where(a > 0, a, 1.0))
+    fl = ex - 1
+    e = np.where(a > 0, fl - E2M1_MAX_EXP, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def mx_quantize_rows(A: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP4 along the last axis (length a multiple of 32): returns (codes
+    uint8 0..15, same shape; exponents int64, one per block of 32)."""
+    A = np.asarray(A, dtype=np.float32)
+    *lead, L = A.shape
+    if L % MX_BLOCK:
+        raise ValueError("MX blocks need a length that is a multiple of 32")
+    B = A.reshape(*lead, L // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    e = mx_block_exponent(np.abs(B).max(axis=-1).astype(np.float32) if L else np.zeros((*lead, 0)))
+    t = B * np.exp2(-e.astype(np.float64))[..., None]       # exact: a power-of-two scaling in fp64
+    codes = e2m1_round(t).reshape(*lead, L)
+    return codes, e
+
+
+def mx_dequantize_rows(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """fp32 values code * 2^e (exact)."""
+    *lead, L = codes.shape
+    v = e2m1_value(codes).reshape(*lead, L // MX_BLOCK, MX_BLOCK) * np.exp2(e.astype(np.float64))[..., None]
+    return v.reshape(*lead, L).astype(np.float32)
+
+
+def calibrate_mx(W: np.ndarray, act_absmax: np.ndarray, *, alpha: float = ALPHA_DEFAULT, r: int) -> dict:
+    """The layer calibrated for MXFP4: s, P and W^ as in calibrate(); Q(W^)
+    in MXFP4 per output column (blocks along K), R on the r salient rows,
+    Q(R) in MXFP4 per output column (blocks along r).
+
+    Returns perm, s_hat_inv, Wq (N x K/2 packed FP4), Wsc (N x K/32 E8M0
+    bytes), Rq (N x r/2), Rsc (N x r/32), and for tests W_hat, Wq_codes and
+    We (N x K codes / N x K/32 exponents), W_deq (K x N), R, Rq_codes, Re."""
+    W = np.asarray(W, dtype=np.float32)
+    K, N = W.shape
+    if K % MX_BLOCK or r % MX_BLOCK or not (0 <= r <= K):
+        raise ValueError("the MX layer needs K and r multiples of 32, 0 <= r <= K")
+    s, s_inv = smoothing_factors(act_absmax, np.abs(W).max(axis=1), alpha)
+    perm = saliency_order(s)
+    W_hat = fold_and_permute(W, s, perm)
+    Wc, We = mx_quantize_rows(W_hat.T)                       # N x K codes, N x K/32 exponents
+    W_deq = mx_dequantize_rows(Wc, We).T                     # K x N
+    R = compensator(W_hat, W_deq, r)                         # r x N
+    if r:
+        Rc, Re = mx_quantize_rows(R.T)
+    else:
+        Rc, Re = np.zeros((N, 0), np.uint8), np.zeros((N, 0), np.int64)
+    return dict(K=K, N=N, r=r, s=s, perm=perm, s_hat_inv=s_inv[perm].astype(np.float32), W_hat=W_hat,
+                Wq_codes=Wc, We=We, W_deq=W_deq, R=R, Rq_codes=Rc, Re=Re,
+                Wq=pack_fp4(Wc), Wsc=(We + 127).astype(np.uint8), Rq=pack_fp4(Rc), Rsc=(Re + 127).astype(np.uint8))
+
+
+def pack_fp4(codes: np.ndarray) -> np.ndarray:
+    """Two FP4 codes per byte, element 2t in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def quant_act_mx(X_perm: np.ndarray, s_hat_inv: np.ndarray) -> dict:
+    """x^ = fl32(x * s_hat_inv), then MXFP4 per token row (blocks along K)."""
+    x_hat = (np.asarray(X_perm, dtype=np.float32) * np.asarray(s_hat_inv, dtype=np.float32)[None, :]).astype(np.float32)
+    codes, e = mx_quantize_rows(x_hat)
+    return dict(codes=codes, e=e, packed=pack_fp4(codes), sc=(e + 127).astype(np.uint8), x_hat=x_hat)
+
+
+def linear_mx(Xq: dict, layer: dict) -> dict:
+    """acc_main[m, n] = sum_b 2^(ex_b + ew_b) sum_{k in b} x_k w_k over K and
+    acc_res over the first r/32 blocks with Q(R); y = acc_main + acc_res.
+    Evaluated in fp64 from the exact element values (each block's sum and
+    every scaled product are exact; across blocks the fp64 rounding is far
+    below fp32's)."""
+    r = layer["r"]
+    xv = e2m1_value(Xq["codes"])                                         # M x K
+    M, K = xv.shape
+    xs = xv.reshape(M, K // MX_BLOCK, MX_BLOCK) * np.exp2(Xq["e"].astype(np.float64))[..., None]
+    wv = e2m1_value(layer["Wq_codes"]).reshape(layer["N"], K // MX_BLOCK, MX_BLOCK)
+    ws = wv * np.exp2(layer["We"].astype(np.float64))[..., None]
+    acc_main = xs.reshape(M, K) @ ws.reshape(layer["N"], K).T
+    if r:
+        rv = e2m1_value(layer["Rq_codes"]).reshape(layer["N"], r // MX_BLOCK, MX_BLOCK)
+        rs = rv * np.exp2(layer["Re"].astype(np.float64))[..., None]
+        acc_res = xs[:, : r // MX_BLOCK].reshape(M, r) @ rs.reshape(layer["N"], r).T
+    else:
+        acc_res = np.zeros_like(acc_main)
+    # magnitude sums for the rounding bound of an fp32 accumulation
+    mag = np.abs(xs.reshape(M, K)) @ np.abs(ws.reshape(layer["N"], K)).T
+    if r:
+        mag = mag + np.abs(xs[:, : r // MX_BLOCK].reshape(M, r)) @ np.abs(rs.reshape(layer["N"], r)).T
+    return dict(acc_main=acc_main, acc_res=acc_res, y64=acc_main + acc_res, mag=mag)
+
+
+# ---------------------------------------------------------------------------
 # Offline propagation of a later layer's permutation into this layer's output
 # columns. [N] 关键设计 3: the activation order a layer needs is produced by
 # permuting the previous layer's weight columns offline (the down projection's

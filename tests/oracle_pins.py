@@ -623,9 +623,110 @@ def check_gptq_reduces_error(O):
             assert eg < 0.9 * et, (seed, r, eg, et)
 
 
+# ---------------------------------------------------------------- MXFP4
+
+def _e2m1_spec_value(c: int) -> float:
+    """E2M1 by its bit fields: sign bit 3, exponent bits 2-1 (bias 1),
+    mantissa bit 0; exponent 0 is subnormal (0.m x 2^0)."""
+    sgn = -1.0 if c & 8 else 1.0
+    e, m = (c >> 1) & 3, c & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+    return sgn * mag
+
+
+def check_mx_quantizer(O):
+    """The MXFP4 quantizer (OCP Microscaling Formats (MX) v1.0; [GDE] 3:
+    SERQ works with MXFP4): the hand-worked blocks of mxfp4_blocks.json, the
+    E2M1 code table from its bit fields, nearest-value rounding with ties to
+    the even mantissa by exhaustive search, saturation at 6, the shared
+    exponent's closed form, and lossless blocks."""
+    fx = golden("mxfp4_blocks.json")
+    for case in fx["cases"]:
+        codes, e = O.mx_quantize_rows(np.array(case["v"], np.float32)[None, :])
+        assert codes[0].tolist() == case["codes"] and int(e[0, 0]) == case["e"], case["e"]
+        assert O.mx_dequantize_rows(codes, e)[0].tolist() == [float(np.float32(v)) for v in case["values"]]
+    for c in range(16):
+        assert float(O.e2m1_value(np.array([c]))[0]) == _e2m1_spec_value(c) + 0.0
+    grid = sorted({abs(_e2m1_spec_value(c)) for c in range(8)})
+    mids = [(a + b) / 2 for a, b in zip(grid, grid[1:])]
+    ts = np.array(sorted(set(np.linspace(-9, 9, 7201).tolist() + mids + [-m for m in mids]
+                              + [m + d for m in mids for d in (1e-9, -1e-9)])))
+    got = O.e2m1_value(O.e2m1_round(ts))
+    for t, g in zip(ts, got):
+        a = min(abs(t), 6.0)
+        dist = [abs(a - v) for v in grid]
+        best = min(dist)
+        near = [v for v, d in zip(grid, dist) if d == best]
+        if len(near) == 2:      # a tie: the value whose mantissa bit is 0
+            want = [v for v in near if [c for c in range(8) if _e2m1_spec_value(c) == v][0] % 2 == 0][0]
+        else:
+            want = near[0]
+        assert abs(g) == want and (g == 0 or (g < 0) == (t < 0)), (t, g, want)
+    rng = np.random.default_rng(4)
+    amax = (np.exp2(rng.uniform(-120, 120, 5000)) * rng.uniform(1, 2, 5000)).astype(np.float32)
+    e = O.mx_block_exponent(amax).astype(np.float64)
+    a = amax.astype(np.float64)
+    assert ((np.exp2(e + 2) <= a) & (a < np.exp2(e + 3))).all()
+    assert O.mx_block_exponent(np.float32([0.0, 1e-42]))[0] == -127
+    # lossless: blocks of E2M1 values times 2^e whose largest magnitude is 4 or 6
+    for trial in range(20):
+        codes = rng.integers(0, 16, 32)
+        codes[rng.integers(0, 32)] = rng.choice([6, 7, 14, 15])
+        ee = int(rng.integers(-100, 100))
+        v = (O.e2m1_value(codes) * 2.0 ** ee).astype(np.float32)
+        c2, e2 = O.mx_quantize_rows(v[None, :])
+        assert np.array_equal(O.mx_dequantize_rows(c2, e2)[0], v)
+
+
+def check_mx_layer(O):
+    """The MXFP4 layer: the block dot products against brute force in exact
+    rationals; R = fl32(W^ - deq Q(W^)) on the salient rows (the definition,
+    [N] 核心 idea) with the exact reconstruction on the Sterbenz set; blocks
+    along K per output column (scaling one column of W by 2^j moves only its
+    exponents); the residual on the first r channels' blocks."""
+    rng = np.random.default_rng(8)
+    K, N, M, r = 96, 5, 3, 32
+    W = (0.05 * rng.standard_normal((K, N))).astype(np.float32)
+    a = (rng.random(K) * 4 + 0.1).astype(np.float32)
+    L = O.calibrate_mx(W, a, r=r)
+    X = rng.standard_normal((M, K)).astype(np.float32) * 3
+    q = O.quant_act_mx(X[:, L["perm"]], L["s_hat_inv"])
+    out = O.linear_mx(q, L)
+    xv = O.e2m1_value(q["codes"])
+    wv = O.e2m1_value(L["Wq_codes"])
+    rv = O.e2m1_value(L["Rq_codes"])
+    for m in range(M):
+        for n in range(N):
+            main = sum(Fraction(float(xv[m, k])) * Fraction(float(wv[n, k]))
+                       * Fraction(2) ** int(q["e"][m, k // 32] + L["We"][n, k // 32]) for k in range(K))
+            res = sum(Fraction(float(xv[m, k])) * Fraction(float(rv[n, k]))
+                      * Fraction(2) ** int(q["e"][m, k // 32] + L["Re"][n, k // 32]) for k in range(r))
+            assert Fraction(float(out["acc_main"][m, n])) == main and Fraction(float(out["acc_res"][m, n])) == res
+    Wd = L["W_deq"]
+    assert np.array_equal(L["R"], (L["W_hat"][:r] - Wd[:r]).astype(np.float32))
+    rec = (Wd[:r] + L["R"]).astype(np.float32)
+    ster = (Wd[:r] == 0) | ((np.abs(Wd[:r]) / 2 <= np.abs(L["W_hat"][:r])) & (np.abs(L["W_hat"][:r]) <= 2 * np.abs(Wd[:r])))
+    assert np.array_equal(rec[ster], L["W_hat"][:r][ster])
+    assert np.array_equal(L["Wq"], O.pack_fp4(L["Wq_codes"])) and L["Wq"].shape == (N, K // 2)
+    assert L["Wsc"].shape == (N, K // 32) and L["Rsc"].shape == (N, r // 32)
+    # scaling W and the activation maxima by 2^6 leaves s and the codes, and
+    # adds 6 to every exponent
+    L2 = O.calibrate_mx((W * np.float32(64.0)).astype(np.float32), a * np.float32(64.0), r=r)
+    assert np.array_equal(L2["perm"], L["perm"]) and np.array_equal(L2["Wq_codes"], L["Wq_codes"])
+    assert (L2["We"] - L["We"] == 6).all()
+    # blocks run along K within one output column: growing one element of W^
+    # changes the codes and exponent of its own block only
+    Wh = L["W_hat"].copy()
+    Wh[40, 3] = np.float32(50.0) * np.abs(Wh[:, 3]).max()
+    c2, e2 = O.mx_quantize_rows(Wh.T)
+    diff = np.argwhere(c2 != L["Wq_codes"])
+    assert len(diff) and set(map(tuple, (diff // [1, 32]).tolist())) == {(3, 1)}
+    assert np.argwhere(e2 != L["We"]).tolist() == [[3, 1]]
+
+
 ALL_CHECKS = [check_pack, check_quantizer_golden, check_quantizer_bruteforce, check_smoothing,
               check_perm, check_fold_identity, check_compensator, check_int_gemm,
               check_dequant_identity, check_special_cases, check_worked_layer, check_bf16,
               check_permute_outputs, check_rank_trend, check_fma32, check_exp32, check_silu_mul,
               check_calibrate_columns, check_exp_split_constant, check_gptq_exact,
-              check_gptq_special_cases, check_gptq_reduces_error]
+              check_gptq_special_cases, check_gptq_reduces_error, check_mx_quantizer, check_mx_layer]

@@ -208,6 +208,57 @@ def _mut_gptq_unflattened_inputs(orig):
     return f
 
 
+def _mut_e2m1_ties_away(orig):
+    """Ties rounded away from zero instead of to the even mantissa."""
+    def f(t):
+        t = np.asarray(t, np.float64)
+        a = np.minimum(np.abs(t), 6.0)
+        d = np.abs(a[..., None] - O.E2M1_VALUES)
+        best = d.min(axis=-1, keepdims=True)
+        cand = d == best
+        mag = 7 - np.argmax(cand[..., ::-1], axis=-1)          # the larger of the nearest
+        sign = (t < 0) & (mag != 0)
+        return (mag | (sign.astype(np.int64) << 3)).astype(np.uint8)
+    return f
+
+
+def _mut_mx_exponent_no_offset(orig):
+    """The shared exponent without E2M1's largest exponent subtracted."""
+    return lambda amax: np.clip(orig(amax) + 2, -127, 127)
+
+
+def _mut_mx_blocks_along_n(orig):
+    """Weight blocks of 32 output channels (along N) instead of along K."""
+    def f(W, act_absmax, *, alpha=O.ALPHA_DEFAULT, r):
+        L = orig(W, act_absmax, alpha=alpha, r=r)
+        Wh = L["W_hat"]
+        K, N = Wh.shape
+        pad = (-N) % 32
+        Wp = np.concatenate([Wh, np.zeros((K, pad), np.float32)], axis=1)
+        c, e = O.mx_quantize_rows(Wp)
+        deq = O.mx_dequantize_rows(c, e)[:, :N]
+        c2, e2 = O.mx_quantize_rows(deq.T)
+        L = dict(L)
+        L.update(Wq_codes=c2, We=e2, W_deq=O.mx_dequantize_rows(c2, e2).T, Wq=O.pack_fp4(c2))
+        return L
+    return f
+
+
+def _mut_mx_residual_last_blocks(orig):
+    def f(Xq, layer):
+        out = orig(Xq, layer)
+        r = layer["r"]
+        if r:
+            Xq2 = dict(Xq)
+            Xq2["codes"] = np.roll(Xq["codes"], r, axis=1)
+            Xq2["e"] = np.roll(Xq["e"], r // 32, axis=1)
+            out2 = orig(Xq2, layer)
+            out = dict(out)
+            out["acc_res"] = out2["acc_res"]
+        return out
+    return f
+
+
 MUTANTS = {
     "compensator_sign": ("compensator", _mut_compensator_sign),
     "saliency_ascending": ("saliency_order", _mut_saliency_ascending),
@@ -232,6 +283,10 @@ MUTANTS = {
     "gptq_update_sign": ("gptq_quantize", _mut_gptq_update_sign),
     "gptq_no_damping": ("gptq_hessian", _mut_gptq_no_damping),
     "gptq_unflattened_inputs": ("calibrate_gptq", _mut_gptq_unflattened_inputs),
+    "e2m1_ties_away": ("e2m1_round", _mut_e2m1_ties_away),
+    "mx_exponent_no_offset": ("mx_block_exponent", _mut_mx_exponent_no_offset),
+    "mx_blocks_along_n": ("calibrate_mx", _mut_mx_blocks_along_n),
+    "mx_residual_last_blocks": ("linear_mx", _mut_mx_residual_last_blocks),
 }
 
 
