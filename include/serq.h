@@ -378,6 +378,79 @@ int serq_linear_bf6(const void* X6, const float* sx,
  */
 const char* serq_linear_bf6_kernel_name(int M, int N, int r);
 
+/*
+ * The MXFP4 variant of the layer.
+ *
+ * The pages run SERQ on MXFP4 as well as INT4 (gist.science/de/paper/
+ * 2603.08185, "Technische Zusammenfassung" 3: compatible with INT4 and
+ * MXFP4; 4, Performance & Latenz: measured on hardware FP4 products, the
+ * residual adding about 1 %). The format is OCP Microscaling (MX): blocks of
+ * 32 consecutive elements along K share an E8M0 exponent e (stored as the
+ * byte e + 127; the scale is 2^e), e = floor(log2(max |v|)) - 2 clamped to
+ * [-127, 127] (-127 for an all-zero block); each element is the FP4 E2M1
+ * value (sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0:
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to v / 2^e, ties to the
+ * even mantissa, saturated at 6; a value that rounds to zero is code 0.
+ * Codes are packed two per byte, element 2t in the low nibble. In the layer
+ * the blocks run along K: per output column of W^, per token row of the
+ * activations, per output column of R over its r rows (K and r multiples of
+ * 32). s, P and W^ are those of serq_calibrate; R = W~_s - Q(W~_s) with the
+ * MX quantizer's own dequantized salient rows, in fp32; Q(R) in MXFP4. The
+ * block exponents are the only scales:
+ *   Y[m, n] = sum over blocks b of 2^(ex_mb + ew_nb) sum_{k in b} x_mk w_nk
+ *           + sum over the first r/32 blocks of 2^(ex_mb + er_nb) sum x_mk rho_nk.
+ */
+
+/*
+ * serq_calibrate_mx -- offline, host memory, synchronous, deterministic.
+ * As serq_calibrate, with MXFP4 outputs:
+ *   Wq   N x K/2 bytes: column n of Q(W^), FP4 codes along K.
+ *   Wsc  N x K/32 bytes: E8M0 exponent bytes of those blocks.
+ *   Rq   N x r/2 bytes, Rsc N x r/32 bytes: Q(R) likewise (NULL when r == 0).
+ * Errors: SERQ_EINVAL for NULL pointers, K or N <= 0, K or r not a multiple
+ * of 32, r outside [0, K], alpha outside [0, 1], unknown w_dtype.
+ */
+int serq_calibrate_mx(const void* W, serq_dtype w_dtype, int K, int N,
+                      const float* act_absmax, float alpha, int r,
+                      int32_t* perm, float* s_hat_inv,
+                      uint8_t* Wq, uint8_t* Wsc, uint8_t* Rq, uint8_t* Rsc);
+
+/*
+ * serq_quant_act_mx -- online, device memory, asynchronous on `stream`.
+ * x^ = fl32(X[m, k] * s_hat_inv[k]) (X already in saliency order), then
+ * MXFP4 per token row in blocks of 32 along K.
+ *   X      M x K, SERQ_F32 or SERQ_BF16; K a multiple of 32.
+ *   Xq     M x K/2 bytes of FP4 codes; Xsc M x K/32 exponent bytes.
+ * M == 0 is a no-op. Errors: SERQ_EINVAL (NULL pointer, M < 0, K not a
+ * positive multiple of 32, bad dtype), SERQ_EALIGN (X, Xq or s_hat_inv not
+ * 16-byte aligned), SERQ_EHIP. Uses no scratch memory.
+ */
+int serq_quant_act_mx(const void* X, serq_dtype x_dtype, int M, int K,
+                      const float* s_hat_inv, uint8_t* Xq, uint8_t* Xsc, void* stream);
+
+/*
+ * serq_linear_mx -- online, device memory, asynchronous on `stream`.
+ * Y = acc_main + acc_res (the formula above) on gfx950's scaled FP4 matrix
+ * instruction, whose operands are these codes and exponent bytes as stored.
+ * Accumulation is fp32 (rounded, unlike the integer layer); Y is stored as
+ * y_dtype (bf16 with round to nearest even).
+ *   Xq, Xsc    from serq_quant_act_mx; Wq, Wsc, Rq, Rsc from
+ *              serq_calibrate_mx (Rq, Rsc may be NULL when r == 0).
+ *   M, K, N, r M >= 0 (0: no-op), K > 0 and 0 <= r <= K multiples of 32,
+ *              N > 0.
+ *   acc_main_dbg, acc_res_dbg  NULL, or both device M x N floats that
+ *              receive the two fp32 accumulators.
+ * Uses no scratch memory. Errors: SERQ_EINVAL, SERQ_EALIGN (Xq, Wq, Rq, Y or
+ * the debug buffers not 16-byte aligned), SERQ_EHIP.
+ */
+int serq_linear_mx(const uint8_t* Xq, const uint8_t* Xsc,
+                   const uint8_t* Wq, const uint8_t* Wsc,
+                   const uint8_t* Rq, const uint8_t* Rsc,
+                   int M, int K, int N, int r,
+                   void* Y, serq_dtype y_dtype,
+                   float* acc_main_dbg, float* acc_res_dbg,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

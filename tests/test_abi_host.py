@@ -381,6 +381,65 @@ def test_calibrate_gptq_argument_errors():
         S.calibrate_gptq(W, a, Xc[:, :6], r=2)
 
 
+# ---------------------------------------------------------------- MXFP4 calibration parity
+
+@pytest.mark.parametrize("K,N,r,dtype,seed", [
+    (256, 40, 64, "f32", 0), (128, 33, 0, "bf16", 1), (96, 17, 96, "f32", 2), (512, 64, 128, "bf16", 3),
+    (32, 1, 32, "f32", 4), (1024, 100, 256, "bf16", 5),
+])
+def test_calibrate_mx_matches_oracle(K, N, r, dtype, seed):
+    """serq_calibrate_mx bit for bit against the oracle's MXFP4 calibration:
+    perm, s_hat_inv, FP4 codes and E8M0 bytes of Q(W^) and Q(R), with an
+    all-zero column, a column of huge values and one of tiny values."""
+    li = make_layer(K, N, 1, n_out=2, factor=30.0, seed=seed, tag=31, dtype=dtype)
+    W = li.W.copy()
+    if N > 3:
+        W[:, 1] = 0.0
+        W[:, 2] *= np.float32(1e30)
+        W[:, 3] *= np.float32(1e-30)
+    W_in = round_to_bf16_bits(W).reshape(K, N) if dtype == "bf16" else W
+    if dtype == "bf16":
+        W = bf16_bits_to_f32(W_in).reshape(K, N)
+    L = S.calibrate_mx(W_in, li.act_absmax, r=r)
+    R = O.calibrate_mx(W, li.act_absmax, r=r)
+    assert np.array_equal(L.perm, R["perm"])
+    assert np.array_equal(L.s_hat_inv.view(np.uint32), R["s_hat_inv"].view(np.uint32))
+    for k in ("Wq", "Wsc", "Rq", "Rsc"):
+        assert np.array_equal(getattr(L, k), R[k]), k
+
+
+def test_mx_argument_errors():
+    W = np.ones((64, 4), np.float32)
+    a = np.ones(64, np.float32)
+    out = [np.zeros(64, np.int32), np.zeros(64, np.float32), np.zeros((4, 32), np.uint8), np.zeros((4, 2), np.uint8),
+           np.zeros((4, 16), np.uint8), np.zeros((4, 1), np.uint8)]
+    p = [o.ctypes.data for o in out]
+    c = _lib.lib.serq_calibrate_mx
+    assert c(W.ctypes.data, 0, 64, 4, a.ctypes.data, 0.5, 32, *p) == _lib.SERQ_OK
+    assert c(W.ctypes.data, 0, 48, 4, a.ctypes.data, 0.5, 32, *p) == _lib.SERQ_EINVAL      # K % 32
+    assert c(W.ctypes.data, 0, 64, 4, a.ctypes.data, 0.5, 16, *p) == _lib.SERQ_EINVAL      # r % 32
+    assert c(W.ctypes.data, 0, 64, 4, a.ctypes.data, 0.5, 96, *p) == _lib.SERQ_EINVAL      # r > K
+    assert c(W.ctypes.data, 0, 64, 4, a.ctypes.data, 0.5, 32, *p[:4], None, None) == _lib.SERQ_EINVAL
+    q = _lib.lib.serq_quant_act_mx
+    assert q(A16, _lib.SERQ_BF16, 4, 48, A16, A16, A16, None) == _lib.SERQ_EINVAL           # K % 32
+    assert q(A16, 5, 4, 64, A16, A16, A16, None) == _lib.SERQ_EINVAL                        # dtype
+    assert q(A16, _lib.SERQ_BF16, -1, 64, A16, A16, A16, None) == _lib.SERQ_EINVAL
+    assert q(A16 + 2, _lib.SERQ_BF16, 4, 64, A16, A16, A16, None) == _lib.SERQ_EALIGN
+    assert q(None, _lib.SERQ_BF16, 0, 64, A16, None, None, None) == _lib.SERQ_OK            # M = 0: no-op
+    f = _lib.lib.serq_linear_mx
+    ok = [A16, A16, A16, A16, A16, A16, 4, 64, 32, 32, A16, _lib.SERQ_BF16, None, None, None]
+    for i, bad, code in ((7, 48, _lib.SERQ_EINVAL), (9, 16, _lib.SERQ_EINVAL), (9, 96, _lib.SERQ_EINVAL),
+                         (8, 0, _lib.SERQ_EINVAL), (11, 7, _lib.SERQ_EINVAL), (2, A16 + 4, _lib.SERQ_EALIGN),
+                         (0, A16 + 8, _lib.SERQ_EALIGN), (10, A16 + 2, _lib.SERQ_EALIGN), (4, None, _lib.SERQ_EINVAL),
+                         (12, A16, _lib.SERQ_EINVAL)):
+        args = list(ok)
+        args[i] = bad
+        assert f(*args) == code, (i, bad)
+    args = list(ok)
+    args[6] = 0
+    assert f(*args) == _lib.SERQ_OK                                                           # M = 0: no-op
+
+
 def test_permute_outputs_matches_oracle():
     li = make_layer(64, 40, 1, n_out=2, factor=30.0, seed=9, tag=1, dtype="f32")
     L = S.calibrate(li.W, li.act_absmax, r=16)

@@ -24,7 +24,7 @@ lib = _lib.lib
 
 __all__ = ["SerqLayer", "DeviceLayer", "calibrate", "calibrate_gptq", "permute_outputs", "quant_act", "silu_mul_quant_act",
            "linear", "kernel_name", "rq_row_bytes", "SerqError", "Bf6Layer", "bf6_bytes", "prepack_bf6", "act_bf6",
-           "linear_bf6", "bf6_kernel_name"]
+           "linear_bf6", "bf6_kernel_name", "MxLayer", "calibrate_mx", "quant_act_mx", "linear_mx"]
 
 
 def _ptr(a: np.ndarray):
@@ -420,3 +420,114 @@ def bf6_kernel_name(M: int, N: int, r: int = 0) -> str | None:
     """The tile serq_linear_bf6 launches for these sizes."""
     s = lib.serq_linear_bf6_kernel_name(M, N, r)
     return s.decode() if s else None
+
+
+# ------------------------------------------------------------------ MXFP4
+
+@dataclass
+class MxLayer:
+    """A layer calibrated for MXFP4 (serq_calibrate_mx): FP4 codes two per
+    byte and one E8M0 exponent byte per 32 elements along K; host numpy
+    arrays or, after ``to``, device tensors."""
+
+    K: int
+    N: int
+    r: int
+    perm: "object"          # K int32
+    s_hat_inv: "object"     # K float32
+    Wq: "object"            # N x K/2 uint8
+    Wsc: "object"           # N x K/32 uint8
+    Rq: "object"            # N x r/2 uint8
+    Rsc: "object"           # N x r/32 uint8
+
+    def to(self, device="cuda") -> "MxLayer":
+        import torch
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+        return MxLayer(K=self.K, N=self.N, r=self.r, perm=t(self.perm), s_hat_inv=t(self.s_hat_inv),
+                       Wq=t(self.Wq), Wsc=t(self.Wsc), Rq=t(self.Rq), Rsc=t(self.Rsc))
+
+
+def calibrate_mx(W, act_absmax, *, r: int, alpha: float = 0.5, w_dtype: str | None = None) -> MxLayer:
+    """Offline MXFP4 calibration (serq_calibrate_mx); arguments as for
+    ``calibrate``; K and r multiples of 32."""
+    W, wdt = _host_matrix(W, w_dtype)
+    K, N = W.shape
+    amax = np.ascontiguousarray(act_absmax, dtype=np.float32)
+    if amax.shape != (K,):
+        raise ValueError("act_absmax must have K entries")
+    perm = np.empty(K, np.int32)
+    shi = np.empty(K, np.float32)
+    Wq = np.empty((N, K // 2), np.uint8)
+    Wsc = np.empty((N, K // 32), np.uint8)
+    Rq = np.zeros((N, r // 2), np.uint8)
+    Rsc = np.zeros((N, r // 32), np.uint8)
+    check("serq_calibrate_mx", lib.serq_calibrate_mx(
+        _ptr(W), wdt, K, N, _ptr(amax), float(alpha), r, _ptr(perm), _ptr(shi), _ptr(Wq), _ptr(Wsc),
+        _ptr(Rq) if r else None, _ptr(Rsc) if r else None))
+    return MxLayer(K=K, N=N, r=r, perm=perm, s_hat_inv=shi, Wq=Wq, Wsc=Wsc, Rq=Rq, Rsc=Rsc)
+
+
+def quant_act_mx(x, layer_or_sinv, *, out=None):
+    """MXFP4 activation quantization (serq_quant_act_mx) on the current
+    stream: ``x`` M x K float32 or bfloat16 in saliency order. Returns
+    (xq uint8 M x K/2, xsc uint8 M x K/32)."""
+    import torch
+    sinv = layer_or_sinv.s_hat_inv if isinstance(layer_or_sinv, MxLayer) else layer_or_sinv
+    _need_cuda(x, sinv)
+    M, K = x.shape
+    if x.dtype == torch.bfloat16:
+        dt = SERQ_BF16
+    elif x.dtype == torch.float32:
+        dt = SERQ_F32
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    if sinv.numel() != K or K % 32:
+        raise ValueError(f"s_hat_inv must have K = {K} entries and K a multiple of 32")
+    if out is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        xsc = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    else:
+        xq, xsc = out
+        _need_cuda(xq, xsc)
+        if tuple(xq.shape) != (M, K // 2) or tuple(xsc.shape) != (M, K // 32) or xq.element_size() != 1 \
+                or xsc.element_size() != 1:
+            raise ValueError(f"out must be (uint8 {M} x {K // 2}, uint8 {M} x {K // 32})")
+    check("serq_quant_act_mx", lib.serq_quant_act_mx(x.data_ptr(), dt, M, K, sinv.data_ptr(), xq.data_ptr(),
+                                                     xsc.data_ptr(), _stream()))
+    return xq, xsc
+
+
+def linear_mx(xq, xsc, layer: MxLayer, *, out_dtype=None, out=None, debug: bool = False):
+    """The MXFP4 SERQ linear (serq_linear_mx) on the current stream. Returns
+    Y (M x N) or, with ``debug=True``, (Y, acc_main, acc_res) in fp32."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    K, N, r = layer.K, layer.N, layer.r
+    _need_cuda(xq, xsc, layer.Wq, layer.Wsc, layer.Rq if r else None, layer.Rsc if r else None)
+    M = xq.shape[0]
+    if tuple(xq.shape) != (M, K // 2) or tuple(xsc.shape) != (M, K // 32):
+        raise ValueError(f"xq, xsc must be M x {K // 2} and M x {K // 32} for this layer")
+    if tuple(layer.Wq.shape) != (N, K // 2) or tuple(layer.Wsc.shape) != (N, K // 32):
+        raise ValueError("layer buffers do not match its sizes")
+    if out_dtype == torch.bfloat16:
+        dt = SERQ_BF16
+    elif out_dtype == torch.float32:
+        dt = SERQ_F32
+    else:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    else:
+        y = out
+        _need_cuda(y)
+        if tuple(y.shape) != (M, N) or y.dtype != out_dtype:
+            raise ValueError(f"out must be a ({M}, {N}) {out_dtype} tensor")
+    am = ar = None
+    if debug:
+        am = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+        ar = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    check("serq_linear_mx", lib.serq_linear_mx(
+        xq.data_ptr(), xsc.data_ptr(), layer.Wq.data_ptr(), layer.Wsc.data_ptr(),
+        layer.Rq.data_ptr() if r else None, layer.Rsc.data_ptr() if r else None, M, K, N, r, y.data_ptr(), dt,
+        am.data_ptr() if debug else None, ar.data_ptr() if debug else None, _stream()))
+    return (y, am, ar) if debug else y

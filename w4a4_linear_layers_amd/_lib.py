@@ -21,7 +21,7 @@ SERQ_F32, SERQ_BF16 = 0, 1
 EXPORTS = ("serq_strerror", "serq_abi_version", "serq_calibrate", "serq_calibrate_gptq", "serq_permute_outputs",
            "serq_quant_act", "serq_silu_mul_quant_act", "serq_linear", "serq_linear_kernel_name",
            "serq_rq_row_bytes", "serq_bf6_bytes", "serq_prepack_bf6", "serq_act_bf6", "serq_linear_bf6",
-           "serq_linear_bf6_kernel_name")
+           "serq_linear_bf6_kernel_name", "serq_calibrate_mx", "serq_quant_act_mx", "serq_linear_mx")
 
 
 class SerqError(RuntimeError):
@@ -74,6 +74,12 @@ def _load() -> ctypes.CDLL:
     lib.serq_linear_bf6.restype = ip
     lib.serq_linear_bf6_kernel_name.argtypes = [ip, ip, ip]
     lib.serq_linear_bf6_kernel_name.restype = ctypes.c_char_p
+    lib.serq_calibrate_mx.argtypes = [vp, i32, ip, ip, vp, fp, ip, vp, vp, vp, vp, vp, vp]
+    lib.serq_calibrate_mx.restype = ip
+    lib.serq_quant_act_mx.argtypes = [vp, i32, ip, ip, vp, vp, vp, vp]
+    lib.serq_quant_act_mx.restype = ip
+    lib.serq_linear_mx.argtypes = [vp, vp, vp, vp, vp, vp, ip, ip, ip, ip, vp, i32, vp, vp, vp]
+    lib.serq_linear_mx.restype = ip
     return lib
 
 

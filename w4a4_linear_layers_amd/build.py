@@ -28,7 +28,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libserq.so")
 ARCH = os.environ.get("SERQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["serq_abi.cpp", "calibrate.cpp", "quant_act.hip", "serq_gemm.hip"]
+SOURCES = ["serq_abi.cpp", "calibrate.cpp", "quant_act.hip", "serq_gemm.hip", "serq_mx.hip"]
 
 
 def hipcc() -> str:

@@ -494,3 +494,113 @@ extern "C" int serq_calibrate_gptq(const void* W, serq_dtype w_dtype, int K, int
           pack2(codes[static_cast<size_t>(i) * N + n], codes[static_cast<size_t>(i + 1) * N + n]);
   return SERQ_OK;
 }
+
+// ---------------------------------------------------------------------------
+// The MXFP4 layer (serq_calibrate_mx). The pages run SERQ on MXFP4 as well as
+// INT4 (gist.science/de "Technische Zusammenfassung" 3 and 4); the format
+// is the OCP Microscaling (MX) one: blocks of 32 elements along the
+// reduction dimension share an E8M0 exponent e = floor(log2(max |v|)) - 2,
+// clamped to [-127, 127] (-127 for an all-zero block), and each element is
+// the FP4 E2M1 value nearest to v / 2^e, ties to the even mantissa,
+// saturated at 6 (a value that rounds to zero is code 0). The scaling by
+// 2^-e is exact, so the code depends only on the binary32 value of v.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+inline int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int ex = 0;
+  (void)std::frexp(amax, &ex);                 // amax = m 2^ex, m in [1/2, 1)
+  return std::max(-127, std::min(127, ex - 1 - 2));
+}
+
+// E2M1 code of t (|t| < 8 by construction): nearest of 0, .5, 1, 1.5, 2, 3,
+// 4, 6, ties to the even mantissa (0, 1, 2, 4), saturated at 6.
+inline int e2m1_code(double t) {
+  const double a = std::fabs(t);
+  int c;
+  if (a <= 0.25) c = 0;
+  else if (a < 0.75) c = 1;
+  else if (a <= 1.25) c = 2;
+  else if (a < 1.75) c = 3;
+  else if (a <= 2.5) c = 4;
+  else if (a < 3.5) c = 5;
+  else if (a <= 5.0) c = 6;
+  else c = 7;
+  return (t < 0.0 && c != 0) ? (c | 8) : c;
+}
+
+const float kE2m1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+// One MX block of n (<= 32) values: codes into `codes`, the exponent
+// returned; `deq` (optional) receives code * 2^e.
+int mx_block(const float* v, int n, int* codes, float* deq) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) amax = std::max(amax, std::fabs(v[i]));
+  const int e = mx_exponent(amax);
+  for (int i = 0; i < n; ++i) {
+    const int c = e2m1_code(std::ldexp(static_cast<double>(v[i]), -e));
+    codes[i] = c;
+    if (deq) {
+      const double mag = std::ldexp(static_cast<double>(kE2m1[c & 7]), e);
+      deq[i] = static_cast<float>((c & 8) ? -mag : mag);
+    }
+  }
+  return e;
+}
+
+void calibrate_mx_columns(const WeightView& W, int K, int r, const float* s, const int32_t* perm, int n0, int n1,
+                          uint8_t* Wq, uint8_t* Wsc, uint8_t* Rq, uint8_t* Rsc) {
+  const size_t Kb = static_cast<size_t>(K) / 2, Kblk = static_cast<size_t>(K) / 32;
+  const size_t rb = static_cast<size_t>(r) / 2, rblk = static_cast<size_t>(r) / 32;
+  std::vector<float> col(K), deq(K), R(r);
+  std::vector<int> codes(K);
+  for (int n = n0; n < n1; ++n) {
+    for (int i = 0; i < K; ++i) {
+      const int j = perm[i];
+      col[i] = s[j] * W.at(j, n);                              // W^[i, n]
+    }
+    for (int b = 0; b < K / 32; ++b)
+      Wsc[n * Kblk + b] = static_cast<uint8_t>(mx_block(&col[32 * b], 32, &codes[32 * b], &deq[32 * b]) + 127);
+    for (int i = 0; i < K; i += 2) Wq[n * Kb + i / 2] = pack2(codes[i], codes[i + 1]);
+    if (r == 0) continue;
+    for (int i = 0; i < r; ++i) R[i] = col[i] - deq[i];        // R = W~_s - Q(W~_s)
+    for (int b = 0; b < r / 32; ++b)
+      Rsc[n * rblk + b] = static_cast<uint8_t>(mx_block(&R[32 * b], 32, &codes[32 * b], nullptr) + 127);
+    for (int i = 0; i < r; i += 2) Rq[n * rb + i / 2] = pack2(codes[i], codes[i + 1]);
+  }
+}
+
+}  // namespace
+
+extern "C" int serq_calibrate_mx(const void* W, serq_dtype w_dtype, int K, int N, const float* act_absmax,
+                                 float alpha, int r, int32_t* perm, float* s_hat_inv, uint8_t* Wq, uint8_t* Wsc,
+                                 uint8_t* Rq, uint8_t* Rsc) {
+  if (!W || !act_absmax || !perm || !s_hat_inv || !Wq || !Wsc) return SERQ_EINVAL;
+  if (w_dtype != SERQ_F32 && w_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (K <= 0 || N <= 0 || (K % 32) || (r % 32) || r < 0 || r > K) return SERQ_EINVAL;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return SERQ_EINVAL;
+  if (r > 0 && (!Rq || !Rsc)) return SERQ_EINVAL;
+  const WeightView wv{W, w_dtype, N};
+  std::vector<float> s(K), s_inv(K);
+  smoothing_factors(wv, K, N, act_absmax, alpha, s.data(), s_inv.data());
+  std::vector<int32_t> idx(K);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) { return s[x] > s[y]; });
+  for (int i = 0; i < K; ++i) {
+    perm[i] = idx[i];
+    s_hat_inv[i] = s_inv[idx[i]];
+  }
+  const int T = worker_count(N);
+  const int per = (N + T - 1) / T;
+  std::vector<std::thread> pool;
+  for (int t = 1; t < T; ++t) {
+    const int n0 = t * per, n1 = std::min(N, n0 + per);
+    if (n0 >= n1) break;
+    pool.emplace_back(calibrate_mx_columns, std::cref(wv), K, r, s.data(), perm, n0, n1, Wq, Wsc, Rq, Rsc);
+  }
+  calibrate_mx_columns(wv, K, r, s.data(), perm, 0, std::min(N, per), Wq, Wsc, Rq, Rsc);
+  for (auto& th : pool) th.join();
+  return SERQ_OK;
+}

@@ -162,3 +162,49 @@ extern "C" const char* serq_linear_bf6_kernel_name(int M, int N, int r) {
   if (M <= 0 || N <= 0 || r < 0) return nullptr;
   return serq::bf6_tile_kind(M, N, r) == 2 ? "bf6_tile256x256" : "bf6_tile128x128";
 }
+
+extern "C" int serq_quant_act_mx(const void* X, serq_dtype x_dtype, int M, int K, const float* s_hat_inv,
+                                 uint8_t* Xq, uint8_t* Xsc, void* stream) {
+  if (x_dtype != SERQ_F32 && x_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (M < 0 || K <= 0 || (K % 32) != 0) return SERQ_EINVAL;
+  if (!s_hat_inv) return SERQ_EINVAL;
+  if (!aligned16(s_hat_inv)) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;
+  if (!X || !Xq || !Xsc) return SERQ_EINVAL;
+  if (!aligned16(X) || !aligned16(Xq)) return SERQ_EALIGN;
+  hipError_t e = serq::launch_quant_act_mx(X, x_dtype == SERQ_BF16, M, K, s_hat_inv, Xq, Xsc,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
+}
+
+extern "C" int serq_linear_mx(const uint8_t* Xq, const uint8_t* Xsc, const uint8_t* Wq, const uint8_t* Wsc,
+                              const uint8_t* Rq, const uint8_t* Rsc, int M, int K, int N, int r, void* Y,
+                              serq_dtype y_dtype, float* acc_main_dbg, float* acc_res_dbg, void* stream) {
+  if (y_dtype != SERQ_F32 && y_dtype != SERQ_BF16) return SERQ_EINVAL;
+  if (M < 0 || K <= 0 || N <= 0 || (K % 32) || r < 0 || r > K || (r % 32)) return SERQ_EINVAL;
+  if (!Wq || !Wsc) return SERQ_EINVAL;
+  if (r > 0 && (!Rq || !Rsc)) return SERQ_EINVAL;
+  if ((acc_main_dbg == nullptr) != (acc_res_dbg == nullptr)) return SERQ_EINVAL;
+  if (!aligned16(Wq) || (r > 0 && !aligned16(Rq))) return SERQ_EALIGN;
+  if (M == 0) return SERQ_OK;
+  if (!Xq || !Xsc || !Y) return SERQ_EINVAL;
+  if (!aligned16(Xq) || !aligned16(Y)) return SERQ_EALIGN;
+  if (acc_main_dbg && (!aligned16(acc_main_dbg) || !aligned16(acc_res_dbg))) return SERQ_EALIGN;
+  serq::MxArgs a{};
+  a.Xq = Xq;
+  a.Xsc = Xsc;
+  a.Wq = Wq;
+  a.Wsc = Wsc;
+  a.Rq = r > 0 ? Rq : nullptr;
+  a.Rsc = r > 0 ? Rsc : nullptr;
+  a.Y = Y;
+  a.dbg_main = acc_main_dbg;
+  a.dbg_res = acc_res_dbg;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.r = r;
+  a.y_bf16 = y_dtype == SERQ_BF16;
+  hipError_t e = serq::launch_linear_mx(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SERQ_OK : SERQ_EHIP;
+}

@@ -53,4 +53,24 @@ hipError_t launch_act_bf6(const void* Xq, int M, int K, void* X6, hipStream_t st
 hipError_t launch_linear_bf6(const LinearArgs& a, hipStream_t stream);
 int bf6_tile_kind(int M, int N, int r);   // serq_linear_bf6's tile: 0 128x128, 2 256x256
 
+// The MXFP4 layer (serq_quant_act_mx, serq_linear_mx): FP4 E2M1 codes two
+// per byte with one E8M0 exponent byte per 32 elements along K.
+struct MxArgs {
+  const uint8_t* Xq;   // M x K/2
+  const uint8_t* Xsc;  // M x K/32
+  const uint8_t* Wq;   // N x K/2
+  const uint8_t* Wsc;  // N x K/32
+  const uint8_t* Rq;   // N x r/2 (may be null when r == 0)
+  const uint8_t* Rsc;  // N x r/32
+  void* Y;             // M x N, fp32 or bf16
+  float* dbg_main;     // optional M x N fp32 accumulators
+  float* dbg_res;
+  int M, K, N, r;
+  int y_bf16;
+};
+
+hipError_t launch_quant_act_mx(const void* X, int x_bf16, int M, int K, const float* s_hat_inv, uint8_t* Xq,
+                               uint8_t* Xsc, hipStream_t stream);
+hipError_t launch_linear_mx(const MxArgs& a, hipStream_t stream);
+
 }  // namespace serq
