@@ -33,8 +33,9 @@ widths, with the unfused pair for comparison), "mlp_step" (the whole 8B MLP:
 quant_act, gate/up, the fused activation, down; at 4096 tokens also on the
 bf6 route, its output compared bit for bit), "bf6_route" (the same
 linear on the scaled FP6 MFMA with int4 codes re-encoded as E3M2, against
-serq_linear on the same codes, for prefill-sized layers) and "cpu_baseline"
-(the oracle on a bounded row sample).
+serq_linear on the same codes, for prefill-sized layers), "mxfp4" (the
+MXFP4 variant of the layer, serq_quant_act_mx + serq_linear_mx, against the
+FP4 peak or HBM) and "cpu_baseline" (the oracle on a bounded row sample).
 """
 
 from __future__ import annotations
@@ -553,6 +554,68 @@ def time_bf6_route(shapes=BF6_SHAPES, reps=20):
     return out
 
 
+FP4_PEAK_TOPS = 10100.0        # MI355X dense FP4 MFMA (no sparsity)
+MX_SHAPES = (                  # (M, K, N, r): decode and prefill on the five layer shapes
+    (1, 4096, 4096, 64), (16, 4096, 4096, 64), (2048, 4096, 4096, 64), (4096, 4096, 28672, 128),
+    (4096, 14336, 4096, 128), (8192, 8192, 28672, 256), (8192, 28672, 8192, 256))
+
+
+def mx_bytes(M, K, N, r, y_bytes=2):
+    """Algorithmic bytes of serq_linear_mx: FP4 codes (1/2 byte) and E8M0
+    bytes (1/32 byte) per element of X, W and R, plus Y."""
+    return (M * K + K * N + r * N) * 17 // 32 + M * N * y_bytes
+
+
+def time_mx_route(shapes=MX_SHAPES, reps=20):
+    """The MXFP4 layer: serq_quant_act_mx and serq_linear_mx on random FP4
+    codes and exponents (weights rotated over copies beyond the last-level
+    cache), per-kernel times from graph replays, TOPS against the FP4 peak or
+    GB/s against HBM by the layer's arithmetic intensity."""
+    import numpy as np
+    import torch
+    import w4a4_linear_layers_amd as S
+    out = []
+    for (M, K, N, r) in shapes:
+        rng = np.random.default_rng(M + K + N + r)
+        Wq = torch.from_numpy(rng.integers(0, 256, (N, K // 2), dtype=np.uint8)).cuda()
+        Wsc = torch.from_numpy(rng.integers(120, 130, (N, K // 32), dtype=np.uint8)).cuda()
+        Rq = torch.from_numpy(rng.integers(0, 256, (N, r // 2), dtype=np.uint8)).cuda()
+        Rsc = torch.from_numpy(rng.integers(115, 125, (N, r // 32), dtype=np.uint8)).cuda()
+        copies = int(min(8, max(2, ROTATE_BYTES // (Wq.numel() + M * K))))
+        Ls = [S.MxLayer(K=K, N=N, r=r, perm=None, s_hat_inv=None, Wq=Wq.clone() if c else Wq, Wsc=Wsc, Rq=Rq,
+                        Rsc=Rsc) for c in range(copies)]
+        X = [torch.randn((M, K), device="cuda").to(torch.bfloat16) for _ in range(copies)]
+        sinv = torch.ones(K, device="cuda")
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+        xsc = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def timed(fn):
+            g = _graph_of(fn, reps)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        tq = timed(lambda i: S.quant_act_mx(X[i % copies], sinv, out=(xq, xsc)))
+        tl = timed(lambda i: S.linear_mx(xq, xsc, Ls[i % copies], out=y))
+        ops = linear_ops(M, K, N, r)
+        byts = mx_bytes(M, K, N, r)
+        if ops / byts > FP4_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            roof = dict(bound="mfma", achieved=round(ops / tl / 1e6, 1), peak=FP4_PEAK_TOPS, unit="TOP/s",
+                        frac=round(ops / tl / 1e6 / FP4_PEAK_TOPS, 4))
+        else:
+            roof = dict(bound="hbm", achieved=round(byts / tl / 1e3, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(byts / tl / 1e3 / HBM_PEAK_GBS, 4))
+        out.append(dict(M=M, K=K, N=N, r=r, linear_mx_us=round(tl, 2), quant_act_mx_us=round(tq, 2),
+                        TOPS=round(ops / tl / 1e6, 1), roofline=roof))
+        del Ls, X, Wq, Rq
+        torch.cuda.empty_cache()
+    return out
+
+
 def _graph_of(fn, reps):
     import torch
     for i in range(2):
@@ -581,6 +644,9 @@ def main(argv=None):
     ap.add_argument("--no-mlp-act", action="store_true", help="skip the MLP activation timing")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bf6", action="store_true", help="skip the bf6 route timings")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP4 layer timings")
+    ap.add_argument("--mx", default=None, metavar="M:K:N:r[,...]",
+                    help="only time the MXFP4 layer on the given shapes (one JSON line each), then exit")
     ap.add_argument("--bf6", default=None, metavar="M:K:N:r[,...]",
                     help="only time the bf6 route on the given shapes (one JSON line each), then exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -596,6 +662,11 @@ def main(argv=None):
         k_s, m_s = args.mlp_act.split(":")
         for e in time_mlp_act(int(k_s), [int(m) for m in m_s.split(",")], n=max(args.steps, 20)):
             print(json.dumps(dict(kernel="serq_silu_mul_quant_act", **e)), flush=True)
+        return 0
+    if args.mx:
+        shapes = [tuple(int(v) for v in sh.split(":")) for sh in args.mx.split(",")]
+        for e in time_mx_route(shapes, reps=max(args.steps, 5) if args.steps != 200 else 20):
+            print(json.dumps(dict(route="mxfp4", **e)), flush=True)
         return 0
     if args.bf6:
         shapes = [tuple(int(v) for v in sh.split(":")) for sh in args.bf6.split(",")]
@@ -639,6 +710,14 @@ def main(argv=None):
     roof = roofline_entry(M, K, N, r, a_bits, l_us, traffic, y_bytes)
     print(f"# step {ms_per_step * 1e3:.2f} us; quant_act {q_us:.2f} us, serq_linear {l_us:.2f} us "
           f"({S.kernel_name(M, K, N, r, a_bits)})", file=sys.stderr, flush=True)
+
+    mx = []
+    if not args.no_sweep and not args.no_mx:
+        mx = time_mx_route()
+        for e in mx:
+            print(f"# mxfp4 M={e['M']} K={e['K']} N={e['N']}: linear_mx {e['linear_mx_us']:.1f} us ({e['TOPS']:.0f} "
+                  f"TOP/s, {e['roofline']['bound']} frac {e['roofline']['frac']:.3f}); quant_act_mx "
+                  f"{e['quant_act_mx_us']:.1f} us", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -704,6 +783,7 @@ def main(argv=None):
         "mlp_activation": mlp_act,
         "mlp_step": mlp_step,
         "bf6_route": bf6,
+        "mxfp4": mx,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -90,8 +90,10 @@ def _check_y(y, out, mag, K, dt):
 
 @pytest.mark.parametrize("M,K,N,r,uniform", [
     (128, 4096, 128, 64, True), (200, 1024, 300, 32, True),          # one shared scale: exact sums
-    (1, 64, 32, 32, False), (37, 320, 200, 96, False), (130, 1024, 260, 0, False),
+    (4096, 256, 4096, 96, True),                                     # the 256 x 256 pipelined tile
+    (1, 64, 32, 32, False), (37, 320, 200, 96, False), (130, 1024, 260, 0, False),   # K % 128: plain kernel
     (256, 4096, 512, 256, False), (300, 2048, 1000, 2048, False), (64, 96, 130, 64, False),
+    (4100, 384, 4104, 128, False), (3, 128, 8, 32, False),         # ragged 256 tiles; one k-tile
 ])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_linear_mx_vs_oracle(M, K, N, r, uniform, out):
@@ -150,6 +152,29 @@ def test_workload_q_proj_mx(M):
     e_with = np.linalg.norm(ref["y64"] - exact)
     e_without = np.linalg.norm(ref["acc_main"] - exact)
     assert e_with < e_without
+
+
+def test_linear_mx_unaligned_exponents():
+    """Exponent arrays at an odd address take the plain kernel: same results."""
+    rng = np.random.default_rng(5)
+    M, K, N = 64, 512, 96
+    Xc, Xe = _random_mx(rng, M, K, -3, 3)
+    Wc, We = _random_mx(rng, N, K, -3, 3)
+    wsc = torch.zeros(N * K // 32 + 1, dtype=torch.uint8, device="cuda")
+    wsc[1:] = dev((We + 127).astype(np.uint8).ravel())
+    xsc = torch.zeros(M * K // 32 + 1, dtype=torch.uint8, device="cuda")
+    xsc[1:] = dev((Xe + 127).astype(np.uint8).ravel())
+    L = S.MxLayer(K=K, N=N, r=0, perm=None, s_hat_inv=None, Wq=dev(O.pack_fp4(Wc)), Wsc=wsc[1:].view(N, K // 32),
+                  Rq=None, Rsc=None)
+    xq = dev(O.pack_fp4(Xc))
+    y = S.linear_mx(xq, xsc[1:].view(M, K // 32), L, out_dtype=torch.float32)
+    L2 = S.MxLayer(K=K, N=N, r=0, perm=None, s_hat_inv=None, Wq=L.Wq, Wsc=dev((We + 127).astype(np.uint8)),
+                   Rq=None, Rsc=None)
+    y2 = S.linear_mx(xq, dev((Xe + 127).astype(np.uint8)), L2, out_dtype=torch.float32)
+    _sync()
+    ref = O.linear_mx(dict(codes=Xc, e=Xe), dict(N=N, r=0, Wq_codes=Wc, We=We))
+    _check_y(host(y), ref, ref["mag"], K, "f32")
+    _check_y(host(y2), ref, ref["mag"], K, "f32")
 
 
 def test_linear_mx_empty_and_side_stream():

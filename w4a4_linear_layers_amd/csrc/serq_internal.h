@@ -72,5 +72,6 @@ struct MxArgs {
 hipError_t launch_quant_act_mx(const void* X, int x_bf16, int M, int K, const float* s_hat_inv, uint8_t* Xq,
                                uint8_t* Xsc, hipStream_t stream);
 hipError_t launch_linear_mx(const MxArgs& a, hipStream_t stream);
+int mx_kernel_kind(int M, int K, int N);   // 0 plain, 1 pipelined 128 x 128, 2 pipelined 256 x 256
 
 }  // namespace serq

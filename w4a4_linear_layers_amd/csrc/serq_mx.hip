@@ -31,6 +31,7 @@
 namespace serq {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -123,6 +124,12 @@ constexpr int kMxTile = 128;
 constexpr int kMxThreads = 256;
 
 __device__ __forceinline__ int mx_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ v16f mfma_mx(v4i a, v4i b, int sa, int sb, v16f c) {
+  const v8i av = v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  const v8i bv = v8i{b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
 
 __device__ __forceinline__ v16f mfma_mx(uint4 a, uint4 b, int sa, int sb, v16f c) {
   const v8i av = v8i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w), 0, 0, 0, 0};
@@ -302,7 +309,287 @@ __global__ __launch_bounds__(kMxThreads, 2) void serq_mx_tile_kernel(MxArgs a, i
     }
 }
 
+// ------------------------------------------------------------ pipelined GEMM
+
+// The same product with a deeper pipeline, for K a multiple of 128: k-tiles
+// of 128 elements (64 bytes of codes and 4 exponent bytes per row) stream
+// through STAGES LDS buffers by direct global->LDS loads, as in the integer
+// and bf6 tile kernels: every wave issues the same loads per k-tile (1 KB
+// chunks of 16 rows x 64 bytes, one 256-byte chunk of 64 rows' exponent
+// dwords), waits with s_waitcnt vmcnt, and one LDS-only barrier per k-tile
+// publishes k-tile t + 1 and frees buffer t, which the loads of k-tile
+// t + STAGES go into. Past the last k-tile the loads repeat it into a buffer
+// that is never read again, so the wait counts are branch-free. A wave holds
+// TN x TM blocks of 32 x 32. Fragment k: in MFMA step s lane half h takes
+// elements [64 s + 32 h, +32) of its row (16 bytes; 16-byte row parts sit at
+// slot part ^ swz(row), conflict-free) and the exponent byte 2 s + h of the
+// row's dword, shifted down to the low byte the instruction reads. The
+// residual (r/64 MFMA steps at most 4) runs in the epilogue from fragments
+// read straight from memory, one weight block row at a time, and the output
+// is y = acc_main + acc_res.
+
+constexpr int kMxKt = 128;                    // elements per k-tile
+
+// M0 is written in the asm and declared clobbered; the compiler sets it
+// itself before every instruction of its own that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void mx_dma16(const void* sbase, uint32_t voff, uint32_t lds_chunk) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "s"(lds_chunk)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void mx_dma4(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" :: "v"(voff), "s"(sbase), "s"(lds_dst)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void mx_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0) only
+  asm volatile("s_barrier" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void mx_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// 16-byte part slot of a 64-byte row (bits 1-3 of the row): the 16-byte
+// reads of 16 consecutive rows at one part hit distinct bank groups.
+__device__ __forceinline__ int mx_swz64(int row) {
+  return (((row >> 1) ^ (row >> 2)) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 1);
+}
+
+template <int TN, int TM, int WNW, int WMW, int STAGES, int OCC>
+struct MxCfg {
+  static constexpr int NW = WNW * WMW, NT = 64 * NW;
+  static constexpr int BN = 32 * TN * WNW, BM = 32 * TM * WMW;
+  static constexpr int W_BYTES = BN * 64, X_BYTES = BM * 64;
+  static constexpr int WS_OFF = W_BYTES + X_BYTES, XS_OFF = WS_OFF + BN * 4;
+  static constexpr int STAGE = XS_OFF + BM * 4;
+  static constexpr int CW = W_BYTES / 1024 / NW, CX = X_BYTES / 1024 / NW;   // 1 KB chunks per wave
+  static constexpr int LOADS = CW + CX + 1;                                  // + one exponent chunk
+  static constexpr int LDS = STAGES * STAGE;
+  static_assert(CW * NW * 1024 == W_BYTES && CX * NW * 1024 == X_BYTES, "operand chunks split over the waves");
+  static_assert((BN + BM) / 64 == NW, "one exponent chunk per wave");
+  static_assert(OCC * LDS <= 160 * 1024 && (STAGES - 1) * LOADS < 64, "LDS, vmcnt range");
+};
+
+template <int TN, int TM, int WNW, int WMW, int STAGES, int OCC>
+__global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArgs a, int n_tiles) {
+  using C = MxCfg<TN, TM, WNW, WMW, STAGES, OCC>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int wn = wv / WMW, wm = wv % WMW;
+  const int l32 = lane & 31, h = lane >> 5;
+  int tile_n, tile_m;
+  mx_tile_coords(blockIdx.x, gridDim.x, n_tiles, tile_n, tile_m);
+  const int n0 = __builtin_amdgcn_readfirstlane(tile_n * C::BN);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile_m * C::BM);
+  const int nk = a.K / kMxKt;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const uint8_t* const Wq = a.Wq;
+  const uint8_t* const Xq = a.Xq;
+  const uint8_t* const Wsc = a.Wsc;
+  const uint8_t* const Xsc = a.Xsc;
+  const uint32_t rowb = static_cast<uint32_t>(a.K / 2), scb = static_cast<uint32_t>(a.K / 32);
+
+  // Per-lane source offsets of this wave's chunks at k-tile 0 (rows past
+  // the matrix read its last row; those outputs are never stored).
+  const int part = (lane & 3) ^ mx_swz64(lane >> 2);
+  uint32_t woff[C::CW], xoff[C::CX];
+#pragma unroll
+  for (int c = 0; c < C::CW; ++c) {
+    const int row = (wv * C::CW + c) * 16 + (lane >> 2);
+    woff[c] = static_cast<uint32_t>(min(n0 + row, a.N - 1)) * rowb + part * 16;
+  }
+#pragma unroll
+  for (int c = 0; c < C::CX; ++c) {
+    const int row = (wv * C::CX + c) * 16 + (lane >> 2);
+    xoff[c] = static_cast<uint32_t>(min(m0 + row, a.M - 1)) * rowb + part * 16;
+  }
+  // exponent chunk: waves [0, BN/64) take weight rows, the rest token rows
+  const bool ws_side = wv < C::BN / 64;
+  const uint8_t* const sc_src = ws_side ? Wsc : Xsc;
+  const int sc_row = ws_side ? n0 + wv * 64 + lane : m0 + (wv - C::BN / 64) * 64 + lane;
+  const uint32_t scoff = static_cast<uint32_t>(min(sc_row, (ws_side ? a.N : a.M) - 1)) * scb;
+  const uint32_t sc_dst = ws_side ? C::WS_OFF + wv * 256 : C::XS_OFF + (wv - C::BN / 64) * 256;
+
+  auto issue = [&](int t) {
+    const int kt = min(t, nk - 1);
+    const uint32_t dst = lds_base + (t % STAGES) * C::STAGE;
+#pragma unroll
+    for (int c = 0; c < C::CW; ++c) mx_dma16(Wq + kt * 64, woff[c], dst + (wv * C::CW + c) * 1024);
+#pragma unroll
+    for (int c = 0; c < C::CX; ++c) mx_dma16(Xq + kt * 64, xoff[c], dst + C::W_BYTES + (wv * C::CX + c) * 1024);
+    mx_dma4(sc_src + kt * 4, scoff, dst + sc_dst);
+  };
+  struct Frags {
+    v4i w[TN], x[TM];
+    int ws[TN], xs[TM];
+  };
+  auto read = [&](int buf, int s, Frags& f) {
+    const uint8_t* sb = lds + buf * C::STAGE;
+    const int p = 2 * s + h;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int row = wn * 32 * TN + 32 * i + l32;
+      f.w[i] = *reinterpret_cast<const v4i*>(sb + row * 64 + ((p ^ mx_swz64(row)) * 16));
+      f.ws[i] = static_cast<int>(*reinterpret_cast<const uint32_t*>(sb + C::WS_OFF + row * 4) >> (8 * p));
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int row = wm * 32 * TM + 32 * j + l32;
+      f.x[j] = *reinterpret_cast<const v4i*>(sb + C::W_BYTES + row * 64 + ((p ^ mx_swz64(row)) * 16));
+      f.xs[j] = static_cast<int>(*reinterpret_cast<const uint32_t*>(sb + C::XS_OFF + row * 4) >> (8 * p));
+    }
+  };
+  v16f acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v16f{};
+  auto mm = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] = mfma_mx(f.w[i], f.x[j], f.ws[i], f.xs[j], acc[i][j]);
+  };
+  // The MFMAs are pure values the compiler could move past the barrier:
+  // empty asm statements on the accumulators and the next fragments keep
+  // them in program order, so the matrix core has work while the wave waits.
+  auto pin = [&]() {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) asm volatile("" : "+v"(acc[i][j]));
+  };
+  auto pin_frags = [&](Frags& f) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) asm volatile("" : "+v"(f.w[i]), "+v"(f.ws[i]));
+#pragma unroll
+    for (int j = 0; j < TM; ++j) asm volatile("" : "+v"(f.x[j]), "+v"(f.xs[j]));
+  };
+
+#pragma unroll
+  for (int p = 0; p < STAGES; ++p) issue(p);
+  mx_wait_vmcnt<(STAGES - 1) * C::LOADS>();
+  mx_lds_barrier();
+  Frags f0, f1;
+  read(0, 0, f0);
+  for (int t = 0; t < nk - 1; ++t) {
+    read(t % STAGES, 1, f1);
+    mm(f0);
+    pin();
+    mx_wait_vmcnt<(STAGES - 2) * C::LOADS>();
+    mx_lds_barrier();
+    issue(t + STAGES);
+    pin_frags(f1);
+    read((t + 1) % STAGES, 0, f0);
+    mm(f1);
+  }
+  read((nk - 1) % STAGES, 1, f1);
+  mm(f0);
+  mm(f1);
+  mx_wait_vmcnt<0>();                            // the repeated loads past the end, unused
+
+  // Epilogue, one weight block row at a time: its residual MFMAs (fragments
+  // read from memory; elements past r contribute zero), then
+  // y = acc_main + acc_res stored four channels per lane and group.
+  const int nw = n0 + wn * 32 * TN, mw = m0 + wm * 32 * TM;
+  const int rsteps = (a.r + 63) / 64;
+  const uint32_t rrow = static_cast<uint32_t>(a.r / 2), rsc = static_cast<uint32_t>(a.r / 32);
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    v16f res[TM];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) res[j] = v16f{};
+    const int nr = min(nw + 32 * i + l32, a.N - 1);
+    for (int s = 0; s < rsteps; ++s) {
+      const int k0 = 64 * s + 32 * h;
+      const bool in = k0 < a.r;
+      const uint4 wf = in ? *reinterpret_cast<const uint4*>(a.Rq + nr * rrow + k0 / 2) : make_uint4(0, 0, 0, 0);
+      const int wsv = in ? a.Rsc[nr * rsc + k0 / 32] : 127;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int mr = min(mw + 32 * j + l32, a.M - 1);
+        const uint4 xf = in ? *reinterpret_cast<const uint4*>(Xq + mr * rowb + k0 / 2) : make_uint4(0, 0, 0, 0);
+        const int xsv = in ? Xsc[mr * scb + k0 / 32] : 127;
+        res[j] = mfma_mx(wf, xf, wsv, xsv, res[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = mw + 32 * j + l32;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nw + 32 * i + 8 * q + 4 * h;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q + e] + res[j][4 * q + e];
+        const size_t base = static_cast<size_t>(m) * a.N + n;
+        if (n + 3 < a.N && (a.N & 3) == 0) {
+          if (a.y_bf16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.Y) + base) =
+                make_uint2(mx_pack_bf16x2(y[0], y[1]), mx_pack_bf16x2(y[2], y[3]));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(a.Y) + base) = make_float4(y[0], y[1], y[2], y[3]);
+          if (a.dbg_main) {
+            *reinterpret_cast<float4*>(a.dbg_main + base) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<float4*>(a.dbg_res + base) =
+                make_float4(res[j][4 * q], res[j][4 * q + 1], res[j][4 * q + 2], res[j][4 * q + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e >= a.N) break;
+            if (a.y_bf16)
+              static_cast<uint16_t*>(a.Y)[base + e] = static_cast<uint16_t>(mx_pack_bf16x2(y[e], 0.0f));
+            else
+              static_cast<float*>(a.Y)[base + e] = y[e];
+            if (a.dbg_main) {
+              a.dbg_main[base + e] = acc[i][j][4 * q + e];
+              a.dbg_res[base + e] = res[j][4 * q + e];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int TN, int TM, int WNW, int WMW, int STAGES, int OCC>
+hipError_t launch_mx_pipe(const MxArgs& a, hipStream_t st) {
+  using C = MxCfg<TN, TM, WNW, WMW, STAGES, OCC>;
+  auto* fn = &serq_mx_pipe_kernel<TN, TM, WNW, WMW, STAGES, OCC>;
+  static bool attr_set = false;              // idempotent: setting it again is harmless
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int n_tiles = (a.N + C::BN - 1) / C::BN;
+  const int m_tiles = (a.M + C::BM - 1) / C::BM;
+  if (static_cast<long long>(n_tiles) * m_tiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  fn<<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS, st>>>(a, n_tiles);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Which MXFP4 kernel serq_linear_mx launches: 0 the plain double-buffered
+// one (K not a multiple of 128, or 32-bit row offsets not enough), 1 the
+// pipelined 128 x 128 tile, 2 the pipelined 256 x 256 tile (when it still
+// gives every CU a tile).
+int mx_kernel_kind(int M, int K, int N) {
+  if (K % kMxKt != 0 || static_cast<uint64_t>(N) * (K / 2) >= (1ull << 32) ||
+      static_cast<uint64_t>(M) * (K / 2) >= (1ull << 32))
+    return 0;
+  const long long t256 = static_cast<long long>((M + 255) / 256) * ((N + 255) / 256);
+  return t256 >= 256 ? 2 : 1;
+}
 
 hipError_t launch_quant_act_mx(const void* X, int x_bf16, int M, int K, const float* s_hat_inv, uint8_t* Xq,
                                uint8_t* Xsc, hipStream_t st) {
@@ -319,6 +606,11 @@ hipError_t launch_quant_act_mx(const void* X, int x_bf16, int M, int K, const fl
 }
 
 hipError_t launch_linear_mx(const MxArgs& a, hipStream_t st) {
+  // the pipelined kernels load exponent dwords, so those arrays must be 4-byte aligned
+  const bool sc_aligned = ((reinterpret_cast<uintptr_t>(a.Wsc) | reinterpret_cast<uintptr_t>(a.Xsc)) & 3u) == 0;
+  const int kind = sc_aligned ? mx_kernel_kind(a.M, a.K, a.N) : 0;
+  if (kind == 2) return launch_mx_pipe<4, 2, 2, 4, 4, 1>(a, st);
+  if (kind == 1) return launch_mx_pipe<2, 2, 2, 2, 4, 2>(a, st);
   const int n_tiles = (a.N + kMxTile - 1) / kMxTile;
   const int m_tiles = (a.M + kMxTile - 1) / kMxTile;
   if (static_cast<long long>(n_tiles) * m_tiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
