@@ -478,8 +478,15 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(5, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(16, 4096, 4096, 64) == "decode16"
     assert S.kernel_name(32, 4096, 14336, 128) == "decode32"
-    assert S.kernel_name(4096, 4096, 14336, 128) == "tile128x128"
-    assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x128"
+    # 256 x 256 tiles where their rounds (256 tiles each) take less time than
+    # the rounds of 128 x 128 tiles (512 each, half the work)
+    assert S.kernel_name(4096, 4096, 28672, 128) == "tile256x256"      # 7 rounds against 14
+    assert S.kernel_name(4096, 4096, 28672, 128, 8) == "tile128x128"   # W4A8: 128 x 128 tiles
+    assert S.kernel_name(4096, 14336, 4096, 128) == "tile256x256"      # 1 round against 2
+    assert S.kernel_name(4096, 4096, 14336, 128) == "tile128x128"      # 3.5 rounds (4) against 7
+    assert S.kernel_name(2048, 4096, 28672, 128) == "tile128x128"      # 3.5 rounds (4) against 7
+    assert S.kernel_name(300, 4096, 32768, 64) == "tile256x256"        # 1 round against 1.5 (2)
+    assert S.kernel_name(2048, 4096, 4096, 64) == "tile128x128"        # 1 round against 1
     assert S.kernel_name(65, 4096, 4096, 64) == "tile32x64k4"          # 128 tiles of 64 x 64: half the CUs
     assert S.kernel_name(128, 14336, 4096, 128) == "tile32x64k4"
     assert S.kernel_name(129, 14336, 4096, 64) == "tile64x64k4"      # 192 tiles of 64 x 64, long K

@@ -264,8 +264,15 @@ LINEAR_CASES = [
     (100, 288, 24600, 128, "tile128x128k2"),  # two k-groups of 128 x 128, a ragged stage
     (130, 4160, 12400, 256, "tile128x128k2"), # an odd number of k-tiles, two residual k-tiles
     (200, 256, 32768, 64, "tile128x128"),     # many workgroups
-    (300, 288, 32768, 128, "tile128x128"),    # K not a multiple of the k-tile, ragged M
-    (520, 1056, 16400, 72, "tile128x128"),    # ragged M and N, r % 32 != 0
+    (300, 288, 32768, 128, "tile256x256"),    # K not a multiple of the k-tile, ragged M
+    (520, 1056, 16400, 72, "tile256x256"),    # ragged M and N, r % 32 != 0
+    (2048, 1056, 28672, 72, "tile128x128"),   # seven full rounds of 128 x 128 tiles
+    # W4A4 256 x 256 tiles (W4A8 takes 128 x 128 tiles on these)
+    (512, 384, 32768, 64, "tile256x256"),     # 256 tiles, fewer k-tiles than stages
+    (500, 992, 32700, 72, "tile256x256"),     # ragged M, N and K
+    (500, 992, 32702, 72, "tile256x256"),     # N % 4 != 0: element stores
+    (480, 4160, 65536, 256, "tile256x256"),   # two residual k-tiles, ragged M
+    (1024, 256, 16384, 0, "tile256x256"),     # r = 0
     (7, 100, 30, 6, "generic"),           # K % 32 != 0, r % 8 != 0
     (3, 384, 10, 320, "generic"),         # r > 256
 ]
@@ -277,6 +284,8 @@ LINEAR_CASES = [
 def test_linear_codes_bit_exact(M, K, N, r, kern, bits, out):
     if kern == "gemv" and bits == 8:
         kern = "decode16"                 # the int4 dot-product kernel is W4A4 only
+    if kern == "tile256x256" and bits == 8:
+        kern = "tile128x128"
     assert S.kernel_name(M, K, N, r, bits).removesuffix("_ksplit") == kern
     _run_codes(M, K, N, r, bits, out, seed=M + K + N + r + bits, col_sample=512 if N > 2048 else None)
 

@@ -47,6 +47,10 @@ constexpr int kKTileW = kKTileCodes / 2;    // packed weight bytes per row per k
 constexpr int kMaxResidual = 256;           // largest r handled by the tile kernels
 constexpr int kWidenMaxK = 1 << 17;         // K bound of the kernels that sum widened codes
 
+// Lambdas that touch a kernel's register arrays must be inlined: a call
+// would pass the arrays by address and put them in scratch memory.
+#define SERQ_INLINE __attribute__((always_inline))
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [0, N). Keeps
 // register-array indices static where #pragma unroll may give up.
 template <int N, typename F, int... I>
@@ -865,6 +869,439 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
 }
 
 // ---------------------------------------------------------------------------
+// 256 x 256 tile kernel (W4A4 prefill on layers with a tile for every CU):
+// one four-wave workgroup per CU, so each wave is its SIMD's only wave and
+// has the SIMD's whole register file: its 4 x 4 blocks of 32 x 32 (128
+// channels x 128 tokens) keep their 256 int32 sums in the accumulation
+// registers and the fragments and widened operands in the vector registers.
+//
+// With 2 x 2 blocks per wave, each MFMA step widens four operands for four
+// MFMAs (six VALU per MFMA), and the two waves of a SIMD together issue
+// nearly as many VALU cycles as the matrix core runs, so the widening sets
+// the pace. With 4 x 4 blocks a step widens eight operands for sixteen
+// MFMAs (three per MFMA), issued by the wave between its own MFMAs. The
+// tile also halves the L2 -> LDS bytes per output.
+//
+// The k pipeline is the macro-tile kernel's: 128-code k-tiles through four
+// 32 KB LDS stages by direct global->LDS loads (eight 1 KB chunks per wave
+// and k-tile), vmcnt-counted waits, one barrier per k-tile, and the residual
+// k-tiles last in the same stream. The residual has no accumulators of its
+// own (they would need 256 more registers): the epilogue runs, per channel
+// block, the residual MFMAs of its four token blocks from the residual
+// k-tiles still in LDS, combines them with the main sums and stores the
+// block's outputs from registers.
+// ---------------------------------------------------------------------------
+
+struct Tile256Cfg {
+  static constexpr int TN = 4, TM = 4;                   // 32 x 32 blocks per wave
+  static constexpr int NW = 4, NT = 64 * NW;
+  static constexpr int BN = 256, BM = 256;
+  static constexpr int XB = kKTileCodes / 2;             // int4 activation bytes per row and k-tile
+  static constexpr int W_BYTES = BN * kKTileW;
+  static constexpr int STAGE = W_BYTES + BM * XB;        // 32 KB
+  static constexpr int CW = W_BYTES / 1024 / NW;         // weight chunks per wave and k-tile
+  static constexpr int CX = BM * XB / 1024 / NW;         // activation chunks per wave and k-tile
+  static constexpr int CPW = CW + CX;
+  static constexpr int STAGES = 4;
+  static constexpr int SCALE_OFF = STAGES * STAGE;
+  static constexpr int SCALE_BYTES = 4 * (2 * BN + BM);
+  static constexpr int LDS_BYTES = SCALE_OFF + SCALE_BYTES;
+  static constexpr int SHIFT = 8;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(CPW * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(STAGES >= (kMaxResidual / 2 + kKTileW - 1) / kKTileW + 1, "residual k-tiles need free stages");
+};
+
+// Store target of the lanes of a partial tile whose outputs fall outside Y
+// (written, never read): 16 bytes per lane.
+__device__ __align__(16) uint8_t tile_store_sink[64 * 16];
+
+__global__ __launch_bounds__(256, 1) void serq_tile256_kernel(LinearArgs a, int n_tiles) {
+  using C = Tile256Cfg;
+  constexpr int STAGES = C::STAGES, CPW = C::CPW, TN = C::TN, TM = C::TM;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave >> 1, wm = wave & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  int tile_n, tile_m;
+  tile_coords(blockIdx.x, gridDim.x, n_tiles, tile_n, tile_m);
+  const int n0 = __builtin_amdgcn_readfirstlane(tile_n * C::BN);
+  const int m0 = __builtin_amdgcn_readfirstlane(tile_m * C::BM);
+  const int Kb = a.K / 2;                      // packed bytes per weight and activation row
+  const int Rb = rq_row_bytes(a.r);
+  const int nkt = (Kb + kKTileW - 1) / kKTileW;
+  const int ntot = nkt + (Rb + kKTileW - 1) / kKTileW;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint8_t* const Wq = a.Wq;
+  const uint8_t* const Rq = a.Rq;
+  const uint8_t* const Xq = a.Xq;
+
+  // Epilogue scales first (older than every k-tile load, so the first
+  // k-tile wait covers them): wave 0 sw, wave 1 sr, wave 2 sx.
+  {
+    const uint32_t sbase = lds_base + C::SCALE_OFF;
+    if (wv == 0) {
+#pragma unroll
+      for (int c = 0; c < C::BN / 64; ++c)
+        if (n0 + 64 * c + lane < a.N) dma4(a.sw + n0 + 64 * c, 4 * lane, sbase + 256 * c);
+    } else if (wv == 1) {
+      if (a.r > 0) {
+#pragma unroll
+        for (int c = 0; c < C::BN / 64; ++c)
+          if (n0 + 64 * c + lane < a.N) dma4(a.sr + n0 + 64 * c, 4 * lane, sbase + 4 * C::BN + 256 * c);
+      } else {                                  // no residual: sr = 0
+#pragma unroll
+        for (int c = 0; c < C::BN / 64; ++c)
+          reinterpret_cast<float*>(lds + C::SCALE_OFF + 4 * C::BN)[64 * c + lane] = 0.0f;
+      }
+    } else if (wv == 2) {
+#pragma unroll
+      for (int c = 0; c < C::BM / 64; ++c)
+        if (m0 + 64 * c + lane < a.M) dma4(a.sx + m0 + 64 * c, 4 * lane, sbase + 8 * C::BN + 256 * c);
+    }
+  }
+
+  // Wave w loads weight chunks [w CW, (w + 1) CW) and activation chunks
+  // [w CX, (w + 1) CX) of every k-tile: 16 rows x 64 bytes each, the lane's
+  // 16-byte part at its swizzled slot (rows past the end clamped to the last).
+  const int part64 = (lane & 3) ^ swz64(lane >> 2);
+  uint32_t woff[C::CW], roff[C::CW], xoff[C::CX];
+#pragma unroll
+  for (int i = 0; i < C::CW; ++i) {
+    const int row = min(n0 + (wv * C::CW + i) * 16 + (lane >> 2), a.N - 1);
+    woff[i] = static_cast<uint32_t>(row) * Kb + part64 * 16;
+    roff[i] = static_cast<uint32_t>(row) * Rb + part64 * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::CX; ++i) {
+    const int row = min(m0 + (wv * C::CX + i) * 16 + (lane >> 2), a.M - 1);
+    xoff[i] = static_cast<uint32_t>(row) * Kb + part64 * 16;
+  }
+  auto wdst = [&](int i) { return static_cast<uint32_t>((wv * C::CW + i) * 1024); };
+  auto xdst = [&](int i) { return static_cast<uint32_t>(C::W_BYTES + (wv * C::CX + i) * 1024); };
+  // k-tile kt (main ones, then residual ones) into stage `stage`; a k-tile
+  // running past the end of its rows zero-fills its missing 16-byte slots
+  // with LDS stores (every load instruction keeps a loading lane: part 0 of
+  // a row is always in range).
+  auto issue = [&](int kt, int stage) SERQ_INLINE {
+    const uint32_t sbase = lds_base + stage * C::STAGE;
+    const bool res = kt >= nkt;
+    const int kx = res ? kt - nkt : kt;
+    const uint8_t* wsrc = (res ? Rq : Wq) + kx * kKTileW;
+    const uint8_t* xsrc = Xq + kx * C::XB;
+    const int wleft = (res ? Rb : Kb) - kx * kKTileW;
+    const int xleft = Kb - kx * C::XB;
+    if (!res && wleft >= kKTileW) {
+#pragma unroll
+      for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + wdst(i));
+#pragma unroll
+      for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + xdst(i));
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < C::CW; ++i) {
+      if (wleft >= kKTileW || part64 * 16 < wleft)
+        dma16(wsrc, res ? roff[i] : woff[i], sbase + wdst(i));
+      else
+        *reinterpret_cast<uint4*>(lds + stage * C::STAGE + wdst(i) + lane * 16) = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::CX; ++i) {
+      if (xleft >= C::XB || part64 * 16 < xleft)
+        dma16(xsrc, xoff[i], sbase + xdst(i));
+      else
+        *reinterpret_cast<uint4*>(lds + stage * C::STAGE + xdst(i) + lane * 16) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  v16i acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v16i{};
+
+  int wrd[2], xrd[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    wrd[p] = (wn * 32 * TN + l32) * kKTileW + (((2 * h + p) ^ swz64(l32)) * 16);
+    xrd[p] = C::W_BYTES + (wm * 32 * TM + l32) * C::XB + (((2 * h + p) ^ swz64(l32)) * 16);
+  }
+  struct Frags {
+    uint4 w[2][TN];
+    uint4 x[2][TM];
+  };
+  // Part p (16 bytes per row and lane) of every block's fragments of the
+  // k-tile in `stage`.
+  auto read_part = [&](int stage, int p, Frags& f) SERQ_INLINE {
+    const uint8_t* sb = lds + stage * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) f.w[p][i] = *reinterpret_cast<const uint4*>(sb + wrd[p] + i * 32 * kKTileW);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) f.x[p][j] = *reinterpret_cast<const uint4*>(sb + xrd[p] + j * 32 * C::XB);
+  };
+  // MFMA step s takes dwords (2 (s & 1), 2 (s & 1) + 1) of part s >> 1.
+  auto op = [&](const uint4& v0, const uint4& v1, int s) SERQ_INLINE {
+    const uint4 v = (s >> 1) ? v1 : v0;
+    return (s & 1) ? widen16(v.z, v.w) : widen16(v.x, v.y);
+  };
+  auto unpack = [&](const Frags& f, int s, v4i (&wa)[TN], v4i (&xb)[TM]) SERQ_INLINE {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) wa[i] = op(f.w[0][i], f.w[1][i], s);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) xb[j] = op(f.x[0][j], f.x[1][j], s);
+  };
+  // The four MFMA steps of the k-tile whose step-0 operands are in wa, xb
+  // and whose fragments are in `f`; step s + 1's widening is issued between
+  // step s's MFMAs. One fragment buffer: once steps 0 and 1 are widened,
+  // part 0 of the next k-tile (stage `next`) is read into its place, and
+  // part 1 once steps 2 and 3 are; step 3's MFMAs cover the widening of the
+  // next k-tile's step 0, so the matrix core has operands right after the
+  // next barrier.
+  v4i wa[TN], xb[TM];
+  auto compute = [&](Frags& f, int next, bool read_next) SERQ_INLINE {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4i wn2[TN], xn2[TM];
+      const bool widen = s < 3 || read_next;
+      if (widen) unpack(f, (s + 1) & 3, wn2, xn2);
+      if (s == 0 || s == 2)
+        if (read_next) read_part(next, s >> 1, f);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32(wa[i], xb[j], acc[i][j]);
+      if (widen) {
+        constexpr int kValuPerMfma = (6 * (TN + TM) + TN * TM - 1) / (TN * TM);
+#pragma unroll
+        for (int q = 0; q < TN * TM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+          if (q == 0 && (s == 0 || s == 2)) __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < TN; ++i) wa[i] = wn2[i];
+#pragma unroll
+        for (int j = 0; j < TM; ++j) xb[j] = xn2[j];
+      }
+      // nothing moves across steps: hoisting later steps' widening would
+      // need more registers than the wave has
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto wait_tiles = [&](int n) SERQ_INLINE {
+    if (n >= STAGES - 2) {
+      wait_vmcnt<CPW * (STAGES - 2)>();
+      return;
+    }
+    static_for<STAGES>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if (n == k) wait_vmcnt<CPW * k>();
+    });
+  };
+  // One k-tile, as in the macro-tile kernel: publish kt + 1 (own loads
+  // done, then a barrier), refill kt's buffer (its fragments are in
+  // registers) with kt + STAGES, then run kt's MFMAs while kt + 1's
+  // fragments are read.
+  auto step = [&](int kt, int st, Frags& f) SERQ_INLINE {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      wait_tiles(min(STAGES - 2, ntot - 2 - kt));
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + STAGES < ntot) issue(kt + STAGES, st);
+    }
+    compute(f, (st + 1) % STAGES, more);
+  };
+  auto fast_step = [&](int kt, int st, Frags& f) SERQ_INLINE {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wait_vmcnt<CPW * (STAGES - 2)>();
+    asm volatile("s_barrier" ::: "memory");
+    const uint32_t sbase = lds_base + st * C::STAGE;
+    const uint8_t* wsrc = Wq + (kt + STAGES) * kKTileW;
+    const uint8_t* xsrc = Xq + (kt + STAGES) * C::XB;
+#pragma unroll
+    for (int i = 0; i < C::CW; ++i) dma16(wsrc, woff[i], sbase + wdst(i));
+#pragma unroll
+    for (int i = 0; i < C::CX; ++i) dma16(xsrc, xoff[i], sbase + xdst(i));
+    compute(f, (st + 1) % STAGES, true);
+  };
+
+#pragma unroll
+  for (int st = 0; st < STAGES; ++st)
+    if (st < ntot) issue(st, st);
+  wait_tiles(min(STAGES, ntot) - 1);
+  lds_barrier();
+  Frags f;
+  read_part(0, 0, f);
+  read_part(0, 1, f);
+  unpack(f, 0, wa, xb);
+  const int nfull = Kb / kKTileW;              // main k-tiles with no ragged end
+  int kt0 = 0;
+  for (; kt0 + STAGES <= nfull - STAGES; kt0 += STAGES)
+    static_for<STAGES>([&](auto ic) { fast_step(kt0 + decltype(ic)::value, decltype(ic)::value, f); });
+  for (; kt0 < nkt; kt0 += STAGES) {
+    static_for<STAGES>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (kt0 + i < nkt) step(kt0 + i, i, f);
+    });
+  }
+
+  // ---- Epilogue: the residual k-tiles (issued during the last main
+  // iterations) and zero-fills published, then channel block by channel
+  // block: t = sw acc_main in fp32, the block's accumulators reused for its
+  // residual MFMAs, y = sx (sr acc_res + t), stores.
+  wait_vmcnt<0>();
+  lds_barrier();
+  const float* s_sw = reinterpret_cast<const float*>(lds + C::SCALE_OFF);
+  const float* s_sr = s_sw + C::BN;
+  const float* s_sx = s_sr + C::BN;
+  const int nres = ntot - nkt;
+  // The sums are 2^SHIFT times the code dot products; the factor comes out
+  // of the token scale (a power of two commutes with fp32 rounding).
+  float sxm[TM];
+  int mrow[TM];
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    mrow[j] = m0 + wm * 32 * TM + j * 32 + l32;
+    sxm[j] = s_sx[wm * 32 * TM + j * 32 + l32] * (1.0f / (1 << C::SHIFT));
+  }
+  // Channel block i: t = sw acc_main (fp32), then the block's accumulators
+  // are reused for its residual sums (four independent MFMA chains, one per
+  // token block).
+  auto residual = [&](auto ic, float (&t)[TM][16], const float4 (&w4)[4]) SERQ_INLINE {
+    constexpr int i = decltype(ic)::value;
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float wv4[4] = {w4[q].x, w4[q].y, w4[q].z, w4[q].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) t[j][4 * q + c] = wv4[c] * static_cast<float>(acc[i][j][4 * q + c]);
+      }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v16i{};
+    for (int u = 0; u < nres; ++u) {
+      const uint8_t* sb = lds + ((nkt + u) % STAGES) * C::STAGE;
+      const uint4 w0 = *reinterpret_cast<const uint4*>(sb + wrd[0] + i * 32 * kKTileW);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(sb + wrd[1] + i * 32 * kKTileW);
+      uint4 x0[TM], x1[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        x0[j] = *reinterpret_cast<const uint4*>(sb + xrd[0] + j * 32 * C::XB);
+        x1[j] = *reinterpret_cast<const uint4*>(sb + xrd[1] + j * 32 * C::XB);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v4i wa = op(w0, w1, s);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = mfma32(wa, op(x0[j], x1[j], s), acc[i][j]);
+      }
+    }
+  };
+  auto load_scales = [&](int nt, float4 (&w4)[4], float4 (&r4)[4]) SERQ_INLINE {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w4[q] = *reinterpret_cast<const float4*>(s_sw + nt + 8 * q);
+      r4[q] = *reinterpret_cast<const float4*>(s_sr + nt + 8 * q);
+    }
+  };
+  if (!a.dbg_main && (a.N & 3) == 0) {
+    // Common case: four-channel vector stores with no branches. A lane
+    // whose token or channel group is past the end writes its vector to a
+    // dummy slot instead, so every store instruction is issued.
+    auto epi = [&](auto ebc) SERQ_INLINE {
+      constexpr int EB = decltype(ebc)::value;
+      uint8_t* yrow[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        yrow[j] = mrow[j] < a.M ? static_cast<uint8_t*>(a.Y) + static_cast<size_t>(mrow[j]) * a.N * EB : nullptr;
+      uint8_t* const sink = reinterpret_cast<uint8_t*>(tile_store_sink) + 16 * lane;
+      static_for<TN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int nt = wn * 32 * TN + i * 32 + 4 * h;
+        float4 w4[4], r4[4];
+        load_scales(nt, w4, r4);
+        float t[TM][16];
+        residual(ic, t, w4);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float rv4[4] = {r4[q].x, r4[q].y, r4[q].z, r4[q].w};
+            float y[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              y[c] = sxm[j] * __builtin_fmaf(rv4[c], static_cast<float>(acc[i][j][4 * q + c]), t[j][4 * q + c]);
+            const int n = n0 + nt + 8 * q;
+            uint8_t* dst = (yrow[j] != nullptr && n < a.N) ? yrow[j] + EB * n : sink;
+            if constexpr (EB == 2)
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            else
+              *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+          }
+        }
+      });
+    };
+    if (a.y_bf16)
+      epi(std::integral_constant<int, 2>{});
+    else
+      epi(std::integral_constant<int, 4>{});
+    return;
+  }
+  // Debug sums or N % 4 != 0: element-wise checks.
+  const int esz = a.y_bf16 ? 2 : 4;
+  static_for<TN>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int nt = wn * 32 * TN + i * 32 + 4 * h;   // first channel (within the tile) of group q = 0
+    float4 w4[4], r4[4];
+    load_scales(nt, w4, r4);
+    if (a.dbg_main) {                            // exact main sums, for tests
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int n = n0 + nt + 8 * (e >> 2) + (e & 3);
+          if (mrow[j] < a.M && n < a.N) a.dbg_main[static_cast<size_t>(mrow[j]) * a.N + n] = acc[i][j][e] >> C::SHIFT;
+        }
+    }
+    float t[TM][16];
+    residual(ic, t, w4);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = mrow[j];
+      if (m >= a.M) continue;
+      if (a.dbg_res) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int n = n0 + nt + 8 * (e >> 2) + (e & 3);
+          if (n < a.N) a.dbg_res[static_cast<size_t>(m) * a.N + n] = acc[i][j][e] >> C::SHIFT;
+        }
+      }
+      uint8_t* yrow = static_cast<uint8_t*>(a.Y) + static_cast<size_t>(m) * a.N * esz;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float rv4[4] = {r4[q].x, r4[q].y, r4[q].z, r4[q].w};
+        float y[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          y[c] = sxm[j] * __builtin_fmaf(rv4[c], static_cast<float>(acc[i][j][4 * q + c]), t[j][4 * q + c]);
+        const int n = n0 + nt + 8 * q;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (n + c >= a.N) break;
+          if (a.y_bf16)
+            reinterpret_cast<uint16_t*>(yrow)[n + c] = f32_to_bf16_rne(y[c]);
+          else
+            reinterpret_cast<float*>(yrow)[n + c] = y[c];
+        }
+      }
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
 // Skinny kernel (4..32 tokens, and W4A8 from one token): eight-wave
 // workgroups, each owning G <= 8 16-channel groups and one K
 // slice of `seg` 256-code chunks (KS slices in all). The workgroup's slice of
@@ -1484,8 +1921,21 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t st) {
   return launch_gemv_kp<MT, 4>(a, st);
 }
 
+hipError_t launch_tile256(const LinearArgs& a, hipStream_t st) {
+  using C = Tile256Cfg;
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(&serq_tile256_kernel), C::LDS_BYTES, lds_set);
+  if (e != hipSuccess) return e;
+  const int n_tiles = (a.N + C::BN - 1) / C::BN;
+  const int m_tiles = (a.M + C::BM - 1) / C::BM;
+  serq_tile256_kernel<<<dim3(n_tiles * m_tiles), dim3(C::NT), C::LDS_BYTES, st>>>(a, n_tiles);
+  return hipGetLastError();
+}
+
 template <int A_BITS>
 hipError_t launch_tile_bits(const LinearArgs& a, const LinearPlan& p, hipStream_t st) {
+  if constexpr (A_BITS == 4)
+    if (p.tn == 4 && p.tm == 4) return launch_tile256(a, st);
   if (p.tn == 2 && p.tm == 2 && p.wgm == 2 && p.kg == 1) return launch_tile<2, 2, A_BITS, 2, 1>(a, st);
   if (p.tn == 2 && p.tm == 2 && p.wgm == 2 && p.kg == 2) return launch_tile<2, 2, A_BITS, 2, 2>(a, st);
   if (p.tn == 2 && p.tm == 1 && p.wgm == 2 && p.kg == 1) return launch_tile<2, 1, A_BITS, 2, 1>(a, st);
@@ -1901,6 +2351,16 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   // measured 12-20 % slower on the LLaMA shapes.) The largest tile that still
   // gives every CU a workgroup; smaller tiles keep more k-tiles in flight.
   auto tiles = [&](int bm, int bn) { return static_cast<long>((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  // W4A4: 256 x 256 tiles (one four-wave workgroup per CU, 4 x 4 blocks per
+  // wave: half the widening per MFMA) where their rounds of 256 tiles take
+  // less time than the rounds of 512 128 x 128 tiles: a round of the large
+  // tiles does twice the work of one of the small ones, measured at 0.93-0.95
+  // of the time on the LLaMA prefill shapes. Padding and a partial last
+  // round count as full ones.
+  const long rounds256 = (tiles(256, 256) + kCUs - 1) / kCUs;
+  const long rounds128 = (tiles(128, 128) + 2 * kCUs - 1) / (2 * kCUs);
+  if (a_bits == 4 && M > 128 && rounds256 * 19 < rounds128 * 10)
+    return {LinearKernel::kTile, 4, 4, 2, 1, "tile256x256"};
   if (M > 64 && tiles(128, 128) >= kCUs) return {LinearKernel::kTile, 2, 2, 2, 1, "tile128x128"};
   // Three quarters of the CUs or more with one 128 x 128 tile each: two
   // k-groups of four waves per tile, one eight-wave workgroup per CU
