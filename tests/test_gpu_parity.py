@@ -221,7 +221,11 @@ def _run_codes(M, K, N, r, bits, out, seed, col_sample=None):
     Xc, Wc, Rc, sx, sw, sr, Xq, layer = _codes_case(M, K, N, r, bits, seed)
     odt = torch.float32 if out == "f32" else torch.bfloat16
     y, am, ar = S.linear(dev(Xq), dev(sx), layer, a_bits=bits, out_dtype=odt, debug=True)
+    # without the debug outputs some kernels take other store paths: same Y
+    y_plain = S.linear(dev(Xq), dev(sx), layer, a_bits=bits, out_dtype=odt)
     _sync()
+    assert torch.equal(y_plain.view(torch.int16 if out == "bf16" else torch.int32),
+                       y.view(torch.int16 if out == "bf16" else torch.int32))
     cols = np.arange(N) if col_sample is None else sample(N, col_sample, seed)
     am_ref, ar_ref = O.linear_int(Xc, Wc[:, cols], Rc[:, cols], r)
     am_g, ar_g = host(am)[:, cols], host(ar)[:, cols]

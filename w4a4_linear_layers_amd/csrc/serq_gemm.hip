@@ -1211,6 +1211,7 @@ __global__ __launch_bounds__(256, 1) void serq_tile256_kernel(LinearArgs a, int 
     // Common case: four-channel vector stores with no branches. A lane
     // whose token or channel group is past the end writes its vector to a
     // dummy slot instead, so every store instruction is issued.
+    const bool wide = (a.N & 7) == 0;            // bf16: eight-channel groups whole or past the end
     auto epi = [&](auto ebc) SERQ_INLINE {
       constexpr int EB = decltype(ebc)::value;
       uint8_t* yrow[TM];
@@ -1227,19 +1228,47 @@ __global__ __launch_bounds__(256, 1) void serq_tile256_kernel(LinearArgs a, int 
         residual(ic, t, w4);
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
+          float y[4][4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float rv4[4] = {r4[q].x, r4[q].y, r4[q].z, r4[q].w};
-            float y[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-              y[c] = sxm[j] * __builtin_fmaf(rv4[c], static_cast<float>(acc[i][j][4 * q + c]), t[j][4 * q + c]);
+              y[q][c] = sxm[j] * __builtin_fmaf(rv4[c], static_cast<float>(acc[i][j][4 * q + c]), t[j][4 * q + c]);
+          }
+          if constexpr (EB == 2) {
+            if (wide) {
+              // Lane half h holds channels 8 q + 4 h + (0..3); one swap of the
+              // halves' packed groups per dword gives half 0 channels
+              // 16 p + (0..7) and half 1 channels 16 p + 8 + (0..7): one
+              // 16-byte store per lane and pair of groups.
+#pragma unroll
+              for (int p = 0; p < 2; ++p) {
+                const uint32_t g0[2] = {pack_bf16x2(y[2 * p][0], y[2 * p][1]), pack_bf16x2(y[2 * p][2], y[2 * p][3])};
+                const uint32_t g1[2] = {pack_bf16x2(y[2 * p + 1][0], y[2 * p + 1][1]),
+                                        pack_bf16x2(y[2 * p + 1][2], y[2 * p + 1][3])};
+                uint32_t lo[2], hi[2];
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                  const auto sw2 = __builtin_amdgcn_permlane32_swap(g0[d], g1[d], false, false);
+                  lo[d] = sw2[0];
+                  hi[d] = sw2[1];
+                }
+                const int n = n0 + nt - 4 * h + 16 * p + 8 * h;
+                uint8_t* dst = (yrow[j] != nullptr && n < a.N) ? yrow[j] + 2 * n : sink;
+                *reinterpret_cast<uint4*>(dst) = make_uint4(lo[0], lo[1], hi[0], hi[1]);
+              }
+              continue;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
             const int n = n0 + nt + 8 * q;
             uint8_t* dst = (yrow[j] != nullptr && n < a.N) ? yrow[j] + EB * n : sink;
             if constexpr (EB == 2)
-              *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(y[q][0], y[q][1]), pack_bf16x2(y[q][2], y[q][3]));
             else
-              *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+              *reinterpret_cast<float4*>(dst) = make_float4(y[q][0], y[q][1], y[q][2], y[q][3]);
           }
         }
       });
