@@ -491,9 +491,12 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(128, 14336, 4096, 128) == "tile32x64k4"
     assert S.kernel_name(129, 14336, 4096, 64) == "tile64x64k4"      # 192 tiles of 64 x 64, long K
     assert S.kernel_name(256, 14336, 4096, 64) == "tile64x64k4"      # 256 tiles of 64 x 64, long K
-    assert S.kernel_name(256, 4096, 4096, 64) == "tile64x64"         # 32 k-tiles: one group
-    assert S.kernel_name(384, 4096, 4096, 64) == "tile64x64"         # 384 tiles of 64 x 64
-    assert S.kernel_name(40, 4096, 28672, 128) == "tile64x64"        # 448 tiles of 64 x 64
+    assert S.kernel_name(256, 4096, 4096, 64) == "tile64x64k2"       # 32 k-tiles: two groups
+    assert S.kernel_name(256, 4096, 4096, 64, 8) == "tile64x64"      # W4A8: one group
+    assert S.kernel_name(384, 4096, 4096, 64) == "tile64x64k2"       # 384 tiles of 64 x 64
+    assert S.kernel_name(40, 4096, 28672, 128) == "tile64x64k2"      # 448 tiles of 64 x 64
+    assert S.kernel_name(256, 1024, 4096, 64) == "tile64x64k2"       # eight k-tiles
+    assert S.kernel_name(256, 992, 4096, 64) == "tile64x64"          # under eight k-tiles: one group
     assert S.kernel_name(64, 4096, 32768, 64) == "tile64x128"        # 256 tiles of 64 x 128
     assert S.kernel_name(768, 4096, 4096, 64) == "tile128x128k2"     # 192 tiles of 128 x 128: two k-groups
     assert S.kernel_name(1024, 4096, 4096, 64) == "tile128x128"

@@ -258,10 +258,12 @@ LINEAR_CASES = [
     (100, 512, 300, 64, "tile32x64k4"),
     (129, 800, 258, 8, "tile32x64k4"),
     (128, 4096, 4096, 64, "tile32x64k4"),       # deep pipeline, 32-token tiles
-    (256, 4096, 4096, 64, "tile64x64"),       # deep pipeline, one workgroup per CU
+    (256, 4096, 4096, 64, "tile64x64k2"),     # two k-groups of two 32 x 64 waves, one workgroup per CU
     (256, 8192, 4096, 64, "tile64x64k4"),     # four k-groups of two 32 x 64 waves
     (200, 8224, 2600, 72, "tile64x64k4"),     # ragged M, N and K
-    (200, 1056, 2600, 72, "tile64x64"),       # ragged M and N
+    (200, 1056, 2600, 72, "tile64x64k2"),     # ragged M and N, a ragged last stage
+    (150, 1184, 3001, 256, "tile64x64k2"),    # N % 4 != 0, two residual k-tiles, an odd stage count
+    (256, 1024, 4096, 0, "tile64x64k2"),      # r = 0, eight k-tiles
     (300, 544, 4000, 40, "tile64x64"),        # ragged M, N and K
     (60, 1056, 32800, 72, "tile64x128"),      # ragged M and N
     (100, 288, 16400, 128, "tile64x128"),
@@ -290,6 +292,8 @@ def test_linear_codes_bit_exact(M, K, N, r, kern, bits, out):
         kern = "decode16"                 # the int4 dot-product kernel is W4A4 only
     if kern == "tile256x256" and bits == 8:
         kern = "tile128x128"
+    if kern == "tile64x64k2" and bits == 8:
+        kern = "tile64x64"
     assert S.kernel_name(M, K, N, r, bits).removesuffix("_ksplit") == kern
     _run_codes(M, K, N, r, bits, out, seed=M + K + N + r + bits, col_sample=512 if N > 2048 else None)
 

@@ -552,9 +552,10 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   // while the matrix core is busy. The wave raises its issue priority for the
   // k-tile's MFMA sequence, so that of the two waves on a SIMD the one feeding
   // the matrix core goes first: 2-3 % on the one-k-group prefill tiles, 3-7 %
-  // on the 64x64 four-k-group tile; on the 32x64 four-k-group tile and the
-  // two-k-group 128x128 tile it cost 1-2 %, so those leave it alone.
-  static constexpr bool kRaisePrio = KG == 1 || (KG == 4 && TM == 2);
+  // on the 64x64 four-k-group tile, up to 6 % on the 64x64 two-k-group tile
+  // when two of its workgroups share a CU; on the 32x64 four-k-group tile and
+  // the two-k-group 128x128 tile it cost 1-2 %, so those leave it alone.
+  static constexpr bool kRaisePrio = KG == 1 || (KG == 4 && TM == 2) || (KG == 2 && WGM == 1);
   auto compute = [&](const Frags& f, v16i (&acc)[AS][TN][TM]) {
     v4i wa[TN], xb[TM];
     unpack(f, 0, wa, xb);
@@ -695,7 +696,43 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
         acc[i][j] += accs[k][i][j];
         ar[i][j] += ars[k][i][j];
       }
-  if constexpr (KG > 1) {
+  // Which k-group finishes block (i, j): with two k-groups and an even
+  // number of blocks per wave, each group takes every other block (the
+  // epilogue's scaling and LDS writes split between them); otherwise group 0
+  // takes them all.
+  constexpr bool kSplitEpi = KG == 2 && (TN * TM) % 2 == 0;
+  auto owns = [&](int i, int j) { return kSplitEpi ? ((i * TM + j) & 1) == kg : kg == 0; };
+  if constexpr (kSplitEpi) {
+    // Each wave leaves the sums of the blocks the other group finishes in LDS
+    // (the stages are free once every wave is here; lane-contiguous words, no
+    // bank conflicts) and adds the other group's sums of its own blocks.
+    constexpr int NH = TN * TM / 2, PL = NH * 16;
+    lds_barrier();
+    int* red = reinterpret_cast<int*>(lds);
+    int* dst = red + (kg * C::NWG + wl) * 2 * PL * 64 + lane;
+    const int* src = red + ((1 - kg) * C::NWG + wl) * 2 * PL * 64 + lane;
+    static_for<TN * TM>([&](auto bc) {
+      constexpr int b = decltype(bc)::value, i = b / TM, j = b % TM, t = b / 2;
+      if ((b & 1) != kg) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          dst[(t * 16 + e) * 64] = acc[i][j][e];
+          dst[(PL + t * 16 + e) * 64] = ar[i][j][e];
+        }
+      }
+    });
+    lds_barrier();
+    static_for<TN * TM>([&](auto bc) {
+      constexpr int b = decltype(bc)::value, i = b / TM, j = b % TM, t = b / 2;
+      if ((b & 1) == kg) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          acc[i][j][e] += src[(t * 16 + e) * 64];
+          ar[i][j][e] += src[(PL + t * 16 + e) * 64];
+        }
+      }
+    });
+  } else if constexpr (KG > 1) {
     // The other k-groups' sums through LDS (the stages are free once every
     // wave is here; lane-contiguous words, no bank conflicts), added up by
     // group 0, which runs the epilogue.
@@ -730,12 +767,13 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
       }
     }
   }
-  if (a.dbg_main && kg == 0) {                 // exact accumulators, for tests
+  if (a.dbg_main) {                            // exact accumulators, for tests
     static_for<TM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int m = m0 + wm * C::WM + j * 32 + l32;
       static_for<TN>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        if (!owns(i, j)) return;
         const int nb = n0 + wn * C::WN + i * 32 + 4 * h;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -758,7 +796,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   float sxm[TM];
 #pragma unroll
   for (int j = 0; j < TM; ++j) sxm[j] = s_sx[wm * C::WM + j * 32 + l32] * (1.0f / (1 << C::SHIFT));
-  if (kg == 0) static_for<TN>([&](auto ic) {
+  if (kSplitEpi || kg == 0) static_for<TN>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
     const int nt = wn * C::WN + i * 32 + 4 * h;   // first channel (within the tile) of group q = 0
     float4 w4[4], r4[4];
@@ -769,6 +807,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
     }
     static_for<TM>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
+      if (!owns(i, j)) return;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float wv4[4] = {w4[q].x, w4[q].y, w4[q].z, w4[q].w};
@@ -785,7 +824,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
   __syncthreads();                              // residual buffers and scales no longer read
 
   // Output tile into LDS, row = token, swizzled 16-byte chunks.
-  if (kg > 0) {
+  if (!kSplitEpi && kg > 0) {
     // the other k-groups only help with the copy-out
   } else if (a.y_bf16) {
     constexpr int RB = C::BN * 2, SWZ = C::out_swz(2);
@@ -796,6 +835,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
       const int hs = (h ^ half_swap(row)) * 8;
       static_for<TN>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        if (!owns(i, j)) return;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = (wn * C::WN + i * 32) / 8 + q;
@@ -814,6 +854,7 @@ void serq_tile_kernel(LinearArgs a, int n_tiles) {
       uint8_t* rp = lds + row * RB;
       static_for<TN>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        if (!owns(i, j)) return;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = (wn * C::WN + i * 32 + 8 * q + 4 * h) / 4;
@@ -1971,6 +2012,8 @@ hipError_t launch_tile_bits(const LinearArgs& a, const LinearPlan& p, hipStream_
   if (p.tn == 1 && p.tm == 1 && p.wgm == 2 && p.kg == 1) return launch_tile<1, 1, A_BITS, 2, 1>(a, st);
   if (p.tn == 1 && p.tm == 1 && p.wgm == 1 && p.kg == 4) return launch_tile<1, 1, A_BITS, 1, 4>(a, st);
   if (p.tn == 1 && p.tm == 2 && p.wgm == 1 && p.kg == 4) return launch_tile<1, 2, A_BITS, 1, 4>(a, st);
+  if constexpr (A_BITS == 4)
+    if (p.tn == 1 && p.tm == 2 && p.wgm == 1 && p.kg == 2) return launch_tile<1, 2, A_BITS, 1, 2>(a, st);
   return hipErrorInvalidValue;
 }
 
@@ -2413,6 +2456,12 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   // few % behind the single group).
   if (tiles(64, 64) <= kCUs && K >= 64 * kKTileCodes)
     return {LinearKernel::kTile, 1, 2, 1, 4, "tile64x64k4"};
+  // Two k-groups of two 32 x 64 waves (each wave 1 x 2 blocks: 9 VALU per
+  // MFMA against 12 for single blocks, the four waves splitting the
+  // epilogue): 0.87-0.89x the time of four single-block waves on 4096 x 4096
+  // at 160-256 tokens and on 8192 x 4096 at 256, 0.94x at 320 tiles; with
+  // fewer than eight k-tiles the group reduction costs more than it saves.
+  if (a_bits == 4 && K >= 8 * kKTileCodes) return {LinearKernel::kTile, 1, 2, 1, 2, "tile64x64k2"};
   return {LinearKernel::kTile, 1, 1, 2, 1, "tile64x64"};
 }
 
