@@ -279,6 +279,10 @@ LINEAR_CASES = [
     (500, 992, 32702, 72, "tile256x256"),     # N % 4 != 0: element stores
     (480, 4160, 65536, 256, "tile256x256"),   # two residual k-tiles, ragged M
     (1024, 256, 16384, 0, "tile256x256"),     # r = 0
+    # more 256 x 256 tiles than CUs (several rounds of workgroups)
+    (760, 1024, 65536, 128, "tile256x256"),   # 768 tiles, ragged M
+    (500, 2048, 65536, 0, "tile256x256"),     # 512 tiles, r = 0
+    (600, 1536, 40960, 72, "tile256x256"),    # 480 tiles, a zero-filled residual k-tile
     (7, 100, 30, 6, "generic"),           # K % 32 != 0, r % 8 != 0
     (3, 384, 10, 320, "generic"),         # r > 256
 ]
