@@ -1431,6 +1431,21 @@ struct SkinnySplit {
   int G, nb, KS, seg;       // groups per workgroup, group sets, K slices, chunks per slice
 };
 
+// f / d for 0 <= f with f d < 2^32, d >= 1, as one high multiply by
+// mul = floor((2^32 - 1) / d) + 1 (mul = 2^32 / d when d is a power of two,
+// else ceil(2^32 / d), whose excess over 2^32 / d, times f, stays below
+// one): the skinny kernel's per-item divisions by wave-uniform divisors are
+// then single scalar multiplies instead of the ~25-instruction sequence of a
+// general division.
+struct SmallDiv {
+  int d;
+  uint32_t mul;
+  __device__ explicit SmallDiv(int d_) : d(d_), mul(d_ > 1 ? 0xFFFFFFFFu / static_cast<uint32_t>(d_) + 1u : 0u) {}
+  __device__ int operator()(int f) const {
+    return d > 1 ? static_cast<int>(__umulhi(static_cast<uint32_t>(f), mul)) : f;
+  }
+};
+
 template <int MG, int A_BITS, int IPW>
 __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearArgs a, SkinnySplit sp) {
   constexpr int SHIFT = A_BITS == 4 ? 8 : 4;
@@ -1483,8 +1498,9 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
   }
   {
     const int per_row = (xlen + 1023) / 1024;
+    const SmallDiv by_row(max(per_row, 1));
     for (int q = wv; q < a.M * per_row; q += kSkxWaves) {
-      const int t = q / per_row, c = q - t * per_row;
+      const int t = by_row(q), c = q - t * per_row;
       if (1024 * c + 16 * lane < xlen)
         dma16(a.Xq + static_cast<size_t>(t) * Xrow + xoff, 1024 * c + 16 * lane, lds_base + t * XS + 1024 * c);
     }
@@ -1498,11 +1514,12 @@ __global__ __launch_bounds__(64 * kSkxWaves, 1) void serq_skinny_kernel(LinearAr
     uint4 w[IPW][LW];
     int j[IPW], t[IPW];
   };
+  const SmallDiv by_item(Ts);
   auto issue = [&](int u, Buf& bf) {
     static_for<IPW>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       const int f = min(wv + kSkxWaves * (u * IPW + k), NI - 1);
-      const int j = f / Ts, t = f - j * Ts;
+      const int j = by_item(f), t = f - j * Ts;
       bf.j[k] = j;
       bf.t[k] = t;
       const bool res = t >= Cs;
