@@ -352,6 +352,11 @@ __device__ __forceinline__ void mx_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// Output-tile swizzle for bf16 rows (16-byte chunks XOR-ed with the row's
+// low bits): the 8-byte half a lane writes moves to the other half of its
+// chunk when mx_half_swap(row), which keeps the 8-byte writes of 16 (and 32)
+// consecutive rows at one column on distinct banks.
+__device__ __forceinline__ int mx_half_swap(int row) { return ((row >> 3) ^ (row >> 4)) & 1; }
 // 16-byte part slot of a 64-byte row (bits 1-3 of the row): the 16-byte
 // reads of 16 consecutive rows at one part hit distinct bank groups.
 __device__ __forceinline__ int mx_swz64(int row) {
@@ -368,6 +373,8 @@ struct MxCfg {
   static constexpr int CW = W_BYTES / 1024 / NW, CX = X_BYTES / 1024 / NW;   // 1 KB chunks per wave
   static constexpr int LOADS = CW + CX + 1;                                  // + one exponent chunk
   static constexpr int LDS = STAGES * STAGE;
+  static constexpr bool F32_VIA_LDS = BM * BN * 4 <= LDS;    // else fp32 outputs are stored element-wise
+  static_assert(BM * BN * 2 <= LDS && BN * 2 / 16 >= 16, "bf16 output tile in LDS");
   static_assert(CW * NW * 1024 == W_BYTES && CX * NW * 1024 == X_BYTES, "operand chunks split over the waves");
   static_assert((BN + BM) / 64 == NW, "one exponent chunk per wave");
   static_assert(OCC * LDS <= 160 * 1024 && (STAGES - 1) * LOADS < 64, "LDS, vmcnt range");
@@ -494,7 +501,12 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArg
 
   // Epilogue, one weight block row at a time: its residual MFMAs (fragments
   // read from memory; elements past r contribute zero), then
-  // y = acc_main + acc_res stored four channels per lane and group.
+  // y = acc_main + acc_res, into an output tile in LDS (the stages are free
+  // once every wave is here) that is then written with 16-byte row stores;
+  // element-wise stores with the debug sums, or for fp32 tiles larger than
+  // the LDS.
+  const bool direct = a.dbg_main != nullptr || (!a.y_bf16 && !C::F32_VIA_LDS);
+  if (!direct) mx_lds_barrier();
   const int nw = n0 + wn * 32 * TN, mw = m0 + wm * 32 * TM;
   const int rsteps = (a.r + 63) / 64;
   const uint32_t rrow = static_cast<uint32_t>(a.r / 2), rsc = static_cast<uint32_t>(a.r / 32);
@@ -527,6 +539,20 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArg
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * q + e] + res[j][4 * q + e];
+        if (!direct) {
+          const int row = wm * 32 * TM + 32 * j + l32;   // token within the tile
+          if (a.y_bf16) {
+            uint8_t* rp = lds + row * (C::BN * 2);
+            const int c = (wn * 32 * TN + 32 * i) / 8 + q;
+            *reinterpret_cast<uint2*>(rp + 16 * (c ^ (row & 15)) + (h ^ mx_half_swap(row)) * 8) =
+                make_uint2(mx_pack_bf16x2(y[0], y[1]), mx_pack_bf16x2(y[2], y[3]));
+          } else if constexpr (C::F32_VIA_LDS) {
+            uint8_t* rp = lds + row * (C::BN * 4);
+            const int c = (wn * 32 * TN + 32 * i + 8 * q + 4 * h) / 4;
+            *reinterpret_cast<float4*>(rp + 16 * (c ^ (row & 15))) = make_float4(y[0], y[1], y[2], y[3]);
+          }
+          continue;
+        }
         const size_t base = static_cast<size_t>(m) * a.N + n;
         if (n + 3 < a.N && (a.N & 3) == 0) {
           if (a.y_bf16)
@@ -557,6 +583,51 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArg
       }
     }
   }
+  if (direct) return;
+  __syncthreads();
+  // 16-byte chunks along the rows of Y (every LDS read first, then the
+  // stores); ragged tails element by element.
+  auto copy_out = [&](auto ebc) {
+    constexpr int EB = decltype(ebc)::value;   // bytes per element
+    constexpr int CPR = C::BN * EB / 16;       // chunks per tile row
+    constexpr int EPC = 16 / EB;               // elements per chunk
+    constexpr int RPP = C::NT / CPR;           // rows per pass
+    constexpr int PASSES = C::BM / RPP;
+    const int tid = threadIdx.x;
+    const int c = tid % CPR;
+    const int n = n0 + c * EPC;
+    const bool vec = (a.N % EPC) == 0 && n + EPC <= a.N;
+    uint4 v[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = p * RPP + tid / CPR;
+      v[p] = *reinterpret_cast<const uint4*>(lds + row * C::BN * EB + 16 * (c ^ (row & 15)));
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = p * RPP + tid / CPR;
+      if (m0 + row >= a.M) break;
+      if (n >= a.N) continue;
+      uint4 w = v[p];
+      if (EB == 2 && mx_half_swap(row)) w = make_uint4(w.z, w.w, w.x, w.y);
+      uint8_t* dst = static_cast<uint8_t*>(a.Y) + (static_cast<size_t>(m0 + row) * a.N + n) * EB;
+      if (vec) {
+        *reinterpret_cast<uint4*>(dst) = w;
+      } else {
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+        for (int e = 0; e < EPC && n + e < a.N; ++e) {
+          if (EB == 2)
+            reinterpret_cast<uint16_t*>(dst)[e] = static_cast<uint16_t>(d[e >> 1] >> (16 * (e & 1)));
+          else
+            reinterpret_cast<uint32_t*>(dst)[e] = d[e];
+        }
+      }
+    }
+  };
+  if (a.y_bf16)
+    copy_out(std::integral_constant<int, 2>{});
+  else if constexpr (C::F32_VIA_LDS)
+    copy_out(std::integral_constant<int, 4>{});
 }
 
 // ---------------------------------------------------------------------------
