@@ -510,23 +510,69 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArg
   const int nw = n0 + wn * 32 * TN, mw = m0 + wm * 32 * TM;
   const int rsteps = (a.r + 63) / 64;
   const uint32_t rrow = static_cast<uint32_t>(a.r / 2), rsc = static_cast<uint32_t>(a.r / 32);
+  // Up to kRS residual steps (r <= 128 on the 256 tile, whose registers are
+  // fuller, 256 on the 128 tile) the fragments wait in registers: the
+  // activation side's, the same for every block row, loaded once, and each
+  // block row's weight side loaded while the row before it is finished, so
+  // that the epilogue waits for one load latency instead of one per block
+  // row. Longer residuals load step by step.
+  constexpr int kRS = TN * TM >= 8 ? 2 : 4;
+  const bool rreg = rsteps <= kRS;
+  uint4 rxf[TM][kRS];
+  int rxs[TM][kRS];
+  uint4 rwf[2][kRS];
+  int rws[2][kRS];
+  auto load_w = [&](int i, int buf) {
+    const int nr = min(nw + 32 * i + l32, a.N - 1);
+#pragma unroll
+    for (int s = 0; s < kRS; ++s) {
+      const int k0 = 64 * s + 32 * h;
+      const bool in = s < rsteps && k0 < a.r;
+      rwf[buf][s] = in ? *reinterpret_cast<const uint4*>(a.Rq + nr * rrow + k0 / 2) : make_uint4(0, 0, 0, 0);
+      rws[buf][s] = in ? a.Rsc[nr * rsc + k0 / 32] : 127;
+    }
+  };
+  if (rreg) {
+#pragma unroll
+    for (int s = 0; s < kRS; ++s) {
+      const int k0 = 64 * s + 32 * h;
+      const bool in = s < rsteps && k0 < a.r;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int mr = min(mw + 32 * j + l32, a.M - 1);
+        rxf[j][s] = in ? *reinterpret_cast<const uint4*>(Xq + mr * rowb + k0 / 2) : make_uint4(0, 0, 0, 0);
+        rxs[j][s] = in ? Xsc[mr * scb + k0 / 32] : 127;
+      }
+    }
+    load_w(0, 0);
+  }
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
     v16f res[TM];
 #pragma unroll
     for (int j = 0; j < TM; ++j) res[j] = v16f{};
-    const int nr = min(nw + 32 * i + l32, a.N - 1);
-    for (int s = 0; s < rsteps; ++s) {
-      const int k0 = 64 * s + 32 * h;
-      const bool in = k0 < a.r;
-      const uint4 wf = in ? *reinterpret_cast<const uint4*>(a.Rq + nr * rrow + k0 / 2) : make_uint4(0, 0, 0, 0);
-      const int wsv = in ? a.Rsc[nr * rsc + k0 / 32] : 127;
+    if (rreg) {
+      if (i + 1 < TN) load_w(i + 1, (i + 1) & 1);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int mr = min(mw + 32 * j + l32, a.M - 1);
-        const uint4 xf = in ? *reinterpret_cast<const uint4*>(Xq + mr * rowb + k0 / 2) : make_uint4(0, 0, 0, 0);
-        const int xsv = in ? Xsc[mr * scb + k0 / 32] : 127;
-        res[j] = mfma_mx(wf, xf, wsv, xsv, res[j]);
+      for (int s = 0; s < kRS; ++s) {
+        if (s >= rsteps) break;
+#pragma unroll
+        for (int j = 0; j < TM; ++j) res[j] = mfma_mx(rwf[i & 1][s], rxf[j][s], rws[i & 1][s], rxs[j][s], res[j]);
+      }
+    } else {
+      const int nr = min(nw + 32 * i + l32, a.N - 1);
+      for (int s = 0; s < rsteps; ++s) {
+        const int k0 = 64 * s + 32 * h;
+        const bool in = k0 < a.r;
+        const uint4 wf = in ? *reinterpret_cast<const uint4*>(a.Rq + nr * rrow + k0 / 2) : make_uint4(0, 0, 0, 0);
+        const int wsv = in ? a.Rsc[nr * rsc + k0 / 32] : 127;
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int mr = min(mw + 32 * j + l32, a.M - 1);
+          const uint4 xf = in ? *reinterpret_cast<const uint4*>(Xq + mr * rowb + k0 / 2) : make_uint4(0, 0, 0, 0);
+          const int xsv = in ? Xsc[mr * scb + k0 / 32] : 127;
+          res[j] = mfma_mx(wf, xf, wsv, xsv, res[j]);
+        }
       }
     }
 #pragma unroll
