@@ -431,11 +431,12 @@ int serq_quant_act_mx(const void* X, serq_dtype x_dtype, int M, int K,
 /*
  * serq_linear_mx -- online, device memory, asynchronous on `stream`.
  * Y = acc_main + acc_res (the formula above) on gfx950's scaled FP4 matrix
- * instruction, whose operands are these codes and exponent bytes as stored;
- * one token (up to eight when N < 16384) takes a dot-product kernel instead
+ * instructions, whose operands are these codes and exponent bytes as
+ * stored; one token (two when N < 16384) takes a dot-product kernel instead
  * (each 32-element block summed exactly, then scaled and added). Either way
  * accumulation is fp32 with one rounding per block (rounded, unlike the
- * integer layer); Y is stored as y_dtype (bf16 with round to nearest even).
+ * integer layer) plus a fixed-order sum of partial sums; Y is stored as
+ * y_dtype (bf16 with round to nearest even).
  *   Xq, Xsc    from serq_quant_act_mx; Wq, Wsc, Rq, Rsc from
  *              serq_calibrate_mx (Rq, Rsc may be NULL when r == 0).
  *   M, K, N, r M >= 0 (0: no-op), K > 0 and 0 <= r <= K multiples of 32,

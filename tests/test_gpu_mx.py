@@ -94,15 +94,24 @@ def _check_y(y, out, mag, K, dt):
     (1, 64, 32, 32, False), (37, 320, 200, 96, False), (130, 1024, 260, 0, False),   # K % 128: plain kernel
     (256, 4096, 512, 256, False), (300, 2048, 1000, 2048, False), (64, 96, 130, 64, False),
     (4100, 384, 4104, 128, False), (3, 128, 8, 32, False),         # ragged 256 tiles; one k-tile
-    # one to four tokens: the GEMV
+    # one or two tokens: the GEMV
     (1, 4096, 256, 64, True),                                        # one shared scale: exact sums
     (2, 384, 100, 96, False),        # a half line at the rows' end, N % 8 != 0, three residual blocks
-    (4, 1024, 72, 1024, False),      # r = K: four residual lines
-    (3, 28672, 24, 256, False),      # long rows
+    (2, 1024, 72, 1024, False),      # r = K: four residual lines
+    (1, 28672, 24, 256, False),      # long rows
     (2, 512, 8200, 32, False),       # four-wave workgroups (many row octets), ragged N
     (1, 2048, 4104, 0, False),       # r = 0
+    # three to sixteen tokens on layers narrower than 16384 channels: the skinny kernel
+    (4, 1024, 72, 1024, False),      # r = K: eight residual chunks
+    (3, 28672, 24, 256, False),      # long rows
     (8, 1024, 300, 96, False),       # eight tokens
     (6, 4096, 64, 64, True),         # six tokens, one shared scale: exact sums
+    (16, 4096, 4096, 64, True),      # one shared scale: exact sums
+    (13, 1152, 300, 96, False),      # nine chunks, a partial residual chunk, ragged N
+    (16, 384, 50, 384, False),       # r = K: three residual chunks
+    (10, 128, 40, 0, False),         # one chunk (most waves idle), r = 0
+    (7, 14336, 100, 128, False),     # fourteen chunks per wave (several rounds of loads in flight)
+    (2, 256, 16400, 32, False),      # two tokens on a wide layer: the tile kernel
 ])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_linear_mx_vs_oracle(M, K, N, r, uniform, out):

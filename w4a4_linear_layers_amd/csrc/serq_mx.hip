@@ -677,7 +677,7 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArg
 }
 
 // ---------------------------------------------------------------------------
-// MX GEMV (one to eight tokens, K a multiple of 128). Per 32-element block
+// MX GEMV (one or two tokens, K a multiple of 128). Per 32-element block
 // the FP4 codes of both operands become bf16 pairs by gfx950's scaled
 // conversion (scale 1: the E2M1 values exactly), and v_dot2c_f32_bf16
 // multiplies and sums them -- exactly, since every product is a multiple of
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArg
 // the waves, in a fixed order.
 // ---------------------------------------------------------------------------
 
-constexpr int kMxGemvMaxTokens = 8;
+constexpr int kMxGemvMaxTokens = 2;
 constexpr int kMxGemvUnit = 4;               // lines per unit and lane, two units in flight
 constexpr int kMxGemvMaxX = 96 * 1024;       // LDS bytes for the activation codes and exponents
 
@@ -863,6 +863,129 @@ __global__ __launch_bounds__(64 * KP) void serq_mx_gemv_kernel(MxArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MX skinny kernel (up to 16 tokens, K a multiple of 128): one eight-wave
+// workgroup per 16 output channels, on v_mfma_scale_f32_16x16x128_f8f6f4
+// with FP4 operands -- A the 16 weight rows, B the (zero-padded) 16 token
+// rows, a lane's operand the 16 stored bytes of its row's 32-element block
+// (row l % 16, block l / 16 of the 128-element chunk) and its scale operand
+// that block's exponent byte, so nothing is converted. Wave w takes chunks
+// w, w + 8, ... of the main K and of the residual, loads running several
+// chunks ahead, and keeps its two 16 x 16 sums in registers; the eight
+// waves' sums are added through LDS in a fixed order (deterministic; one
+// rounding per block in the matrix instruction, eight more).
+// ---------------------------------------------------------------------------
+
+constexpr int kMxSkinnyMaxTokens = 16;
+constexpr int kMxSkinnyWaves = 8;
+constexpr int kMxSkinnyRing = 4;              // chunks in flight per wave
+
+typedef float mx_v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ mx_v4f mfma_mx16(const uint4& a, const uint4& b, int sa, int sb, mx_v4f c) {
+  const v8i av = v8i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w), 0, 0, 0, 0};
+  const v8i bv = v8i{static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
+__global__ __launch_bounds__(64 * kMxSkinnyWaves) void serq_mx_skinny_kernel(MxArgs a) {
+  __shared__ mx_v4f red[kMxSkinnyWaves][2][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int Kb = a.K / 2, Kblk = a.K / 32;
+  const int rblk = a.r / 32;
+  const int nch = a.K / 128;                       // main chunks
+  const int rch = (a.r + 127) / 128;               // residual chunks (the last may be partial)
+  const int ch = min(static_cast<int>(blockIdx.x) * 16 + l16, a.N - 1);   // this lane's weight row
+  const int tk = min(l16, a.M - 1);                                      // this lane's token row
+  const bool tok_in = l16 < a.M;
+  const uint8_t* wrow = a.Wq + static_cast<size_t>(ch) * Kb;
+  const uint8_t* wsc = a.Wsc + static_cast<size_t>(ch) * Kblk;
+  const uint8_t* rrow = a.r > 0 ? a.Rq + static_cast<size_t>(ch) * (a.r / 2) : wrow;
+  const uint8_t* rsc = a.r > 0 ? a.Rsc + static_cast<size_t>(ch) * rblk : wsc;
+  const uint8_t* xrow = a.Xq + static_cast<size_t>(tk) * Kb;
+  const uint8_t* xsc = a.Xsc + static_cast<size_t>(tk) * Kblk;
+  // This wave's items: main chunks wv, wv + 8, ..., then residual chunks
+  // wv, wv + 8, ...
+  const int nmain = nch > wv ? (nch - wv + kMxSkinnyWaves - 1) / kMxSkinnyWaves : 0;
+  const int nres = rch > wv ? (rch - wv + kMxSkinnyWaves - 1) / kMxSkinnyWaves : 0;
+  const int total = nmain + nres;
+  struct Item {
+    uint4 w, x;
+    uint32_t ew, ex;
+  };
+  // Item i's loads (past the end: the last item's, never used); a block past
+  // r reads block 0 of the row and is zeroed before use.
+  auto load = [&](int i, Item& it) {
+    const int ii = min(i, max(total - 1, 0));
+    const bool res = ii >= nmain;
+    const int c = wv + kMxSkinnyWaves * (res ? ii - nmain : ii);
+    const int blk = 4 * c + kq;
+    const int b = res ? (blk < rblk ? blk : 0) : min(blk, Kblk - 1);
+    it.w = *reinterpret_cast<const uint4*>((res ? rrow : wrow) + 16 * b);
+    it.ew = (res ? rsc : wsc)[b];
+    it.x = *reinterpret_cast<const uint4*>(xrow + 16 * b);
+    it.ex = xsc[b];
+  };
+  mx_v4f acc = mx_v4f{0.f, 0.f, 0.f, 0.f}, accr = mx_v4f{0.f, 0.f, 0.f, 0.f};
+  auto use = [&](int i, const Item& it) {
+    if (i >= total) return;
+    const bool res = i >= nmain;
+    const int c = wv + kMxSkinnyWaves * (res ? i - nmain : i);
+    const bool blk_in = !res || 4 * c + kq < rblk;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint4 w = blk_in ? it.w : z;
+    const uint4 x = (blk_in && tok_in) ? it.x : z;
+    const int ew = static_cast<int>(it.ew & 0xFFu), ex = static_cast<int>(it.ex & 0xFFu);
+    if (res)
+      accr = mfma_mx16(w, x, ew, ex, accr);
+    else
+      acc = mfma_mx16(w, x, ew, ex, acc);
+  };
+  Item ring[kMxSkinnyRing];
+#pragma unroll
+  for (int k = 0; k < kMxSkinnyRing; ++k) load(k, ring[k]);
+  for (int i0 = 0; i0 < total; i0 += kMxSkinnyRing) {
+#pragma unroll
+    for (int k = 0; k < kMxSkinnyRing; ++k) {
+      use(i0 + k, ring[k]);
+      load(i0 + k + kMxSkinnyRing, ring[k]);
+    }
+  }
+  red[wv][0][lane] = acc;
+  red[wv][1][lane] = accr;
+  __syncthreads();
+  if (wv == 0) {
+    mx_v4f sm = red[0][0][lane], sr = red[0][1][lane];
+#pragma unroll
+    for (int w = 1; w < kMxSkinnyWaves; ++w) {
+      sm += red[w][0][lane];
+      sr += red[w][1][lane];
+    }
+    // lane: token l16, channels 16 g + 4 kq + (0..3)
+    const int n = static_cast<int>(blockIdx.x) * 16 + 4 * kq;
+    if (tok_in) {
+      const size_t o = static_cast<size_t>(l16) * a.N + n;
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = sm[e] + sr[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e >= a.N) break;
+        if (a.y_bf16)
+          static_cast<uint16_t*>(a.Y)[o + e] = static_cast<uint16_t>(mx_pack_bf16x2(y[e], 0.0f));
+        else
+          static_cast<float*>(a.Y)[o + e] = y[e];
+        if (a.dbg_main) {
+          a.dbg_main[o + e] = sm[e];
+          a.dbg_res[o + e] = sr[e];
+        }
+      }
+    }
+  }
+}
+
 // LDS bytes of the GEMV's activations: codes, then exponents.
 inline long long mx_gemv_lds(int M, int K) {
   return static_cast<long long>(M) * (K / 2) + static_cast<long long>(M) * (K / 32);
@@ -939,23 +1062,28 @@ hipError_t launch_quant_act_mx(const void* X, int x_bf16, int M, int K, const fl
 hipError_t launch_linear_mx(const MxArgs& a, hipStream_t st) {
   // the pipelined kernels load exponent dwords, so those arrays must be 4-byte aligned
   const bool sc_aligned = ((reinterpret_cast<uintptr_t>(a.Wsc) | reinterpret_cast<uintptr_t>(a.Xsc)) & 3u) == 0;
-  // The GEMV for one token, and for up to eight on layers whose 128-channel
-  // tiles would leave half the CUs idle or more (N < 16384); on wider
-  // layers the tile kernel fills the CUs and from two tokens on is as fast
-  // or faster (4096 x 28672: 20.5 against 29.4 us at four tokens).
-  if (sc_aligned && (a.M == 1 || (a.M <= kMxGemvMaxTokens && a.N < 16384)) && a.K % kMxKt == 0 &&
+  // Few tokens. On layers whose 128-channel tiles would leave half the CUs
+  // idle or more (N < 16384): the GEMV up to two tokens, the skinny kernel
+  // up to sixteen (its time grows slowly with the tokens, the GEMV's by a
+  // conversion pass per token: 8B down at four tokens 17.2 us on the GEMV,
+  // 14.9 at five on the skinny kernel; q_proj at 16 tokens 9.2 against 15.1
+  // tiled, 8B down 19.9 against 41.5). On wider layers the tile kernel
+  // fills the CUs and from two tokens on is faster than both (4096 x 28672:
+  // 20.3 us at four tokens, 29.4 on the GEMV; 21.0 at sixteen, 48.5 on the
+  // skinny kernel); one token takes the GEMV there too.
+  const bool narrow = a.N < 16384;
+  if (sc_aligned && (a.M == 1 || (a.M <= kMxGemvMaxTokens && narrow)) && a.K % kMxKt == 0 &&
       mx_gemv_lds(a.M, a.K) <= kMxGemvMaxX &&
       static_cast<uint64_t>(a.N) * (a.K / 2) < (1ull << 32)) {
     switch (a.M) {
       case 1: return launch_mx_gemv<1>(a, st);
-      case 2: return launch_mx_gemv<2>(a, st);
-      case 3: return launch_mx_gemv<3>(a, st);
-      case 4: return launch_mx_gemv<4>(a, st);
-      case 5: return launch_mx_gemv<5>(a, st);
-      case 6: return launch_mx_gemv<6>(a, st);
-      case 7: return launch_mx_gemv<7>(a, st);
-      default: return launch_mx_gemv<8>(a, st);
+      default: return launch_mx_gemv<2>(a, st);
     }
+  }
+  if (narrow && a.M <= kMxSkinnyMaxTokens && a.K % kMxKt == 0 &&
+      static_cast<uint64_t>(a.N) * (a.K / 2) < (1ull << 32)) {
+    serq_mx_skinny_kernel<<<dim3((a.N + 15) / 16), dim3(64 * kMxSkinnyWaves), 0, st>>>(a);
+    return hipGetLastError();
   }
   const int kind = sc_aligned ? mx_kernel_kind(a.M, a.K, a.N) : 0;
   if (kind == 2) return launch_mx_pipe<4, 2, 2, 4, 4, 1>(a, st);
