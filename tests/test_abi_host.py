@@ -498,6 +498,18 @@ def test_kernel_dispatch_rules():
     assert S.kernel_name(256, 1024, 4096, 64) == "tile64x64k2"       # eight k-tiles
     assert S.kernel_name(256, 992, 4096, 64) == "tile64x64"          # under eight k-tiles: one group
     assert S.kernel_name(64, 4096, 32768, 64) == "tile64x128"        # 256 tiles of 64 x 128
+    # W4A4 from 256 tokens: 64 x 64 tiles with two k-groups where they are one round of two per CU
+    assert S.kernel_name(512, 4096, 4096, 64) == "tile64x64k2"
+    assert S.kernel_name(512, 14336, 4096, 128) == "tile64x64k2"
+    assert S.kernel_name(256, 28672, 8192, 256) == "tile64x64k2"
+    assert S.kernel_name(512, 4096, 4096, 64, 8) == "tile64x128"      # W4A8 unchanged
+    assert S.kernel_name(640, 4096, 4096, 64) == "tile64x128"        # 640 tiles of 64 x 64: more than a round
+    assert S.kernel_name(512, 992, 4096, 64) == "tile64x128"         # under eight k-tiles
+    # exactly one 128 x 128 tile per CU and K >= 8192 (W4A4): two k-groups
+    assert S.kernel_name(1024, 14336, 4096, 128) == "tile128x128k2"
+    assert S.kernel_name(512, 28672, 8192, 256) == "tile128x128k2"
+    assert S.kernel_name(1024, 14336, 4096, 128, 8) == "tile128x128"
+    assert S.kernel_name(1024, 28672, 8192, 256) == "tile128x128"    # 512 tiles
     assert S.kernel_name(768, 4096, 4096, 64) == "tile128x128k2"     # 192 tiles of 128 x 128: two k-groups
     assert S.kernel_name(1024, 4096, 4096, 64) == "tile128x128"
     assert S.kernel_name(64, 4096, 4096, 64) == "tile32x64k4"

@@ -302,6 +302,27 @@ def test_linear_codes_bit_exact(M, K, N, r, kern, bits, out):
     _run_codes(M, K, N, r, bits, out, seed=M + K + N + r + bits, col_sample=512 if N > 2048 else None)
 
 
+# W4A4 shapes whose tile choice differs from W4A8's: 64 x 64 tiles with two
+# k-groups where they make one round of two per CU (W4A8: 64 x 128 tiles),
+# and the two-k-group 128 x 128 tile where exactly one such tile falls on
+# each CU and K is long (W4A8: one k-group).
+W4A4_ROUTE_CASES = [
+    (512, 1056, 4096, 72, "tile64x64k2"),     # 512 tiles of 64 x 64, eight k-tiles and a ragged stage
+    (256, 1056, 8192, 0, "tile64x64k2"),      # r = 0
+    (500, 1184, 4000, 256, "tile64x64k2"),    # ragged M and N, two residual k-tiles
+    (128, 8192, 32768, 64, "tile128x128k2"),  # 256 tiles of 128 x 128, K = 8192
+    (200, 8224, 16300, 72, "tile128x128k2"),  # ragged M, N and K
+]
+
+
+@pytest.mark.parametrize("M,K,N,r,kern", W4A4_ROUTE_CASES,
+                         ids=[c[4] + f"-{c[0]}x{c[1]}x{c[2]}r{c[3]}" for c in W4A4_ROUTE_CASES])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_linear_w4a4_routes_bit_exact(M, K, N, r, kern, out):
+    assert S.kernel_name(M, K, N, r, 4) == kern
+    _run_codes(M, K, N, r, 4, out, seed=M + K + N + r, col_sample=512)
+
+
 def test_linear_extreme_codes():
     """All codes at the int4/int8 extremes: the largest accumulators."""
     for bits in (4, 8):

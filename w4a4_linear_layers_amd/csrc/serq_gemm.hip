@@ -2450,13 +2450,24 @@ LinearPlan plan_linear(int M, int K, int N, int r, int a_bits) {
   const long rounds128 = (tiles(128, 128) + 2 * kCUs - 1) / (2 * kCUs);
   if (a_bits == 4 && M > 128 && rounds256 * 19 < rounds128 * 10)
     return {LinearKernel::kTile, 4, 4, 2, 1, "tile256x256"};
-  if (M > 64 && tiles(128, 128) >= kCUs) return {LinearKernel::kTile, 2, 2, 2, 1, "tile128x128"};
+  // Exactly one 128 x 128 tile per CU and K of 64 k-tiles or more (W4A4):
+  // the two-k-group tile below, whose eight waves share each CU's one tile
+  // (1.03x on 14336 x 4096 at 1024 tokens, 1.07x on 28672 x 8192 at 512;
+  // even with K = 4096).
+  const bool one_tile_per_cu = a_bits == 4 && tiles(128, 128) == kCUs && K >= 64 * kKTileCodes;
+  if (M > 64 && tiles(128, 128) >= kCUs && !one_tile_per_cu)
+    return {LinearKernel::kTile, 2, 2, 2, 1, "tile128x128"};
   // Three quarters of the CUs or more with one 128 x 128 tile each: two
   // k-groups of four waves per tile, one eight-wave workgroup per CU
   // (1.1-1.2x on 4096 x 28672, 8192 x 28672 at 65-128 tokens and on
   // 4096 x 4096 at 768; with half the CUs it lost to the 64-row tiles).
   if (M > 64 && tiles(128, 128) >= 3 * kCUs / 4) return {LinearKernel::kTile, 2, 2, 2, 2, "tile128x128k2"};
-  if (tiles(64, 128) >= kCUs) return {LinearKernel::kTile, 2, 1, 2, 1, "tile64x128"};
+  // W4A4 from 256 tokens whose 64 x 64 tiles are one round of two per CU:
+  // those tiles with two k-groups (below) rather than 64 x 128 tiles
+  // (1.06x on 4096 x 4096 and 1.15x on 14336 x 4096 at 512 tokens, 1.09x
+  // on 28672 x 8192 at 256).
+  const bool k2_round = a_bits == 4 && M >= 256 && K >= 8 * kKTileCodes && tiles(64, 64) <= 2 * kCUs;
+  if (tiles(64, 128) >= kCUs && !k2_round) return {LinearKernel::kTile, 2, 1, 2, 1, "tile64x128"};
   // When 64 x 64 tiles would leave half the CUs idle, 32 x 64 tiles whose
   // eight waves form four k-groups (each a k-tile of every four-k-tile
   // stage): every CU gets work and all four SIMDs of a CU share one tile's
