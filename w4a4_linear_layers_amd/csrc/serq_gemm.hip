@@ -1923,14 +1923,22 @@ hipError_t launch_tile(const LinearArgs& a, hipStream_t st) {
 // G and KS: about one workgroup per CU, the slice fitting LDS beside the
 // group slots; one slice if the activations fit, else the choice with the
 // least activation traffic (every workgroup loads its slice of the M rows)
-// plus partial-sum traffic (KS x the outputs, written and read back).
+// plus partial-sum traffic (KS x the outputs, written and read back). Between
+// two choices whose slices both hold eight chunks or more, that traffic is
+// weighted by the padding of the work grid (groups per workgroup times
+// workgroups, slices times their length, over the layer's groups and
+// chunks): every workgroup runs as many items as the fullest one, so a
+// ragged last slice or group set costs its padding in time (8B down at 32
+// tokens: 4 x 4 even slices 13.6 us against 15.9 for 5 x 5 of 12, 8 of the
+// last; 1.2-1.5x on the 28672-, 14336- and 11008-long rows at 9-32 tokens;
+// with shorter slices the split's fixed tail outweighs it).
 template <int MG, int A_BITS>
 SkinnySplit plan_skinny(const LinearArgs& a) {
   constexpr int CXB = 2 * A_BITS * 16;
   const int ngroups = (a.N + 15) / 16;
   const int C = (a.K + 255) / 256;
   SkinnySplit best{0, 0, 0, 0};
-  double best_cost = 0.0;
+  double best_cost = 0.0, best_pad = 1.0;
   for (int G = 1; G <= kSkxMaxGroups; ++G) {
     const int nb = (ngroups + G - 1) / G;
     if (G > 1 && (ngroups + G - 2) / (G - 1) == nb) continue;   // same group sets as G - 1
@@ -1949,13 +1957,17 @@ SkinnySplit plan_skinny(const LinearArgs& a) {
     const double xbytes = static_cast<double>(nb) * a.M * (a.K * A_BITS / 8);
     const double pbytes = ks_used > 1 ? 2.0 * ks_used * ngroups * skx_slot_bytes<MG>() : 0.0;
     const double cost = xbytes + pbytes;
+    const double pad = static_cast<double>(nb) * G * ks_used * seg / (static_cast<double>(ngroups) * C);
+    const bool long_slices = seg >= 8 && best.seg >= 8;
+    const double cmp_new = long_slices ? cost * pad : cost, cmp_best = long_slices ? best_cost * best_pad : best_cost;
     // One slice whenever the activations fit: the split's tail (partial sums
     // out, counter, the last workgroup's reads) measured several us.
     const bool better = best.G == 0 || (ks_used == 1 && best.KS > 1) ||
-                        (cost < best_cost && !(ks_used > 1 && best.KS == 1));
+                        (cmp_new < cmp_best && !(ks_used > 1 && best.KS == 1));
     if (better) {
       best = SkinnySplit{G, nb, ks_used, seg};
       best_cost = cost;
+      best_pad = pad;
     }
   }
   return best;
