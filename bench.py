@@ -674,7 +674,7 @@ def main(argv=None):
             print(json.dumps(dict(route="bf6", **e)), flush=True)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path)", file=sys.stderr)
         return 2
 

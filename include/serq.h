@@ -52,7 +52,7 @@ typedef enum {
   SERQ_OK = 0,
   SERQ_EINVAL = -1,       /* bad size, NULL pointer, bad enum value           */
   SERQ_EALIGN = -2,       /* a device pointer is not 16-byte aligned          */
-  SERQ_EUNSUPPORTED = -3, /* valid request this build does not implement      */
+  SERQ_EUNSUPPORTED = -3, /* valid request the library does not implement    */
   SERQ_EHIP = -4          /* the HIP runtime reported an error at launch      */
 } serq_status;
 

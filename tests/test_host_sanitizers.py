@@ -3,7 +3,7 @@
 calibrate.cpp (calibration, GPTQ, MXFP4, the permutation helper, the bf6
 prepack; host threads) and serq_abi.cpp (every argument validator) are
 built with g++ together with tests/host/sanitizer_driver.cpp, whose stubs
-stand in for the device launchers. The driver runs the offline calls on
+stand in for the device launchers. That program runs the offline calls on
 random layers with every output buffer exactly its documented size, and the
 online validators with valid and invalid arguments. AddressSanitizer +
 UndefinedBehaviorSanitizer (aborting on the first report), then

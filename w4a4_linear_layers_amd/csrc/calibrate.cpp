@@ -298,7 +298,7 @@ extern "C" int serq_prepack_bf6(const uint8_t* codes, int rows, int k, int pitch
 //
 // All of it is fp64 with every element updated by the same sequence of
 // single operations in the same order as the reference statement of the
-// algorithm (no contraction into fused multiply-adds in this build), so the
+// algorithm (compiled with -ffp-contract=off: no fused multiply-adds), so the
 // codes do not depend on the thread count:
 //   H[i][j]  = sum over t in order of x^[t][i] x^[t][j], then damp * mean(diag)
 //              on the diagonal (all-zero H: the identity);
