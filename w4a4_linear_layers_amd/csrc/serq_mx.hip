@@ -869,16 +869,22 @@ __global__ __launch_bounds__(64 * KP) void serq_mx_gemv_kernel(MxArgs a) {
 // with FP4 operands -- A the 16 weight rows, B the (zero-padded) 16 token
 // rows, a lane's operand the 16 stored bytes of its row's 32-element block
 // (row l % 16, block l / 16 of the 128-element chunk) and its scale operand
-// that block's exponent byte, so nothing is converted. Wave w takes chunks
-// w, w + 8, ... of the main K and of the residual, loads running several
-// chunks ahead, and keeps its two 16 x 16 sums in registers; the eight
-// waves' sums are added through LDS in a fixed order (deterministic; one
-// rounding per block in the matrix instruction, eight more).
+// that block's exponent byte, so nothing is converted. Wave w takes pairs
+// of chunks w, w + 8, ... of the main K and of the residual, a lane loading
+// two adjacent blocks of its rows (a 128-byte line of a row per four lanes),
+// the next pair's loads issued as the current pair's two MFMAs go out (two
+// blocks per lane with one pair in flight measured faster than four chunks
+// of single blocks in flight, 20 % on q_proj at 16 tokens, 11 % on
+// 28672 x 8192; deeper rings and wider lanes were slower), and keeps its two
+// 16 x 16 sums in registers; the eight waves' sums are added through LDS in
+// a fixed order (deterministic; one rounding per block in the matrix
+// instruction, eight more).
 // ---------------------------------------------------------------------------
 
 constexpr int kMxSkinnyMaxTokens = 16;
 constexpr int kMxSkinnyWaves = 8;
-constexpr int kMxSkinnyRing = 4;              // chunks in flight per wave
+constexpr int kMxSkinnyRing = 1;              // items in flight per wave
+constexpr int kMxSkinnyP = 2;                 // consecutive blocks per lane and item
 
 typedef float mx_v4f __attribute__((ext_vector_type(4)));
 
@@ -906,42 +912,54 @@ __global__ __launch_bounds__(64 * kMxSkinnyWaves) void serq_mx_skinny_kernel(MxA
   const uint8_t* rsc = a.r > 0 ? a.Rsc + static_cast<size_t>(ch) * rblk : wsc;
   const uint8_t* xrow = a.Xq + static_cast<size_t>(tk) * Kb;
   const uint8_t* xsc = a.Xsc + static_cast<size_t>(tk) * Kblk;
-  // This wave's items: main chunks wv, wv + 8, ..., then residual chunks
-  // wv, wv + 8, ...
-  const int nmain = nch > wv ? (nch - wv + kMxSkinnyWaves - 1) / kMxSkinnyWaves : 0;
-  const int nres = rch > wv ? (rch - wv + kMxSkinnyWaves - 1) / kMxSkinnyWaves : 0;
+  // This wave's items: P consecutive main chunks (blocks 4 P p .. 4 P p +
+  // 4 P - 1 of the row), p = wv, wv + 8, ..., then P residual chunks at a
+  // time. A lane loads the 16 P contiguous bytes of blocks P kq .. P kq + P - 1
+  // of its rows, so four lanes read 64 P contiguous bytes of a row per
+  // request; MFMA e of the item takes every lane's block P kq + e -- the same
+  // products, the same block on both sides.
+  constexpr int P = kMxSkinnyP;
+  const int npm = (nch + P - 1) / P, npr = (rch + P - 1) / P;   // main and residual items
+  const int nmain = npm > wv ? (npm - wv + kMxSkinnyWaves - 1) / kMxSkinnyWaves : 0;
+  const int nres = npr > wv ? (npr - wv + kMxSkinnyWaves - 1) / kMxSkinnyWaves : 0;
   const int total = nmain + nres;
   struct Item {
-    uint4 w, x;
-    uint32_t ew, ex;
+    uint4 w[P], x[P];
+    uint32_t ew[P], ex[P];
   };
   // Item i's loads (past the end: the last item's, never used); a block past
-  // r reads block 0 of the row and is zeroed before use.
+  // the row (K or r) reads block 0 of the row and is zeroed before use.
   auto load = [&](int i, Item& it) {
     const int ii = min(i, max(total - 1, 0));
     const bool res = ii >= nmain;
-    const int c = wv + kMxSkinnyWaves * (res ? ii - nmain : ii);
-    const int blk = 4 * c + kq;
-    const int b = res ? (blk < rblk ? blk : 0) : min(blk, Kblk - 1);
-    it.w = *reinterpret_cast<const uint4*>((res ? rrow : wrow) + 16 * b);
-    it.ew = (res ? rsc : wsc)[b];
-    it.x = *reinterpret_cast<const uint4*>(xrow + 16 * b);
-    it.ex = xsc[b];
+    const int pp = wv + kMxSkinnyWaves * (res ? ii - nmain : ii);
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int blk = 4 * P * pp + P * kq + e;
+      const int b = blk < (res ? rblk : Kblk) ? blk : 0;
+      it.w[e] = *reinterpret_cast<const uint4*>((res ? rrow : wrow) + 16 * b);
+      it.ew[e] = (res ? rsc : wsc)[b];
+      it.x[e] = *reinterpret_cast<const uint4*>(xrow + 16 * b);
+      it.ex[e] = xsc[b];
+    }
   };
   mx_v4f acc = mx_v4f{0.f, 0.f, 0.f, 0.f}, accr = mx_v4f{0.f, 0.f, 0.f, 0.f};
   auto use = [&](int i, const Item& it) {
     if (i >= total) return;
     const bool res = i >= nmain;
-    const int c = wv + kMxSkinnyWaves * (res ? i - nmain : i);
-    const bool blk_in = !res || 4 * c + kq < rblk;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint4 w = blk_in ? it.w : z;
-    const uint4 x = (blk_in && tok_in) ? it.x : z;
-    const int ew = static_cast<int>(it.ew & 0xFFu), ex = static_cast<int>(it.ex & 0xFFu);
-    if (res)
-      accr = mfma_mx16(w, x, ew, ex, accr);
-    else
-      acc = mfma_mx16(w, x, ew, ex, acc);
+    const int pp = wv + kMxSkinnyWaves * (res ? i - nmain : i);
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const bool blk_in = 4 * P * pp + P * kq + e < (res ? rblk : Kblk);
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 w = blk_in ? it.w[e] : z;
+      const uint4 x = (blk_in && tok_in) ? it.x[e] : z;
+      const int ew = static_cast<int>(it.ew[e] & 0xFFu), ex = static_cast<int>(it.ex[e] & 0xFFu);
+      if (res)
+        accr = mfma_mx16(w, x, ew, ex, accr);
+      else
+        acc = mfma_mx16(w, x, ew, ex, acc);
+    }
   };
   Item ring[kMxSkinnyRing];
 #pragma unroll
