@@ -697,7 +697,11 @@ __global__ __launch_bounds__(64 * WNW * WMW, OCC) void serq_mx_pipe_kernel(MxArg
 // ---------------------------------------------------------------------------
 
 constexpr int kMxGemvMaxTokens = 2;
-constexpr int kMxGemvUnit = 4;               // lines per unit and lane, two units in flight
+// Lines per unit and lane, two units in flight. One line per unit measured
+// fastest at one token (8B gate/up 14.5 us against 17.5 with four, 8B down
+// 8.1 against 9.8, q_proj 4.5 against 5.0; the 70B-shaped layers 24.5-25.3
+// against 26.5-26.8); eight was slower still.
+constexpr int kMxGemvUnit = 1;
 constexpr int kMxGemvMaxX = 96 * 1024;       // LDS bytes for the activation codes and exponents
 
 typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
