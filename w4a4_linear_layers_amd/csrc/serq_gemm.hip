@@ -1386,7 +1386,7 @@ __global__ __launch_bounds__(256, 1) void serq_tile256_kernel(LinearArgs a, int 
 // last in slice 0, the zero-padded Q(R) rows against the first activation
 // codes. Wave w takes items w, w + 8, ... in units of IPW, issues a unit's
 // loads, then computes it while the next unit's loads are in flight (a unit
-// is about one group's items per wave). So at
+// is two or three items). So at
 // any moment a CU's loads fall in a few tens of KB of contiguous weight rows
 // (measured faster than deeper per-wave rings spread over several groups,
 // whose scattered requests streamed at about two thirds of the rate). Every
@@ -1989,14 +1989,15 @@ template <int MG, int A_BITS>
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t st) {
   const SkinnySplit sp = plan_skinny<MG, A_BITS>(a);
   if (sp.G == 0) return hipErrorInvalidValue;   // plan_linear only picks the skinny kernel when a plan exists
-  // About one group's items per unit and wave: the CU's loads in flight then
-  // stay within one or two groups' rows.
+  // A wave's items of one group in a single unit when they are three or
+  // fewer (q_proj-sized rows: 4.95 us at 8 tokens against 5.6 in units of
+  // two), else units of two items (two units in flight): on long rows fewer
+  // loads in flight stream faster than a group's items at once (8B down at
+  // 16 tokens 9.0 against 9.8 us in units of eight; 28672 x 8192 at 8 tokens
+  // 24.6 against 30.1; 8192 x 28672 at 32 tokens 27.7 against 32.0).
   const int per = max(2, (sp.seg + (a.r > 0 ? 1 : 0) + kSkxWaves - 1) / kSkxWaves);
-  if (per <= 2) return launch_skinny_ipw<MG, A_BITS, 2>(a, sp, st);
-  if (per <= 3) return launch_skinny_ipw<MG, A_BITS, 3>(a, sp, st);
-  if (per <= 4) return launch_skinny_ipw<MG, A_BITS, 4>(a, sp, st);
-  if (per <= 6) return launch_skinny_ipw<MG, A_BITS, 6>(a, sp, st);
-  return launch_skinny_ipw<MG, A_BITS, 8>(a, sp, st);
+  if (per == 3) return launch_skinny_ipw<MG, A_BITS, 3>(a, sp, st);
+  return launch_skinny_ipw<MG, A_BITS, 2>(a, sp, st);
 }
 
 template <int MT, int KP>
